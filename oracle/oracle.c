@@ -1,0 +1,440 @@
+/*
+ * oracle.c -- plain CPU oracle for the W8A8 INT8 mixture-of-experts feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the package
+ * entry file and the cpu_baseline leg of bench.py may load or call this code.  The
+ * GPU library never links, includes or calls it, and this file includes nothing
+ * from the GPU library: the two share no headers, helpers, tables or constants.
+ *
+ * Every step is written as the plainest loop that states what the scheme
+ * computes.  There is no blocking, fusion or reordering.  The only
+ * parallelism is an OpenMP "parallel for" over independent rows (tokens or
+ * routed pairs): every row is computed by one thread in the same order as in
+ * a serial run, so the results do not depend on the thread count.
+ *
+ * Sources (web pages; each cited by its title and section):
+ *   [30B-W8A8]   "Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer:
+ *                section 1 (model profile), 2 (quantisation config), 3.1-3.3
+ *                (why mlp.gate stays bf16), 7 (FAQ).
+ *   [3.6-CFG]    "Qwen3.6-35B-A3B-w8a8 config.json and recipe.yaml" walkthrough:
+ *                the quantization_config group_0 block, its "weights" and
+ *                "input_activations" parameter lists.
+ *   [235B-FILES] "Qwen3-235B-A22B-quantized.w8a8" file-structure guide: model
+ *                overview table, shard contents, W8A8 section.
+ *   [NEXT-AMCT]  "Qwen3-Next-80B-A3B-Instruct in AMCT" adaptation case:
+ *                section 2.2 (packed gate_up_proj / down_proj), section 6
+ *                (packed MoE GMM performance note).
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *   R1  codes are clamped to [-127, 127]; -128 is never produced (symmetric).
+ *   R2  rounding of x/s to an integer is round-half-to-even (rintf in the
+ *       default rounding mode).
+ *   R3  scale s = amax / 127 is one IEEE fp32 divide, and the code is
+ *       rint(x / s) with a second IEEE fp32 divide (not x * (127 / amax)).
+ *   R4  a row whose amax is 0 gets s = 0 and all codes 0.
+ *   R5  scales are fp32.
+ *   R6  router logits: fp32, accumulated as one fused multiply-add chain over
+ *       the hidden index in ascending order, starting from +0.0f.
+ *   R7  top-k selects on the fp32 logits, larger first, equal logits ordered
+ *       by the lower expert index.
+ *   R8  the k selected softmax probabilities are renormalised to sum to 1.
+ *   R9  the expert MLP is SwiGLU: h = silu(gate) * up, silu(g) = g / (1 + e^-g).
+ *   R10 h is rounded once to bf16 (round-half-to-even) before it is quantised
+ *       for down_proj; down_proj is int8 like gate/up ([235B-FILES]).
+ *   R11 the permutation inside one expert's group is by ascending pair index
+ *       p = t * k + j.
+ *   Floating-point results that are compared within a tolerance (dequantised
+ *   GEMM outputs, SwiGLU, softmax weights, the combine) are computed here in
+ *   fp64.  Floating-point work that decides an integer (int8 codes, top-k
+ *   ids) is done in fp32, the precision the GPU takes the same decision in.
+ *
+ * Preconditions: inputs are finite.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ bf16 --- */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static float or_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a double to the nearest bf16 (8 significant bits, binary32 exponent
+ * range), ties to even, in one rounding.  Results beyond the largest finite
+ * bf16 become infinity. */
+static uint16_t or_f64_to_bf16(double v)
+{
+    int neg = signbit(v) ? 1 : 0;
+    double a = fabs(v);
+    uint16_t bits;
+    if (a == 0.0) {
+        bits = 0;
+    } else {
+        int e;
+        (void)frexp(a, &e);              /* a = m * 2^e with 0.5 <= m < 1 */
+        int quantum = e - 8;             /* weight of the last of 8 significant bits */
+        if (quantum < -133) quantum = -133; /* bf16 subnormal spacing is 2^-133 */
+        double r = ldexp(nearbyint(ldexp(a, -quantum)), quantum);
+        if (r >= ldexp(1.0, 128)) {
+            bits = 0x7f80;               /* overflow to +inf */
+        } else {
+            float f = (float)r;          /* exact: r has at most 8 significant bits */
+            uint32_t u;
+            memcpy(&u, &f, sizeof u);
+            bits = (uint16_t)(u >> 16);
+        }
+    }
+    return (uint16_t)(bits | (neg ? 0x8000 : 0));
+}
+
+uint16_t oracle_f64_to_bf16(double v) { return or_f64_to_bf16(v); }
+double oracle_bf16_to_f64(uint16_t b) { return (double)or_bf16_to_f32(b); }
+
+/* Load element i of a row given as bf16 (dtype 0) or fp32 (dtype 1). */
+static float or_load(const void *x, int dtype, int64_t i)
+{
+    if (dtype == 0) return or_bf16_to_f32(((const uint16_t *)x)[i]);
+    return ((const float *)x)[i];
+}
+
+/* ------------------------------------------------------ row quantisation --- */
+
+/*
+ * Symmetric int8 quantisation of one row (R1-R5).
+ * Static per-output-channel weight quantisation ([3.6-CFG] group_0 "weights":
+ * 8 bits, strategy channel, symmetric, minmax observer, not dynamic; [30B-W8A8]
+ * section 2) and dynamic per-token activation quantisation ([3.6-CFG] group_0
+ * "input_activations": 8 bits, strategy token, symmetric, dynamic) are the same
+ * computation on a row: a row of W is one output channel, a row of x is one token.
+ */
+static void or_quant_row(const void *x, int dtype, int64_t cols, int8_t *q, float *scale)
+{
+    float amax = 0.0f;
+    for (int64_t c = 0; c < cols; ++c) {
+        float a = fabsf(or_load(x, dtype, c));
+        if (a > amax) amax = a;
+    }
+    float s = amax / 127.0f;
+    *scale = s;
+    for (int64_t c = 0; c < cols; ++c) {
+        if (s == 0.0f) {
+            q[c] = 0;
+            continue;
+        }
+        float v = rintf(or_load(x, dtype, c) / s);
+        if (v > 127.0f) v = 127.0f;
+        if (v < -127.0f) v = -127.0f;
+        q[c] = (int8_t)v;
+    }
+}
+
+/* Quantise `rows` rows of `cols` elements, row stride ld (elements). */
+void oracle_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       int8_t *q, float *scales)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        const void *row = (dtype == 0) ? (const void *)((const uint16_t *)x + r * ld)
+                                       : (const void *)((const float *)x + r * ld);
+        or_quant_row(row, dtype, cols, q + r * cols, &scales[r]);
+    }
+}
+
+/* ---------------------------------------------------------------- router --- */
+
+/*
+ * The unquantised router ([30B-W8A8] sections 3.1-3.3; [235B-FILES] shard
+ * contents: mlp.gate stays bf16): hidden state -> one score per expert ->
+ * softmax -> the top-k experts, whose weights are renormalised (R6-R8).
+ *   x      [T][H]  bf16 (dtype 0) or fp32 (dtype 1)
+ *   wg     [E][H]  bf16 bits
+ *   ids    [T][k]  out, expert ids by descending logit
+ *   w      [T][k]  out, routing weights
+ *   logits [T][E]  out, may be NULL
+ */
+void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H,
+                       int E, int k, int renormalize, int32_t *ids, float *w, float *logits)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        float *l = (float *)malloc(sizeof(float) * (size_t)E);
+        double *p = (double *)malloc(sizeof(double) * (size_t)E);
+        unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+        const void *xrow = (dtype == 0) ? (const void *)((const uint16_t *)x + t * H)
+                                        : (const void *)((const float *)x + t * H);
+        for (int e = 0; e < E; ++e) {
+            float acc = 0.0f;
+            for (int64_t h = 0; h < H; ++h)
+                acc = fmaf(or_load(xrow, dtype, h), or_bf16_to_f32(wg[(int64_t)e * H + h]), acc);
+            l[e] = acc;
+            if (logits) logits[t * E + e] = acc;
+        }
+        /* top-k by repeated selection: strict ">" over ascending e keeps the
+         * lower index first among equal logits. */
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+            ids[t * k + j] = best;
+        }
+        /* softmax over all E scores (fp64) */
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m) m = l[e];
+        double Z = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            Z += p[e];
+        }
+        for (int e = 0; e < E; ++e) p[e] = p[e] / Z;
+        double S = 0.0;
+        for (int j = 0; j < k; ++j) S += p[ids[t * k + j]];
+        for (int j = 0; j < k; ++j) {
+            double v = p[ids[t * k + j]];
+            w[t * k + j] = (float)(renormalize ? v / S : v);
+        }
+        free(l);
+        free(p);
+        free(taken);
+    }
+}
+
+/* --------------------------------------------------------------- permute --- */
+
+/*
+ * Group the routed pairs by expert so that each expert's rows are contiguous
+ * ([NEXT-AMCT] section 6: the packed MoE GMM runs one grouped matmul over all
+ * experts).  Pair p = t*k + j goes to expert ids[p].  Within a group the
+ * pairs keep ascending p (R11).
+ *   offsets     [E+1] out, exclusive prefix of the group sizes
+ *   sorted_pair [T*k] out, pair index at each grouped row
+ *   pair_pos    [T*k] out, grouped row of each pair
+ */
+void oracle_permute(const int32_t *ids, int64_t T, int k, int E,
+                    int32_t *offsets, int32_t *sorted_pair, int32_t *pair_pos)
+{
+    int64_t P = T * k;
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e) {
+        offsets[e] = (int32_t)pos;
+        for (int64_t p = 0; p < P; ++p)
+            if (ids[p] == e) sorted_pair[pos++] = (int32_t)p;
+    }
+    offsets[E] = (int32_t)pos;
+    for (int64_t r = 0; r < P; ++r) pair_pos[sorted_pair[r]] = (int32_t)r;
+}
+
+/* ---------------------------------------------------------- int8 matmul --- */
+
+/* Exact int8 x int8 dot product with an int32 sum ([30B-W8A8] FAQ Q1: W8A8
+ * runs the matmul on integers).  |sum| <= K * 127^2 < 2^31 for K < 133144. */
+static int32_t or_dot_i8(const int8_t *a, const int8_t *b, int64_t K)
+{
+    int32_t acc = 0;
+    for (int64_t i = 0; i < K; ++i) acc += (int32_t)a[i] * (int32_t)b[i];
+    return acc;
+}
+
+static double or_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* Output casts: dtype 0 bf16 (one RNE rounding of the fp64 value), 1 fp32. */
+static void or_store(void *out, int dtype, int64_t i, double v)
+{
+    if (dtype == 0) ((uint16_t *)out)[i] = or_f64_to_bf16(v);
+    else ((float *)out)[i] = (float)v;
+}
+
+/*
+ * Grouped W8A8 GEMM.  Group g owns grouped rows [offsets[g], offsets[g+1]).
+ * Grouped row r reads activation row a = gather ? gather[r] / gather_div : r.
+ *   A        [*][K]    int8 codes, a_scales[a] its per-token scale
+ *   B        [G][N][K] int8 codes (nn.Linear [out][in]), b_scales[g][n]
+ * Epilogues (acc is the exact int32 dot product):
+ *   0 RAW_I32        out[r][n] = acc                              (int32 [M][N])
+ *   1 DEQUANT        out[r][n] = acc * a_scales[a] * b_scales[g][n] (out dtype [M][N])
+ *   2 DEQUANT_SWIGLU N = 2*Ih; gate = columns [0, Ih), up = [Ih, 2*Ih) of the
+ *                    packed gate_up_proj ([NEXT-AMCT] section 2.2);
+ *                    out[r][n] = silu(gate_n) * up_n              (out dtype [M][Ih])
+ */
+void oracle_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
+                         const int8_t *B, const float *b_scales, const int32_t *offsets, int G,
+                         int64_t N, int64_t K, int epilogue, int out_dtype, void *out)
+{
+    for (int g = 0; g < G; ++g) {
+        int64_t r;
+#pragma omp parallel for schedule(static)
+        for (r = offsets[g]; r < offsets[g + 1]; ++r) {
+            int64_t a = gather ? gather[r] / gather_div : r;
+            const int8_t *arow = A + a * K;
+            const int8_t *Bg = B + (int64_t)g * N * K;
+            const float *sg = b_scales ? b_scales + (int64_t)g * N : NULL;
+            if (epilogue == 0) {
+                for (int64_t n = 0; n < N; ++n)
+                    ((int32_t *)out)[r * N + n] = or_dot_i8(arow, Bg + n * K, K);
+            } else if (epilogue == 1) {
+                for (int64_t n = 0; n < N; ++n) {
+                    int32_t acc = or_dot_i8(arow, Bg + n * K, K);
+                    or_store(out, out_dtype, r * N + n, (double)acc * (double)a_scales[a] * (double)sg[n]);
+                }
+            } else {
+                int64_t Ih = N / 2;
+                for (int64_t n = 0; n < Ih; ++n) {
+                    int32_t ag = or_dot_i8(arow, Bg + n * K, K);
+                    int32_t au = or_dot_i8(arow, Bg + (Ih + n) * K, K);
+                    double gate = (double)ag * (double)a_scales[a] * (double)sg[n];
+                    double up = (double)au * (double)a_scales[a] * (double)sg[Ih + n];
+                    or_store(out, out_dtype, r * Ih + n, or_silu(gate) * up);
+                }
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- combine --- */
+
+/*
+ * out[t][n] = sum over the token's k slots of w[t][j] * y[pair_pos[t*k+j]][n],
+ * summed in fp64 in slot order, then cast once to the output dtype.
+ * y is given as fp64 (oracle-internal) or as bf16/fp32 (y_dtype 0/1).
+ */
+static double or_load_y(const void *y, int y_dtype, int64_t i)
+{
+    if (y_dtype == 2) return ((const double *)y)[i];
+    return (double)or_load(y, y_dtype, i);
+}
+
+void oracle_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos,
+                    int64_t T, int k, int64_t H, void *out, int out_dtype)
+{
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < H; ++n) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j)
+                acc += (double)w[t * k + j] * or_load_y(y, y_dtype, (int64_t)pair_pos[t * k + j] * H + n);
+            or_store(out, out_dtype, t * H + n, acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------ whole layer --- */
+
+/*
+ * The W8A8 MoE layer, step by step:
+ *   1 route (bf16 router, fp32 logits, softmax, top-k, renormalise)
+ *   2 quantise x per token
+ *   3 group the (token, slot) pairs by expert
+ *   4 gate_up_proj int8 GEMM -> dequantise -> SwiGLU -> h (bf16);
+ *     quantise h per row; down_proj int8 GEMM -> dequantise -> y (fp64)
+ *   5 combine y with the routing weights.
+ * Weights: wgu [E][2I][H] int8 (gate rows then up rows), sgu [E][2I];
+ *          wd [E][H][I] int8, sd [E][H]; wg [E][H] bf16.
+ * Optional outputs (any may be NULL) expose the intermediate results:
+ *   ids/w [T][k], xq [T][H] + sx [T], offsets [E+1], sorted_pair/pair_pos [T*k],
+ *   acc_gu [T*k][2I] int32, h [T*k][I] bf16, hq [T*k][I] + sh [T*k],
+ *   acc_d [T*k][H] int32.
+ * out [T][H] has the dtype of x.
+ */
+void oracle_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
+                      const uint16_t *wg, const int8_t *wgu, const float *sgu,
+                      const int8_t *wd, const float *sd, void *out,
+                      int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
+                      int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
+                      int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o)
+{
+    int64_t P = T * k;
+    int32_t *ids = ids_o ? ids_o : (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
+    float *w = w_o ? w_o : (float *)malloc(sizeof(float) * (size_t)P);
+    int8_t *xq = xq_o ? xq_o : (int8_t *)malloc((size_t)(T * H));
+    float *sx = sx_o ? sx_o : (float *)malloc(sizeof(float) * (size_t)T);
+    int32_t *offsets = offsets_o ? offsets_o : (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t *sorted = sorted_o ? sorted_o : (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
+    int32_t *pos = pos_o ? pos_o : (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
+    uint16_t *h = h_o ? h_o : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(P * I));
+    int8_t *hq = hq_o ? hq_o : (int8_t *)malloc((size_t)(P * I));
+    float *sh = sh_o ? sh_o : (float *)malloc(sizeof(float) * (size_t)P);
+    double *y = (double *)malloc(sizeof(double) * (size_t)(P * H));
+
+    /* 1 */
+    oracle_route_topk(x, dtype, wg, T, H, E, k, 1, ids, w, NULL);
+    /* 2 */
+    oracle_quant_rows(x, dtype, T, H, H, xq, sx);
+    /* 3 */
+    oracle_permute(ids, T, k, E, offsets, sorted, pos);
+    /* 4 gate_up + SwiGLU, one grouped row at a time */
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < P; ++r) {
+        int64_t p = sorted[r];
+        int64_t t = p / k;
+        int64_t e = ids[p];
+        const int8_t *arow = xq + t * H;
+        for (int64_t n = 0; n < I; ++n) {
+            int32_t ag = or_dot_i8(arow, wgu + (e * 2 * I + n) * H, H);
+            int32_t au = or_dot_i8(arow, wgu + (e * 2 * I + I + n) * H, H);
+            if (acc_gu_o) {
+                acc_gu_o[r * 2 * I + n] = ag;
+                acc_gu_o[r * 2 * I + I + n] = au;
+            }
+            double gate = (double)ag * (double)sx[t] * (double)sgu[e * 2 * I + n];
+            double up = (double)au * (double)sx[t] * (double)sgu[e * 2 * I + I + n];
+            h[r * I + n] = or_f64_to_bf16(or_silu(gate) * up);
+        }
+    }
+    /* 4 quantise h per grouped row, then down_proj */
+    oracle_quant_rows(h, 0, P, I, I, hq, sh);
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < P; ++r) {
+        int64_t e = ids[sorted[r]];
+        for (int64_t n = 0; n < H; ++n) {
+            int32_t ad = or_dot_i8(hq + r * I, wd + (e * H + n) * I, I);
+            if (acc_d_o) acc_d_o[r * H + n] = ad;
+            y[r * H + n] = (double)ad * (double)sh[r] * (double)sd[e * H + n];
+        }
+    }
+    /* 5 */
+    oracle_combine(y, 2, w, pos, T, k, H, out, dtype);
+
+    if (!ids_o) free(ids);
+    if (!w_o) free(w);
+    if (!xq_o) free(xq);
+    if (!sx_o) free(sx);
+    if (!offsets_o) free(offsets);
+    if (!sorted_o) free(sorted);
+    if (!pos_o) free(pos);
+    if (!h_o) free(h);
+    if (!hq_o) free(hq);
+    if (!sh_o) free(sh);
+    free(y);
+}
+
+/*
+ * The same layer restricted to a subset of tokens.  The layer has no term that
+ * couples tokens (each token's output depends on its own row of x only), so the
+ * rows of `out` for tokens `tok[0..n)` equal those of the full layer.  Used to
+ * check full-size runs on a sample.  out is [n][H].
+ */
+void oracle_moe_layer_tokens(const void *x, int dtype, int64_t H, int E, int k, int64_t I,
+                             const uint16_t *wg, const int8_t *wgu, const float *sgu,
+                             const int8_t *wd, const float *sd,
+                             const int64_t *tok, int64_t n, void *out)
+{
+    size_t esz = dtype == 0 ? 2 : 4;
+    unsigned char *xs = (unsigned char *)malloc(esz * (size_t)(n * H));
+    for (int64_t i = 0; i < n; ++i)
+        memcpy(xs + esz * (size_t)(i * H), (const unsigned char *)x + esz * (size_t)(tok[i] * H), esz * (size_t)H);
+    oracle_moe_layer(xs, dtype, n, H, E, k, I, wg, wgu, sgu, wd, sd, out,
+                     NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+    free(xs);
+}
