@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the W8A8 INT8 MoE layer on one MI355X.
+
+One step = one pass of the whole layer (route, quantise x, permute, gate_up
+GEMM + SwiGLU, quantise h, down GEMM, combine) over one batch of synthetic
+tokens already resident in HBM.  Weights are quantised once before timing
+(static per-channel weights) and rotated over several copies so that no step
+finds the previous step's weights in the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is tokens/s of the layer; `roofline` describes
+the dominant kernel (the stage with the largest average time, timed with HIP
+events recorded on the layer's stream inside the timed loop); `cpu_baseline`
+is the CPU oracle timed on a bounded sample of the same tokens.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5033.0       # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
+HBM_PEAK_GBS = 8000.0
+RIDGE = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+DEFAULT_WORKLOAD = "moe_30b_prefill_T4096"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_model(cfg, E_hit):
+    """Algorithmic int8 ops and HBM bytes per launch of each stage kernel."""
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    P = T * k
+    xb = 2 if cfg.x_dtype == "bf16" else 4
+    m = {}
+    m["route"] = dict(ops=0, bytes=T * H * xb + E * H * 2 + P * 8)
+    m["quant_x"] = dict(ops=0, bytes=T * H * xb + T * H + T * 4)
+    m["permute"] = dict(ops=0, bytes=P * 4 * 3 + (E + 1) * 4)
+    m["gate_up_gemm"] = dict(ops=2 * P * 2 * I * H,
+                             bytes=E_hit * 2 * I * H + E_hit * 2 * I * 4 + T * H + T * 4 + P * 4 + (E + 1) * 4
+                             + P * I * 2)
+    m["quant_h"] = dict(ops=0, bytes=P * I * 2 + P * I + P * 4)
+    m["down_gemm"] = dict(ops=2 * P * H * I, bytes=E_hit * H * I + E_hit * H * 4 + P * I + P * 4 + (E + 1) * 4
+                          + P * H * 4)
+    m["combine"] = dict(ops=0, bytes=P * H * 4 + P * 8 + T * H * xb)
+    return m
+
+
+def layer_model(cfg, E_hit):
+    """Whole-layer algorithmic work: int8 ops, and the bytes the method must
+    move: int8 weights and scales of the experts hit, the router, x in, out."""
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    xb = 2 if cfg.x_dtype == "bf16" else 4
+    ops = 2 * T * k * 3 * H * I
+    byts = E_hit * 3 * H * I + E_hit * (2 * I + H) * 4 + E * H * 2 + 2 * T * H * xb
+    return ops, byts
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters, if the record in
+    profiles/ was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "w8a8_int8_quantized_bf16_amd", "csrc", rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(case, target_s):
+    """The CPU oracle, as is, on a bounded sample of the workload's tokens."""
+    import numpy as np
+
+    import oracle
+    import synth
+    cfg = case["cfg"]
+    t0 = time.time()
+    qgu, sgu = oracle.quant_rows(case["gu"].reshape(-1, cfg.H))
+    qd, sd = oracle.quant_rows(case["dn"].reshape(-1, cfg.I))
+    wq = (case["wg"], qgu.reshape(case["gu"].shape), sgu.reshape(cfg.E, -1), qd.reshape(case["dn"].shape),
+          sd.reshape(cfg.E, -1), cfg.k)
+    log("oracle weight quantisation (untimed setup): %.1f s" % (time.time() - t0))
+    rng = np.random.default_rng(0)
+    n = min(32, cfg.T)
+    tok = np.sort(rng.choice(cfg.T, n, replace=False))
+    t0 = time.perf_counter()
+    oracle.moe_layer_tokens(case["x"], *wq, tok)
+    dt = time.perf_counter() - t0
+    n2 = int(min(cfg.T, max(n, n * target_s / max(dt, 1e-6))))
+    if n2 > n:
+        tok = np.sort(rng.choice(cfg.T, n2, replace=False))
+        t0 = time.perf_counter()
+        oracle.moe_layer_tokens(case["x"], *wq, tok)
+        dt = time.perf_counter() - t0
+        n = n2
+    del synth
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of the %d tokens of %s (the layer couples no tokens), %.1f s of CPU time; "
+                      "weights quantised by the oracle beforehand, untimed" % (n, cfg.T, cfg.name, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_int8_quantized_bf16_amd as w8
+
+    cfg = synth.MOE_CONFIGS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    x, wg, gu, dn = synth.moe_inputs(cfg)
+    log("inputs generated in %.1f s" % (time.time() - t0))
+    xd = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
+    if x.dtype == np.uint16:
+        xd = xd.view(torch.bfloat16)
+    wgd = torch.from_numpy(wg.view(np.int16)).to(dev).view(torch.bfloat16)
+    W0 = w8.MoEWeights.quantize(wgd, torch.from_numpy(gu).to(dev), torch.from_numpy(dn).to(dev), cfg.k)
+    wbytes = cfg.E * 3 * cfg.H * cfg.I
+    copies = args.copies or max(1, min(4, (1 << 30) // max(wbytes, 1) + 1))
+    Ws = [W0] + [w8.MoEWeights(*[t.clone() for t in W0.tensors], k=cfg.k) for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    ws = w8.moe_layer_workspace(W0, cfg.T, w8.BF16 if x.dtype == np.uint16 else w8.F32, dev)
+    out = torch.empty_like(xd)
+    nst = w8.LAYER_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    for row in evs:            # torch creates the HIP event on first record
+        for e in row:
+            e.record()
+
+    for i in range(args.warmup):
+        w8.moe_layer(Ws[i % copies], xd, ws=ws, out=out)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        w8.moe_layer(Ws[i % copies], xd, ws=ws, out=out, events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    stage_us = [0.0] * nst
+    for i in range(args.steps):
+        for j in range(nst):
+            stage_us[j] += evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 / args.steps
+    inter = w8.moe_layer_intermediates(W0, cfg.T, ws, w8.BF16 if x.dtype == np.uint16 else w8.F32)
+    counts = np.diff(inter["offsets"].cpu().numpy())
+    E_hit = int(np.sum(counts > 0))
+    km = kernel_model(cfg, E_hit)
+    dom = int(np.argmax(stage_us))
+    name = w8.STAGE_NAMES[dom]
+    t_dom = stage_us[dom] * 1e-6
+    ops, byts = km[name]["ops"], km[name]["bytes"]
+    mfma_bound = ops > 0 and ops / byts > RIDGE
+    if mfma_bound:
+        achieved, peak, unit = ops / t_dom / 1e12, INT8_PEAK_TOPS, "TOP/s"
+    else:
+        achieved, peak, unit = byts / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
+    ms_per_step = elapsed * 1e3 / args.steps
+    lops, lbytes = layer_model(cfg, E_hit)
+    t_step = elapsed / args.steps
+    roof_t = max(lops / (INT8_PEAK_TOPS * 1e12), lbytes / (HBM_PEAK_GBS * 1e9))
+    result = {
+        "metric": "W8A8 MoE layer tokens/s; int8 TOPS and HBM GB/s as % of MI355X roofline",
+        "value": cfg.T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k,
+                   "expert_intermediate": cfg.I, "x_dtype": cfg.x_dtype, "experts_hit": E_hit,
+                   "weight_copies_rotated": copies},
+        "roofline": {"kernel": name, "bound": "mfma" if mfma_bound else "hbm", "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": traffic_for(name, cfg.name),
+                     "avg_launch_us": stage_us[dom], "alg_bytes_per_launch": byts, "int8_ops_per_launch": ops},
+        "layer": {"int8_tops": lops / t_step / 1e12, "int8_tops_frac": lops / t_step / 1e12 / INT8_PEAK_TOPS,
+                  "alg_gbs": lbytes / t_step / 1e9, "alg_gbs_frac": lbytes / t_step / 1e9 / HBM_PEAK_GBS,
+                  "roof_time_us": roof_t * 1e6, "roofline_frac": roof_t / t_step,
+                  "stage_us": dict(zip(w8.STAGE_NAMES, [round(v, 2) for v in stage_us])),
+                  "expert_rows_min_max": [int(counts.min()), int(counts.max())]},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dict(cfg=cfg, x=x, wg=wg, gu=gu, dn=dn), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * w8a8moe.h -- C ABI of the W8A8 INT8 mixture-of-experts feed-forward layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources are web pages, cited by title and section):
+ *   1. an unquantised bf16 router scores every expert, applies softmax, keeps
+ *      the top-k experts and renormalises their weights
+ *      ("Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer, sections
+ *      3.1-3.3; "Qwen3-235B-A22B-quantized.w8a8" file guide, shard contents);
+ *   2. activations are quantised to int8 per token at run time, symmetric,
+ *      scale = max|x| / 127 ("Qwen3.6-35B-A3B-w8a8 config.json and
+ *      recipe.yaml" walkthrough, group_0 "input_activations");
+ *   3. the (token, slot) pairs are grouped by expert (the packed MoE grouped
+ *      matmul of the "Qwen3-Next-80B-A3B-Instruct in AMCT" case, section 6);
+ *   4. gate_proj / up_proj / down_proj run as int8 x int8 -> int32 grouped
+ *      GEMMs against static per-output-channel symmetric int8 weights
+ *      (group_0 "weights" of the same walkthrough), with a per-token x
+ *      per-channel dequantisation and SwiGLU;
+ *   5. the expert outputs are summed with the routing weights.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument named as device memory is a device pointer owned
+ *     by the caller; the library allocates nothing and keeps no state between
+ *     calls.  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream) and never synchronise the host.
+ *   - Matrices are row-major and contiguous unless a leading dimension is
+ *     given.  Weights use the nn.Linear [out][in] layout.
+ *   - Contraction lengths (H, I, K, cols of a quantised row) and output widths
+ *     N must be multiples of 16, and every device pointer must be 16-byte
+ *     aligned.  1 <= k <= E <= 256.  A zero row/token count is a valid no-op.
+ *   - Inputs must be finite; results for non-finite inputs are unspecified.
+ *   - Arguments are checked before anything is launched; a rejected call
+ *     returns a negative status and writes nothing.  W8A8_ERR_HIP reports a
+ *     failed launch (the HIP error is cleared).  Kernel faults surface on the
+ *     caller's next synchronisation, like any HIP kernel.
+ *   - Number formats (the one scheme supported, nothing else is accepted):
+ *     int8 codes in [-127, 127] (-128 never produced), round-half-to-even,
+ *     fp32 scales, bf16 stored as its 16-bit pattern.
+ */
+#ifndef W8A8MOE_H
+#define W8A8MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define W8A8_OK 0
+#define W8A8_ERR_INVALID_ARG (-1)        /* null pointer, bad enum, k > E, negative size */
+#define W8A8_ERR_UNSUPPORTED_SHAPE (-2)  /* contraction or width not a multiple of 16, E > 256 */
+#define W8A8_ERR_ALIGNMENT (-3)          /* a pointer or leading dimension not 16-byte aligned */
+#define W8A8_ERR_WORKSPACE_TOO_SMALL (-4)
+#define W8A8_ERR_HIP (-5)                /* a HIP launch failed */
+
+/* element types */
+#define W8A8_BF16 0
+#define W8A8_F32 1
+#define W8A8_I32 2
+
+/* grouped GEMM epilogues */
+#define W8A8_EPI_RAW_I32 0        /* out = int32 accumulator */
+#define W8A8_EPI_DEQUANT 1        /* out = acc * a_scale[row] * b_scale[group][col] */
+#define W8A8_EPI_DEQUANT_SWIGLU 2 /* N = 2*I packed gate|up; out[:, n] = silu(gate_n) * up_n */
+
+/* Text of a status code (static storage). */
+const char *w8a8_status_string(int status);
+
+/*
+ * Per-row symmetric int8 quantisation: for each row r,
+ *   scales[r] = max_c |x[r][c]| / 127   (fp32 divide; 0 for an all-zero row)
+ *   q[r][c]   = clamp(round_half_even(x[r][c] / scales[r]), -127, 127)
+ * Used for the per-token dynamic activation quantisation and, with the rows
+ * of a weight matrix, for the static per-output-channel weight quantisation
+ * (the same computation; "Qwen3.6-35B-A3B-w8a8 config.json and recipe.yaml"
+ * walkthrough, group_0 "input_activations" and "weights").
+ *   x       device, [rows][ld_x] of x_dtype (W8A8_BF16 or W8A8_F32), read
+ *   q       device, [rows][cols] int8, written
+ *   scales  device, [rows] fp32, written
+ * cols % 16 == 0, ld_x >= cols, ld_x * element size % 16 == 0.
+ */
+int w8a8_quant_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   int8_t *q, float *scales, void *stream);
+
+/*
+ * MoE router ("Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer,
+ * section 3.1: hidden state -> one score per expert -> softmax -> top-k).
+ *   logit[t][e] = fp32 fused multiply-add chain over h = 0..H-1 in ascending
+ *                 order from +0 of x[t][h] * w_gate[e][h] (bf16 operands widened
+ *                 exactly; fp32 x used as is)
+ *   topk_ids[t][0..k) = the k largest logits, larger first, equal logits by
+ *                 lower expert index
+ *   topk_w[t][j]  = softmax probability of topk_ids[t][j]; with renormalize != 0
+ *                 divided by the sum over the k selected
+ *   x         device, [T][H] x_dtype (W8A8_BF16 or W8A8_F32)
+ *   w_gate    device, [E][H] bf16 (unquantised router weight)
+ *   topk_ids  device, [T][k] int32, written
+ *   topk_w    device, [T][k] fp32, written
+ *   logits_out device, [T][E] fp32, written when not NULL
+ */
+int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, int64_t H,
+                   int E, int k, int renormalize, int32_t *topk_ids, float *topk_w,
+                   float *logits_out, void *stream);
+
+/*
+ * Group the routed pairs by expert (the packed MoE grouped matmul,
+ * "Qwen3-Next-80B-A3B-Instruct in AMCT" case, section 6).  Pair p = t*k + j is
+ * routed to expert topk_ids[p]; pairs are stably sorted by (expert, p).
+ *   offsets     device, [E+1] int32, written: offsets[e] = first grouped row of
+ *               expert e, offsets[E] = T*k
+ *   sorted_pair device, [T*k] int32, written: pair index at each grouped row
+ *   pair_pos    device, [T*k] int32, written: grouped row of each pair
+ *   ws          device scratch of at least moe_permute_workspace_size() bytes
+ * Every id must lie in [0, E) (ids out of range are not detected).
+ */
+size_t moe_permute_workspace_size(int64_t T, int k, int E);
+int moe_permute(const int32_t *topk_ids, int64_t T, int k, int E, int32_t *offsets,
+                int32_t *sorted_pair, int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Grouped W8A8 GEMM: for group g and every grouped row r in
+ * [group_offsets[g], group_offsets[g+1]), with activation row
+ * a = a_row_gather ? a_row_gather[r] / gather_div : r,
+ *   acc[r][n] = sum_k A[a][k] * B[g][n][k]     (exact int32)
+ * then the epilogue (W8A8_EPI_*):
+ *   RAW_I32        out [M_total][N] int32 = acc
+ *   DEQUANT        out [M_total][N] out_dtype = acc * a_scales[a] * b_scales[g][n]
+ *   DEQUANT_SWIGLU out [M_total][N/2] out_dtype = silu(gate) * up with
+ *                  gate = dequant(acc[r][n]), up = dequant(acc[r][N/2 + n]) (the
+ *                  packed gate_up_proj layout of the AMCT case, section 2.2)
+ *   A             device, [*][K] int8 (rows addressed by a)
+ *   a_scales      device, fp32 per activation row (unused for RAW_I32)
+ *   a_row_gather  device, [M_total] int32 or NULL
+ *   B             device, [G][N][K] int8;  b_scales device [G][N] fp32
+ *   group_offsets device, [G+1] int32, non-decreasing, group_offsets[0] = 0,
+ *                 group_offsets[G] = M_total (not checked: device memory)
+ *   ws            device scratch of at least w8a8_grouped_gemm_workspace_size() bytes
+ * out_dtype: W8A8_BF16 or W8A8_F32 (W8A8_I32 with RAW_I32).  K % 16 == 0,
+ * N % 16 == 0 (N % 32 == 0 for SWIGLU).
+ */
+size_t w8a8_grouped_gemm_workspace_size(int64_t M_total, int64_t N, int G);
+int w8a8_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *a_row_gather,
+                      int gather_div, const int8_t *B, const float *b_scales,
+                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K,
+                      int epilogue, int out_dtype, void *out, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/*
+ * Weighted combine of the expert outputs:
+ *   out[t][n] = sum_{j<k} topk_w[t][j] * y[pair_pos[t*k+j]][n]
+ * accumulated in fp32 in slot order, then rounded once to out_dtype.
+ *   y device [T*k][H] y_dtype;  topk_w device [T][k];  pair_pos device [T*k]
+ *   out device [T][H] out_dtype
+ */
+int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *pair_pos,
+                int64_t T, int k, int64_t H, void *out, int out_dtype, void *stream);
+
+/*
+ * Layer weights (caller-owned device memory):
+ *   w_gate    [E][H]    bf16 router (not quantised)
+ *   w_gate_up [E][2I][H] int8, rows 0..I-1 gate_proj, rows I..2I-1 up_proj
+ *   s_gate_up [E][2I]   fp32 per-output-channel scales
+ *   w_down    [E][H][I] int8;  s_down [E][H] fp32
+ */
+typedef struct {
+    int E, k;
+    int64_t H, I;
+    const uint16_t *w_gate;
+    const int8_t *w_gate_up;
+    const float *s_gate_up;
+    const int8_t *w_down;
+    const float *s_down;
+} w8a8_moe_weights;
+
+/*
+ * The whole layer: route -> quantise x -> permute -> gate_up GEMM + SwiGLU ->
+ * quantise h -> down GEMM -> combine, all launched on `stream`.
+ *   x   device [T][H] x_dtype (W8A8_BF16 or W8A8_F32);  out device [T][H] x_dtype
+ *   ws  device scratch of at least w8a8_moe_layer_workspace_size() bytes
+ * Returns 0 (also for T = 0) or a negative status.
+ */
+size_t w8a8_moe_layer_workspace_size(const w8a8_moe_weights *W, int64_t T, int x_dtype);
+int w8a8_moe_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, void *out,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The same layer, recording `n_events` (<= W8A8_LAYER_STAGES + 1) hipEvent_t
+ * handles on `stream`: events[0] before the first stage and events[i] after
+ * stage i, stages in the order route, quantise x, permute, gate_up GEMM,
+ * quantise h, down GEMM, combine.  Used to time the stages from the host.
+ */
+#define W8A8_LAYER_STAGES 7
+int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T,
+                          void *out, void *ws, size_t ws_bytes, void *stream,
+                          void *const *events, int n_events);
+
+/*
+ * Pointers into the layer workspace of the intermediate results of the last
+ * call with the same (W, T, x_dtype, ws): ids [T][k] i32, w [T][k] f32,
+ * xq [T][H] i8, sx [T] f32, offsets [E+1] i32, sorted_pair / pair_pos [T*k] i32,
+ * h [T*k][I] bf16, hq [T*k][I] i8, sh [T*k] f32,
+ * y [T*k][H] fp32.  Index order of `ptrs`: as listed.  For inspection
+ * and stage-by-stage checks.
+ */
+#define W8A8_LAYER_INTERMEDIATES 11
+int w8a8_moe_layer_intermediates(const w8a8_moe_weights *W, int64_t T, int x_dtype, void *ws,
+                                 void **ptrs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8MOE_H */

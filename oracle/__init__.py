@@ -53,6 +53,7 @@ def lib():
         L.oracle_combine.argtypes = [P, i32, P, P, i64, i32, i64, P, i32]
         L.oracle_moe_layer.argtypes = [P, i32, i64, i64, i32, i32, i64, P, P, P, P, P, P] + [P] * 12
         L.oracle_moe_layer_tokens.argtypes = [P, i32, i64, i32, i32, i64, P, P, P, P, P, P, i64, P]
+        L.oracle_num_threads.restype = i32
         L.oracle_f64_to_bf16.argtypes = [d]
         L.oracle_f64_to_bf16.restype = ctypes.c_uint16
         L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -77,6 +78,10 @@ def _xdtype(x):
     if x.dtype == np.float32:
         return F32
     raise TypeError("x must be bf16 bits (uint16) or float32, got %s" % x.dtype)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def f64_to_bf16(v: float) -> int:

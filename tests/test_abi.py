@@ -1,0 +1,149 @@
+"""The C ABI library: it builds for gfx950, loads, exports every function the
+header declares, and rejects invalid arguments with the documented status
+before touching the GPU.  CPU only: no call here launches a kernel."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import w8a8_int8_quantized_bf16_amd as w8
+
+OK, INVALID, SHAPE, ALIGN, WS_SMALL, HIP = 0, -1, -2, -3, -4, -5
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: every call below returns before any launch
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(w8.LIB_PATH):
+        from w8a8_int8_quantized_bf16_amd import build
+        build.build()
+    return w8.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = w8.header_functions()
+    assert len(names) == 12
+    for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
+              "w8a8_moe_layer"):
+        assert n in names
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", w8.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported
+
+
+def test_library_holds_gfx950_code(L):
+    """The device code objects embedded in the library target gfx950 only."""
+    blob = open(w8.LIB_PATH, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+    assert b"amdgcn-amd-amdhsa--gfx942" not in blob
+
+
+def test_status_strings(L):
+    for code in (OK, INVALID, SHAPE, ALIGN, WS_SMALL, HIP):
+        assert w8.status_string(code)
+    assert w8.status_string(-99) == "unknown status"
+
+
+def test_quant_act_rejects(L):
+    s = None
+    assert L.w8a8_quant_act(FAKE, 0, 4, 24, 24, FAKE, FAKE, s) == SHAPE       # cols % 16
+    assert L.w8a8_quant_act(FAKE, 0, 4, 32, 16, FAKE, FAKE, s) == INVALID     # ld < cols
+    assert L.w8a8_quant_act(FAKE, 7, 4, 32, 32, FAKE, FAKE, s) == INVALID     # dtype
+    assert L.w8a8_quant_act(None, 0, 4, 32, 32, FAKE, FAKE, s) == INVALID
+    assert L.w8a8_quant_act(MIS, 0, 4, 32, 32, FAKE, FAKE, s) == ALIGN
+    assert L.w8a8_quant_act(FAKE, 0, 4, 32, 36, FAKE, FAKE, s) == ALIGN       # 72-byte rows
+    assert L.w8a8_quant_act(FAKE, 0, -1, 32, 32, FAKE, FAKE, s) == INVALID
+    assert L.w8a8_quant_act(None, 0, 0, 32, 32, None, None, s) == OK          # empty: no-op
+
+
+def test_route_rejects(L):
+    s = None
+    assert L.moe_route_topk(FAKE, 0, FAKE, 8, 64, 8, 9, 1, FAKE, FAKE, None, s) == INVALID   # k > E
+    assert L.moe_route_topk(FAKE, 0, FAKE, 8, 64, 300, 8, 1, FAKE, FAKE, None, s) == SHAPE  # E > 256
+    assert L.moe_route_topk(FAKE, 0, FAKE, 8, 72, 8, 2, 1, FAKE, FAKE, None, s) == SHAPE    # H % 16
+    assert L.moe_route_topk(FAKE, 0, None, 8, 64, 8, 2, 1, FAKE, FAKE, None, s) == INVALID
+    assert L.moe_route_topk(FAKE, 0, FAKE, 8, 64, 8, 2, 1, MIS, FAKE, None, s) == ALIGN
+    assert L.moe_route_topk(FAKE, 2, FAKE, 8, 64, 8, 2, 1, FAKE, FAKE, None, s) == INVALID  # dtype
+    assert L.moe_route_topk(None, 0, None, 0, 64, 8, 2, 1, None, None, None, s) == OK
+
+
+def test_permute_rejects(L):
+    s = None
+    need = L.moe_permute_workspace_size(4096, 8, 128)
+    assert need >= 16 * 128 * 4
+    assert L.moe_permute(FAKE, 4096, 8, 128, FAKE, FAKE, FAKE, FAKE, need - 1, s) == WS_SMALL
+    assert L.moe_permute(FAKE, 4096, 8, 4, FAKE, FAKE, FAKE, FAKE, need, s) == INVALID       # k > E
+    assert L.moe_permute(FAKE, 16, 2, 512, FAKE, FAKE, FAKE, FAKE, need, s) == SHAPE
+    assert L.moe_permute(FAKE, 16, 2, 8, FAKE, MIS, FAKE, FAKE, need, s) == ALIGN
+    assert L.moe_permute(FAKE, 16, 2, 8, None, FAKE, FAKE, FAKE, need, s) == INVALID
+
+
+def test_grouped_gemm_rejects(L):
+    s = None
+    ws = L.w8a8_grouped_gemm_workspace_size(1024, 256, 8)
+    args = lambda **kw: [kw.get("A", FAKE), kw.get("sa", FAKE), kw.get("gat", None), kw.get("div", 1),
+                         kw.get("B", FAKE), kw.get("sb", FAKE), kw.get("off", FAKE), kw.get("G", 8),
+                         kw.get("M", 1024), kw.get("N", 256), kw.get("K", 256), kw.get("epi", 1),
+                         kw.get("od", 0), kw.get("out", FAKE), kw.get("ws", FAKE), kw.get("wsb", ws), s]
+    assert L.w8a8_grouped_gemm(*args(K=200)) == SHAPE
+    assert L.w8a8_grouped_gemm(*args(N=200)) == SHAPE
+    assert L.w8a8_grouped_gemm(*args(N=272, epi=2)) == SHAPE                  # SwiGLU needs N % 32
+    assert L.w8a8_grouped_gemm(*args(epi=3)) == INVALID
+    assert L.w8a8_grouped_gemm(*args(epi=0, od=0)) == INVALID                 # RAW needs int32 out
+    assert L.w8a8_grouped_gemm(*args(od=2)) == INVALID                        # dequant cannot be int32
+    assert L.w8a8_grouped_gemm(*args(sb=None)) == INVALID
+    assert L.w8a8_grouped_gemm(*args(gat=FAKE, div=0)) == INVALID
+    assert L.w8a8_grouped_gemm(*args(A=MIS)) == ALIGN
+    assert L.w8a8_grouped_gemm(*args(wsb=ws - 1)) == WS_SMALL
+    assert L.w8a8_grouped_gemm(*args(G=0)) == INVALID
+    assert L.w8a8_grouped_gemm(*args(M=0, A=None, out=None)) == OK
+
+
+def test_combine_rejects(L):
+    s = None
+    assert L.moe_combine(FAKE, 0, FAKE, FAKE, 16, 2, 72, FAKE, 0, s) == SHAPE
+    assert L.moe_combine(FAKE, 3, FAKE, FAKE, 16, 2, 64, FAKE, 0, s) == INVALID
+    assert L.moe_combine(FAKE, 0, FAKE, None, 16, 2, 64, FAKE, 0, s) == INVALID
+    assert L.moe_combine(FAKE, 0, FAKE, FAKE, 16, 2, 64, MIS, 0, s) == ALIGN
+    assert L.moe_combine(None, 0, None, None, 0, 2, 64, None, 0, s) == OK
+
+
+def _weights(E=8, k=2, H=64, I=32, ptr=FAKE):
+    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value)
+
+
+def test_layer_rejects_and_sizes_workspace(L):
+    s = None
+    W = _weights()
+    need = L.w8a8_moe_layer_workspace_size(ctypes.byref(W), 16, 1)
+    # ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y (fp32), permute, gemm map
+    assert need >= 32 * 4 * 4 + 16 * 64 + 32 * 32 * 3 + 32 * 64 * 4
+    assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 1, 16, FAKE, FAKE, need - 1, s) == WS_SMALL
+    assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 1, 16, FAKE, MIS, need, s) == ALIGN
+    assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 5, 16, FAKE, FAKE, need, s) == INVALID
+    assert L.w8a8_moe_layer(ctypes.byref(_weights(H=72)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
+    assert L.w8a8_moe_layer(ctypes.byref(_weights(I=40)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
+    assert L.w8a8_moe_layer(ctypes.byref(_weights(k=9)), FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
+    assert L.w8a8_moe_layer(ctypes.byref(_weights(E=257, k=2)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
+    assert L.w8a8_moe_layer(ctypes.byref(_weights(ptr=MIS)), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN
+    assert L.w8a8_moe_layer(None, FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
+    assert L.w8a8_moe_layer(ctypes.byref(W), None, 1, 0, None, None, 0, s) == OK
+    # intermediates are laid out inside the workspace, in order, without overlap
+    ptrs = (ctypes.c_void_p * 11)()
+    base = 1 << 30
+    assert L.w8a8_moe_layer_intermediates(ctypes.byref(W), 16, 1, ctypes.c_void_p(base), ptrs) == OK
+    offs = [p - base for p in ptrs]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < need
+    big = _weights(E=128, k=8, H=4096, I=1536)
+    assert L.w8a8_moe_layer_workspace_size(ctypes.byref(big), 8192, 0) > 8192 * 8 * 4096 * 4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(w8, "_lib", None)
+    monkeypatch.setattr(w8, "LIB_PATH", "/nonexistent/libw8a8moe.so")
+    with pytest.raises(ImportError):
+        w8.lib()

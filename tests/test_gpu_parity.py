@@ -1,0 +1,466 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: int8 codes and scales, router scores and expert ids, the
+permutation, int32 accumulators.  Within tolerance: dequantised outputs, routing
+weights and the layer output (max|d| / max|ref| <= 1e-2 and mean |d| <= 1e-3).
+Full-size workloads compare every token where the oracle is fast enough and a
+seeded sample of tokens otherwise (the layer couples no tokens)."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w8a8_int8_quantized_bf16_amd as w8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NORM_TOL, MAE_TOL = 1e-2, 1e-3
+
+
+# ------------------------------------------------------------------ helpers ---
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host_bf16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return dev_bf16(a)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def to_host(t):
+    if t.dtype == torch.bfloat16:
+        return host_bf16(t)
+    return t.cpu().numpy()
+
+
+def f64(a):
+    if a.dtype == np.uint16:
+        return synth.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def tol_check(got, want, what):
+    g, w = f64(got), f64(want)
+    d = np.abs(g - w)
+    norm = d.max() / max(np.abs(w).max(), 1e-30)
+    mae = d.mean()
+    say("%s: max|d|/max|ref| = %.3e, mean|d| = %.3e, max|ref| = %.3e" % (what, norm, mae, np.abs(w).max()))
+    assert norm <= NORM_TOL and mae <= MAE_TOL, what
+    return norm, mae
+
+
+def oracle_quant_w(gu, dn):
+    E, twoI, H = gu.shape
+    I = twoI // 2
+    qgu, sgu = oracle.quant_rows(gu.reshape(-1, H))
+    qd, sd = oracle.quant_rows(dn.reshape(-1, I))
+    return qgu.reshape(gu.shape), sgu.reshape(E, twoI), qd.reshape(dn.shape), sd.reshape(E, H)
+
+
+class Case:
+    """One MoE workload: inputs, the oracle's weights and the GPU's weights."""
+
+    def __init__(self, cfg):
+        t0 = time.time()
+        self.cfg = cfg
+        self.x, self.wg, gu, dn = synth.moe_inputs(cfg)
+        self.o_qgu, self.o_sgu, self.o_qd, self.o_sd = oracle_quant_w(gu, dn)
+        gu_d, dn_d = to_dev(gu), to_dev(dn)
+        del gu, dn
+        self.W = w8.MoEWeights.quantize(dev_bf16(self.wg), gu_d, dn_d, cfg.k)
+        del gu_d, dn_d
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        self.xd = to_dev(self.x)
+        say("case %s ready in %.1f s" % (cfg.name, time.time() - t0))
+
+    def oracle_args(self):
+        return (self.wg, self.o_qgu, self.o_sgu, self.o_qd, self.o_sd, self.cfg.k)
+
+    def check_weights_bit_exact(self):
+        assert np.array_equal(to_host(self.W.w_gate_up), self.o_qgu)
+        assert np.array_equal(to_host(self.W.s_gate_up), self.o_sgu)
+        assert np.array_equal(to_host(self.W.w_down), self.o_qd)
+        assert np.array_equal(to_host(self.W.s_down), self.o_sd)
+
+    def run_layer(self):
+        T = self.cfg.T
+        dt = w8.BF16 if self.x.dtype == np.uint16 else w8.F32
+        ws = w8.moe_layer_workspace(self.W, T, dt)
+        out = w8.moe_layer(self.W, self.xd, ws=ws)
+        torch.cuda.synchronize()
+        return out, w8.moe_layer_intermediates(self.W, T, ws, dt), ws
+
+
+_cases = {}
+
+
+def get_case(name):
+    if name not in _cases:
+        for k in list(_cases):
+            if k != name:
+                del _cases[k]
+        torch.cuda.empty_cache()
+        _cases[name] = Case(synth.MOE_CONFIGS[name])
+    return _cases[name]
+
+
+# ---------------------------------------------------------- quantisation ---
+
+@pytest.mark.parametrize("rows,cols,dtype,scale", [
+    (1, 16, "bf16", 1.0), (5, 48, "f32", 3.0), (37, 1040, "bf16", 0.01), (16, 64, "f32", 1.0),
+    (300, 2048, "bf16", 5.0), (3, 4096, "f32", 1e-3), (64, 768, "bf16", 100.0)])
+def test_quant_act_bit_exact(rows, cols, dtype, scale):
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = (rng.standard_t(4, (rows, cols)) * scale).astype(np.float32)
+    x[rows // 2] = 0.0                                   # an all-zero row
+    if rows > 2:
+        x[1, : cols // 2] = -x[1, : cols // 2]
+        x[2] = np.round(x[2] * 4) / 4                    # many exact halves
+    xa = synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    q, s = w8.quant_act(to_dev(xa))
+    oq, os_ = oracle.quant_rows(xa)
+    assert np.array_equal(to_host(q), oq)
+    assert np.array_equal(to_host(s), os_)
+    assert np.all(to_host(s)[rows // 2] == 0)
+
+
+def test_quant_act_leading_dimension():
+    """A view with a row stride larger than the row (ld_x > cols)."""
+    rng = np.random.default_rng(1)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((40, 96)).astype(np.float32))
+    xd = to_dev(x)
+    L = w8.lib()
+    q = torch.empty((40, 64), dtype=torch.int8, device=DEV)
+    s = torch.empty(40, dtype=torch.float32, device=DEV)
+    rc = L.w8a8_quant_act(w8._p(xd), w8.BF16, 40, 64, 96, w8._p(q), w8._p(s), w8._stream())
+    assert rc == 0
+    oq, os_ = oracle.quant_rows(np.ascontiguousarray(x[:, :64]))
+    assert np.array_equal(to_host(q), oq) and np.array_equal(to_host(s), os_)
+
+
+# ---------------------------------------------------------------- router ---
+
+@pytest.mark.parametrize("k,renorm", [(2, True), (1, True), (8, True), (3, False), (8, False)])
+def test_route_tiny(k, renorm):
+    cfg = synth.MOE_CONFIGS["moe_tiny_T16_H64_E8_k2_I32"]
+    x, wg = synth.moe_x(cfg), synth.moe_router(cfg)
+    ids, w, logits = w8.route_topk(to_dev(x), dev_bf16(wg), k, renorm, return_logits=True)
+    oids, ow, ologits = oracle.route_topk(x, wg, k, renorm)
+    assert np.array_equal(to_host(logits), ologits)
+    assert np.array_equal(to_host(ids), oids)
+    assert np.abs(to_host(w) - ow).max() <= 2e-6
+
+
+def test_route_ties_lower_index_first():
+    cfg = synth.MOE_CONFIGS["moe_tiny_T16_H64_E8_k2_I32"]
+    x, wg = synth.moe_x(cfg), synth.moe_router(cfg).copy()
+    wg[6] = wg[2]
+    wg[7] = wg[2]
+    for xx in (x, synth.f32_to_bf16_bits(x)):
+        ids, w, logits = w8.route_topk(to_dev(xx), dev_bf16(wg), 4, True, return_logits=True)
+        oids, ow, ologits = oracle.route_topk(xx, wg, 4)
+        lg = to_host(logits)
+        assert np.array_equal(lg[:, 2], lg[:, 6]) and np.array_equal(lg[:, 2], lg[:, 7])
+        assert np.array_equal(to_host(ids), oids)
+    # an all-equal router: every token selects 0..k-1 in order with equal weights
+    flat = np.zeros_like(wg)
+    ids, w = w8.route_topk(to_dev(x), dev_bf16(flat), 3)
+    assert np.all(to_host(ids) == np.array([0, 1, 2]))
+    assert np.allclose(to_host(w), 1.0 / 3.0, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_30b_decode_T64"])
+def test_route_full_size(name):
+    cfg = synth.MOE_CONFIGS[name]
+    wg = synth.moe_router(cfg)
+    x = synth.moe_x(cfg, wg_bits=wg)
+    ids, w, logits = w8.route_topk(to_dev(x), dev_bf16(wg), cfg.k, True, return_logits=True)
+    t0 = time.time()
+    oids, ow, ologits = oracle.route_topk(x, wg, cfg.k)
+    say("oracle router %s: %.1f s" % (name, time.time() - t0))
+    assert np.array_equal(to_host(logits), ologits)
+    assert np.array_equal(to_host(ids), oids)
+    assert np.abs(to_host(w) - ow).max() <= 2e-6
+
+
+# --------------------------------------------------------------- permute ---
+
+@pytest.mark.parametrize("T,k,E,mode", [
+    (1, 1, 1, "rand"), (16, 2, 8, "rand"), (37, 8, 128, "rand"), (4096, 8, 128, "rand"),
+    (8192, 8, 128, "zipf"), (300, 4, 256, "rand"), (1000, 2, 8, "one"), (2049, 1, 3, "rand"),
+    (513, 8, 16, "rand")])
+def test_permute_bit_exact(T, k, E, mode):
+    rng = np.random.default_rng(T + k + E)
+    if mode == "one":
+        ids = np.zeros((T, k), np.int32)
+        ids[:, 1] = 5
+    elif mode == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    else:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    off, sp, pos = w8.permute(to_dev(ids), E)
+    ooff, osp, opos = oracle.permute(ids, E)
+    assert np.array_equal(to_host(off), ooff)
+    assert np.array_equal(to_host(sp), osp)
+    assert np.array_equal(to_host(pos), opos)
+
+
+# ---------------------------------------------------------- grouped GEMM ---
+
+def _groups(rng, sizes):
+    off = np.zeros(len(sizes) + 1, np.int32)
+    off[1:] = np.cumsum(sizes)
+    return off
+
+
+@pytest.mark.parametrize("sizes,N,K,gather", [
+    ([5, 0, 33, 1, 64], 48, 144, 0),          # ragged, an empty group, K tail
+    ([3] * 40, 256, 2048, 2),                 # decode-like: tiny groups
+    ([60, 70, 0, 45], 272, 1040, 0),          # N tail, mid-size groups
+    ([300, 129, 1000], 512, 384, 8),          # large groups
+    ([17], 16, 16, 0),                        # minimum sizes
+])
+def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather):
+    rng = np.random.default_rng(sum(sizes) + N + K)
+    G, M = len(sizes), int(sum(sizes))
+    off = _groups(rng, sizes)
+    B = rng.integers(-127, 128, (G, N, K), dtype=np.int8)
+    if gather:
+        nA = max(M // gather + 1, 1)
+        A = rng.integers(-127, 128, (nA, K), dtype=np.int8)
+        gat = rng.integers(0, nA * gather, M).astype(np.int32)
+    else:
+        A = rng.integers(-127, 128, (M, K), dtype=np.int8)
+        gat = None
+    A[0, :] = 127                              # extremes
+    B[0, 0, :] = -127
+    out = w8.grouped_gemm(to_dev(A), None, None if gat is None else to_dev(gat), max(gather, 1), to_dev(B), None,
+                          to_dev(off), w8.EPI_RAW_I32, M_total=M)
+    got = to_host(out)
+    want = oracle.grouped_gemm(A, None, gat, max(gather, 1), B, None, off, oracle.RAW_I32)
+    assert np.array_equal(got, want)
+    # independent exact check of one group
+    g = int(np.argmax(sizes))
+    rows = np.arange(off[g], off[g + 1])
+    arow = gat[rows] // gather if gat is not None else rows
+    assert np.array_equal(got[rows].astype(np.float64), A[arow].astype(np.float64) @ B[g].astype(np.float64).T)
+
+
+@pytest.mark.parametrize("epi,od", [(w8.EPI_DEQUANT, w8.BF16), (w8.EPI_DEQUANT, w8.F32),
+                                    (w8.EPI_DEQUANT_SWIGLU, w8.BF16), (w8.EPI_DEQUANT_SWIGLU, w8.F32)])
+@pytest.mark.parametrize("sizes", [[7, 0, 90, 33], [200, 300]])
+def test_grouped_gemm_dequant_epilogues(epi, od, sizes):
+    rng = np.random.default_rng(len(sizes) + epi * 10 + od)
+    G, M, N, K = len(sizes), sum(sizes), 320, 528
+    off = _groups(rng, sizes)
+    x = rng.standard_t(4, (M, K)).astype(np.float32)
+    Wf = (rng.standard_normal((G * N, K)) * 0.02).astype(np.float32)
+    qa, sa = oracle.quant_rows(x)
+    qb, sb = oracle.quant_rows(Wf)
+    qb, sb = qb.reshape(G, N, K), sb.reshape(G, N)
+    out = w8.grouped_gemm(to_dev(qa), to_dev(sa), None, 1, to_dev(qb), to_dev(sb), to_dev(off), epi, od)
+    want = oracle.grouped_gemm(qa, sa, None, 1, qb, sb, off, epi, od)
+    got = to_host(out)
+    g64, w64 = f64(got), f64(want)
+    # fp32 epilogue vs fp64 reference: a few fp32 ulps, plus one output rounding
+    rel = 2.0 ** -7 if od == w8.BF16 else 1e-5
+    assert np.all(np.abs(g64 - w64) <= rel * np.abs(w64) + 1e-6 * np.abs(w64).max())
+
+
+# --------------------------------------------------------------- combine ---
+
+@pytest.mark.parametrize("T,k,H,yd", [(16, 2, 64, "f32"), (64, 8, 2048, "bf16"), (3, 1, 16, "bf16"),
+                                      (100, 8, 4096, "bf16")])
+def test_combine(T, k, H, yd):
+    rng = np.random.default_rng(T * k + H)
+    y = rng.standard_normal((T * k, H)).astype(np.float32)
+    ya = synth.f32_to_bf16_bits(y) if yd == "bf16" else y
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    pos = rng.permutation(T * k).astype(np.int32)
+    od = w8.BF16 if yd == "bf16" else w8.F32
+    out = to_host(w8.combine(to_dev(ya), to_dev(w), to_dev(pos), od))
+    want = oracle.combine(ya, w, pos, od)
+    g64, w64 = f64(out), f64(want)
+    rel = 2.0 ** -7 if od == w8.BF16 else 1e-6     # one bf16 ulp: fp32 vs fp64 sum can round apart
+    assert np.all(np.abs(g64 - w64) <= rel * np.abs(w64) + 1e-6)
+
+
+# ----------------------------------------------------------- whole layer ---
+
+def _check_stages(case, inter, tokens=None):
+    """Bit-exact stage checks of a layer run against the oracle."""
+    cfg = case.cfg
+    x = case.x
+    oids, ow, _ = oracle.route_topk(x if tokens is None else x[tokens], case.wg, cfg.k)
+    ids = to_host(inter["ids"])
+    w = to_host(inter["w"])
+    if tokens is not None:
+        ids, w = ids[tokens], w[tokens]
+    assert np.array_equal(ids, oids)
+    assert np.abs(w - ow).max() <= 2e-6
+    oxq, osx = oracle.quant_rows(x if tokens is None else x[tokens])
+    xq, sx = to_host(inter["xq"]), to_host(inter["sx"])
+    if tokens is not None:
+        xq, sx = xq[tokens], sx[tokens]
+    assert np.array_equal(xq, oxq) and np.array_equal(sx, osx)
+    if tokens is None:
+        off, sp, pos = oracle.permute(oids, cfg.E)
+        assert np.array_equal(to_host(inter["offsets"]), off)
+        assert np.array_equal(to_host(inter["sorted_pair"]), sp)
+        assert np.array_equal(to_host(inter["pair_pos"]), pos)
+
+
+def _check_gate_up_int32(case, inter, n_rows=48):
+    """int32 gate/up accumulators of sampled grouped rows, bit-exact (exact
+    float64 products of the codes), recomputed through the RAW_I32 epilogue on
+    the layer's own permutation."""
+    cfg = case.cfg
+    P = cfg.T * cfg.k
+    acc = w8.grouped_gemm(inter["xq"], None, inter["sorted_pair"], cfg.k, case.W.w_gate_up, None, inter["offsets"],
+                          w8.EPI_RAW_I32, M_total=P)
+    rows = np.random.default_rng(7).choice(P, min(n_rows, P), replace=False)
+    acc_h = to_host(acc[torch.from_numpy(rows).to(DEV)])
+    sp = to_host(inter["sorted_pair"])
+    off = to_host(inter["offsets"])
+    xq = to_host(inter["xq"])
+    for i, r in enumerate(rows):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        t = sp[r] // cfg.k
+        want = case.o_qgu[e].astype(np.float64) @ xq[t].astype(np.float64)
+        assert np.array_equal(acc_h[i].astype(np.float64), want)
+    # down accumulators on the GPU's own h codes
+    accd = w8.grouped_gemm(inter["hq"], None, None, 1, case.W.w_down, None, inter["offsets"], w8.EPI_RAW_I32,
+                           M_total=P)
+    accd_h = to_host(accd[torch.from_numpy(rows).to(DEV)])
+    hq = to_host(inter["hq"])
+    for i, r in enumerate(rows):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        want = case.o_qd[e].astype(np.float64) @ hq[r].astype(np.float64)
+        assert np.array_equal(accd_h[i].astype(np.float64), want)
+    # h quantisation of the GPU's own h is bit-exact
+    h = to_host(inter["h"])[rows]
+    oq, os_ = oracle.quant_rows(h)
+    assert np.array_equal(hq[rows], oq) and np.array_equal(to_host(inter["sh"])[rows], os_)
+
+
+def test_layer_tiny_full():
+    case = get_case("moe_tiny_T16_H64_E8_k2_I32")
+    case.check_weights_bit_exact()
+    out, inter, _ = case.run_layer()
+    _check_stages(case, inter)
+    _check_gate_up_int32(case, inter, 32)
+    want, oi = oracle.moe_layer(case.x, *case.oracle_args(), intermediates=True)
+    mism = int(np.sum(to_host(inter["hq"]) != oi["hq"]))
+    say("tiny: h-code mismatches %d of %d" % (mism, oi["hq"].size))
+    tol_check(to_host(out), want, "tiny layer")
+
+
+def test_layer_30b_decode_full():
+    case = get_case("moe_30b_decode_T64")
+    case.check_weights_bit_exact()
+    out, inter, _ = case.run_layer()
+    _check_stages(case, inter)
+    _check_gate_up_int32(case, inter)
+    t0 = time.time()
+    want, oi = oracle.moe_layer(case.x, *case.oracle_args(), intermediates=True)
+    say("oracle decode layer: %.1f s" % (time.time() - t0))
+    hit = int(np.sum(np.diff(oi["offsets"]) > 0))
+    say("decode: %d of %d experts hit; h-code mismatches %d of %d" %
+        (hit, case.cfg.E, int(np.sum(to_host(inter["hq"]) != oi["hq"])), oi["hq"].size))
+    tol_check(to_host(out), want, "30b decode layer")
+
+
+def _sampled_layer(name, n_tok=48):
+    case = get_case(name)
+    if name == "moe_30b_prefill_T4096":
+        case.check_weights_bit_exact()
+    out, inter, _ = case.run_layer()
+    tokens = np.sort(np.random.default_rng(3).choice(case.cfg.T, n_tok, replace=False))
+    _check_stages(case, inter, tokens)
+    _check_gate_up_int32(case, inter)
+    t0 = time.time()
+    want = oracle.moe_layer_tokens(case.x, *case.oracle_args(), tokens)
+    say("oracle %s on %d tokens: %.1f s" % (name, n_tok, time.time() - t0))
+    tol_check(to_host(out)[tokens], want, name + " (sampled tokens)")
+    counts = np.diff(to_host(inter["offsets"]))
+    say("%s expert loads: min %d max %d mean %.1f cv %.2f" % (name, counts.min(), counts.max(), counts.mean(),
+                                                             counts.std() / counts.mean()))
+    return case, out, inter
+
+
+def test_layer_30b_prefill_sampled():
+    _sampled_layer("moe_30b_prefill_T4096")
+
+
+def test_layer_determinism_and_token_shuffle():
+    case = get_case("moe_30b_prefill_T4096")
+    out1, _, _ = case.run_layer()
+    out2, _, _ = case.run_layer()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(case.cfg.T)).to(DEV)
+    ws = w8.moe_layer_workspace(case.W, case.cfg.T)
+    out_p = w8.moe_layer(case.W, case.xd[perm].contiguous(), ws=ws)
+    assert torch.equal(out_p.view(torch.int16), out1[perm].view(torch.int16))
+    # a prefix of the tokens reproduces its rows
+    out_s = w8.moe_layer(case.W, case.xd[:37].contiguous())
+    assert torch.equal(out_s.view(torch.int16), out1[:37].view(torch.int16))
+
+
+def test_layer_edge_cases():
+    case = get_case("moe_30b_prefill_T4096")
+    out1, _, _ = case.run_layer()
+    # one token
+    o = w8.moe_layer(case.W, case.xd[5:6].contiguous())
+    assert torch.equal(o.view(torch.int16), out1[5:6].view(torch.int16))
+    # zero tokens: no-op
+    empty = torch.empty((0, case.cfg.H), dtype=torch.bfloat16, device=DEV)
+    assert w8.moe_layer(case.W, empty).shape == (0, case.cfg.H)
+    # k = 1 and k = E on a tiny layer
+    tiny = get_case("moe_tiny_T16_H64_E8_k2_I32")
+    for k in (1, tiny.cfg.E):
+        W = w8.MoEWeights(*tiny.W.tensors, k=k)
+        out = w8.moe_layer(W, tiny.xd)
+        want = oracle.moe_layer(tiny.x, tiny.wg, tiny.o_qgu, tiny.o_sgu, tiny.o_qd, tiny.o_sd, k)
+        tol_check(to_host(out), want, "tiny layer k=%d" % k)
+
+
+def test_layer_235b_zipf_sampled():
+    case, out, inter = _sampled_layer("moe_235b_zipf_T8192", 32)
+    counts = np.diff(to_host(inter["offsets"]))
+    assert counts.max() > 5 * counts.mean()      # the Zipf skew is there
+
+
+def test_dense_linear_sampled():
+    cfg = synth.DENSE_CONFIGS["dense_M4096_K2048_N4096"]
+    xb, Wf = synth.dense_inputs(cfg)
+    qx, sx = w8.quant_act(to_dev(xb))
+    qw, sw = w8.quant_act(to_dev(Wf))
+    oqx, osx = oracle.quant_rows(xb)
+    oqw, osw = oracle.quant_rows(Wf)
+    assert np.array_equal(to_host(qx), oqx) and np.array_equal(to_host(sx), osx)
+    assert np.array_equal(to_host(qw), oqw) and np.array_equal(to_host(sw), osw)
+    off = to_dev(np.array([0, cfg.M], np.int32))
+    out = w8.grouped_gemm(qx, sx, None, 1, qw.view(1, cfg.N, cfg.K), sw.view(1, cfg.N), off, w8.EPI_DEQUANT, w8.BF16)
+    rows = np.sort(np.random.default_rng(2).choice(cfg.M, 96, replace=False))
+    want = oracle.grouped_gemm(oqx[rows], osx[rows], None, 1, oqw[None], osw[None],
+                               np.array([0, len(rows)], np.int32), oracle.DEQUANT, oracle.BF16)
+    tol_check(to_host(out)[rows], want, "dense W8A8 linear (sampled rows)")
+    acc = w8.grouped_gemm(qx, None, None, 1, qw.view(1, cfg.N, cfg.K), None, off, w8.EPI_RAW_I32)
+    r = rows[:8]
+    assert np.array_equal(to_host(acc)[r].astype(np.float64), oqx[r].astype(np.float64) @ oqw.astype(np.float64).T)

@@ -1,0 +1,280 @@
+"""W8A8 INT8 mixture-of-experts feed-forward layer for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libw8a8moe.so`` (declared in
+``include/w8a8moe.h``).  This module only marshals arguments: it checks dtype,
+device and contiguity, allocates outputs with torch, and passes raw device
+pointers plus the current HIP stream.  Every computation runs in the HIP
+kernels of the library; there is no CPU or PyTorch fallback, and every call
+raises if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw8a8moe.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "w8a8moe.h")
+
+BF16, F32, I32 = 0, 1, 2
+EPI_RAW_I32, EPI_DEQUANT, EPI_DEQUANT_SWIGLU = 0, 1, 2
+LAYER_STAGES = 7
+STAGE_NAMES = ("route", "quant_x", "permute", "gate_up_gemm", "quant_h", "down_gemm", "combine")
+INTERMEDIATES = ("ids", "w", "xq", "sx", "offsets", "sorted_pair", "pair_pos", "h", "hq", "sh", "y")
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int), ("k", ctypes.c_int), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("w_gate", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libw8a8moe.so (built by ``w8a8_int8_quantized_bf16_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libw8a8moe.so is not built (run w8a8_int8_quantized_bf16_amd.build.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.w8a8_status_string.argtypes = [i32]
+    L.w8a8_status_string.restype = ctypes.c_char_p
+    L.w8a8_quant_act.argtypes = [P, i32, i64, i64, i64, P, P, P]
+    L.moe_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, P]
+    L.moe_permute_workspace_size.argtypes = [i64, i32, i32]
+    L.moe_permute_workspace_size.restype = sz
+    L.moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P, sz, P]
+    L.w8a8_grouped_gemm_workspace_size.argtypes = [i64, i64, i32]
+    L.w8a8_grouped_gemm_workspace_size.restype = sz
+    L.w8a8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
+    L.moe_combine.argtypes = [P, i32, P, P, i64, i32, i64, P, i32, P]
+    WP = ctypes.POINTER(_Weights)
+    L.w8a8_moe_layer_workspace_size.argtypes = [WP, i64, i32]
+    L.w8a8_moe_layer_workspace_size.restype = sz
+    L.w8a8_moe_layer.argtypes = [WP, P, i32, i64, P, P, sz, P]
+    L.w8a8_moe_layer_events.argtypes = [WP, P, i32, i64, P, P, sz, P, ctypes.POINTER(P), i32]
+    L.w8a8_moe_layer_intermediates.argtypes = [WP, i64, i32, P, ctypes.POINTER(P)]
+    for name in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
+                 "w8a8_moe_layer", "w8a8_moe_layer_events", "w8a8_moe_layer_intermediates"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def header_functions():
+    """Names of the functions declared in include/w8a8moe.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_\w+|moe_\w+)\s*\(", text)))
+
+
+def status_string(status):
+    return lib().w8a8_status_string(int(status)).decode()
+
+
+def _check(rc, where):
+    if rc != 0:
+        raise W8A8Error(rc, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _act_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("expected bfloat16 or float32, got %s" % t.dtype)
+
+
+def _torch_dtype(code):
+    return {BF16: torch.bfloat16, F32: torch.float32, I32: torch.int32}[code]
+
+
+def _need(t, name, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if dim is not None and t.dim() != dim:
+        raise ValueError("%s must have %d dims" % (name, dim))
+
+
+# ------------------------------------------------------------------ stages ---
+
+def quant_act(x):
+    """Per-row symmetric int8 quantisation: returns (codes int8 [rows, cols], scales fp32 [rows])."""
+    _need(x, "x", dim=2)
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(lib().w8a8_quant_act(_p(x), _act_dtype(x), rows, cols, cols, _p(q), _p(s), _stream(x.device)),
+           "w8a8_quant_act")
+    return q, s
+
+
+def route_topk(x, w_gate, k, renormalize=True, return_logits=False):
+    """Router: (ids int32 [T,k], weights fp32 [T,k][, logits fp32 [T,E]])."""
+    _need(x, "x", dim=2)
+    _need(w_gate, "w_gate", torch.bfloat16, 2)
+    T, H = x.shape
+    E = w_gate.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
+    _check(lib().moe_route_topk(_p(x), _act_dtype(x), _p(w_gate), T, H, E, k, int(bool(renormalize)), _p(ids),
+                                _p(w), _p(logits), _stream(x.device)), "moe_route_topk")
+    return (ids, w, logits) if return_logits else (ids, w)
+
+
+def permute(ids, E):
+    """Stable grouping of pairs by expert: (offsets [E+1], sorted_pair [P], pair_pos [P]) int32."""
+    _need(ids, "ids", torch.int32, 2)
+    T, k = ids.shape
+    dev = ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    nws = max(int(lib().moe_permute_workspace_size(T, k, E)), 256)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(lib().moe_permute(_p(ids), T, k, E, _p(offsets), _p(sp), _p(pos), _p(ws), nws, _stream(dev)),
+           "moe_permute")
+    return offsets, sp, pos
+
+
+def grouped_gemm(A, a_scales, gather, gather_div, B, b_scales, offsets, epilogue, out_dtype=BF16, M_total=None):
+    """Grouped W8A8 GEMM (see include/w8a8moe.h).  B is [G, N, K] int8."""
+    _need(A, "A", torch.int8, 2)
+    _need(B, "B", torch.int8, 3)
+    _need(offsets, "offsets", torch.int32, 1)
+    G, N, K = B.shape
+    if M_total is None:
+        M_total = gather.shape[0] if gather is not None else A.shape[0]
+    if epilogue == EPI_RAW_I32:
+        out_dtype = I32
+        out = torch.empty((M_total, N), dtype=torch.int32, device=A.device)
+    else:
+        ncol = N if epilogue == EPI_DEQUANT else N // 2
+        out = torch.empty((M_total, ncol), dtype=_torch_dtype(out_dtype), device=A.device)
+    nws = int(lib().w8a8_grouped_gemm_workspace_size(M_total, N, G))
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=A.device)
+    _check(lib().w8a8_grouped_gemm(_p(A), _p(a_scales), _p(gather), int(gather_div), _p(B), _p(b_scales),
+                                   _p(offsets), G, M_total, N, K, epilogue, out_dtype, _p(out), _p(ws), ws.numel(),
+                                   _stream(A.device)), "w8a8_grouped_gemm")
+    return out
+
+
+def combine(y, w, pair_pos, out_dtype=None):
+    """out[t] = sum_j w[t,j] * y[pair_pos[t*k+j]]."""
+    _need(y, "y", dim=2)
+    _need(w, "w", torch.float32, 2)
+    _need(pair_pos, "pair_pos", torch.int32, 1)
+    T, k = w.shape
+    H = y.shape[1]
+    od = _act_dtype(y) if out_dtype is None else out_dtype
+    out = torch.empty((T, H), dtype=_torch_dtype(od), device=y.device)
+    _check(lib().moe_combine(_p(y), _act_dtype(y), _p(w), _p(pair_pos), T, k, H, _p(out), od, _stream(y.device)),
+           "moe_combine")
+    return out
+
+
+# ------------------------------------------------------------------- layer ---
+
+class MoEWeights:
+    """Device tensors of one layer in the library's layout.
+    w_gate [E,H] bf16; w_gate_up [E,2I,H] int8 (gate rows, then up rows);
+    s_gate_up [E,2I] fp32; w_down [E,H,I] int8; s_down [E,H] fp32."""
+
+    def __init__(self, w_gate, w_gate_up, s_gate_up, w_down, s_down, k):
+        _need(w_gate, "w_gate", torch.bfloat16, 2)
+        _need(w_gate_up, "w_gate_up", torch.int8, 3)
+        _need(s_gate_up, "s_gate_up", torch.float32, 2)
+        _need(w_down, "w_down", torch.int8, 3)
+        _need(s_down, "s_down", torch.float32, 2)
+        E, twoI, H = w_gate_up.shape
+        self.E, self.H, self.I, self.k = E, H, twoI // 2, int(k)
+        self.tensors = (w_gate, w_gate_up, s_gate_up, w_down, s_down)
+        self.w_gate, self.w_gate_up, self.s_gate_up, self.w_down, self.s_down = self.tensors
+        self.c = _Weights(E, self.k, H, self.I, *[t.data_ptr() for t in self.tensors])
+
+    @classmethod
+    def quantize(cls, w_gate, gate_up_f32, down_f32, k):
+        """Static per-output-channel int8 quantisation of fp32 expert weights on
+        the GPU (the same row quantisation kernel as the activations)."""
+        E, twoI, H = gate_up_f32.shape
+        qgu, sgu = quant_act(gate_up_f32.reshape(E * twoI, H))
+        qd, sd = quant_act(down_f32.reshape(E * H, twoI // 2))
+        return cls(w_gate, qgu.view(E, twoI, H), sgu.view(E, twoI), qd.view(E, H, twoI // 2), sd.view(E, H), k)
+
+
+def moe_layer_workspace_size(W: MoEWeights, T, x_dtype=BF16):
+    return int(lib().w8a8_moe_layer_workspace_size(ctypes.byref(W.c), T, x_dtype))
+
+
+def moe_layer_workspace(W: MoEWeights, T, x_dtype=BF16, device="cuda"):
+    return torch.empty(max(moe_layer_workspace_size(W, T, x_dtype), 256), dtype=torch.uint8, device=device)
+
+
+def moe_layer(W: MoEWeights, x, ws=None, out=None, events=None):
+    """The W8A8 MoE layer: out [T,H] in the dtype of x."""
+    _need(x, "x", dim=2)
+    T, H = x.shape
+    dt = _act_dtype(x)
+    if ws is None:
+        ws = moe_layer_workspace(W, T, dt, x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    if events is None:
+        rc = lib().w8a8_moe_layer(ctypes.byref(W.c), _p(x), dt, T, _p(out), _p(ws), ws.numel(), _stream(x.device))
+    else:
+        if any(e.cuda_event == 0 for e in events):
+            raise ValueError("events must have been recorded once (torch creates the HIP event lazily)")
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        rc = lib().w8a8_moe_layer_events(ctypes.byref(W.c), _p(x), dt, T, _p(out), _p(ws), ws.numel(),
+                                         _stream(x.device), arr, len(events))
+    _check(rc, "w8a8_moe_layer")
+    return out
+
+
+def moe_layer_intermediates(W: MoEWeights, T, ws, x_dtype=BF16):
+    """Views into `ws` of the intermediate results of the last layer call."""
+    ptrs = (ctypes.c_void_p * len(INTERMEDIATES))()
+    _check(lib().w8a8_moe_layer_intermediates(ctypes.byref(W.c), T, x_dtype, _p(ws), ptrs),
+           "w8a8_moe_layer_intermediates")
+    P, E, H, I = T * W.k, W.E, W.H, W.I
+    spec = dict(ids=((T, W.k), torch.int32), w=((T, W.k), torch.float32), xq=((T, H), torch.int8),
+                sx=((T,), torch.float32), offsets=((E + 1,), torch.int32), sorted_pair=((P,), torch.int32),
+                pair_pos=((P,), torch.int32), h=((P, I), torch.bfloat16), hq=((P, I), torch.int8),
+                sh=((P,), torch.float32), y=((P, H), torch.float32))
+    base = ws.data_ptr()
+    out = {}
+    for name, p in zip(INTERMEDIATES, ptrs):
+        shape, dtype = spec[name]
+        off = p - base
+        n = 1
+        for d in shape:
+            n *= d
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        out[name] = ws[off:off + nbytes].view(dtype).view(shape)
+    return out

@@ -1,0 +1,287 @@
+// C ABI of the W8A8 MoE library: argument checks, workspace layout and the
+// launch sequence of the layer.  Every entry point validates its arguments
+// completely before the first launch; nothing here synchronises the host.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w8a8moe.h"
+#include "launch.h"
+
+using namespace w8a8;
+
+namespace {
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool act_dtype_ok(int d) { return d == W8A8_BF16 || d == W8A8_F32; }
+inline size_t elem_size(int d) { return d == W8A8_BF16 ? 2 : 4; }
+inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return W8A8_OK;
+    (void)hipGetLastError();
+    return W8A8_ERR_HIP;
+}
+
+int check_route(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, int64_t H, int E, int k,
+                const int32_t *ids, const float *w, const float *logits)
+{
+    if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (E > 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (H % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (T > 0 && (!x || !w_gate || !ids || !w)) return W8A8_ERR_INVALID_ARG;
+    if (T > 0 && (!aligned16(x) || !aligned16(w_gate) || !aligned16(ids) || !aligned16(w) ||
+                  (logits && !aligned16(logits))))
+        return W8A8_ERR_ALIGNMENT;
+    return W8A8_OK;
+}
+
+// Layer workspace layout (every part 256-byte aligned).
+struct LayerWs {
+    size_t ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y, perm, gemm1, gemm2, total;
+};
+
+LayerWs layer_ws(const w8a8_moe_weights *W, int64_t T, int x_dtype)
+{
+    const int64_t P = T * W->k;
+    LayerWs L;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o += round256(bytes);
+        return at;
+    };
+    L.ids = take(sizeof(int32_t) * P);
+    L.w = take(sizeof(float) * P);
+    L.xq = take((size_t)(T * W->H));
+    L.sx = take(sizeof(float) * T);
+    L.offsets = take(sizeof(int32_t) * (W->E + 1));
+    L.sorted = take(sizeof(int32_t) * P);
+    L.pos = take(sizeof(int32_t) * P);
+    L.h = take(2 * (size_t)(P * W->I));
+    L.hq = take((size_t)(P * W->I));
+    L.sh = take(sizeof(float) * P);
+    L.y = take(sizeof(float) * (size_t)(P * W->H));   // fp32: no rounding before the combine
+    L.perm = take(permute_ws_bytes(T, W->k, W->E));
+    L.gemm1 = take(gemm_ws_bytes(P, 2 * W->I, W->E));
+    L.gemm2 = take(gemm_ws_bytes(P, W->H, W->E));
+    L.total = o;
+    return L;
+}
+
+int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, const void *out)
+{
+    if (!W || T < 0 || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (W->E <= 0 || W->k <= 0 || W->k > W->E || W->H <= 0 || W->I <= 0) return W8A8_ERR_INVALID_ARG;
+    if (W->E > 256 || W->H % 16 || W->I % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!W->w_gate || !W->w_gate_up || !W->s_gate_up || !W->w_down || !W->s_down) return W8A8_ERR_INVALID_ARG;
+    if (T > 0 && (!x || !out)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(W->w_gate) || !aligned16(W->w_gate_up) || !aligned16(W->s_gate_up) || !aligned16(W->w_down) ||
+        !aligned16(W->s_down))
+        return W8A8_ERR_ALIGNMENT;
+    if (T > 0 && (!aligned16(x) || !aligned16(out))) return W8A8_ERR_ALIGNMENT;
+    return W8A8_OK;
+}
+
+int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, void *out, void *ws,
+              size_t ws_bytes, hipStream_t st, void *const *events, int n_events)
+{
+    int rc = check_layer(W, x, x_dtype, T, out);
+    if (rc) return rc;
+    if (n_events < 0 || n_events > W8A8_LAYER_STAGES + 1 || (n_events > 0 && !events)) return W8A8_ERR_INVALID_ARG;
+    if (T == 0) return W8A8_OK;
+    const LayerWs L = layer_ws(W, T, x_dtype);
+    if (!ws) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(ws)) return W8A8_ERR_ALIGNMENT;
+    if (ws_bytes < L.total) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+
+    char *base = (char *)ws;
+    int32_t *ids = (int32_t *)(base + L.ids);
+    float *w = (float *)(base + L.w);
+    int8_t *xq = (int8_t *)(base + L.xq);
+    float *sx = (float *)(base + L.sx);
+    int32_t *offsets = (int32_t *)(base + L.offsets);
+    int32_t *sorted = (int32_t *)(base + L.sorted);
+    int32_t *pos = (int32_t *)(base + L.pos);
+    uint16_t *h = (uint16_t *)(base + L.h);
+    int8_t *hq = (int8_t *)(base + L.hq);
+    float *sh = (float *)(base + L.sh);
+    void *y = base + L.y;
+    void *perm = base + L.perm;
+    void *gws1 = base + L.gemm1;
+    void *gws2 = base + L.gemm2;
+    const int64_t P = T * W->k;
+    const int E = W->E, k = W->k;
+    const int64_t H = W->H, I = W->I;
+
+    int ev = 0;
+    auto mark = [&]() -> hipError_t {
+        if (ev < n_events) return hipEventRecord((hipEvent_t)events[ev++], st);
+        return hipSuccess;
+    };
+    hipError_t e;
+    if ((e = mark()) != hipSuccess) return hip_status(e);
+    // 1 route
+    if ((e = launch_route_topk(x, x_dtype, W->w_gate, T, H, E, k, 1, ids, w, nullptr, st)) != hipSuccess ||
+        (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // 2 quantise x once per token (before the permutation: one scale per token
+    //   serves all k experts)
+    if ((e = launch_quant_rows(x, x_dtype, T, H, H, xq, sx, st)) != hipSuccess || (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // 3 permute, and the tile maps of both grouped GEMMs
+    if ((e = launch_permute(ids, T, k, E, offsets, sorted, pos, perm, st)) != hipSuccess ||
+        (e = launch_gemm_tilemap(offsets, E, P, 2 * I, W8A8_EPI_DEQUANT_SWIGLU, gws1, st)) != hipSuccess ||
+        (e = launch_gemm_tilemap(offsets, E, P, H, W8A8_EPI_DEQUANT, gws2, st)) != hipSuccess ||
+        (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // 4a gate_up GEMM + SwiGLU -> h (bf16)
+    if ((e = launch_gemm_main(xq, sx, sorted, k, W->w_gate_up, W->s_gate_up, offsets, E, P, 2 * I, H,
+                              W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)) != hipSuccess ||
+        (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // quantise h per grouped row
+    if ((e = launch_quant_rows(h, W8A8_BF16, P, I, I, hq, sh, st)) != hipSuccess || (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // 4b down GEMM -> y (fp32)
+    if ((e = launch_gemm_main(hq, sh, nullptr, 1, W->w_down, W->s_down, offsets, E, P, H, I, W8A8_EPI_DEQUANT,
+                              W8A8_F32, y, gws2, st)) != hipSuccess ||
+        (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // 5 combine
+    if ((e = launch_combine(y, W8A8_F32, w, pos, T, k, H, out, x_dtype, st)) != hipSuccess ||
+        (e = mark()) != hipSuccess)
+        return hip_status(e);
+    return W8A8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *w8a8_status_string(int status)
+{
+    switch (status) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_INVALID_ARG: return "invalid argument";
+    case W8A8_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case W8A8_ERR_ALIGNMENT: return "pointer or leading dimension not 16-byte aligned";
+    case W8A8_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case W8A8_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int w8a8_quant_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, int8_t *q, float *scales,
+                   void *stream)
+{
+    if (rows < 0 || cols <= 0 || ld_x < cols || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (cols % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (rows == 0) return W8A8_OK;
+    if (!x || !q || !scales) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(q) || ((size_t)ld_x * elem_size(x_dtype)) % 16) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_quant_rows(x, x_dtype, rows, cols, ld_x, q, scales, (hipStream_t)stream));
+}
+
+int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, int64_t H, int E, int k,
+                   int renormalize, int32_t *topk_ids, float *topk_w, float *logits_out, void *stream)
+{
+    int rc = check_route(x, x_dtype, w_gate, T, H, E, k, topk_ids, topk_w, logits_out);
+    if (rc) return rc;
+    if (T == 0) return W8A8_OK;
+    return hip_status(launch_route_topk(x, x_dtype, w_gate, T, H, E, k, renormalize, topk_ids, topk_w, logits_out,
+                                        (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_size(int64_t T, int k, int E)
+{
+    if (T < 0 || k <= 0 || E <= 0) return 0;
+    return round256(permute_ws_bytes(T, k, E));
+}
+
+int moe_permute(const int32_t *topk_ids, int64_t T, int k, int E, int32_t *offsets, int32_t *sorted_pair,
+                int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream)
+{
+    if (T < 0 || k <= 0 || E <= 0 || k > E) return W8A8_ERR_INVALID_ARG;
+    if (E > 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!offsets) return W8A8_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_ids || !sorted_pair || !pair_pos || !ws)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(offsets) || (T > 0 && (!aligned16(topk_ids) || !aligned16(sorted_pair) || !aligned16(pair_pos) ||
+                                          !aligned16(ws))))
+        return W8A8_ERR_ALIGNMENT;
+    if (ws_bytes < permute_ws_bytes(T, k, E)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(
+        launch_permute(topk_ids, T, k, E, offsets, sorted_pair, pair_pos, ws, (hipStream_t)stream));
+}
+
+size_t w8a8_grouped_gemm_workspace_size(int64_t M_total, int64_t N, int G)
+{
+    if (M_total < 0 || N <= 0 || G <= 0) return 0;
+    return gemm_ws_bytes(M_total, N, G);
+}
+
+int w8a8_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *a_row_gather, int gather_div,
+                      const int8_t *B, const float *b_scales, const int32_t *group_offsets, int G, int64_t M_total,
+                      int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws, size_t ws_bytes,
+                      void *stream)
+{
+    if (M_total < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
+    if (epilogue < W8A8_EPI_RAW_I32 || epilogue > W8A8_EPI_DEQUANT_SWIGLU) return W8A8_ERR_INVALID_ARG;
+    if (epilogue == W8A8_EPI_RAW_I32 ? out_dtype != W8A8_I32 : !act_dtype_ok(out_dtype))
+        return W8A8_ERR_INVALID_ARG;
+    if (a_row_gather && gather_div <= 0) return W8A8_ERR_INVALID_ARG;
+    if (K % 16 || N % 16 || (epilogue == W8A8_EPI_DEQUANT_SWIGLU && N % 32)) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!B || !group_offsets || !ws) return W8A8_ERR_INVALID_ARG;
+    if (M_total > 0 && (!A || !out)) return W8A8_ERR_INVALID_ARG;
+    if (epilogue != W8A8_EPI_RAW_I32 && (!b_scales || (M_total > 0 && !a_scales))) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(out) || !aligned16(ws) || !aligned16(group_offsets) ||
+        (a_row_gather && !aligned16(a_row_gather)) || (a_scales && !aligned16(a_scales)) ||
+        (b_scales && !aligned16(b_scales)))
+        return W8A8_ERR_ALIGNMENT;
+    if (ws_bytes < gemm_ws_bytes(M_total, N, G)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+    if (M_total == 0) return W8A8_OK;
+    return hip_status(launch_grouped_gemm(A, a_scales, a_row_gather, gather_div, B, b_scales, group_offsets, G,
+                                          M_total, N, K, epilogue, out_dtype, out, ws, (hipStream_t)stream));
+}
+
+int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *pair_pos, int64_t T, int k, int64_t H,
+                void *out, int out_dtype, void *stream)
+{
+    if (T < 0 || k <= 0 || H <= 0 || !act_dtype_ok(y_dtype) || !act_dtype_ok(out_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (H % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (T == 0) return W8A8_OK;
+    if (!y || !topk_w || !pair_pos || !out) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(topk_w) || !aligned16(pair_pos) || !aligned16(out)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_combine(y, y_dtype, topk_w, pair_pos, T, k, H, out, out_dtype, (hipStream_t)stream));
+}
+
+size_t w8a8_moe_layer_workspace_size(const w8a8_moe_weights *W, int64_t T, int x_dtype)
+{
+    if (!W || T < 0 || !act_dtype_ok(x_dtype) || W->E <= 0 || W->k <= 0 || W->H <= 0 || W->I <= 0) return 0;
+    return layer_ws(W, T, x_dtype).total;
+}
+
+int w8a8_moe_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, void *out, void *ws,
+                   size_t ws_bytes, void *stream)
+{
+    return run_layer(W, x, x_dtype, T, out, ws, ws_bytes, (hipStream_t)stream, nullptr, 0);
+}
+
+int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, void *out, void *ws,
+                          size_t ws_bytes, void *stream, void *const *events, int n_events)
+{
+    return run_layer(W, x, x_dtype, T, out, ws, ws_bytes, (hipStream_t)stream, events, n_events);
+}
+
+int w8a8_moe_layer_intermediates(const w8a8_moe_weights *W, int64_t T, int x_dtype, void *ws, void **ptrs)
+{
+    if (!W || !ws || !ptrs || T < 0 || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
+    const LayerWs L = layer_ws(W, T, x_dtype);
+    char *b = (char *)ws;
+    const size_t offs[W8A8_LAYER_INTERMEDIATES] = {L.ids, L.w, L.xq, L.sx, L.offsets, L.sorted,
+                                                   L.pos, L.h, L.hq, L.sh, L.y};
+    for (int i = 0; i < W8A8_LAYER_INTERMEDIATES; ++i) ptrs[i] = b + offs[i];
+    return W8A8_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Weighted combine of the expert outputs: each token's output is the sum, over
+// its k routed slots, of the routing weight times that slot's expert output
+// (the top-k experts of the router take part in the token's forward pass:
+// "Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer, section 3.1).
+//
+// One block per token; each thread owns 8 consecutive columns (16-byte bf16
+// loads), accumulates the k slots in fp32 in slot order and rounds once.
+#include "device_common.h"
+#include "launch.h"
+
+namespace w8a8 {
+
+template <typename YT, typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y, const float *__restrict__ w,
+                                                      const int32_t *__restrict__ pair_pos, int k, int64_t H,
+                                                      OT *__restrict__ out)
+{
+    const int64_t t = blockIdx.x;
+    for (int64_t c = (int64_t)threadIdx.x * 8; c < H; c += 256 * 8) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const float wj = w[t * k + j];
+            const int64_t row = pair_pos[t * k + j];
+            float v[8];
+            load8_f32(y + row * H + c, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+        }
+        store8(out + t * H + c, acc);
+    }
+}
+
+hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T, int k,
+                          int64_t H, void *out, int out_dtype, hipStream_t st)
+{
+    if (T == 0) return hipSuccess;
+    dim3 grid((unsigned)T), block(256);
+    if (y_dtype == 0 && out_dtype == 0)
+        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, block, 0, st, (const uint16_t *)y, w,
+                           pair_pos, k, H, (uint16_t *)out);
+    else if (y_dtype == 0)
+        hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, block, 0, st, (const uint16_t *)y, w, pair_pos,
+                           k, H, (float *)out);
+    else if (out_dtype == 0)
+        hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, block, 0, st, (const float *)y, w, pair_pos, k,
+                           H, (uint16_t *)out);
+    else
+        hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, st, (const float *)y, w, pair_pos, k, H,
+                           (float *)out);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -1,0 +1,66 @@
+// Device-side helpers shared by the HIP kernels of the W8A8 MoE library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// bf16 is the upper half of a binary32: widening is exact.
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round a finite fp32 to bf16, nearest with ties to even.
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Load 8 consecutive elements (16-byte aligned) widened to fp32.
+__device__ __forceinline__ void load8_f32(const uint16_t *p, float v[8])
+{
+    uint4 u = *reinterpret_cast<const uint4 *>(p);
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void load8_f32(const float *p, float v[8])
+{
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(uint16_t *p, const float v[8])
+{
+    uint4 u;
+    u.x = float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16);
+    u.y = float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16);
+    u.z = float_to_bf16_bits(v[4]) | (float_to_bf16_bits(v[5]) << 16);
+    u.w = float_to_bf16_bits(v[6]) | (float_to_bf16_bits(v[7]) << 16);
+    *reinterpret_cast<uint4 *>(p) = u;
+}
+
+__device__ __forceinline__ void store8(float *p, const float v[8])
+{
+    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}

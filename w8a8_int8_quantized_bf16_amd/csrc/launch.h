@@ -1,0 +1,35 @@
+// Host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+hipError_t launch_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                             int8_t *q, float *scales, hipStream_t st);
+
+hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H, int E,
+                             int k, int renormalize, int32_t *ids, float *w, float *logits, hipStream_t st);
+
+size_t permute_ws_bytes(int64_t T, int k, int E);
+hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets,
+                          int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t st);
+
+size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G);
+// tile map of a grouped GEMM (into ws), then the GEMM itself reading that map
+hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
+                               hipStream_t st);
+hipError_t launch_gemm_main(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
+                            const int8_t *B, const float *b_scales, const int32_t *offsets, int G, int64_t M_total,
+                            int64_t N, int64_t K, int epilogue, int out_dtype, void *out, const void *ws,
+                            hipStream_t st);
+hipError_t launch_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
+                               const int8_t *B, const float *b_scales, const int32_t *offsets, int G,
+                               int64_t M_total, int64_t N, int64_t K, int epilogue, int out_dtype, void *out,
+                               void *ws, hipStream_t st);
+
+hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T,
+                          int k, int64_t H, void *out, int out_dtype, hipStream_t st);
+
+}  // namespace w8a8

@@ -1,0 +1,131 @@
+// Grouping of the routed (token, slot) pairs by expert, for the grouped GEMM
+// ("Qwen3-Next-80B-A3B-Instruct in AMCT" case, section 6: the MoE runs as one
+// packed grouped matmul over the experts).
+//
+// A deterministic, stable counting sort of the P = T*k pair ids by expert:
+//   1. count:   one block per chunk of 2048 pairs -> per-chunk histograms
+//   2. scan:    one block; per expert an exclusive scan over the chunks, then
+//               an exclusive scan over experts -> offsets[E+1]
+//   3. scatter: one block per chunk; pairs are ranked in pair order, 256 at a
+//               time: equal experts inside a wavefront are matched with eight
+//               ballots (one per bit of the id), waves are ordered through LDS
+// The result depends only on the ids: no atomics decide any position.
+#include "device_common.h"
+#include "launch.h"
+
+namespace w8a8 {
+
+namespace {
+constexpr int PM_THREADS = 256;
+constexpr int PM_PER_THREAD = 8;
+constexpr int PM_CHUNK = PM_THREADS * PM_PER_THREAD;   // pairs per chunk
+constexpr int PM_MAX_E = 256;
+
+inline int64_t pm_chunks(int64_t P) { return (P + PM_CHUNK - 1) / PM_CHUNK; }
+}  // namespace
+
+__global__ __launch_bounds__(PM_THREADS) void permute_count_kernel(const int32_t *__restrict__ ids, int64_t P,
+                                                                   int E, int32_t *__restrict__ chunk_counts)
+{
+    __shared__ int32_t hist[PM_MAX_E];
+    const int tid = threadIdx.x;
+    hist[tid] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * PM_CHUNK;
+    for (int i = 0; i < PM_PER_THREAD; ++i) {
+        const int64_t p = base + i * PM_THREADS + tid;
+        if (p < P) atomicAdd(&hist[ids[p]], 1);
+    }
+    __syncthreads();
+    if (tid < E) chunk_counts[(int64_t)blockIdx.x * E + tid] = hist[tid];
+}
+
+// chunk_counts[c][e] -> exclusive prefix over c (in place); offsets = exclusive
+// prefix over e of the totals.
+__global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__restrict__ chunk_counts,
+                                                                  int64_t nchunks, int E, int64_t P,
+                                                                  int32_t *__restrict__ offsets)
+{
+    __shared__ int32_t tot[PM_MAX_E];
+    const int tid = threadIdx.x;
+    int32_t run = 0;
+    if (tid < E) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int32_t v = chunk_counts[c * E + tid];
+            chunk_counts[c * E + tid] = run;
+            run += v;
+        }
+    }
+    tot[tid] = (tid < E) ? run : 0;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over 256 entries
+    for (int d = 1; d < PM_THREADS; d <<= 1) {
+        const int32_t v = (tid >= d) ? tot[tid - d] : 0;
+        __syncthreads();
+        tot[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) offsets[tid] = tot[tid] - run;
+    if (tid == 0) offsets[E] = (int32_t)P;
+}
+
+__global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
+                                                                     int E, const int32_t *__restrict__ chunk_base,
+                                                                     const int32_t *__restrict__ offsets,
+                                                                     int32_t *__restrict__ sorted_pair,
+                                                                     int32_t *__restrict__ pair_pos)
+{
+    __shared__ int32_t base[PM_MAX_E];     // next free row of each expert inside this chunk
+    __shared__ int32_t wcnt[4][PM_MAX_E];  // per-wave counts of the current round
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (tid < E) base[tid] = offsets[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int round = 0; round < PM_PER_THREAD; ++round) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+        __syncthreads();
+        const int64_t p = (int64_t)blockIdx.x * PM_CHUNK + (int64_t)round * PM_THREADS + tid;
+        const bool valid = p < P;
+        const int e = valid ? ids[p] : 0;
+        // lanes of this wave holding the same expert id
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+            same &= ((e >> b) & 1) ? ones : ~ones;
+        }
+        const int rank_in_wave = __popcll(same & lt_mask);
+        if (valid && rank_in_wave == 0) wcnt[wave][e] = __popcll(same);
+        __syncthreads();
+        if (valid) {
+            int32_t before = 0;
+            for (int w = 0; w < wave; ++w) before += wcnt[w][e];
+            const int32_t row = base[e] + before + rank_in_wave;
+            sorted_pair[row] = (int32_t)p;
+            pair_pos[p] = row;
+        }
+        __syncthreads();
+        if (tid < E) base[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+        __syncthreads();
+    }
+}
+
+size_t permute_ws_bytes(int64_t T, int k, int E) { return (size_t)pm_chunks(T * k) * (size_t)E * sizeof(int32_t); }
+
+hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets, int32_t *sorted_pair,
+                          int32_t *pair_pos, void *ws, hipStream_t st)
+{
+    const int64_t P = T * k;
+    const int64_t nch = pm_chunks(P);
+    int32_t *cc = (int32_t *)ws;
+    // with P == 0 only the scan runs: it writes all-zero offsets
+    if (nch > 0)
+        hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets);
+    if (nch > 0)
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc,
+                           offsets, sorted_pair, pair_pos);
+    return hipGetLastError();
+}
+
+}  // namespace w8a8
