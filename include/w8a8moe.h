@@ -60,6 +60,10 @@ extern "C" {
 #define W8A8_F32 1
 #define W8A8_I32 2
 
+/* weight layouts of the grouped GEMM */
+#define W8A8_B_ROWMAJOR 0 /* [G][N][K], nn.Linear [out][in] per group */
+#define W8A8_B_PACKED 1   /* the MFMA-fragment layout written by w8a8_pack_weights */
+
 /* grouped GEMM epilogues */
 #define W8A8_EPI_RAW_I32 0        /* out = int32 accumulator */
 #define W8A8_EPI_DEQUANT 1        /* out = acc * a_scale[row] * b_scale[group][col] */
@@ -120,6 +124,21 @@ int moe_permute(const int32_t *topk_ids, int64_t T, int k, int E, int32_t *offse
                 int32_t *sorted_pair, int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Static weights are re-laid once, after quantisation, so that every
+ * wavefront of the grouped GEMM fetches its matrix-core operand as 1 KiB of
+ * contiguous memory.  For group g, 32-row block nb and 128-byte K step ks, a
+ * 4 KiB chunk at byte ((g * NB + nb) * KS + ks) * 4096 holds, at offset
+ * s * 1024 + l * 16 (s = 0..3, l = 0..63), bytes [64 * (l / 32) + 16 * s, +16)
+ * of step ks of row 32 * nb + l % 32; rows beyond N and bytes beyond K are
+ * zero.  NB = ceil(N / 32), KS = ceil(K / 128).
+ *   B       device, [G][N][K] int8, read
+ *   packed  device, w8a8_packed_weights_size(G, N, K) bytes, written
+ * K % 16 == 0, N % 16 == 0.
+ */
+size_t w8a8_packed_weights_size(int G, int64_t N, int64_t K);
+int w8a8_pack_weights(const int8_t *B, int G, int64_t N, int64_t K, int8_t *packed, void *stream);
+
+/*
  * Grouped W8A8 GEMM: for group g and every grouped row r in
  * [group_offsets[g], group_offsets[g+1]), with activation row
  * a = a_row_gather ? a_row_gather[r] / gather_div : r,
@@ -130,22 +149,26 @@ int moe_permute(const int32_t *topk_ids, int64_t T, int k, int E, int32_t *offse
  *   DEQUANT_SWIGLU out [M_total][N/2] out_dtype = silu(gate) * up with
  *                  gate = dequant(acc[r][n]), up = dequant(acc[r][N/2 + n]) (the
  *                  packed gate_up_proj layout of the AMCT case, section 2.2)
- *   A             device, [*][K] int8 (rows addressed by a)
+ *   A             device, [A_rows][K] int8 (rows addressed by a, all < A_rows)
  *   a_scales      device, fp32 per activation row (unused for RAW_I32)
  *   a_row_gather  device, [M_total] int32 or NULL
- *   B             device, [G][N][K] int8;  b_scales device [G][N] fp32
+ *   B             device, int8 in layout b_layout (W8A8_B_ROWMAJOR [G][N][K] or
+ *                 W8A8_B_PACKED as written by w8a8_pack_weights);
+ *   b_scales      device [G][N] fp32
  *   group_offsets device, [G+1] int32, non-decreasing, group_offsets[0] = 0,
  *                 group_offsets[G] = M_total (not checked: device memory)
  *   ws            device scratch of at least w8a8_grouped_gemm_workspace_size() bytes
  * out_dtype: W8A8_BF16 or W8A8_F32 (W8A8_I32 with RAW_I32).  K % 16 == 0,
- * N % 16 == 0 (N % 32 == 0 for SWIGLU).
+ * N % 16 == 0, N % 64 == 0 for SWIGLU.  A_rows * K and one group of B must stay
+ * below 2^31 bytes (the kernels address them with 32-bit byte offsets); larger
+ * shapes return W8A8_ERR_UNSUPPORTED_SHAPE.
  */
 size_t w8a8_grouped_gemm_workspace_size(int64_t M_total, int64_t N, int G);
-int w8a8_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *a_row_gather,
-                      int gather_div, const int8_t *B, const float *b_scales,
-                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K,
-                      int epilogue, int out_dtype, void *out, void *ws, size_t ws_bytes,
-                      void *stream);
+int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
+                      const int32_t *a_row_gather, int gather_div, const int8_t *B, int b_layout,
+                      const float *b_scales, const int32_t *group_offsets, int G, int64_t M_total,
+                      int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws,
+                      size_t ws_bytes, void *stream);
 
 /*
  * Weighted combine of the expert outputs:
@@ -160,9 +183,12 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
 /*
  * Layer weights (caller-owned device memory):
  *   w_gate    [E][H]    bf16 router (not quantised)
- *   w_gate_up [E][2I][H] int8, rows 0..I-1 gate_proj, rows I..2I-1 up_proj
+ *   w_gate_up int8 gate_up_proj codes [E][2I][H] (rows 0..I-1 gate_proj, rows
+ *             I..2I-1 up_proj) in the packed layout of w8a8_pack_weights
  *   s_gate_up [E][2I]   fp32 per-output-channel scales
- *   w_down    [E][H][I] int8;  s_down [E][H] fp32
+ *   w_down    int8 down_proj codes [E][H][I], packed the same way
+ *   s_down    [E][H]    fp32
+ * H % 16 == 0, I % 32 == 0.
  */
 typedef struct {
     int E, k;

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
               "w8a8_moe_layer"):
         assert n in names
@@ -85,13 +85,15 @@ def test_permute_rejects(L):
 def test_grouped_gemm_rejects(L):
     s = None
     ws = L.w8a8_grouped_gemm_workspace_size(1024, 256, 8)
-    args = lambda **kw: [kw.get("A", FAKE), kw.get("sa", FAKE), kw.get("gat", None), kw.get("div", 1),
-                         kw.get("B", FAKE), kw.get("sb", FAKE), kw.get("off", FAKE), kw.get("G", 8),
+    args = lambda **kw: [kw.get("A", FAKE), kw.get("Arows", 1024), kw.get("sa", FAKE), kw.get("gat", None),
+                         kw.get("div", 1),
+                         kw.get("B", FAKE), kw.get("lay", 0), kw.get("sb", FAKE), kw.get("off", FAKE), kw.get("G", 8),
                          kw.get("M", 1024), kw.get("N", 256), kw.get("K", 256), kw.get("epi", 1),
                          kw.get("od", 0), kw.get("out", FAKE), kw.get("ws", FAKE), kw.get("wsb", ws), s]
     assert L.w8a8_grouped_gemm(*args(K=200)) == SHAPE
     assert L.w8a8_grouped_gemm(*args(N=200)) == SHAPE
-    assert L.w8a8_grouped_gemm(*args(N=272, epi=2)) == SHAPE                  # SwiGLU needs N % 32
+    assert L.w8a8_grouped_gemm(*args(N=288, epi=2)) == SHAPE                  # SwiGLU needs N % 64
+    assert L.w8a8_grouped_gemm(*args(lay=2)) == INVALID
     assert L.w8a8_grouped_gemm(*args(epi=3)) == INVALID
     assert L.w8a8_grouped_gemm(*args(epi=0, od=0)) == INVALID                 # RAW needs int32 out
     assert L.w8a8_grouped_gemm(*args(od=2)) == INVALID                        # dequant cannot be int32
@@ -101,6 +103,17 @@ def test_grouped_gemm_rejects(L):
     assert L.w8a8_grouped_gemm(*args(wsb=ws - 1)) == WS_SMALL
     assert L.w8a8_grouped_gemm(*args(G=0)) == INVALID
     assert L.w8a8_grouped_gemm(*args(M=0, A=None, out=None)) == OK
+    assert L.w8a8_grouped_gemm(*args(Arows=1 << 20, K=4096)) == SHAPE        # 32-bit offsets
+    assert L.w8a8_grouped_gemm(*args(Arows=-1)) == INVALID
+
+
+def test_pack_rejects(L):
+    s = None
+    assert L.w8a8_packed_weights_size(2, 100, 200) == 2 * 4 * 2 * 4096
+    assert L.w8a8_pack_weights(FAKE, 2, 40, 64, FAKE, s) == SHAPE
+    assert L.w8a8_pack_weights(FAKE, 0, 48, 64, FAKE, s) == INVALID
+    assert L.w8a8_pack_weights(MIS, 1, 48, 64, FAKE, s) == ALIGN
+    assert L.w8a8_pack_weights(None, 1, 48, 64, FAKE, s) == INVALID
 
 
 def test_combine_rejects(L):
@@ -126,7 +139,7 @@ def test_layer_rejects_and_sizes_workspace(L):
     assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 1, 16, FAKE, MIS, need, s) == ALIGN
     assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 5, 16, FAKE, FAKE, need, s) == INVALID
     assert L.w8a8_moe_layer(ctypes.byref(_weights(H=72)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
-    assert L.w8a8_moe_layer(ctypes.byref(_weights(I=40)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
+    assert L.w8a8_moe_layer(ctypes.byref(_weights(I=48)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
     assert L.w8a8_moe_layer(ctypes.byref(_weights(k=9)), FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
     assert L.w8a8_moe_layer(ctypes.byref(_weights(E=257, k=2)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
     assert L.w8a8_moe_layer(ctypes.byref(_weights(ptr=MIS)), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN

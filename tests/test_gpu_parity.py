@@ -229,6 +229,7 @@ def _groups(rng, sizes):
     return off
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("sizes,N,K,gather", [
     ([5, 0, 33, 1, 64], 48, 144, 0),          # ragged, an empty group, K tail
     ([3] * 40, 256, 2048, 2),                 # decode-like: tiny groups
@@ -236,7 +237,7 @@ def _groups(rng, sizes):
     ([300, 129, 1000], 512, 384, 8),          # large groups
     ([17], 16, 16, 0),                        # minimum sizes
 ])
-def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather):
+def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather, packed):
     rng = np.random.default_rng(sum(sizes) + N + K)
     G, M = len(sizes), int(sum(sizes))
     off = _groups(rng, sizes)
@@ -250,8 +251,10 @@ def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather):
         gat = None
     A[0, :] = 127                              # extremes
     B[0, 0, :] = -127
-    out = w8.grouped_gemm(to_dev(A), None, None if gat is None else to_dev(gat), max(gather, 1), to_dev(B), None,
-                          to_dev(off), w8.EPI_RAW_I32, M_total=M)
+    Bd = to_dev(B)
+    out = w8.grouped_gemm(to_dev(A), None, None if gat is None else to_dev(gat), max(gather, 1),
+                          w8.pack_weights(Bd) if packed else Bd, None, to_dev(off), w8.EPI_RAW_I32, M_total=M,
+                          b_shape=(G, N, K) if packed else None)
     got = to_host(out)
     want = oracle.grouped_gemm(A, None, gat, max(gather, 1), B, None, off, oracle.RAW_I32)
     assert np.array_equal(got, want)
@@ -262,10 +265,11 @@ def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather):
     assert np.array_equal(got[rows].astype(np.float64), A[arow].astype(np.float64) @ B[g].astype(np.float64).T)
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("epi,od", [(w8.EPI_DEQUANT, w8.BF16), (w8.EPI_DEQUANT, w8.F32),
                                     (w8.EPI_DEQUANT_SWIGLU, w8.BF16), (w8.EPI_DEQUANT_SWIGLU, w8.F32)])
 @pytest.mark.parametrize("sizes", [[7, 0, 90, 33], [200, 300]])
-def test_grouped_gemm_dequant_epilogues(epi, od, sizes):
+def test_grouped_gemm_dequant_epilogues(epi, od, sizes, packed):
     rng = np.random.default_rng(len(sizes) + epi * 10 + od)
     G, M, N, K = len(sizes), sum(sizes), 320, 528
     off = _groups(rng, sizes)
@@ -274,13 +278,38 @@ def test_grouped_gemm_dequant_epilogues(epi, od, sizes):
     qa, sa = oracle.quant_rows(x)
     qb, sb = oracle.quant_rows(Wf)
     qb, sb = qb.reshape(G, N, K), sb.reshape(G, N)
-    out = w8.grouped_gemm(to_dev(qa), to_dev(sa), None, 1, to_dev(qb), to_dev(sb), to_dev(off), epi, od)
+    qbd = to_dev(qb)
+    out = w8.grouped_gemm(to_dev(qa), to_dev(sa), None, 1, w8.pack_weights(qbd) if packed else qbd, to_dev(sb),
+                          to_dev(off), epi, od, b_shape=(G, N, K) if packed else None)
     want = oracle.grouped_gemm(qa, sa, None, 1, qb, sb, off, epi, od)
     got = to_host(out)
     g64, w64 = f64(got), f64(want)
     # fp32 epilogue vs fp64 reference: a few fp32 ulps, plus one output rounding
     rel = 2.0 ** -7 if od == w8.BF16 else 1e-5
     assert np.all(np.abs(g64 - w64) <= rel * np.abs(w64) + 1e-6 * np.abs(w64).max())
+
+
+def test_pack_weights_layout():
+    """Every byte of the packed layout is where the layout definition puts it
+    (checked against an independent numpy gather), padding included."""
+    rng = np.random.default_rng(12)
+    for G, N, K in ((1, 32, 128), (2, 48, 144), (3, 96, 400)):
+        B = rng.integers(-127, 128, (G, N, K), dtype=np.int8)
+        got = to_host(w8.pack_weights(to_dev(B)))
+        NB, KS = (N + 31) // 32, (K + 127) // 128
+        Bp = np.zeros((G, NB * 32, KS * 128), np.int8)
+        Bp[:, :N, :K] = B
+        want = np.zeros(G * NB * KS * 4096, np.int8)
+        for g in range(G):
+            for nb in range(NB):
+                for ks in range(KS):
+                    base = ((g * NB + nb) * KS + ks) * 4096
+                    for s_ in range(4):
+                        for l in range(64):
+                            row = nb * 32 + l % 32
+                            k0 = ks * 128 + 64 * (l // 32) + 16 * s_
+                            want[base + s_ * 1024 + l * 16: base + s_ * 1024 + l * 16 + 16] = Bp[g, row, k0:k0 + 16]
+        assert np.array_equal(got, want)
 
 
 # --------------------------------------------------------------- combine ---

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libw8a8moe.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "w8a8moe.h")
 
 BF16, F32, I32 = 0, 1, 2
+B_ROWMAJOR, B_PACKED = 0, 1
 EPI_RAW_I32, EPI_DEQUANT, EPI_DEQUANT_SWIGLU = 0, 1, 2
 LAYER_STAGES = 7
 STAGE_NAMES = ("route", "quant_x", "permute", "gate_up_gemm", "quant_h", "down_gemm", "combine")
@@ -59,7 +60,10 @@ def lib():
     L.moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P, sz, P]
     L.w8a8_grouped_gemm_workspace_size.argtypes = [i64, i64, i32]
     L.w8a8_grouped_gemm_workspace_size.restype = sz
-    L.w8a8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
+    L.w8a8_grouped_gemm.argtypes = [P, i64, P, P, i32, P, i32, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
+    L.w8a8_packed_weights_size.argtypes = [i32, i64, i64]
+    L.w8a8_packed_weights_size.restype = sz
+    L.w8a8_pack_weights.argtypes = [P, i32, i64, i64, P, P]
     L.moe_combine.argtypes = [P, i32, P, P, i64, i32, i64, P, i32, P]
     WP = ctypes.POINTER(_Weights)
     L.w8a8_moe_layer_workspace_size.argtypes = [WP, i64, i32]
@@ -68,6 +72,7 @@ def lib():
     L.w8a8_moe_layer_events.argtypes = [WP, P, i32, i64, P, P, sz, P, ctypes.POINTER(P), i32]
     L.w8a8_moe_layer_intermediates.argtypes = [WP, i64, i32, P, ctypes.POINTER(P)]
     for name in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
+                 "w8a8_pack_weights",
                  "w8a8_moe_layer", "w8a8_moe_layer_events", "w8a8_moe_layer_intermediates"):
         getattr(L, name).restype = i32
     _lib = L
@@ -163,12 +168,31 @@ def permute(ids, E):
     return offsets, sp, pos
 
 
-def grouped_gemm(A, a_scales, gather, gather_div, B, b_scales, offsets, epilogue, out_dtype=BF16, M_total=None):
-    """Grouped W8A8 GEMM (see include/w8a8moe.h).  B is [G, N, K] int8."""
-    _need(A, "A", torch.int8, 2)
+def pack_weights(B):
+    """Re-lay int8 weights [G, N, K] into the packed MFMA-fragment layout (uint8 bytes)."""
     _need(B, "B", torch.int8, 3)
-    _need(offsets, "offsets", torch.int32, 1)
     G, N, K = B.shape
+    n = int(lib().w8a8_packed_weights_size(G, N, K))
+    out = torch.empty(n, dtype=torch.int8, device=B.device)
+    _check(lib().w8a8_pack_weights(_p(B), G, N, K, _p(out), _stream(B.device)), "w8a8_pack_weights")
+    return out
+
+
+def grouped_gemm(A, a_scales, gather, gather_div, B, b_scales, offsets, epilogue, out_dtype=BF16, M_total=None,
+                 b_shape=None):
+    """Grouped W8A8 GEMM (see include/w8a8moe.h).  B is [G, N, K] int8, or the
+    1-D packed bytes of pack_weights() with b_shape=(G, N, K)."""
+    _need(A, "A", torch.int8, 2)
+    _need(B, "B", torch.int8)
+    _need(offsets, "offsets", torch.int32, 1)
+    if b_shape is None:
+        if B.dim() != 3:
+            raise ValueError("B must be [G, N, K] unless b_shape is given for packed weights")
+        G, N, K = B.shape
+        layout = B_ROWMAJOR
+    else:
+        G, N, K = b_shape
+        layout = B_PACKED
     if M_total is None:
         M_total = gather.shape[0] if gather is not None else A.shape[0]
     if epilogue == EPI_RAW_I32:
@@ -179,9 +203,9 @@ def grouped_gemm(A, a_scales, gather, gather_div, B, b_scales, offsets, epilogue
         out = torch.empty((M_total, ncol), dtype=_torch_dtype(out_dtype), device=A.device)
     nws = int(lib().w8a8_grouped_gemm_workspace_size(M_total, N, G))
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=A.device)
-    _check(lib().w8a8_grouped_gemm(_p(A), _p(a_scales), _p(gather), int(gather_div), _p(B), _p(b_scales),
-                                   _p(offsets), G, M_total, N, K, epilogue, out_dtype, _p(out), _p(ws), ws.numel(),
-                                   _stream(A.device)), "w8a8_grouped_gemm")
+    _check(lib().w8a8_grouped_gemm(_p(A), A.shape[0], _p(a_scales), _p(gather), int(gather_div), _p(B), layout,
+                                   _p(b_scales), _p(offsets), G, M_total, N, K, epilogue, out_dtype, _p(out),
+                                   _p(ws), ws.numel(), _stream(A.device)), "w8a8_grouped_gemm")
     return out
 
 
@@ -202,9 +226,10 @@ def combine(y, w, pair_pos, out_dtype=None):
 # ------------------------------------------------------------------- layer ---
 
 class MoEWeights:
-    """Device tensors of one layer in the library's layout.
-    w_gate [E,H] bf16; w_gate_up [E,2I,H] int8 (gate rows, then up rows);
-    s_gate_up [E,2I] fp32; w_down [E,H,I] int8; s_down [E,H] fp32."""
+    """Device tensors of one layer.
+    w_gate [E,H] bf16; w_gate_up [E,2I,H] int8 codes (gate rows, then up rows);
+    s_gate_up [E,2I] fp32; w_down [E,H,I] int8 codes; s_down [E,H] fp32.
+    The layer reads the codes in the packed layout (pack_weights), built here."""
 
     def __init__(self, w_gate, w_gate_up, s_gate_up, w_down, s_down, k):
         _need(w_gate, "w_gate", torch.bfloat16, 2)
@@ -216,7 +241,10 @@ class MoEWeights:
         self.E, self.H, self.I, self.k = E, H, twoI // 2, int(k)
         self.tensors = (w_gate, w_gate_up, s_gate_up, w_down, s_down)
         self.w_gate, self.w_gate_up, self.s_gate_up, self.w_down, self.s_down = self.tensors
-        self.c = _Weights(E, self.k, H, self.I, *[t.data_ptr() for t in self.tensors])
+        self.p_gate_up = pack_weights(w_gate_up)
+        self.p_down = pack_weights(w_down)
+        self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), self.p_gate_up.data_ptr(), s_gate_up.data_ptr(),
+                          self.p_down.data_ptr(), s_down.data_ptr())
 
     @classmethod
     def quantize(cls, w_gate, gate_up_f32, down_f32, k):

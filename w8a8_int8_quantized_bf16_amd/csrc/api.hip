@@ -73,7 +73,13 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
 {
     if (!W || T < 0 || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
     if (W->E <= 0 || W->k <= 0 || W->k > W->E || W->H <= 0 || W->I <= 0) return W8A8_ERR_INVALID_ARG;
-    if (W->E > 256 || W->H % 16 || W->I % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (W->E > 256 || W->H % 16 || W->I % 32) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    // the grouped GEMMs address one expert's weights and the activation codes
+    // with 32-bit byte offsets
+    if ((int64_t)packed_weights_bytes(1, 2 * W->I, W->H) > INT32_MAX - 256 ||
+        (int64_t)packed_weights_bytes(1, W->H, W->I) > INT32_MAX - 256 || T * W->k * W->I > INT32_MAX - 256 ||
+        T * W->H > INT32_MAX - 256)
+        return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (!W->w_gate || !W->w_gate_up || !W->s_gate_up || !W->w_down || !W->s_down) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!x || !out)) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(W->w_gate) || !aligned16(W->w_gate_up) || !aligned16(W->s_gate_up) || !aligned16(W->w_down) ||
@@ -136,7 +142,7 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 4a gate_up GEMM + SwiGLU -> h (bf16)
-    if ((e = launch_gemm_main(xq, sx, sorted, k, W->w_gate_up, W->s_gate_up, offsets, E, P, 2 * I, H,
+    if ((e = launch_gemm_main(xq, T, sx, sorted, k, W->w_gate_up, 1, W->s_gate_up, offsets, E, P, 2 * I, H,
                               W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
@@ -144,7 +150,7 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     if ((e = launch_quant_rows(h, W8A8_BF16, P, I, I, hq, sh, st)) != hipSuccess || (e = mark()) != hipSuccess)
         return hip_status(e);
     // 4b down GEMM -> y (fp32)
-    if ((e = launch_gemm_main(hq, sh, nullptr, 1, W->w_down, W->s_down, offsets, E, P, H, I, W8A8_EPI_DEQUANT,
+    if ((e = launch_gemm_main(hq, P, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, E, P, H, I, W8A8_EPI_DEQUANT,
                               W8A8_F32, y, gws2, st)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
@@ -214,23 +220,40 @@ int moe_permute(const int32_t *topk_ids, int64_t T, int k, int E, int32_t *offse
         launch_permute(topk_ids, T, k, E, offsets, sorted_pair, pair_pos, ws, (hipStream_t)stream));
 }
 
+size_t w8a8_packed_weights_size(int G, int64_t N, int64_t K)
+{
+    if (G <= 0 || N <= 0 || K <= 0) return 0;
+    return packed_weights_bytes(G, N, K);
+}
+
+int w8a8_pack_weights(const int8_t *B, int G, int64_t N, int64_t K, int8_t *packed, void *stream)
+{
+    if (G <= 0 || N <= 0 || K <= 0 || !B || !packed) return W8A8_ERR_INVALID_ARG;
+    if (N % 16 || K % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(B) || !aligned16(packed)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_pack_weights(B, G, N, K, packed, (hipStream_t)stream));
+}
+
 size_t w8a8_grouped_gemm_workspace_size(int64_t M_total, int64_t N, int G)
 {
     if (M_total < 0 || N <= 0 || G <= 0) return 0;
     return gemm_ws_bytes(M_total, N, G);
 }
 
-int w8a8_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *a_row_gather, int gather_div,
-                      const int8_t *B, const float *b_scales, const int32_t *group_offsets, int G, int64_t M_total,
-                      int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws, size_t ws_bytes,
-                      void *stream)
+int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *a_row_gather,
+                      int gather_div, const int8_t *B, int b_layout, const float *b_scales,
+                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                      int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream)
 {
-    if (M_total < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
+    if (M_total < 0 || A_rows < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
+    if (b_layout != W8A8_B_ROWMAJOR && b_layout != W8A8_B_PACKED) return W8A8_ERR_INVALID_ARG;
     if (epilogue < W8A8_EPI_RAW_I32 || epilogue > W8A8_EPI_DEQUANT_SWIGLU) return W8A8_ERR_INVALID_ARG;
     if (epilogue == W8A8_EPI_RAW_I32 ? out_dtype != W8A8_I32 : !act_dtype_ok(out_dtype))
         return W8A8_ERR_INVALID_ARG;
     if (a_row_gather && gather_div <= 0) return W8A8_ERR_INVALID_ARG;
-    if (K % 16 || N % 16 || (epilogue == W8A8_EPI_DEQUANT_SWIGLU && N % 32)) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (K % 16 || N % 16 || (epilogue == W8A8_EPI_DEQUANT_SWIGLU && N % 64)) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    const int64_t group_bytes = b_layout == W8A8_B_PACKED ? (int64_t)packed_weights_bytes(1, N, K) : N * K;
+    if (A_rows * K > INT32_MAX - 256 || group_bytes > INT32_MAX - 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (!B || !group_offsets || !ws) return W8A8_ERR_INVALID_ARG;
     if (M_total > 0 && (!A || !out)) return W8A8_ERR_INVALID_ARG;
     if (epilogue != W8A8_EPI_RAW_I32 && (!b_scales || (M_total > 0 && !a_scales))) return W8A8_ERR_INVALID_ARG;
@@ -240,8 +263,9 @@ int w8a8_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *a_r
         return W8A8_ERR_ALIGNMENT;
     if (ws_bytes < gemm_ws_bytes(M_total, N, G)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
     if (M_total == 0) return W8A8_OK;
-    return hip_status(launch_grouped_gemm(A, a_scales, a_row_gather, gather_div, B, b_scales, group_offsets, G,
-                                          M_total, N, K, epilogue, out_dtype, out, ws, (hipStream_t)stream));
+    return hip_status(launch_grouped_gemm(A, A_rows, a_scales, a_row_gather, gather_div, B, b_layout, b_scales,
+                                          group_offsets, G, M_total, N, K, epilogue, out_dtype, out, ws,
+                                          (hipStream_t)stream));
 }
 
 int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *pair_pos, int64_t T, int k, int64_t H,

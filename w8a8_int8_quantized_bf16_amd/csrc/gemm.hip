@@ -34,6 +34,8 @@
 //     offsets, so the host never waits for the routing result.
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,8 +44,6 @@ namespace w8a8 {
 namespace {
 constexpr int G_THREADS = 256;
 constexpr int G_BK = 128;          // K bytes per step
-constexpr int G_COLS_PER_WAVE = 64;
-constexpr int G_BLOCK_COLS = 4 * G_COLS_PER_WAVE;
 
 struct GemmArgs {
     const int8_t *A;
@@ -55,9 +55,12 @@ struct GemmArgs {
     const int32_t *offsets;
     int G;
     int64_t M_total, N, K;
+    int64_t A_bytes;              // bytes of A addressable (rows * K)
     void *out;
     const int32_t *tile_prefix;   // [G+1]: first tile of each group; [G] = total tiles
+    const int4 *tiles;            // per launched block: {group, first grouped row, rows, column block}
     int nblocks_n;                // column blocks per group
+    int packed_b;                 // B in the MFMA-fragment packed layout (see w8a8_pack_weights)
 };
 
 template <typename T>
@@ -68,160 +71,245 @@ template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) { *p = (uint16_t)float_to_bf16_bits(v); }
 }  // namespace
 
-// tile_prefix[g] = sum over g' < g of ceil(rows(g') / BM) * nblocks_n
+// tile_prefix[g] = sum over g' < g of ceil(rows(g') / BM) * nblocks_n, and the
+// tile table in dispatch order.  Tiles are numbered group-major, then column
+// block, then row tile; tile v runs as block bid where the blocks of XCD x
+// (bid % 8 == x, the hardware's round-robin placement) take one contiguous
+// range of v, so tiles that share a weight block or an activation block run
+// side by side on one XCD's L2.
 __global__ __launch_bounds__(256) void gemm_tilemap_kernel(const int32_t *__restrict__ offsets, int G, int BM,
-                                                           int nblocks_n, int32_t *__restrict__ tile_prefix)
+                                                           int nblocks_n, int32_t *__restrict__ tile_prefix,
+                                                           int4 *__restrict__ tiles)
 {
     __shared__ int32_t sc[256];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
-    if (tid == 0) carry = 0;
-    __syncthreads();
-    for (int g0 = 0; g0 < G; g0 += 256) {
-        const int g = g0 + tid;
-        int32_t cnt = 0;
-        if (g < G) {
-            const int32_t rows = offsets[g + 1] - offsets[g];
-            cnt = (rows + BM - 1) / BM * nblocks_n;
-        }
-        sc[tid] = cnt;
+    int total = 0;
+    // pass 0: the total tile count; pass 1: prefixes and the table
+    for (int pass = 0; pass < 2; ++pass) {
+        if (tid == 0) carry = 0;
         __syncthreads();
-        for (int d = 1; d < 256; d <<= 1) {
-            const int32_t v = tid >= d ? sc[tid - d] : 0;
+        const int q = total >> 3, r = total & 7;
+        for (int g0 = 0; g0 < G; g0 += 256) {
+            const int g = g0 + tid;
+            int32_t cnt = 0, row_begin = 0, rows_g = 0;
+            if (g < G) {
+                row_begin = offsets[g];
+                rows_g = offsets[g + 1] - row_begin;
+                cnt = (rows_g + BM - 1) / BM * nblocks_n;
+            }
+            sc[tid] = cnt;
             __syncthreads();
-            sc[tid] += v;
+            for (int d = 1; d < 256; d <<= 1) {
+                const int32_t v = tid >= d ? sc[tid - d] : 0;
+                __syncthreads();
+                sc[tid] += v;
+                __syncthreads();
+            }
+            if (pass == 1 && g < G) {
+                const int v0 = carry + sc[tid] - cnt;
+                tile_prefix[g] = v0;
+                const int mt_g = (rows_g + BM - 1) / BM;
+                for (int local = 0; local < cnt; ++local) {
+                    const int v = v0 + local;
+                    const int nb = local / mt_g, mt = local - nb * mt_g;
+                    int x = 7;   // XCD x owns v in [x*q + min(x, r), (x+1)*q + min(x+1, r))
+                    while (x > 0 && v < x * q + (x < r ? x : r)) --x;
+                    const int slot = v - (x * q + (x < r ? x : r));
+                    tiles[slot * 8 + x] = make_int4(g, row_begin + mt * BM, min(BM, rows_g - mt * BM), nb);
+                }
+            }
+            __syncthreads();
+            if (tid == 255) carry += sc[255];
             __syncthreads();
         }
-        if (g < G) tile_prefix[g] = carry + sc[tid] - cnt;
-        __syncthreads();
-        if (tid == 255) carry += sc[255];
-        __syncthreads();
+        total = carry;
     }
-    if (tid == 0) tile_prefix[G] = carry;
+    if (tid == 0) tile_prefix[G] = total;
 }
 
-template <int BM, int EPI, typename OutT, int DEPTH>
+// Packed weight layout: B [G][N][K] int8 re-laid so that one wavefront's
+// MFMA operand fetch is 1 KiB of contiguous memory.  For group g, 32-row block
+// nb and 128-byte K step ks, a 4 KiB chunk at ((g * NB + nb) * KS + ks) * 4096
+// holds, at s * 1024 + l * 16 (sub-step s, lane l), bytes
+// [64 * (l / 32) + 16 * s, +16) of step ks of row 32 * nb + l % 32.  Rows
+// beyond N and bytes beyond K are zero.  NB = ceil(N / 32), KS = ceil(K / 128).
+__global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restrict__ B, int64_t G, int64_t N,
+                                                           int64_t K, int8_t *__restrict__ P)
+{
+    const int64_t NB = (N + 31) / 32, KS = (K + 127) / 128;
+    const int64_t n16 = G * NB * KS * 256;   // 16-byte pieces
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+        const int64_t chunk = i >> 8;
+        const int within = (int)(i & 255);
+        const int s = within >> 6, l = within & 63;
+        const int64_t ks = chunk % KS, nbk = (chunk / KS) % NB, g = chunk / (KS * NB);
+        const int64_t row = nbk * 32 + (l & 31);
+        const int64_t k0 = ks * 128 + 64 * (l >> 5) + 16 * s;
+        v4i v = {0, 0, 0, 0};
+        if (row < N && k0 < K) v = *reinterpret_cast<const v4i *>(B + (g * N + row) * K + k0);
+        *reinterpret_cast<v4i *>(P + i * 16) = v;
+    }
+}
+
+// Buffer-resource loads: an offset at or beyond num_records returns zero
+// without touching memory, which masks ragged rows, column tails and the K
+// tail without branches (so the compiler's wait counters stay exact and the
+// prefetch ring below keeps its loads in flight).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr int OOB = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes)
+{
+    const int n = bytes > 0x7ffffff0LL ? 0x7ffffff0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_bit_cast(v4i, v);
+}
+
+// BM rows x (4 waves x WN fragments of 32 columns); DEPTH K steps of B in flight.
+template <int BM, int WN, int DEPTH, int EPI, typename OutT>
 __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
 {
+    static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH and alternates two LDS buffers");
+    static_assert(EPI != 2 || WN % 2 == 0, "SwiGLU pairs gate and up fragments");
     constexpr int MI = BM / 32;      // 32-row MFMA tiles per wave
-    constexpr int APASS = BM / 32;   // A chunks staged per thread per K step
+    constexpr int APASS = BM / 32;   // 16-byte A chunks staged per thread per K step
+    constexpr int WCOLS = 32 * WN;   // B rows (output columns) per wave
     __shared__ __attribute__((aligned(16))) int8_t As[2][BM * G_BK];
     __shared__ int32_t arow[BM];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ float ascale[BM];
 
-    // ---- which tile
-    const int total = a.tile_prefix[a.G];
+    // ---- which tile (one table load)
     const int bid = blockIdx.x;
-    if (bid >= total) return;
-    const int xq = total >> 3, xr = total & 7, xcd = bid & 7;
-    const int v = xcd * xq + (xcd < xr ? xcd : xr) + (bid >> 3);
-    int lo = 0, hi = a.G;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.tile_prefix[mid] <= v) lo = mid;
-        else hi = mid;
-    }
-    const int g = lo;
-    const int32_t row_begin = a.offsets[g];
-    const int32_t rows_g = a.offsets[g + 1] - row_begin;
-    const int mt_g = (rows_g + BM - 1) / BM;
-    const int local = v - a.tile_prefix[g];
-    const int nb = local / mt_g, mt = local - nb * mt_g;
-    const int64_t row0 = (int64_t)row_begin + (int64_t)mt * BM;
-    const int rows = min(BM, rows_g - mt * BM);
-    const int64_t N = a.N, K = a.K;
+    if (bid >= a.tile_prefix[a.G]) return;
+    const int4 tinfo = a.tiles[bid];
+    const int g = tinfo.x, rows = tinfo.z, nb = tinfo.w;
+    const int64_t row0 = tinfo.y;
+    const int N = (int)a.N, K = (int)a.K;
+    const int nk = (K + G_BK - 1) / G_BK;
 
+    // ---- B rows (output columns) of this lane, one per fragment
+    int col[WN];
+    bool cvalid[WN];
+    if constexpr (EPI == 2) {
+        const int Nh = N >> 1;
+        const int hc0 = nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) + (lane & 31);
+#pragma unroll
+        for (int f = 0; f < WN / 2; ++f) {
+            col[f] = hc0 + 32 * f;
+            col[WN / 2 + f] = Nh + hc0 + 32 * f;
+            cvalid[f] = cvalid[WN / 2 + f] = hc0 + 32 * f < Nh;
+        }
+    } else {
+        const int c0 = nb * (4 * WCOLS) + wave * WCOLS + (lane & 31);
+#pragma unroll
+        for (int f = 0; f < WN; ++f) {
+            col[f] = c0 + 32 * f;
+            cvalid[f] = col[f] < N;
+        }
+    }
+    // B is [N][K] row-major, or packed: per 32-row block and 128-byte K step a
+    // 4 KiB chunk holding, for sub-step s and lane l, the 16 bytes that lane l
+    // feeds to the MFMA (row l%32, bytes 64*(l/32) + 16*s of the step).
+    const int64_t b_bytes = a.packed_b ? (int64_t)((N + 31) / 32) * nk * 4096 : (int64_t)N * K;
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B + (int64_t)g * b_bytes, b_bytes);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
+    const int khalf = 64 * (lane >> 5);
+    int boff[WN];
+#pragma unroll
+    for (int f = 0; f < WN; ++f)
+        boff[f] = !cvalid[f] ? OOB : (a.packed_b ? (col[f] >> 5) * nk * 4096 + lane * 16 : col[f] * K + khalf);
+    const int bstep = a.packed_b ? 4096 : G_BK, bsub = a.packed_b ? 1024 : 16;
+
+    // per-column weight scales, kept in registers for the epilogue
+    float bsc[WN];
+#pragma unroll
+    for (int f = 0; f < WN; ++f) bsc[f] = (EPI != 0 && cvalid[f]) ? a.b_scales[(int64_t)g * N + col[f]] : 0.0f;
+
+    // ---- activation rows of the tile and their scales
     if (tid < BM) {
         int32_t src = -1;
         if (tid < rows) src = a.gather ? a.gather[row0 + tid] / a.gather_div : (int32_t)(row0 + tid);
         arow[tid] = src;
+        ascale[tid] = (EPI != 0 && src >= 0) ? a.a_scales[src] : 0.0f;
     }
-
-    // ---- B rows of this lane
-    const int8_t *brow[2];
-    bool bvalid[2];
-    int64_t col[2];
-    if constexpr (EPI == 2) {
-        const int64_t Nh = N >> 1;
-        const int64_t hc = (int64_t)nb * (G_BLOCK_COLS / 2) + wave * 32 + (lane & 31);
-        col[0] = hc;
-        col[1] = Nh + hc;
-        bvalid[0] = bvalid[1] = hc < Nh;
-    } else {
-        const int64_t c0 = (int64_t)nb * G_BLOCK_COLS + wave * G_COLS_PER_WAVE + (lane & 31);
-        col[0] = c0;
-        col[1] = c0 + 32;
-        bvalid[0] = c0 < N;
-        bvalid[1] = c0 + 32 < N;
-    }
-    const int8_t *Bg = a.B + (int64_t)g * N * K;
-#pragma unroll
-    for (int f = 0; f < 2; ++f) brow[f] = Bg + (bvalid[f] ? col[f] : 0) * K + 64 * (lane >> 5);
-
     __syncthreads();
 
-    // ---- A staging assignment: chunk c of rows (tid/8) + 32j
+    // ---- A staging assignment: 16-byte chunk ac of rows (tid/8) + 32j
     const int ac = tid & 7;
-    const int8_t *asrc[APASS];
-    int arr[APASS];
+    int aoff[APASS], arr[APASS];
 #pragma unroll
     for (int j = 0; j < APASS; ++j) {
         arr[j] = (tid >> 3) + 32 * j;
-        const int32_t s = arow[arr[j]];
-        asrc[j] = s >= 0 ? a.A + (int64_t)s * K + 16 * ac : nullptr;
+        const int32_t sr = arow[arr[j]];
+        aoff[j] = sr >= 0 ? sr * K + 16 * ac : OOB;
     }
 
-    const int nk = (int)((K + G_BK - 1) / G_BK);
-    const v4i zero4 = {0, 0, 0, 0};
-
-    v4i breg[DEPTH][2][4];
-    v4i areg[APASS];
-    v16i acc[MI][2];
+    // Software pipeline over K steps of 128 bytes.  A ring of DEPTH register
+    // slots holds the B fragments of the next DEPTH steps and the A chunks of
+    // the steps after the current one; A(j) sits in slot j % DEPTH from its
+    // load (DEPTH steps ahead) until it is copied into LDS at the end of step
+    // j - 1.  LDS holds two A buffers (current step, next step).
+    v4i breg[DEPTH][WN][4];
+    v4i areg[DEPTH][APASS];
+    v16i acc[MI][WN];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < WN; ++f)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][f][i] = 0;
 
     auto load_b = [&](int slot, int it) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int s = 0; s < 4; ++s) {
+            const int kk = it * G_BK + khalf + 16 * s;
+            const bool kin = a.packed_b ? it < nk : kk < K;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int64_t koff = (int64_t)it * G_BK + 64 * (lane >> 5) + 16 * s;
-                breg[slot][f][s] = (it < nk && bvalid[f] && koff < K)
-                                       ? *reinterpret_cast<const v4i *>(brow[f] + (int64_t)it * G_BK + 16 * s)
-                                       : zero4;
-            }
+            for (int f = 0; f < WN; ++f)
+                breg[slot][f][s] = buf_load16(rB, (kin && boff[f] != OOB) ? boff[f] + it * bstep + s * bsub : OOB);
+        }
     };
-    auto load_a = [&](int it) {
-        const int64_t koff = (int64_t)it * G_BK + 16 * ac;
+    auto load_a = [&](int slot, int it) {
+        const int kk = it * G_BK + 16 * ac;
 #pragma unroll
         for (int j = 0; j < APASS; ++j)
-            areg[j] = (asrc[j] && koff < K) ? *reinterpret_cast<const v4i *>(asrc[j] + (int64_t)it * G_BK) : zero4;
+            areg[slot][j] = buf_load16(rA, (kk < K && aoff[j] != OOB) ? aoff[j] + it * G_BK : OOB);
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int slot, int buf) {
 #pragma unroll
         for (int j = 0; j < APASS; ++j)
-            *reinterpret_cast<v4i *>(&As[buf][arr[j] * G_BK + ((ac ^ (arr[j] & 7)) << 4)]) = areg[j];
+            *reinterpret_cast<v4i *>(&As[buf][arr[j] * G_BK + ((ac ^ (arr[j] & 7)) << 4)]) = areg[slot][j];
     };
 
+    // Prologue, in the loop's own issue order (B, then A) so that the wait
+    // counts at the loop entry match the steady state.
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_a(d, d);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_b(d, d);
-    load_a(0);
-    store_a(0);
+    store_a(0, 0);
+    load_a(0, DEPTH);
     __syncthreads();
 
-    for (int it0 = 0; it0 < nk; it0 += DEPTH) {
+    // The trip count is padded to a multiple of DEPTH; the padding steps issue
+    // only out-of-range (zero, no traffic) loads and skip the MFMAs.  Loads are
+    // never inside a branch, so the compiler counts outstanding loads exactly
+    // and each wait covers only the data it needs.
+    const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
+    for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int it = it0 + d;
             if (it < nk) {
-                const bool more = it + 1 < nk;
-                if (more) load_a(it + 1);
-                const int8_t *Ab = As[it & 1];
+                const int8_t *Ab = As[d & 1];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -230,14 +318,17 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
                         const int ch = 4 * (lane >> 5) + s;
                         const v4i av = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
 #pragma unroll
-                        for (int f = 0; f < 2; ++f)
-                            acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, breg[d][f][s], acc[mi][f], 0, 0, 0);
+                        for (int f = 0; f < WN; ++f)
+                            acc[mi][f] =
+                                __builtin_amdgcn_mfma_i32_32x32x32_i8(av, breg[d][f][s], acc[mi][f], 0, 0, 0);
                     }
                 }
-                load_b(d, it + DEPTH);
-                if (more) store_a((it + 1) & 1);
-                __syncthreads();
             }
+            load_b(d, it + DEPTH);
+            const int dn = (d + 1) % DEPTH;
+            store_a(dn, (d + 1) & 1);     // A(it+1), loaded DEPTH steps ago
+            load_a(dn, it + 1 + DEPTH);
+            __syncthreads();
         }
     }
 
@@ -251,83 +342,103 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
             const int64_t grow = row0 + r;
             if constexpr (EPI == 0) {
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
-                    if (bvalid[f]) reinterpret_cast<int32_t *>(a.out)[grow * N + col[f]] = acc[mi][f][i];
+                for (int f = 0; f < WN; ++f)
+                    if (cvalid[f]) reinterpret_cast<int32_t *>(a.out)[grow * N + col[f]] = acc[mi][f][i];
             } else if constexpr (EPI == 1) {
-                const float sa = a.a_scales[arow[r]];
+                const float sa = ascale[r];
 #pragma unroll
-                for (int f = 0; f < 2; ++f)
-                    if (bvalid[f]) {
-                        const float sb = a.b_scales[(int64_t)g * N + col[f]];
+                for (int f = 0; f < WN; ++f)
+                    if (cvalid[f])
                         store_out<OutT>(reinterpret_cast<OutT *>(a.out) + grow * N + col[f],
-                                        ((float)acc[mi][f][i] * sa) * sb);
-                    }
+                                        ((float)acc[mi][f][i] * sa) * bsc[f]);
             } else {
-                if (bvalid[0]) {
-                    const float sa = a.a_scales[arow[r]];
-                    const float gate = ((float)acc[mi][0][i] * sa) * a.b_scales[(int64_t)g * N + col[0]];
-                    const float up = ((float)acc[mi][1][i] * sa) * a.b_scales[(int64_t)g * N + col[1]];
-                    const float h = gate / (1.0f + expf(-gate)) * up;
-                    store_out<OutT>(reinterpret_cast<OutT *>(a.out) + grow * (N >> 1) + col[0], h);
-                }
+                const float sa = ascale[r];
+#pragma unroll
+                for (int f = 0; f < WN / 2; ++f)
+                    if (cvalid[f]) {
+                        const float gate = ((float)acc[mi][f][i] * sa) * bsc[f];
+                        const float up = ((float)acc[mi][WN / 2 + f][i] * sa) * bsc[WN / 2 + f];
+                        const float h = gate / (1.0f + expf(-gate)) * up;
+                        store_out<OutT>(reinterpret_cast<OutT *>(a.out) + grow * (N >> 1) + col[f], h);
+                    }
             }
         }
     }
 }
 
-size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G)
-{
-    (void)M_total;
-    (void)N;
-    return ((size_t)(G + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
-}
-
 namespace {
-int gemm_bm(int64_t M_total, int G)
+// Tile shapes: decode-like groups (a few rows per expert) use 32-row tiles with
+// a deep B ring; prefill-like groups use taller tiles that reuse each weight
+// byte over more rows.
+struct TileCfg {
+    int BM, WN;
+};
+
+TileCfg gemm_cfg(int64_t M_total, int G)
 {
     const double avg_rows = (double)M_total / (double)G;
-    return avg_rows <= 32.0 ? 32 : (avg_rows <= 64.0 ? 64 : 128);
+    if (avg_rows <= 32.0) return {32, 2};
+    if (avg_rows <= 384.0) return {64, 2};
+    return {128, 4};
 }
 
-int gemm_nblocks(int64_t N, int epilogue)
+// column blocks per group: 4 waves x WN fragments of 32 B rows; with SwiGLU
+// half of them are gate rows and half the matching up rows
+int gemm_nblocks(int64_t N, int epilogue, int WN)
 {
     const int64_t cols = epilogue == 2 ? N / 2 : N;
-    const int64_t per_block = epilogue == 2 ? G_BLOCK_COLS / 2 : G_BLOCK_COLS;
+    const int64_t per_block = epilogue == 2 ? 4 * 32 * WN / 2 : 4 * 32 * WN;
     return (int)((cols + per_block - 1) / per_block);
 }
 
-template <int BM, int DEPTH>
-hipError_t launch_main_bm(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
+int64_t gemm_max_tiles(int64_t M_total, int64_t N, int G)
+{
+    const TileCfg c = gemm_cfg(M_total, G);
+    const int nb = std::max(gemm_nblocks(N, 1, c.WN), gemm_nblocks(N, 2, c.WN));
+    return ((M_total + c.BM - 1) / c.BM + G) * nb;
+}
+
+size_t prefix_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
+
+template <int BM, int WN, int DEPTH>
+hipError_t launch_main_cfg(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
 {
     const int64_t max_tiles = ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
     dim3 grid((unsigned)max_tiles), block(G_THREADS);
     if (epilogue == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, 0, int32_t, DEPTH>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 0, int32_t>), grid, block, 0, st, ga);
     else if (epilogue == 1 && out_dtype == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, 1, uint16_t, DEPTH>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, uint16_t>), grid, block, 0, st, ga);
     else if (epilogue == 1)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, 1, float, DEPTH>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, float>), grid, block, 0, st, ga);
     else if (out_dtype == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, 2, uint16_t, DEPTH>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, uint16_t>), grid, block, 0, st, ga);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, 2, float, DEPTH>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, float>), grid, block, 0, st, ga);
     return hipGetLastError();
 }
 }  // namespace
+
+// workspace: tile prefix [G+1] int32 (256-byte aligned), then the tile table
+size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G)
+{
+    return prefix_bytes(G) + (size_t)gemm_max_tiles(M_total, N, G) * sizeof(int4);
+}
 
 hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
                                hipStream_t st)
 {
     if (M_total == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_tilemap_kernel, dim3(1), dim3(256), 0, st, offsets, G, gemm_bm(M_total, G),
-                       gemm_nblocks(N, epilogue), (int32_t *)ws);
+    const TileCfg c = gemm_cfg(M_total, G);
+    hipLaunchKernelGGL(gemm_tilemap_kernel, dim3(1), dim3(256), 0, st, offsets, G, c.BM,
+                       gemm_nblocks(N, epilogue, c.WN), (int32_t *)ws, (int4 *)((char *)ws + prefix_bytes(G)));
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_main(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
-                            const int8_t *B, const float *b_scales, const int32_t *offsets, int G, int64_t M_total,
-                            int64_t N, int64_t K, int epilogue, int out_dtype, void *out, const void *ws,
-                            hipStream_t st)
+hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                            int gather_div, const int8_t *B, int b_packed, const float *b_scales,
+                            const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                            int out_dtype, void *out, const void *ws, hipStream_t st)
 {
     if (M_total == 0) return hipSuccess;
     GemmArgs ga;
@@ -344,23 +455,36 @@ hipError_t launch_gemm_main(const int8_t *A, const float *a_scales, const int32_
     ga.K = K;
     ga.out = out;
     ga.tile_prefix = (const int32_t *)ws;
-    ga.nblocks_n = gemm_nblocks(N, epilogue);
-    switch (gemm_bm(M_total, G)) {
-    case 32: return launch_main_bm<32, 4>(ga, epilogue, out_dtype, st);
-    case 64: return launch_main_bm<64, 3>(ga, epilogue, out_dtype, st);
-    default: return launch_main_bm<128, 2>(ga, epilogue, out_dtype, st);
-    }
+    ga.tiles = (const int4 *)((const char *)ws + prefix_bytes(G));
+    ga.A_bytes = A_rows * K;
+    ga.packed_b = b_packed;
+    const TileCfg c = gemm_cfg(M_total, G);
+    ga.nblocks_n = gemm_nblocks(N, epilogue, c.WN);
+    if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, epilogue, out_dtype, st);
+    if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, epilogue, out_dtype, st);
+    return launch_main_cfg<128, 4, 2>(ga, epilogue, out_dtype, st);
 }
 
-hipError_t launch_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
-                               const int8_t *B, const float *b_scales, const int32_t *offsets, int G,
-                               int64_t M_total, int64_t N, int64_t K, int epilogue, int out_dtype, void *out,
-                               void *ws, hipStream_t st)
+hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                               int gather_div, const int8_t *B, int b_packed, const float *b_scales,
+                               const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                               int out_dtype, void *out, void *ws, hipStream_t st)
 {
     hipError_t e = launch_gemm_tilemap(offsets, G, M_total, N, epilogue, ws, st);
     if (e != hipSuccess) return e;
-    return launch_gemm_main(A, a_scales, gather, gather_div, B, b_scales, offsets, G, M_total, N, K, epilogue,
-                            out_dtype, out, ws, st);
+    return launch_gemm_main(A, A_rows, a_scales, gather, gather_div, B, b_packed, b_scales, offsets, G, M_total, N,
+                            K, epilogue, out_dtype, out, ws, st);
+}
+
+size_t packed_weights_bytes(int64_t G, int64_t N, int64_t K) { return (size_t)(G * ((N + 31) / 32) * ((K + 127) / 128) * 4096); }
+
+hipError_t launch_pack_weights(const int8_t *B, int64_t G, int64_t N, int64_t K, int8_t *P, hipStream_t st)
+{
+    const int64_t n16 = (int64_t)packed_weights_bytes(G, N, K) / 16;
+    if (n16 == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 65536);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, st, B, G, N, K, P);
+    return hipGetLastError();
 }
 
 }  // namespace w8a8

@@ -20,14 +20,16 @@ size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G);
 // tile map of a grouped GEMM (into ws), then the GEMM itself reading that map
 hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
                                hipStream_t st);
-hipError_t launch_gemm_main(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
-                            const int8_t *B, const float *b_scales, const int32_t *offsets, int G, int64_t M_total,
-                            int64_t N, int64_t K, int epilogue, int out_dtype, void *out, const void *ws,
-                            hipStream_t st);
-hipError_t launch_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
-                               const int8_t *B, const float *b_scales, const int32_t *offsets, int G,
-                               int64_t M_total, int64_t N, int64_t K, int epilogue, int out_dtype, void *out,
-                               void *ws, hipStream_t st);
+hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                            int gather_div, const int8_t *B, int b_packed, const float *b_scales,
+                            const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                            int out_dtype, void *out, const void *ws, hipStream_t st);
+hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                               int gather_div, const int8_t *B, int b_packed, const float *b_scales,
+                               const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                               int out_dtype, void *out, void *ws, hipStream_t st);
+size_t packed_weights_bytes(int64_t G, int64_t N, int64_t K);
+hipError_t launch_pack_weights(const int8_t *B, int64_t G, int64_t N, int64_t K, int8_t *P, hipStream_t st);
 
 hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T,
                           int k, int64_t H, void *out, int out_dtype, hipStream_t st);
