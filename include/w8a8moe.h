@@ -103,6 +103,7 @@ int w8a8_quant_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
  *   topk_ids  device, [T][k] int32, written
  *   topk_w    device, [T][k] fp32, written
  *   logits_out device, [T][E] fp32, written when not NULL
+ * T * H * 4 and E * H * 2 must stay below 2^31 (32-bit byte offsets).
  */
 int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, int64_t H,
                    int E, int k, int renormalize, int32_t *topk_ids, float *topk_w,
@@ -159,7 +160,7 @@ int w8a8_pack_weights(const int8_t *B, int G, int64_t N, int64_t K, int8_t *pack
  *                 group_offsets[G] = M_total (not checked: device memory)
  *   ws            device scratch of at least w8a8_grouped_gemm_workspace_size() bytes
  * out_dtype: W8A8_BF16 or W8A8_F32 (W8A8_I32 with RAW_I32).  K % 16 == 0,
- * N % 16 == 0, N % 64 == 0 for SWIGLU.  A_rows * K and one group of B must stay
+ * N % 16 == 0, N % 64 == 0 for SWIGLU, G <= 4096.  A_rows * K and one group of B must stay
  * below 2^31 bytes (the kernels address them with 32-bit byte offsets); larger
  * shapes return W8A8_ERR_UNSUPPORTED_SHAPE.
  */

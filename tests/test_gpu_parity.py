@@ -183,18 +183,37 @@ def test_route_ties_lower_index_first():
     assert np.allclose(to_host(w), 1.0 / 3.0, atol=1e-7)
 
 
-@pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_30b_decode_T64"])
+@pytest.mark.parametrize("T,H,E,k", [(1, 16, 1, 1), (5, 48, 8, 2), (37, 2048, 63, 8), (9, 64, 64, 64),
+                                     (17, 128, 65, 3), (33, 256, 96, 8), (12, 4096, 128, 8), (7, 80, 200, 11),
+                                     (40, 32, 256, 16)])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_route_shapes(T, H, E, k, xdt):
+    """Expert counts that fill 1..4 slices of 64 (ragged ones included), odd
+    token counts, short and long hidden sizes; bf16 and fp32 activations."""
+    rng = np.random.default_rng(T * 1000 + E)
+    x = rng.standard_t(4, (T, H)).astype(np.float32)
+    xa = synth.f32_to_bf16_bits(x) if xdt == "bf16" else x
+    wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    ids, w, logits = w8.route_topk(to_dev(xa), dev_bf16(wg), k, True, return_logits=True)
+    oids, ow, ologits = oracle.route_topk(xa, wg, k)
+    assert np.array_equal(to_host(logits), ologits)
+    assert np.array_equal(to_host(ids), oids)
+    assert np.abs(to_host(w) - ow).max() <= 2e-6
+
+
+@pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_30b_decode_T64", "moe_235b_zipf_T8192"])
 def test_route_full_size(name):
     cfg = synth.MOE_CONFIGS[name]
     wg = synth.moe_router(cfg)
     x = synth.moe_x(cfg, wg_bits=wg)
     ids, w, logits = w8.route_topk(to_dev(x), dev_bf16(wg), cfg.k, True, return_logits=True)
     t0 = time.time()
-    oids, ow, ologits = oracle.route_topk(x, wg, cfg.k)
-    say("oracle router %s: %.1f s" % (name, time.time() - t0))
-    assert np.array_equal(to_host(logits), ologits)
-    assert np.array_equal(to_host(ids), oids)
-    assert np.abs(to_host(w) - ow).max() <= 2e-6
+    tok = np.arange(cfg.T) if cfg.T <= 4096 else np.sort(np.random.default_rng(4).choice(cfg.T, 2048, replace=False))
+    oids, ow, ologits = oracle.route_topk(x[tok], wg, cfg.k)
+    say("oracle router %s on %d tokens: %.1f s" % (name, len(tok), time.time() - t0))
+    assert np.array_equal(to_host(logits)[tok], ologits)
+    assert np.array_equal(to_host(ids)[tok], oids)
+    assert np.abs(to_host(w)[tok] - ow).max() <= 2e-6
 
 
 # --------------------------------------------------------------- permute ---

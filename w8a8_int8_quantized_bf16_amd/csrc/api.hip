@@ -29,6 +29,8 @@ int check_route(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, i
     if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
     if (E > 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (H % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    // activations and router rows are addressed with 32-bit byte offsets
+    if (T * H * 4 > INT32_MAX - 256 || (int64_t)E * H * 2 > INT32_MAX - 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (T > 0 && (!x || !w_gate || !ids || !w)) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!aligned16(x) || !aligned16(w_gate) || !aligned16(ids) || !aligned16(w) ||
                   (logits && !aligned16(logits))))
@@ -135,10 +137,15 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     //   serves all k experts)
     if ((e = launch_quant_rows(x, x_dtype, T, H, H, xq, sx, st)) != hipSuccess || (e = mark()) != hipSuccess)
         return hip_status(e);
-    // 3 permute, and the tile maps of both grouped GEMMs
-    if ((e = launch_permute(ids, T, k, E, offsets, sorted, pos, perm, st)) != hipSuccess ||
-        (e = launch_gemm_tilemap(offsets, E, P, 2 * I, W8A8_EPI_DEQUANT_SWIGLU, gws1, st)) != hipSuccess ||
-        (e = launch_gemm_tilemap(offsets, E, P, H, W8A8_EPI_DEQUANT, gws2, st)) != hipSuccess ||
+    // 3 permute; its scan also builds the tile tables of both grouped GEMMs
+    TileTableReq req[2];
+    gemm_tile_params(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
+    gemm_tile_params(P, H, E, W8A8_EPI_DEQUANT, &req[1].BM, &req[1].nblocks_n);
+    req[0].prefix = (int32_t *)gws1;
+    req[0].tiles = (int4 *)gemm_tiles_ptr(gws1, E);
+    req[1].prefix = (int32_t *)gws2;
+    req[1].tiles = (int4 *)gemm_tiles_ptr(gws2, E);
+    if ((e = launch_permute(ids, T, k, E, offsets, sorted, pos, perm, st, req, 2)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 4a gate_up GEMM + SwiGLU -> h (bf16)
@@ -246,6 +253,7 @@ int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, co
                       int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream)
 {
     if (M_total < 0 || A_rows < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
+    if (G > 4096) return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (b_layout != W8A8_B_ROWMAJOR && b_layout != W8A8_B_PACKED) return W8A8_ERR_INVALID_ARG;
     if (epilogue < W8A8_EPI_RAW_I32 || epilogue > W8A8_EPI_DEQUANT_SWIGLU) return W8A8_ERR_INVALID_ARG;
     if (epilogue == W8A8_EPI_RAW_I32 ? out_dtype != W8A8_I32 : !act_dtype_ok(out_dtype))

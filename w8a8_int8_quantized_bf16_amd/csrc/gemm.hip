@@ -35,9 +35,11 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "tiles.h"
 
 namespace w8a8 {
 
@@ -64,68 +66,21 @@ struct GemmArgs {
 };
 
 template <typename T>
-__device__ __forceinline__ void store_out(T *p, float v);
+__device__ __forceinline__ T to_out(float v);
 template <>
-__device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
+__device__ __forceinline__ float to_out<float>(float v) { return v; }
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t *p, float v) { *p = (uint16_t)float_to_bf16_bits(v); }
+__device__ __forceinline__ uint16_t to_out<uint16_t>(float v) { return (uint16_t)float_to_bf16_bits(v); }
 }  // namespace
 
-// tile_prefix[g] = sum over g' < g of ceil(rows(g') / BM) * nblocks_n, and the
-// tile table in dispatch order.  Tiles are numbered group-major, then column
-// block, then row tile; tile v runs as block bid where the blocks of XCD x
-// (bid % 8 == x, the hardware's round-robin placement) take one contiguous
-// range of v, so tiles that share a weight block or an activation block run
-// side by side on one XCD's L2.
+// Stand-alone tile map of one grouped GEMM (see tiles.h).
 __global__ __launch_bounds__(256) void gemm_tilemap_kernel(const int32_t *__restrict__ offsets, int G, int BM,
                                                            int nblocks_n, int32_t *__restrict__ tile_prefix,
                                                            int4 *__restrict__ tiles)
 {
+    __shared__ int32_t pre[TILES_MAX_G + 1];
     __shared__ int32_t sc[256];
-    __shared__ int32_t carry;
-    const int tid = threadIdx.x;
-    int total = 0;
-    // pass 0: the total tile count; pass 1: prefixes and the table
-    for (int pass = 0; pass < 2; ++pass) {
-        if (tid == 0) carry = 0;
-        __syncthreads();
-        const int q = total >> 3, r = total & 7;
-        for (int g0 = 0; g0 < G; g0 += 256) {
-            const int g = g0 + tid;
-            int32_t cnt = 0, row_begin = 0, rows_g = 0;
-            if (g < G) {
-                row_begin = offsets[g];
-                rows_g = offsets[g + 1] - row_begin;
-                cnt = (rows_g + BM - 1) / BM * nblocks_n;
-            }
-            sc[tid] = cnt;
-            __syncthreads();
-            for (int d = 1; d < 256; d <<= 1) {
-                const int32_t v = tid >= d ? sc[tid - d] : 0;
-                __syncthreads();
-                sc[tid] += v;
-                __syncthreads();
-            }
-            if (pass == 1 && g < G) {
-                const int v0 = carry + sc[tid] - cnt;
-                tile_prefix[g] = v0;
-                const int mt_g = (rows_g + BM - 1) / BM;
-                for (int local = 0; local < cnt; ++local) {
-                    const int v = v0 + local;
-                    const int nb = local / mt_g, mt = local - nb * mt_g;
-                    int x = 7;   // XCD x owns v in [x*q + min(x, r), (x+1)*q + min(x+1, r))
-                    while (x > 0 && v < x * q + (x < r ? x : r)) --x;
-                    const int slot = v - (x * q + (x < r ? x : r));
-                    tiles[slot * 8 + x] = make_int4(g, row_begin + mt * BM, min(BM, rows_g - mt * BM), nb);
-                }
-            }
-            __syncthreads();
-            if (tid == 255) carry += sc[255];
-            __syncthreads();
-        }
-        total = carry;
-    }
-    if (tid == 0) tile_prefix[G] = total;
+    build_tile_table(offsets, G, BM, nblocks_n, tile_prefix, tiles, pre, sc);
 }
 
 // Packed weight layout: B [G][N][K] int8 re-laid so that one wavefront's
@@ -157,7 +112,7 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restr
 // tail without branches (so the compiler's wait counters stay exact and the
 // prefetch ring below keeps its loads in flight).
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-constexpr int OOB = 0x7fffffff;
+constexpr uint32_t OOB_BASE = 0xC0000000u;   // above any resource size (< 2^31)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes)
 {
@@ -165,14 +120,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
 }
 
-__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, int off)
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return __builtin_bit_cast(v4i, v);
 }
 
 // BM rows x (4 waves x WN fragments of 32 columns); DEPTH K steps of B in flight.
-template <int BM, int WN, int DEPTH, int EPI, typename OutT>
+template <int BM, int WN, int DEPTH, int EPI, typename OutT, bool PACKED>
 __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
 {
     static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH and alternates two LDS buffers");
@@ -180,7 +135,10 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
     constexpr int MI = BM / 32;      // 32-row MFMA tiles per wave
     constexpr int APASS = BM / 32;   // 16-byte A chunks staged per thread per K step
     constexpr int WCOLS = 32 * WN;   // B rows (output columns) per wave
-    __shared__ __attribute__((aligned(16))) int8_t As[2][BM * G_BK];
+    // LDS: the two A buffers during the K loop, the epilogue staging after it
+    constexpr int SMEM = (2 * BM * G_BK > 4 * 32 * (64 * 4 + 16)) ? 2 * BM * G_BK : 4 * 32 * (64 * 4 + 16);
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    int8_t(*As)[BM * G_BK] = reinterpret_cast<int8_t(*)[BM * G_BK]>(smem);
     __shared__ int32_t arow[BM];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -217,16 +175,21 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
     }
     // B is [N][K] row-major, or packed: per 32-row block and 128-byte K step a
     // 4 KiB chunk holding, for sub-step s and lane l, the 16 bytes that lane l
-    // feeds to the MFMA (row l%32, bytes 64*(l/32) + 16*s of the step).
-    const int64_t b_bytes = a.packed_b ? (int64_t)((N + 31) / 32) * nk * 4096 : (int64_t)N * K;
+    // feeds to the MFMA (row l%32, bytes 64*(l/32) + 16*s of the step), zero
+    // padded in N and K.  Offsets are unsigned: an invalid lane starts at
+    // OOB_BASE, above every resource size, and stays out of range as steps are
+    // added, so its loads return zeros.
+    const int64_t b_bytes = PACKED ? (int64_t)((N + 31) / 32) * nk * 4096 : (int64_t)N * K;
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B + (int64_t)g * b_bytes, b_bytes);
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
     const int khalf = 64 * (lane >> 5);
-    int boff[WN];
+    uint32_t boff[WN];
 #pragma unroll
     for (int f = 0; f < WN; ++f)
-        boff[f] = !cvalid[f] ? OOB : (a.packed_b ? (col[f] >> 5) * nk * 4096 + lane * 16 : col[f] * K + khalf);
-    const int bstep = a.packed_b ? 4096 : G_BK, bsub = a.packed_b ? 1024 : 16;
+        boff[f] = !cvalid[f] ? OOB_BASE
+                             : (PACKED ? (uint32_t)((col[f] >> 5) * nk * 4096 + lane * 16)
+                                       : (uint32_t)(col[f] * K + khalf));
+    constexpr uint32_t BSTEP = PACKED ? 4096 : G_BK, BSUB = PACKED ? 1024 : 16;
 
     // per-column weight scales, kept in registers for the epilogue
     float bsc[WN];
@@ -244,12 +207,13 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
 
     // ---- A staging assignment: 16-byte chunk ac of rows (tid/8) + 32j
     const int ac = tid & 7;
-    int aoff[APASS], arr[APASS];
+    uint32_t aoff[APASS];
+    int arr[APASS];
 #pragma unroll
     for (int j = 0; j < APASS; ++j) {
         arr[j] = (tid >> 3) + 32 * j;
         const int32_t sr = arow[arr[j]];
-        aoff[j] = sr >= 0 ? sr * K + 16 * ac : OOB;
+        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + 16 * ac) : OOB_BASE;
     }
 
     // Software pipeline over K steps of 128 bytes.  A ring of DEPTH register
@@ -267,21 +231,26 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][f][i] = 0;
 
+    // Steps at or beyond nk (the padding of the trip count) load nothing: the
+    // step index is wave-uniform, so that choice is a scalar select.  With
+    // packed (zero-padded) weights the K tail needs no masking of A: whatever
+    // A bytes lie beyond K meet zero weights.
     auto load_b = [&](int slot, int it) {
+        const bool live = it < nk;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int kk = it * G_BK + khalf + 16 * s;
-            const bool kin = a.packed_b ? it < nk : kk < K;
+            const bool kin = PACKED || it * G_BK + khalf + 16 * s < K;
 #pragma unroll
             for (int f = 0; f < WN; ++f)
-                breg[slot][f][s] = buf_load16(rB, (kin && boff[f] != OOB) ? boff[f] + it * bstep + s * bsub : OOB);
+                breg[slot][f][s] = buf_load16(rB, (live && kin) ? boff[f] + it * BSTEP + s * BSUB : OOB_BASE);
         }
     };
     auto load_a = [&](int slot, int it) {
-        const int kk = it * G_BK + 16 * ac;
+        const bool live = it < nk;
+        const bool kin = PACKED || it * G_BK + 16 * ac < K;
 #pragma unroll
         for (int j = 0; j < APASS; ++j)
-            areg[slot][j] = buf_load16(rA, (kk < K && aoff[j] != OOB) ? aoff[j] + it * G_BK : OOB);
+            areg[slot][j] = buf_load16(rA, (live && kin) ? aoff[j] + it * G_BK : OOB_BASE);
     };
     auto store_a = [&](int slot, int buf) {
 #pragma unroll
@@ -332,36 +301,59 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
         }
     }
 
-    // ---- epilogue
+    // ---- epilogue.  Each wave stages its results through its own LDS region,
+    // one 32-row block and at most two 32-column fragments at a time, and
+    // writes them back as 16-byte row segments (the MFMA layout gives a lane
+    // one column of many rows; a store wants many columns of one row).
+    using ET = std::conditional_t<EPI == 0, int32_t, OutT>;
+    constexpr int NOF = EPI == 2 ? WN / 2 : WN;          // output fragments of 32 columns
+    constexpr int FP = NOF < 2 ? NOF : 2;                 // fragments per pass
+    constexpr int ROWB = 32 * FP * (int)sizeof(ET) + 16;  // padded staging row, bytes
+    constexpr int CPR = 32 * FP * (int)sizeof(ET) / 16;   // 16-byte chunks per staged row
+    static_assert(4 * 32 * ROWB <= (int)sizeof(smem), "epilogue staging exceeds the LDS buffer");
+    unsigned char *stage = smem + wave * 32 * ROWB;
+    const int ldo = EPI == 2 ? (N >> 1) : N;
+    // first output column of this wave's fragment f is ocol0 + 32 f
+    const int ocol0 = EPI == 2 ? nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) : nb * (4 * WCOLS) + wave * WCOLS;
+    __syncthreads();   // every wave is done with the A buffers
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r >= rows) continue;
-            const int64_t grow = row0 + r;
-            if constexpr (EPI == 0) {
+        for (int f0 = 0; f0 < NOF; f0 += FP) {
 #pragma unroll
-                for (int f = 0; f < WN; ++f)
-                    if (cvalid[f]) reinterpret_cast<int32_t *>(a.out)[grow * N + col[f]] = acc[mi][f][i];
-            } else if constexpr (EPI == 1) {
-                const float sa = ascale[r];
+            for (int i = 0; i < 16; ++i) {
+                const int rl = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                const float sa = ascale[mi * 32 + rl];
 #pragma unroll
-                for (int f = 0; f < WN; ++f)
-                    if (cvalid[f])
-                        store_out<OutT>(reinterpret_cast<OutT *>(a.out) + grow * N + col[f],
-                                        ((float)acc[mi][f][i] * sa) * bsc[f]);
-            } else {
-                const float sa = ascale[r];
-#pragma unroll
-                for (int f = 0; f < WN / 2; ++f)
-                    if (cvalid[f]) {
+                for (int ff = 0; ff < FP; ++ff) {
+                    const int f = f0 + ff;
+                    ET val;
+                    if constexpr (EPI == 0) {
+                        val = acc[mi][f][i];
+                    } else if constexpr (EPI == 1) {
+                        val = to_out<OutT>(((float)acc[mi][f][i] * sa) * bsc[f]);
+                    } else {
                         const float gate = ((float)acc[mi][f][i] * sa) * bsc[f];
-                        const float up = ((float)acc[mi][WN / 2 + f][i] * sa) * bsc[WN / 2 + f];
-                        const float h = gate / (1.0f + expf(-gate)) * up;
-                        store_out<OutT>(reinterpret_cast<OutT *>(a.out) + grow * (N >> 1) + col[f], h);
+                        const float up = ((float)acc[mi][NOF + f][i] * sa) * bsc[NOF + f];
+                        // silu(g) = g / (1 + e^-g); the result is rounded to bf16 (or
+                        // compared within a tolerance), so the hardware exp and
+                        // reciprocal are accurate enough
+                        val = to_out<OutT>(gate * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)));
                     }
+                    *reinterpret_cast<ET *>(stage + rl * ROWB + (32 * ff + (lane & 31)) * (int)sizeof(ET)) = val;
+                }
             }
+            __syncthreads();
+#pragma unroll
+            for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                const int rl = idx / CPR, ch = idx % CPR;
+                const int r = mi * 32 + rl;
+                const int ocol = ocol0 + 32 * f0 + ch * (16 / (int)sizeof(ET));
+                if (r < rows && ocol < ldo)
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<ET *>(a.out) + (row0 + r) * ldo + ocol) =
+                        *reinterpret_cast<const uint4 *>(stage + rl * ROWB + ch * 16);
+            }
+            __syncthreads();
         }
     }
 }
@@ -400,22 +392,29 @@ int64_t gemm_max_tiles(int64_t M_total, int64_t N, int G)
 
 size_t prefix_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
 
-template <int BM, int WN, int DEPTH>
-hipError_t launch_main_cfg(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
+template <int BM, int WN, int DEPTH, bool PACKED>
+hipError_t launch_main_layout(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
 {
     const int64_t max_tiles = ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
     dim3 grid((unsigned)max_tiles), block(G_THREADS);
     if (epilogue == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 0, int32_t>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 0, int32_t, PACKED>), grid, block, 0, st, ga);
     else if (epilogue == 1 && out_dtype == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, uint16_t>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, uint16_t, PACKED>), grid, block, 0, st, ga);
     else if (epilogue == 1)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, float>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, float, PACKED>), grid, block, 0, st, ga);
     else if (out_dtype == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, uint16_t>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, uint16_t, PACKED>), grid, block, 0, st, ga);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, float>), grid, block, 0, st, ga);
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, float, PACKED>), grid, block, 0, st, ga);
     return hipGetLastError();
+}
+
+template <int BM, int WN, int DEPTH>
+hipError_t launch_main_cfg(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
+{
+    return ga.packed_b ? launch_main_layout<BM, WN, DEPTH, true>(ga, epilogue, out_dtype, st)
+                       : launch_main_layout<BM, WN, DEPTH, false>(ga, epilogue, out_dtype, st);
 }
 }  // namespace
 
@@ -424,6 +423,15 @@ size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G)
 {
     return prefix_bytes(G) + (size_t)gemm_max_tiles(M_total, N, G) * sizeof(int4);
 }
+
+void gemm_tile_params(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n)
+{
+    const TileCfg c = gemm_cfg(M_total, G);
+    *BM = c.BM;
+    *nblocks_n = gemm_nblocks(N, epilogue, c.WN);
+}
+
+void *gemm_tiles_ptr(void *ws, int G) { return (char *)ws + prefix_bytes(G); }
 
 hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
                                hipStream_t st)

@@ -13,10 +13,19 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, int64
                              int k, int renormalize, int32_t *ids, float *w, float *logits, hipStream_t st);
 
 size_t permute_ws_bytes(int64_t T, int k, int E);
+// Tile tables the permutation builds for grouped GEMMs over its groups.
+struct TileTableReq {
+    int BM, nblocks_n;
+    int32_t *prefix;   // [E+1]
+    int4 *tiles;
+};
 hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets,
-                          int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t st);
+                          int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t st,
+                          const TileTableReq *req = nullptr, int nreq = 0);
 
 size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G);
+void gemm_tile_params(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n);
+void *gemm_tiles_ptr(void *ws, int G);
 // tile map of a grouped GEMM (into ws), then the GEMM itself reading that map
 hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
                                hipStream_t st);

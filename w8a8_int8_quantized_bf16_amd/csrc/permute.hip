@@ -12,6 +12,7 @@
 // The result depends only on the ids: no atomics decide any position.
 #include "device_common.h"
 #include "launch.h"
+#include "tiles.h"
 
 namespace w8a8 {
 
@@ -41,12 +42,20 @@ __global__ __launch_bounds__(PM_THREADS) void permute_count_kernel(const int32_t
 }
 
 // chunk_counts[c][e] -> exclusive prefix over c (in place); offsets = exclusive
-// prefix over e of the totals.
+// prefix over e of the totals; then the tile tables of up to two grouped GEMMs
+// over these groups.
+struct ScanTables {
+    TileTableReq r[2];
+    int n;
+};
+
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__restrict__ chunk_counts,
                                                                   int64_t nchunks, int E, int64_t P,
-                                                                  int32_t *__restrict__ offsets)
+                                                                  int32_t *__restrict__ offsets, ScanTables tt)
 {
     __shared__ int32_t tot[PM_MAX_E];
+    __shared__ int32_t pre[PM_MAX_E + 1];
+    __shared__ int32_t off_l[PM_MAX_E + 1];
     const int tid = threadIdx.x;
     int32_t run = 0;
     if (tid < E) {
@@ -65,8 +74,19 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__res
         tot[tid] += v;
         __syncthreads();
     }
-    if (tid < E) offsets[tid] = tot[tid] - run;
-    if (tid == 0) offsets[E] = (int32_t)P;
+    if (tid < E) {
+        offsets[tid] = tot[tid] - run;
+        off_l[tid] = tot[tid] - run;
+    }
+    if (tid == 0) {
+        offsets[E] = (int32_t)P;
+        off_l[E] = (int32_t)P;
+    }
+    __syncthreads();
+    for (int j = 0; j < tt.n; ++j) {
+        build_tile_table(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, tt.r[j].prefix, tt.r[j].tiles, pre, tot);
+        __syncthreads();
+    }
 }
 
 __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
@@ -113,15 +133,18 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32
 size_t permute_ws_bytes(int64_t T, int k, int E) { return (size_t)pm_chunks(T * k) * (size_t)E * sizeof(int32_t); }
 
 hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets, int32_t *sorted_pair,
-                          int32_t *pair_pos, void *ws, hipStream_t st)
+                          int32_t *pair_pos, void *ws, hipStream_t st, const TileTableReq *req, int nreq)
 {
+    ScanTables tt;
+    tt.n = nreq < 2 ? nreq : 2;
+    for (int j = 0; j < tt.n; ++j) tt.r[j] = req[j];
     const int64_t P = T * k;
     const int64_t nch = pm_chunks(P);
     int32_t *cc = (int32_t *)ws;
     // with P == 0 only the scan runs: it writes all-zero offsets
     if (nch > 0)
         hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc);
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets, tt);
     if (nch > 0)
         hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc,
                            offsets, sorted_pair, pair_pos);

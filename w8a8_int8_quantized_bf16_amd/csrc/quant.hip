@@ -9,8 +9,10 @@
 //
 // One 64-lane wavefront per row.  Each lane owns 8 consecutive elements of
 // every 512-element stripe (16-byte loads of bf16, 32 bytes of fp32), so a
-// wave reads 1 KiB of bf16 per instruction, fully coalesced.  The row is
-// read twice (max pass, then code pass); the second read hits L2.
+// wave reads 1 KiB of bf16 per instruction, fully coalesced.  Rows of up to
+// 512 * MAXC elements are read once and held in registers (all loads issued
+// before the max reduction); longer rows are read twice (max pass, then code
+// pass; the second read hits L2).
 #include "device_common.h"
 #include "launch.h"
 
@@ -57,17 +59,67 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T *__restrict__ x
     }
 }
 
+template <typename T, int MAXC>
+__global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T *__restrict__ x, int64_t rows, int64_t cols,
+                                                             int64_t ld, int8_t *__restrict__ q,
+                                                             float *__restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const T *xr = x + r * ld;
+    float v[MAXC][8];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int64_t col = (int64_t)lane * 8 + 512 * c;
+        if (col < cols) load8_f32(xr + col, v[c]);
+        else
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+    amax = wave_max(amax);
+    const float s = amax / 127.0f;
+    if (lane == 0) scales[r] = s;
+    int8_t *qr = q + r * cols;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int64_t col = (int64_t)lane * 8 + 512 * c;
+        if (col >= cols) break;
+        uint2 packed = make_uint2(0u, 0u);
+        if (s != 0.0f) {
+            packed.x = quant_code(v[c][0], s) | (quant_code(v[c][1], s) << 8) | (quant_code(v[c][2], s) << 16) |
+                       (quant_code(v[c][3], s) << 24);
+            packed.y = quant_code(v[c][4], s) | (quant_code(v[c][5], s) << 8) | (quant_code(v[c][6], s) << 16) |
+                       (quant_code(v[c][7], s) << 24);
+        }
+        *reinterpret_cast<uint2 *>(qr + col) = packed;
+    }
+}
+
+template <typename T>
+static void launch_typed(const T *x, int64_t rows, int64_t cols, int64_t ld, int8_t *q, float *scales,
+                         hipStream_t st)
+{
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const int64_t nc = (cols + 511) / 512;
+    if (nc <= 1) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 1>), grid, block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 2) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 2>), grid, block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 4) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 4>), grid, block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 8) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8>), grid, block, 0, st, x, rows, cols, ld, q, scales);
+    else hipLaunchKernelGGL(quant_rows_kernel<T>, grid, block, 0, st, x, rows, cols, ld, q, scales);
+}
+
 hipError_t launch_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld, int8_t *q,
                              float *scales, hipStream_t st)
 {
     if (rows == 0) return hipSuccess;
-    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    if (dtype == 0)
-        hipLaunchKernelGGL(quant_rows_kernel<uint16_t>, grid, block, 0, st, (const uint16_t *)x, rows, cols, ld,
-                           q, scales);
-    else
-        hipLaunchKernelGGL(quant_rows_kernel<float>, grid, block, 0, st, (const float *)x, rows, cols, ld, q,
-                           scales);
+    if (dtype == 0) launch_typed((const uint16_t *)x, rows, cols, ld, q, scales, st);
+    else launch_typed((const float *)x, rows, cols, ld, q, scales, st);
     return hipGetLastError();
 }
 

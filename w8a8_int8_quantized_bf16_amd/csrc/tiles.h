@@ -1,0 +1,65 @@
+// Device-side construction of a grouped GEMM's tile table (shared by the
+// permutation kernel, which builds the layer's tables right after the group
+// offsets are known, and by the stand-alone tile-map kernel).
+#pragma once
+#include "device_common.h"
+
+namespace w8a8 {
+
+constexpr int TILES_MAX_G = 4096;   // groups a tile table supports (LDS prefix)
+
+// One 256-thread block.  Tiles are numbered group-major, then column block,
+// then row tile (v = prefix[g] + nb * mt_g + mt); tile v runs as block bid,
+// where the blocks of XCD x (bid % 8 == x, the hardware's round-robin
+// placement) take one contiguous range of v, so tiles that share a weight
+// block or an activation block run side by side on one XCD's L2.
+//   offsets  [G+1] group row offsets (global)
+//   pre      LDS scratch of TILES_MAX_G + 1 ints;  sc LDS scratch of 256 ints
+//   prefix   [G+1] written: first tile of each group, prefix[G] = total
+//   tiles    [total] written: {group, first grouped row, rows, column block}
+__device__ inline void build_tile_table(const int32_t *__restrict__ offsets, int G, int BM, int nbn,
+                                        int32_t *__restrict__ prefix, int4 *__restrict__ tiles, int32_t *pre,
+                                        int32_t *sc)
+{
+    const int tid = threadIdx.x;
+    int carry = 0;
+    for (int g0 = 0; g0 < G; g0 += 256) {
+        const int g = g0 + tid;
+        const int32_t cnt = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM * nbn : 0;
+        sc[tid] = cnt;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int32_t v = tid >= d ? sc[tid - d] : 0;
+            __syncthreads();
+            sc[tid] += v;
+            __syncthreads();
+        }
+        if (g < G) pre[g] = carry + sc[tid] - cnt;
+        carry += sc[255];
+        __syncthreads();
+    }
+    const int total = carry;
+    if (tid == 0) pre[G] = total;
+    __syncthreads();
+    for (int g = tid; g <= G; g += 256) prefix[g] = pre[g];
+    const int q = total >> 3, r = total & 7;
+    for (int v = tid; v < total; v += 256) {
+        int lo = 0, hi = G;   // largest g with pre[g] <= v
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pre[mid] <= v) lo = mid;
+            else hi = mid;
+        }
+        const int g = lo;
+        const int32_t row_begin = offsets[g], rows_g = offsets[g + 1] - row_begin;
+        const int mt_g = (rows_g + BM - 1) / BM;
+        const int local = v - pre[g];
+        const int nb = local / mt_g, mt = local - nb * mt_g;
+        int x = 7;   // XCD x owns v in [x*q + min(x, r), (x+1)*q + min(x+1, r))
+        while (x > 0 && v < x * q + (x < r ? x : r)) --x;
+        const int slot = v - (x * q + (x < r ? x : r));
+        tiles[slot * 8 + x] = make_int4(g, row_begin + mt * BM, min(BM, rows_g - mt * BM), nb);
+    }
+}
+
+}  // namespace w8a8
