@@ -13,8 +13,7 @@
 // the chain).  In the vector kernel a block holds 16 tokens x all E (<= 256)
 // experts; thread (wave w, lane l) owns tokens 4w..4w+3 and experts l, l+64,
 // l+128, l+192, with x and W_g staged through LDS in 32-wide slices of the
-// hidden dimension.  Top-k is a wave argmax repeated k times (ties -> lower
-// expert index).
+// hidden dimension.
 #include <math.h>
 
 #include "device_common.h"
@@ -35,67 +34,149 @@ template <>
 __device__ __forceinline__ float load_elem<float>(const float *p) { return *p; }
 
 // Top-k of one token whose E (<= 256) scores sit in one wavefront, lane l
-// holding experts l + 64 j in l4[j]: k rounds of a wave argmax (ties -> lower
-// expert index), then softmax weights of the selected experts.
+// holding experts l + 64 j in l4[j].
+//   1. Scores map to order-preserving 32-bit keys (-0 read as +0, so equal
+//      scores give equal keys); absent experts get key 0, below every score.
+//   2. The k-th largest key is found bit by bit from the top: a candidate is
+//      kept when at least k keys reach it, counted with wave ballots (no
+//      cross-lane data movement, so each of the 32 steps is a few cycles).
+//   3. The selection is every key above that threshold plus, among keys equal
+//      to it, the lowest expert indices up to k in total.
+//   4. The k selected (key, expert) pairs are compacted into the wave's LDS
+//      scratch.  Every lane then reads all k pairs: a pair's output position
+//      is the number of pairs that order before it (larger score, or equal
+//      score and lower index), the largest score is their maximum, and the
+//      renormalised softmax denominator is their sum of exponentials.
+// Weights are softmax probabilities of the selected experts, optionally
+// renormalised over the k (then only the k scores enter).  scr: this wave's
+// LDS scratch of 2 x 256 words.
+__device__ __forceinline__ uint32_t score_key(float v, bool valid)
+{
+    const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    return !valid ? 0u : ((u >> 31) ? ~u : (u | 0x80000000u));
+}
+
+// inverse of score_key for a present expert (the score's exact bits)
+__device__ __forceinline__ float key_score(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+template <int S>   // 64-expert slots per lane (E <= 64 S)
 __device__ __forceinline__ void select_topk(const float l4[4], int64_t t, int E, int k, int renorm,
                                             int32_t *__restrict__ ids, float *__restrict__ wout,
-                                            float *__restrict__ logits_out)
+                                            float *__restrict__ logits_out, uint32_t *scr)
 {
     const int lane = threadIdx.x & 63;
-    bool taken[4];
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t key[S];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        taken[j] = !(lane + 64 * j < E);
-        if (logits_out && !taken[j]) logits_out[t * E + lane + 64 * j] = l4[j];
+    for (int j = 0; j < S; ++j) {
+        const bool valid = lane + 64 * j < E;
+        key[j] = score_key(l4[j], valid);
+        if (valid && logits_out) logits_out[t * E + lane + 64 * j] = l4[j];
     }
-    float m = 0.0f;
-    float mysel[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // score of slot lane + 64q
-    for (int s = 0; s < k; ++s) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
+    // k-th largest key (straight-line: 32 ballot rounds)
+    uint32_t thr = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + 64 * j;
-            if (!taken[j] && (l4[j] > bv || (l4[j] == bv && e < bi))) {
-                bv = l4[j];
-                bi = e;
-            }
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = thr | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < S; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+        thr = cnt >= k ? cand : thr;
+    }
+    // selection and compaction (expert order: slot j major, lane minor)
+    int above = 0;
+#pragma unroll
+    for (int j = 0; j < S; ++j) above += __popcll(__ballot(key[j] > thr));
+    const int need_eq = k - above;
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const uint64_t eq = __ballot(key[j] == thr);
+        const bool sel = key[j] > thr || (key[j] == thr && eq_before + __popcll(eq & lt) < need_eq);
+        const uint64_t sm = __ballot(sel);
+        if (sel) {
+            const int slot = sel_before + __popcll(sm & lt);
+            scr[slot] = key[j];
+            scr[256 + slot] = lane + 64 * j;
         }
+        eq_before += __popcll(eq);
+        sel_before += __popcll(sm);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (k <= 8) {
+        // the (at most 8) pairs in registers, unused slots ordered last
+        uint32_t kq[8];
+        int eqi[8];
+        const uint4 ka = *reinterpret_cast<const uint4 *>(scr), kb = *reinterpret_cast<const uint4 *>(scr + 4);
+        const uint4 ia = *reinterpret_cast<const uint4 *>(scr + 256), ib = *reinterpret_cast<const uint4 *>(scr + 260);
+        kq[0] = ka.x; kq[1] = ka.y; kq[2] = ka.z; kq[3] = ka.w; kq[4] = kb.x; kq[5] = kb.y; kq[6] = kb.z; kq[7] = kb.w;
+        eqi[0] = ia.x; eqi[1] = ia.y; eqi[2] = ia.z; eqi[3] = ia.w; eqi[4] = ib.x; eqi[5] = ib.y; eqi[6] = ib.z; eqi[7] = ib.w;
 #pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) {
-            const float ov = __shfl_xor(bv, msk, 64);
-            const int oi = __shfl_xor(bi, msk, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
+        for (int q = 0; q < 8; ++q)
+            if (q >= k) kq[q] = 0u;
+        uint32_t kmax = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) kmax = max(kmax, kq[q]);
+        const float mx = key_score(kmax);
+        float denom = 0.0f;
+        if (renorm) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (q < k) denom += expf(key_score(kq[q]) - mx);
+        } else {
+            float zsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+                if (lane + 64 * j < E) zsum += expf(l4[j] - mx);
+            denom = wave_sum(zsum);
         }
+        if (lane < k) {
+            uint32_t ki = kq[0];
+            int ei = eqi[0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + 64 * j == bi) taken[j] = true;
-        if (lane == 0) ids[t * k + s] = bi;
+            for (int q = 1; q < 8; ++q)
+                if (lane == q) { ki = kq[q]; ei = eqi[q]; }
+            int pos = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (lane == (s & 63) && q == (s >> 6)) mysel[q] = bv;
-        if (s == 0) m = bv;
+            for (int q = 0; q < 8; ++q)
+                pos += (q < k && (kq[q] > ki || (kq[q] == ki && eqi[q] < ei))) ? 1 : 0;
+            ids[t * k + pos] = ei;
+            wout[t * k + pos] = expf(key_score(ki) - mx) / denom;
+        }
+    } else {
+        uint32_t kmax = 0;
+        for (int q = 0; q < k; ++q) kmax = max(kmax, scr[q]);
+        const float mx = key_score(kmax);
+        float denom = 0.0f;
+        if (renorm) {
+            for (int q = 0; q < k; ++q) denom += expf(key_score(scr[q]) - mx);
+        } else {
+            float zsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+                if (lane + 64 * j < E) zsum += expf(l4[j] - mx);
+            denom = wave_sum(zsum);
+        }
+        for (int i = lane; i < k; i += 64) {
+            const uint32_t ki = scr[i];
+            const int ei = (int)scr[256 + i];
+            int pos = 0;
+            for (int q = 0; q < k; ++q) {
+                const uint32_t kq = scr[q];
+                pos += (kq > ki || (kq == ki && (int)scr[256 + q] < ei)) ? 1 : 0;
+            }
+            ids[t * k + pos] = ei;
+            wout[t * k + pos] = expf(key_score(ki) - mx) / denom;
+        }
     }
-    // softmax over all E scores; weights of the selected, optionally renormalised
-    float zsum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j < E) zsum += expf(l4[j] - m);
-    zsum = wave_sum(zsum);
-    float z[4], ssum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        z[q] = (lane + 64 * q < k) ? expf(mysel[q] - m) : 0.0f;
-        ssum += z[q];
-    }
-    ssum = wave_sum(ssum);
-    const float denom = renorm ? ssum : zsum;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (lane + 64 * q < k) wout[t * k + lane + 64 * q] = z[q] / denom;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <typename T>
@@ -106,6 +187,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x
 {
     __shared__ float xs[RT_TOK][RT_KC];
     __shared__ float wsl[256][RT_KC + 1];
+    __shared__ __attribute__((aligned(16))) uint32_t tk_scr[4][512];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
 
@@ -147,43 +229,49 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x
     for (int i = 0; i < 4; ++i) {
         const int64_t t = t0 + wave * 4 + i;
         if (t >= T_) break;
-        select_topk(acc[i], t, E, k, renorm, ids, wout, logits_out);
+        select_topk<4>(acc[i], t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
     }
 }
 
 // bf16 activations: the score chains run on the matrix cores.  With bf16
 // operands every product is exact in fp32, so one v_mfma_f32_4x4x1_16b step
 // (c += a * b, one rounding) is exactly one fused multiply-add of the chain;
-// the instruction keeps 16 independent 4x4 outer products.  A wavefront owns
-// 4 tokens x 64 experts: lane l feeds token l % 4 and expert 64 s + l, and
-// after the H steps holds the scores of tokens 0..3 for expert 64 s + l.
-// A block of S x TG wavefronts (S slices of 64 experts, TG groups of 4
-// tokens) stages 64-wide hidden slices of W_g and x through LDS (rows padded
-// to 144 bytes: the 16-byte reads of 8 consecutive rows hit distinct banks),
-// three slices in flight.  Zero padding beyond H or E adds +0 * 0 terms,
-// which leave every chain unchanged.
+// the instruction keeps 16 independent 4x4 outer products: lane l feeds
+// token l % 4 and expert 64 s + l, and after the H steps holds the scores of
+// tokens 0..3 for expert 64 s + l.
+//
+// A block is 8 wavefronts (two per SIMD, so that one wave's staging work and
+// LDS waits overlap the other's matrix work); each owns one slice of 64
+// experts (S slices) and one chunk of 4 tokens (8 / S chunks per block).
+// x and W_g are staged through LDS in 32-wide
+// hidden slices, widened to fp32 once when staged (so the inner loop is LDS
+// reads and MFMAs only), rows padded to 144 bytes (the 16-byte reads of 16
+// consecutive rows hit distinct bank groups), three slices in flight in
+// registers.  Zero padding beyond H or E adds +0 * 0 terms, which leave every
+// chain unchanged.
 namespace {
-constexpr int RM_KC = 64;                  // hidden indices per staged slice
-constexpr int RM_ROW = RM_KC * 2 + 16;     // padded LDS row, bytes
+constexpr int RM_KC = 32;                  // hidden indices per staged slice
+constexpr int RM_ROW = RM_KC * 4 + 16;     // padded fp32 LDS row, bytes
 constexpr int RM_STAGES = 3;               // slices in flight (registers)
 }
 
-template <int S>   // 64-expert slices (E <= 64 S)
+template <int S>   // 64-expert slices (E <= 64 S), S in {1, 2, 4}
 __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
                                                          int E, int k, int renorm, int32_t *__restrict__ ids,
                                                          float *__restrict__ wout, float *__restrict__ logits_out)
 {
-    constexpr int TG = S == 1 ? 8 : (S == 2 ? 4 : 2);   // token groups of 4 per block
-    constexpr int NT = 64 * S * TG;                       // threads
-    constexpr int WROWS = 64 * S, XROWS = 4 * TG;
-    constexpr int WPIECES = WROWS * 8, XPIECES = XROWS * 8;        // 16-byte pieces per slice
+    constexpr int NT = 512;                                    // threads
+    constexpr int TC = 8 / S;                                  // 4-token chunks per block
+    constexpr int WROWS = 64 * S, XROWS = 4 * TC;
+    constexpr int WPIECES = WROWS * 4, XPIECES = XROWS * 4;   // 16-byte bf16 pieces per slice
     constexpr int WPT = (WPIECES + NT - 1) / NT, XPT = (XPIECES + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) unsigned char wl[2][WROWS * RM_ROW];
     __shared__ __attribute__((aligned(16))) unsigned char xl[2][XROWS * RM_ROW];
     __shared__ float lg[XROWS][WROWS + 1];
+    __shared__ __attribute__((aligned(16))) uint32_t tk_scr[8][512];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tg = wave / S, sl = wave % S;
+    const int sl = wave % S, ch = wave / S;
     const int64_t tb = (int64_t)blockIdx.x * XROWS;
     const int nsl = (int)((H + RM_KC - 1) / RM_KC);
 
@@ -192,99 +280,112 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, 0x7ffffff0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, 0x7ffffff0, 0x00020000);
-    // staging assignment: piece p = row * 8 + c (16 bytes, hidden 8c..8c+7 of the slice)
+    // staging assignment: piece p = row * 4 + c holds hidden 8c..8c+7 of the slice
     int woff[WPT], xoff[XPT];
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
-        const int p = tid + j * NT, row = p >> 3, c = p & 7;
+        const int p = tid + j * NT, row = p >> 2, c = p & 3;
         woff[j] = (p < WPIECES && row < E) ? (int)((int64_t)row * H * 2) + 16 * c : 0x7fffffff;
     }
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-        const int p = tid + j * NT, row = p >> 3, c = p & 7;
+        const int p = tid + j * NT, row = p >> 2, c = p & 3;
         xoff[j] = (p < XPIECES && tb + row < T_) ? (int)((tb + row) * H * 2) + 16 * c : 0x7fffffff;
     }
     uint4 wr[RM_STAGES][WPT], xr[RM_STAGES][XPT];
     auto load = [&](int st, int slc) {
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
-            const int p = tid + j * NT, c = p & 7;
+            const int c = (tid + j * NT) & 3;
             const bool ok = woff[j] != 0x7fffffff && slc * RM_KC + 8 * c < H;
             wr[st][j] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? woff[j] + slc * RM_KC * 2 : 0x7fffffff, 0, 0));
         }
 #pragma unroll
         for (int j = 0; j < XPT; ++j) {
-            const int p = tid + j * NT, c = p & 7;
+            const int c = (tid + j * NT) & 3;
             const bool ok = xoff[j] != 0x7fffffff && slc * RM_KC + 8 * c < H;
             xr[st][j] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xoff[j] + slc * RM_KC * 2 : 0x7fffffff, 0, 0));
         }
     };
-    auto store = [&](int st, int buf) {
-#pragma unroll
-        for (int j = 0; j < WPT; ++j) {
-            const int p = tid + j * NT;
-            if (p < WPIECES) *reinterpret_cast<uint4 *>(&wl[buf][(p >> 3) * RM_ROW + 16 * (p & 7)]) = wr[st][j];
-        }
-#pragma unroll
-        for (int j = 0; j < XPT; ++j) {
-            const int p = tid + j * NT;
-            if (p < XPIECES) *reinterpret_cast<uint4 *>(&xl[buf][(p >> 3) * RM_ROW + 16 * (p & 7)]) = xr[st][j];
+    // widen 8 bf16 to fp32 (exact) into LDS row `row`, hidden 8c..8c+7
+    auto put = [&](unsigned char *base, int p, const uint4 &v) {
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        uint4 lo, hi;
+        lo.x = u[0] << 16; lo.y = u[0] & 0xffff0000u; lo.z = u[1] << 16; lo.w = u[1] & 0xffff0000u;
+        hi.x = u[2] << 16; hi.y = u[2] & 0xffff0000u; hi.z = u[3] << 16; hi.w = u[3] & 0xffff0000u;
+        unsigned char *d = base + (p >> 2) * RM_ROW + 32 * (p & 3);
+        *reinterpret_cast<uint4 *>(d) = lo;
+        *reinterpret_cast<uint4 *>(d + 16) = hi;
+    };
+    // staging work of one slice: WPT pieces of W_g, then XPT of x
+    constexpr int NITEMS = WPT + XPT;
+    auto stage_item = [&](int item, int st, int buf) {
+        if (item < WPT) {
+            const int p = tid + item * NT;
+            if (p < WPIECES) put(wl[buf], p, wr[st][item]);
+        } else {
+            const int p = tid + (item - WPT) * NT;
+            if (p < XPIECES) put(xl[buf], p, xr[st][item - WPT]);
         }
     };
 
 #pragma unroll
     for (int st = 0; st < RM_STAGES; ++st) load(st, st);
-    store(0, 0);
+#pragma unroll
+    for (int it = 0; it < NITEMS; ++it) stage_item(it, 0, 0);
     load(0, RM_STAGES);
     __syncthreads();
 
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const unsigned char *wrow0 = &wl[0][(sl * 64 + lane) * RM_ROW];
-    const unsigned char *xrow0 = &xl[0][(tg * 4 + (lane & 3)) * RM_ROW];
+    const unsigned char *xrow0 = &xl[0][(ch * 4 + (lane & 3)) * RM_ROW];
     const int nsl_pad = (nsl + RM_STAGES - 1) / RM_STAGES * RM_STAGES;
     for (int s0 = 0; s0 < nsl_pad; s0 += RM_STAGES) {
 #pragma unroll
         for (int d = 0; d < RM_STAGES; ++d) {
             const int slc = s0 + d;
             const int buf = slc & 1;
+            const int dn = (d + 1) % RM_STAGES;   // register slot of slice slc+1
             if (slc < nsl) {
                 const unsigned char *wrow = wrow0 + buf * (WROWS * RM_ROW);
                 const unsigned char *xrow = xrow0 + buf * (XROWS * RM_ROW);
+                // operands of the next 4 hidden indices are read while the
+                // current ones feed the chain
+                v4f wv = *reinterpret_cast<const v4f *>(wrow);
+                v4f xa = *reinterpret_cast<const v4f *>(xrow);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const uint4 wv = *reinterpret_cast<const uint4 *>(wrow + 16 * c);
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(xrow + 16 * c);
-                    const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-                    const uint32_t x4[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(x4[j] << 16),
-                                                                __uint_as_float(w4[j] << 16), acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_4x4x1f32(__uint_as_float(x4[j] & 0xffff0000u),
-                                                                __uint_as_float(w4[j] & 0xffff0000u), acc, 0, 0, 0);
+                for (int c = 0; c < RM_KC / 4; ++c) {
+                    v4f wn = wv, xan = xa;
+                    if (c + 1 < RM_KC / 4) {
+                        wn = *reinterpret_cast<const v4f *>(wrow + 16 * (c + 1));
+                        xan = *reinterpret_cast<const v4f *>(xrow + 16 * (c + 1));
                     }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[j], wv[j], acc, 0, 0, 0);
+                    wv = wn;
+                    xa = xan;
                 }
             }
-            const int dn = (d + 1) % RM_STAGES;
-            store(dn, (slc + 1) & 1);            // slice slc+1, loaded RM_STAGES slices ago
+            // slice slc+1 (loaded RM_STAGES slices ago) into the other buffer
+#pragma unroll
+            for (int it = 0; it < NITEMS; ++it) stage_item(it, dn, (slc + 1) & 1);
             load(dn, slc + 1 + RM_STAGES);
             __syncthreads();
         }
     }
-    // lane l, value i: score of token tb + 4 tg + i for expert 64 sl + l
+    // lane l, value i: score of token 4 ch + i for expert 64 sl + l
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[tg * 4 + i][sl * 64 + lane] = acc[i];
+    for (int i = 0; i < 4; ++i) lg[ch * 4 + i][sl * 64 + lane] = acc[i];
     __syncthreads();
-    constexpr int NW = S * TG;
-    for (int tt = wave; tt < XROWS; tt += NW) {
+    for (int tt = wave; tt < XROWS; tt += 8) {
         const int64_t t = tb + tt;
         if (t >= T_) break;
         float l4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? lg[tt][lane + 64 * j] : 0.0f;
-        select_topk(l4, t, E, k, renorm, ids, wout, logits_out);
+        select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
     }
 }
 
@@ -293,14 +394,12 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, int64
 {
     if (T == 0) return hipSuccess;
     if (dtype == 0) {
-        const int S = (E + 63) / 64;
-        const int TG = S == 1 ? 8 : (S == 2 ? 4 : 2);
-        dim3 g((unsigned)((T + 4 * TG - 1) / (4 * TG))), b(64 * S * TG);
+        const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
+        dim3 g((unsigned)((T + 32 / S - 1) / (32 / S))), b(512);
         const uint16_t *xb = (const uint16_t *)x;
         switch (S) {
         case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
         case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
-        case 3: hipLaunchKernelGGL(route_mfma_kernel<3>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
         default: hipLaunchKernelGGL(route_mfma_kernel<4>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
         }
         return hipGetLastError();
