@@ -73,14 +73,19 @@ template <>
 __device__ __forceinline__ uint16_t to_out<uint16_t>(float v) { return (uint16_t)float_to_bf16_bits(v); }
 }  // namespace
 
-// Stand-alone tile map of one grouped GEMM (see tiles.h).
+// Stand-alone tile map of one grouped GEMM (see tiles.h): every block forms
+// the tile prefix from the offsets, block 0 stores it, and the blocks share
+// the descriptor writes.
 __global__ __launch_bounds__(256) void gemm_tilemap_kernel(const int32_t *__restrict__ offsets, int G, int BM,
                                                            int nblocks_n, int32_t *__restrict__ tile_prefix,
                                                            int4 *__restrict__ tiles)
 {
     __shared__ int32_t pre[TILES_MAX_G + 1];
     __shared__ int32_t sc[256];
-    build_tile_table(offsets, G, BM, nblocks_n, tile_prefix, tiles, pre, sc);
+    const int total = tile_table_prefix(offsets, G, BM, nblocks_n, pre, sc);
+    if (blockIdx.x == 0)
+        for (int g = threadIdx.x; g <= G; g += 256) tile_prefix[g] = pre[g];
+    tile_fill(offsets, G, BM, nblocks_n, pre, total, tiles, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
 }
 
 // Packed weight layout: B [G][N][K] int8 re-laid so that one wavefront's
@@ -438,7 +443,8 @@ hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, i
 {
     if (M_total == 0) return hipSuccess;
     const TileCfg c = gemm_cfg(M_total, G);
-    hipLaunchKernelGGL(gemm_tilemap_kernel, dim3(1), dim3(256), 0, st, offsets, G, c.BM,
+    const int64_t blocks = std::min<int64_t>((gemm_max_tiles(M_total, N, G) + 255) / 256, 64);
+    hipLaunchKernelGGL(gemm_tilemap_kernel, dim3((unsigned)blocks), dim3(256), 0, st, offsets, G, c.BM,
                        gemm_nblocks(N, epilogue, c.WN), (int32_t *)ws, (int4 *)((char *)ws + prefix_bytes(G)));
     return hipGetLastError();
 }

@@ -3,12 +3,13 @@
 // packed grouped matmul over the experts).
 //
 // A deterministic, stable counting sort of the P = T*k pair ids by expert:
-//   1. count:   one block per chunk of 2048 pairs -> per-chunk histograms
+//   1. count:   one block per chunk of 512 pairs -> per-chunk histograms
 //   2. scan:    one block; per expert an exclusive scan over the chunks, then
 //               an exclusive scan over experts -> offsets[E+1]
 //   3. scatter: one block per chunk; pairs are ranked in pair order, 256 at a
 //               time: equal experts inside a wavefront are matched with eight
-//               ballots (one per bit of the id), waves are ordered through LDS
+//               ballots (one per bit of the id), waves are ordered through LDS.
+//               The same blocks first write the grouped GEMMs' tile tables.
 // The result depends only on the ids: no atomics decide any position.
 #include "device_common.h"
 #include "launch.h"
@@ -18,7 +19,7 @@ namespace w8a8 {
 
 namespace {
 constexpr int PM_THREADS = 256;
-constexpr int PM_PER_THREAD = 8;
+constexpr int PM_PER_THREAD = 2;
 constexpr int PM_CHUNK = PM_THREADS * PM_PER_THREAD;   // pairs per chunk
 constexpr int PM_MAX_E = 256;
 
@@ -42,24 +43,27 @@ __global__ __launch_bounds__(PM_THREADS) void permute_count_kernel(const int32_t
 }
 
 // chunk_counts[c][e] -> exclusive prefix over c (in place); offsets = exclusive
-// prefix over e of the totals; then the tile tables of up to two grouped GEMMs
-// over these groups.
-struct ScanTables {
-    TileTableReq r[2];
-    int n;
-};
-
+// prefix over e of the totals.
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__restrict__ chunk_counts,
                                                                   int64_t nchunks, int E, int64_t P,
-                                                                  int32_t *__restrict__ offsets, ScanTables tt)
+                                                                  int32_t *__restrict__ offsets)
 {
     __shared__ int32_t tot[PM_MAX_E];
-    __shared__ int32_t pre[PM_MAX_E + 1];
-    __shared__ int32_t off_l[PM_MAX_E + 1];
     const int tid = threadIdx.x;
     int32_t run = 0;
     if (tid < E) {
-        for (int64_t c = 0; c < nchunks; ++c) {
+        int64_t c = 0;
+        for (; c + 8 <= nchunks; c += 8) {   // eight independent loads in flight
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = chunk_counts[(c + u) * E + tid];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                chunk_counts[(c + u) * E + tid] = run;
+                run += v[u];
+            }
+        }
+        for (; c < nchunks; ++c) {
             const int32_t v = chunk_counts[c * E + tid];
             chunk_counts[c * E + tid] = run;
             run += v;
@@ -74,31 +78,44 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__res
         tot[tid] += v;
         __syncthreads();
     }
-    if (tid < E) {
-        offsets[tid] = tot[tid] - run;
-        off_l[tid] = tot[tid] - run;
-    }
-    if (tid == 0) {
-        offsets[E] = (int32_t)P;
-        off_l[E] = (int32_t)P;
-    }
-    __syncthreads();
-    for (int j = 0; j < tt.n; ++j) {
-        build_tile_table(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, tt.r[j].prefix, tt.r[j].tiles, pre, tot);
-        __syncthreads();
-    }
+    if (tid < E) offsets[tid] = tot[tid] - run;
+    if (tid == 0) offsets[E] = (int32_t)P;
 }
+
+// The tile tables of up to two grouped GEMMs over the expert groups: every
+// block forms the tile prefixes from the offsets, block 0 stores them, and the
+// blocks of the scatter grid share the descriptor writes.
+struct ScanTables {
+    TileTableReq r[2];
+    int n;
+};
 
 __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
                                                                      int E, const int32_t *__restrict__ chunk_base,
                                                                      const int32_t *__restrict__ offsets,
                                                                      int32_t *__restrict__ sorted_pair,
-                                                                     int32_t *__restrict__ pair_pos)
+                                                                     int32_t *__restrict__ pair_pos, ScanTables tt)
 {
     __shared__ int32_t base[PM_MAX_E];     // next free row of each expert inside this chunk
     __shared__ int32_t wcnt[4][PM_MAX_E];  // per-wave counts of the current round
+    __shared__ int32_t off_l[PM_MAX_E + 1];
+    __shared__ int32_t pre[PM_MAX_E + 1];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (tid < E) base[tid] = offsets[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
+
+    // ---- tile tables
+    for (int g = tid; g <= E; g += PM_THREADS) off_l[g] = offsets[g];
+    __syncthreads();
+    for (int j = 0; j < tt.n; ++j) {
+        const int total = tile_table_prefix(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, &wcnt[0][0]);
+        if (blockIdx.x == 0)
+            for (int g = tid; g <= E; g += PM_THREADS) tt.r[j].prefix[g] = pre[g];
+        tile_fill(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, total, tt.r[j].tiles,
+                  blockIdx.x * PM_THREADS + tid, gridDim.x * PM_THREADS);
+        __syncthreads();
+    }
+
+    // ---- scatter
+    if (tid < E) base[tid] = off_l[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int round = 0; round < PM_PER_THREAD; ++round) {
 #pragma unroll
@@ -141,13 +158,14 @@ hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *
     const int64_t P = T * k;
     const int64_t nch = pm_chunks(P);
     int32_t *cc = (int32_t *)ws;
-    // with P == 0 only the scan runs: it writes all-zero offsets
+    // with P == 0 only the scan runs: it writes all-zero offsets (and no tile
+    // table is needed: a GEMM over zero rows launches nothing)
     if (nch > 0)
         hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc);
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets, tt);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets);
     if (nch > 0)
         hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc,
-                           offsets, sorted_pair, pair_pos);
+                           offsets, sorted_pair, pair_pos, tt);
     return hipGetLastError();
 }
 

@@ -8,18 +8,17 @@ namespace w8a8 {
 
 constexpr int TILES_MAX_G = 4096;   // groups a tile table supports (LDS prefix)
 
-// One 256-thread block.  Tiles are numbered group-major, then column block,
-// then row tile (v = prefix[g] + nb * mt_g + mt); tile v runs as block bid,
+// Tiles are numbered group-major, then column block, then row tile
+// (v = prefix[g] + nb * mt_g + mt), where mt_g = ceil(rows_g / BM) and there
+// are nbn column blocks per group.  A launched block v runs tile tiles[v'],
 // where the blocks of XCD x (bid % 8 == x, the hardware's round-robin
 // placement) take one contiguous range of v, so tiles that share a weight
 // block or an activation block run side by side on one XCD's L2.
-//   offsets  [G+1] group row offsets (global)
-//   pre      LDS scratch of TILES_MAX_G + 1 ints;  sc LDS scratch of 256 ints
-//   prefix   [G+1] written: first tile of each group, prefix[G] = total
-//   tiles    [total] written: {group, first grouped row, rows, column block}
-__device__ inline void build_tile_table(const int32_t *__restrict__ offsets, int G, int BM, int nbn,
-                                        int32_t *__restrict__ prefix, int4 *__restrict__ tiles, int32_t *pre,
-                                        int32_t *sc)
+
+// Exclusive prefix of the tile counts over the groups into pre[0..G] (LDS);
+// returns the total.  Called by all 256 threads of a block; sc is LDS scratch
+// of 256 ints.  offsets may be in LDS or global memory.
+__device__ inline int tile_table_prefix(const int32_t *offsets, int G, int BM, int nbn, int32_t *pre, int32_t *sc)
 {
     const int tid = threadIdx.x;
     int carry = 0;
@@ -38,12 +37,19 @@ __device__ inline void build_tile_table(const int32_t *__restrict__ offsets, int
         carry += sc[255];
         __syncthreads();
     }
-    const int total = carry;
-    if (tid == 0) pre[G] = total;
+    if (tid == 0) pre[G] = carry;
     __syncthreads();
-    for (int g = tid; g <= G; g += 256) prefix[g] = pre[g];
+    return carry;
+}
+
+// Writes the descriptors {group, first grouped row, rows, column block} of
+// the tiles v = first, first + stride, ... below total, each at its dispatch
+// slot (see above).
+__device__ inline void tile_fill(const int32_t *offsets, int G, int BM, int nbn, const int32_t *pre, int total,
+                                 int4 *__restrict__ tiles, int first, int stride)
+{
     const int q = total >> 3, r = total & 7;
-    for (int v = tid; v < total; v += 256) {
+    for (int v = first; v < total; v += stride) {
         int lo = 0, hi = G;   // largest g with pre[g] <= v
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
