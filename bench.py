@@ -76,6 +76,54 @@ def traffic_for(kernel, workload):
     return rec["bytes_per_launch"]
 
 
+def copy_probe(mib):
+    """Plain device-to-device copies of a known size: the reference that
+    scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+
+
+def counter_kib(csv_path, kernel_prefix, counter):
+    """Mean per-dispatch value of a rocprofv3 --pmc counter over the dispatches
+    whose kernel name starts with kernel_prefix."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Kernel_Name"].startswith(kernel_prefix) and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit("no %s dispatches of %s in %s" % (counter, kernel_prefix, csv_path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(args):
+    """profiles/traffic_<stage>_<workload>.json from four rocprofv3 --pmc
+    counter files: FETCH_SIZE and WRITE_SIZE of the bench run, and of the copy
+    probe (whose true bytes scale the counters)."""
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.traffic
+    stage, kernel, source = args.traffic_kernel
+    n = args.copy_mib << 20
+    cf, _ = counter_kib(cfetch_csv, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
+    cw, _ = counter_kib(cwrite_csv, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
+    f, nf = counter_kib(fetch_csv, kernel, "FETCH_SIZE")
+    w, nw = counter_kib(write_csv, kernel, "WRITE_SIZE")
+    sf, sw = n / (cf * 1024.0), n / (cw * 1024.0)
+    rec = {"stage": stage, "kernel": kernel, "workload": args.workload, "source": source,
+           "source_sha256": hashlib.sha256(open(os.path.join(ROOT, "w8a8_int8_quantized_bf16_amd", "csrc", source),
+                                                "rb").read()).hexdigest(),
+           "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w, "dispatches": [nf, nw],
+           "copy_probe_bytes": n, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": sf, "write_scale": sw,
+           "bytes_per_launch": f * 1024.0 * sf + w * 1024.0 * sw}
+    out = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (stage, args.workload))
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(case, target_s):
     """The CPU oracle, as is, on a bounded sample of the workload's tokens."""
     import numpy as np
@@ -117,7 +165,21 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<stage>_<workload>.json from rocprofv3 counter files and exit")
+    ap.add_argument("--traffic-kernel", nargs=3, metavar=("STAGE", "KERNEL_PREFIX", "SOURCE"),
+                    default=["gate_up_gemm", "void w8a8::grouped_gemm_kernel<64, 2, 2, 2, unsigned short, true>",
+                             "gemm.hip"])
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args)
+        return
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

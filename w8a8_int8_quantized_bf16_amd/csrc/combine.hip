@@ -4,13 +4,15 @@
 // "Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer, section 3.1).
 //
 // One block per token; each thread owns 8 consecutive columns (16-byte bf16
-// loads), accumulates the k slots in fp32 in slot order and rounds once.
+// loads), accumulates the k slots in fp32 in slot order and rounds once.  For
+// k <= 8 the k rows' columns are all loaded before the sum starts, so the k
+// reads are in flight together rather than one after another.
 #include "device_common.h"
 #include "launch.h"
 
 namespace w8a8 {
 
-template <typename YT, typename OT>
+template <typename YT, typename OT, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y, const float *__restrict__ w,
                                                       const int32_t *__restrict__ pair_pos, int k, int64_t H,
                                                       OT *__restrict__ out)
@@ -20,35 +22,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y, 
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const float wj = w[t * k + j];
-            const int64_t row = pair_pos[t * k + j];
-            float v[8];
-            load8_f32(y + row * H + c, v);
+        if constexpr (KMAX > 0) {
+            float v[KMAX][8];
+            float wj[KMAX];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+            for (int j = 0; j < KMAX; ++j) {
+                if (j < k) {
+                    wj[j] = w[t * k + j];
+                    load8_f32(y + (int64_t)pair_pos[t * k + j] * H + c, v[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j)
+                if (j < k)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], v[j][i], acc[i]);
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const float wj = w[t * k + j];
+                const int64_t row = pair_pos[t * k + j];
+                float v[8];
+                load8_f32(y + row * H + c, v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+            }
         }
         store8(out + t * H + c, acc);
     }
+}
+
+template <typename YT, typename OT>
+static void launch_typed(const YT *y, const float *w, const int32_t *pair_pos, int64_t T, int k, int64_t H, OT *out,
+                         hipStream_t st)
+{
+    dim3 grid((unsigned)T), block(256);
+    if (k <= 8) hipLaunchKernelGGL((combine_kernel<YT, OT, 8>), grid, block, 0, st, y, w, pair_pos, k, H, out);
+    else hipLaunchKernelGGL((combine_kernel<YT, OT, 0>), grid, block, 0, st, y, w, pair_pos, k, H, out);
 }
 
 hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T, int k,
                           int64_t H, void *out, int out_dtype, hipStream_t st)
 {
     if (T == 0) return hipSuccess;
-    dim3 grid((unsigned)T), block(256);
     if (y_dtype == 0 && out_dtype == 0)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t>), grid, block, 0, st, (const uint16_t *)y, w,
-                           pair_pos, k, H, (uint16_t *)out);
+        launch_typed((const uint16_t *)y, w, pair_pos, T, k, H, (uint16_t *)out, st);
     else if (y_dtype == 0)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, block, 0, st, (const uint16_t *)y, w, pair_pos,
-                           k, H, (float *)out);
+        launch_typed((const uint16_t *)y, w, pair_pos, T, k, H, (float *)out, st);
     else if (out_dtype == 0)
-        hipLaunchKernelGGL((combine_kernel<float, uint16_t>), grid, block, 0, st, (const float *)y, w, pair_pos, k,
-                           H, (uint16_t *)out);
+        launch_typed((const float *)y, w, pair_pos, T, k, H, (uint16_t *)out, st);
     else
-        hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, st, (const float *)y, w, pair_pos, k, H,
-                           (float *)out);
+        launch_typed((const float *)y, w, pair_pos, T, k, H, (float *)out, st);
     return hipGetLastError();
 }
 
