@@ -240,15 +240,16 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
     // step index is wave-uniform, so that choice is a scalar select.  With
     // packed (zero-padded) weights the K tail needs no masking of A: whatever
     // A bytes lie beyond K meet zero weights.
-    auto load_b = [&](int slot, int it) {
+    auto load_b_sub = [&](int slot, int it, int s) {
         const bool live = it < nk;
+        const bool kin = PACKED || it * G_BK + khalf + 16 * s < K;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const bool kin = PACKED || it * G_BK + khalf + 16 * s < K;
+        for (int f = 0; f < WN; ++f)
+            breg[slot][f][s] = buf_load16(rB, (live && kin) ? boff[f] + it * BSTEP + s * BSUB : OOB_BASE);
+    };
+    auto load_b = [&](int slot, int it) {
 #pragma unroll
-            for (int f = 0; f < WN; ++f)
-                breg[slot][f][s] = buf_load16(rB, (live && kin) ? boff[f] + it * BSTEP + s * BSUB : OOB_BASE);
-        }
+        for (int s = 0; s < 4; ++s) load_b_sub(slot, it, s);
     };
     auto load_a = [&](int slot, int it) {
         const bool live = it < nk;
@@ -274,34 +275,45 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
     __syncthreads();
 
     // The trip count is padded to a multiple of DEPTH; the padding steps issue
-    // only out-of-range (zero, no traffic) loads and skip the MFMAs.  Loads are
-    // never inside a branch, so the compiler counts outstanding loads exactly
-    // and each wait covers only the data it needs.
+    // only out-of-range (zero, no traffic) loads.  Loads are never inside a
+    // branch, so the compiler counts outstanding loads exactly and each wait
+    // covers only the data it needs.
     const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
     for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             const int it = it0 + d;
-            if (it < nk) {
-                const int8_t *Ab = As[d & 1];
+            // Padding steps (it >= nk) multiply zeros: their A rows and B
+            // fragments were loaded out of range.  Each sub-step's B registers
+            // are refilled with step it + DEPTH as soon as its MFMAs are
+            // issued, so the weight loads are spread through the step.
+            const int8_t *Ab = As[d & 1];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < 4; ++s) {
 #pragma unroll
-                    for (int mi = 0; mi < MI; ++mi) {
-                        const int r = mi * 32 + (lane & 31);
-                        const int ch = 4 * (lane >> 5) + s;
-                        const v4i av = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int r = mi * 32 + (lane & 31);
+                    const int ch = 4 * (lane >> 5) + s;
+                    const v4i av = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
 #pragma unroll
-                        for (int f = 0; f < WN; ++f)
-                            acc[mi][f] =
-                                __builtin_amdgcn_mfma_i32_32x32x32_i8(av, breg[d][f][s], acc[mi][f], 0, 0, 0);
-                    }
+                    for (int f = 0; f < WN; ++f)
+                        acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, breg[d][f][s], acc[mi][f], 0, 0, 0);
                 }
+                load_b_sub(d, it + DEPTH, s);
             }
-            load_b(d, it + DEPTH);
             const int dn = (d + 1) % DEPTH;
             store_a(dn, (d + 1) & 1);     // A(it+1), loaded DEPTH steps ago
             load_a(dn, it + 1 + DEPTH);
+            // issue order of the step: per sub-step the A fragment reads, its
+            // MFMAs, then the refill of its B registers; then the A staging
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);        // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);   // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);        // B loads
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, APASS, 0);         // LDS stores
+            __builtin_amdgcn_sched_group_barrier(0x020, APASS, 0);         // A loads
             __syncthreads();
         }
     }
@@ -364,9 +376,10 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
 }
 
 namespace {
-// Tile shapes: decode-like groups (a few rows per expert) use 32-row tiles with
-// a deep B ring; prefill-like groups use taller tiles that reuse each weight
-// byte over more rows.
+// Tile shapes: decode-like groups (a few rows per expert) use 32 x 256 tiles,
+// mid-sized groups 64 x 256, prefill-sized groups (over 192 rows per group on
+// average) 128 x 512 tiles that reuse each weight byte over more rows and each
+// activation row over more columns.
 struct TileCfg {
     int BM, WN;
 };
@@ -375,7 +388,7 @@ TileCfg gemm_cfg(int64_t M_total, int G)
 {
     const double avg_rows = (double)M_total / (double)G;
     if (avg_rows <= 32.0) return {32, 2};
-    if (avg_rows <= 384.0) return {64, 2};
+    if (avg_rows <= 192.0) return {64, 2};
     return {128, 4};
 }
 
