@@ -228,10 +228,13 @@ int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype,
  * call with the same (W, T, x_dtype, ws): ids [T][k] i32, w [T][k] f32,
  * xq [T][H] i8, sx [T] f32, offsets [E+1] i32, sorted_pair / pair_pos [T*k] i32,
  * h [T*k][I] bf16, hq [T*k][I] i8, sh [T*k] f32,
- * y [T*k][H] fp32.  Index order of `ptrs`: as listed.  For inspection
- * and stage-by-stage checks.
+ * y [T*k][H] i16 and y_exp [T*k][ceil(H/64)] i8: the down projection's
+ * output (grouped row order) as 16-bit fixed point, value = y * 2^y_exp of its
+ * row and 64-column segment, the exponent chosen so that the segment's largest
+ * magnitude lies in [2^13, 2^14) (absolute error at most 2^-14 of it).
+ * Index order of `ptrs`: as listed.  For inspection and stage-by-stage checks.
  */
-#define W8A8_LAYER_INTERMEDIATES 11
+#define W8A8_LAYER_INTERMEDIATES 12
 int w8a8_moe_layer_intermediates(const w8a8_moe_weights *W, int64_t T, int x_dtype, void *ws,
                                  void **ptrs);
 

@@ -133,8 +133,8 @@ def test_layer_rejects_and_sizes_workspace(L):
     s = None
     W = _weights()
     need = L.w8a8_moe_layer_workspace_size(ctypes.byref(W), 16, 1)
-    # ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y (fp32), permute, gemm map
-    assert need >= 32 * 4 * 4 + 16 * 64 + 32 * 32 * 3 + 32 * 64 * 4
+    # ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y (int16) + exponents, permute, gemm map
+    assert need >= 32 * 4 * 4 + 16 * 64 + 32 * 32 * 3 + 32 * 64 * 2 + 32
     assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 1, 16, FAKE, FAKE, need - 1, s) == WS_SMALL
     assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 1, 16, FAKE, MIS, need, s) == ALIGN
     assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 5, 16, FAKE, FAKE, need, s) == INVALID
@@ -146,13 +146,13 @@ def test_layer_rejects_and_sizes_workspace(L):
     assert L.w8a8_moe_layer(None, FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
     assert L.w8a8_moe_layer(ctypes.byref(W), None, 1, 0, None, None, 0, s) == OK
     # intermediates are laid out inside the workspace, in order, without overlap
-    ptrs = (ctypes.c_void_p * 11)()
+    ptrs = (ctypes.c_void_p * 12)()
     base = 1 << 30
     assert L.w8a8_moe_layer_intermediates(ctypes.byref(W), 16, 1, ctypes.c_void_p(base), ptrs) == OK
     offs = [p - base for p in ptrs]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < need
     big = _weights(E=128, k=8, H=4096, I=1536)
-    assert L.w8a8_moe_layer_workspace_size(ctypes.byref(big), 8192, 0) > 8192 * 8 * 4096 * 4
+    assert L.w8a8_moe_layer_workspace_size(ctypes.byref(big), 8192, 0) > 8192 * 8 * 4096 * 2
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

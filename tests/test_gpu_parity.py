@@ -405,6 +405,25 @@ def _check_gate_up_int32(case, inter, n_rows=48):
     h = to_host(inter["h"])[rows]
     oq, os_ = oracle.quant_rows(h)
     assert np.array_equal(hq[rows], oq) and np.array_equal(to_host(inter["sh"])[rows], os_)
+    # y, carried as 16-bit fixed point with one power-of-two exponent per row and
+    # 64-column segment: within 2^-14 of its segment's largest magnitude of the
+    # exact dequantised value, and the segment maximum lands in [2^13, 2^14]
+    sh = to_host(inter["sh"])
+    y16 = to_host(inter["y"])[rows].astype(np.float64)
+    yexp = to_host(inter["y_exp"])[rows].astype(np.int64)
+    H = cfg.H
+    nseg = (H + 63) // 64
+    for i, r in enumerate(rows):
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        ref = accd_h[i].astype(np.float64) * float(sh[r]) * case.o_sd[e].astype(np.float64)
+        got = y16[i] * np.exp2(np.repeat(yexp[i], 64)[:H])
+        for sg in range(nseg):
+            cols = slice(64 * sg, min(H, 64 * sg + 64))
+            m = np.abs(ref[cols]).max()
+            assert np.all(np.abs(got[cols] - ref[cols]) <= 2.0 ** -14 * m * 1.0001 + 1e-6 * np.abs(ref[cols]) + 1e-30)
+            if m > 0:
+                cm = np.abs(y16[i][cols]).max()
+                assert 2 ** 13 - 1 <= cm <= 2 ** 14
 
 
 def test_layer_tiny_full():

@@ -24,7 +24,7 @@ B_ROWMAJOR, B_PACKED = 0, 1
 EPI_RAW_I32, EPI_DEQUANT, EPI_DEQUANT_SWIGLU = 0, 1, 2
 LAYER_STAGES = 7
 STAGE_NAMES = ("route", "quant_x", "permute", "gate_up_gemm", "quant_h", "down_gemm", "combine")
-INTERMEDIATES = ("ids", "w", "xq", "sx", "offsets", "sorted_pair", "pair_pos", "h", "hq", "sh", "y")
+INTERMEDIATES = ("ids", "w", "xq", "sx", "offsets", "sorted_pair", "pair_pos", "h", "hq", "sh", "y", "y_exp")
 
 
 class W8A8Error(RuntimeError):
@@ -294,7 +294,7 @@ def moe_layer_intermediates(W: MoEWeights, T, ws, x_dtype=BF16):
     spec = dict(ids=((T, W.k), torch.int32), w=((T, W.k), torch.float32), xq=((T, H), torch.int8),
                 sx=((T,), torch.float32), offsets=((E + 1,), torch.int32), sorted_pair=((P,), torch.int32),
                 pair_pos=((P,), torch.int32), h=((P, I), torch.bfloat16), hq=((P, I), torch.int8),
-                sh=((P,), torch.float32), y=((P, H), torch.float32))
+                sh=((P,), torch.float32), y=((P, H), torch.int16), y_exp=((P, (H + 63) // 64), torch.int8))
     base = ws.data_ptr()
     out = {}
     for name, p in zip(INTERMEDIATES, ptrs):

@@ -40,7 +40,7 @@ int check_route(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, i
 
 // Layer workspace layout (every part 256-byte aligned).
 struct LayerWs {
-    size_t ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y, perm, gemm1, gemm2, total;
+    size_t ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y, yexp, perm, gemm1, gemm2, total;
 };
 
 LayerWs layer_ws(const w8a8_moe_weights *W, int64_t T, int x_dtype)
@@ -63,7 +63,9 @@ LayerWs layer_ws(const w8a8_moe_weights *W, int64_t T, int x_dtype)
     L.h = take(2 * (size_t)(P * W->I));
     L.hq = take((size_t)(P * W->I));
     L.sh = take(sizeof(float) * P);
-    L.y = take(sizeof(float) * (size_t)(P * W->H));   // fp32: no rounding before the combine
+    // y: 16-bit fixed point with a power-of-two exponent per row and 64 columns
+    L.y = take(sizeof(int16_t) * (size_t)(P * W->H));
+    L.yexp = take((size_t)(P * ((W->H + 63) / 64)));
     L.perm = take(permute_ws_bytes(T, W->k, W->E));
     L.gemm1 = take(gemm_ws_bytes(P, 2 * W->I, W->E));
     L.gemm2 = take(gemm_ws_bytes(P, W->H, W->E));
@@ -114,7 +116,8 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     uint16_t *h = (uint16_t *)(base + L.h);
     int8_t *hq = (int8_t *)(base + L.hq);
     float *sh = (float *)(base + L.sh);
-    void *y = base + L.y;
+    int16_t *y = (int16_t *)(base + L.y);
+    int8_t *yexp = (int8_t *)(base + L.yexp);
     void *perm = base + L.perm;
     void *gws1 = base + L.gemm1;
     void *gws2 = base + L.gemm2;
@@ -140,7 +143,7 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     // 3 permute; its scan also builds the tile tables of both grouped GEMMs
     TileTableReq req[2];
     gemm_tile_params(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
-    gemm_tile_params(P, H, E, W8A8_EPI_DEQUANT, &req[1].BM, &req[1].nblocks_n);
+    gemm_tile_params(P, H, E, EPI_FIXED16, &req[1].BM, &req[1].nblocks_n);
     req[0].prefix = (int32_t *)gws1;
     req[0].tiles = (int4 *)gemm_tiles_ptr(gws1, E);
     req[1].prefix = (int32_t *)gws2;
@@ -156,13 +159,13 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     // quantise h per grouped row
     if ((e = launch_quant_rows(h, W8A8_BF16, P, I, I, hq, sh, st)) != hipSuccess || (e = mark()) != hipSuccess)
         return hip_status(e);
-    // 4b down GEMM -> y (fp32)
-    if ((e = launch_gemm_main(hq, P, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, E, P, H, I, W8A8_EPI_DEQUANT,
-                              W8A8_F32, y, gws2, st)) != hipSuccess ||
+    // 4b down GEMM -> y (16-bit fixed point + exponents)
+    if ((e = launch_gemm_main(hq, P, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, E, P, H, I, EPI_FIXED16,
+                              W8A8_F32, y, gws2, st, yexp)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 5 combine
-    if ((e = launch_combine(y, W8A8_F32, w, pos, T, k, H, out, x_dtype, st)) != hipSuccess ||
+    if ((e = launch_combine_fixed16(y, yexp, w, pos, T, k, H, out, x_dtype, st)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     return W8A8_OK;
@@ -311,7 +314,7 @@ int w8a8_moe_layer_intermediates(const w8a8_moe_weights *W, int64_t T, int x_dty
     const LayerWs L = layer_ws(W, T, x_dtype);
     char *b = (char *)ws;
     const size_t offs[W8A8_LAYER_INTERMEDIATES] = {L.ids, L.w, L.xq, L.sx, L.offsets, L.sorted,
-                                                   L.pos, L.h, L.hq, L.sh, L.y};
+                                                   L.pos, L.h, L.hq, L.sh, L.y, L.yexp};
     for (int i = 0; i < W8A8_LAYER_INTERMEDIATES; ++i) ptrs[i] = b + offs[i];
     return W8A8_OK;
 }

@@ -60,6 +60,68 @@ static void launch_typed(const YT *y, const float *w, const int32_t *pair_pos, i
     else hipLaunchKernelGGL((combine_kernel<YT, OT, 0>), grid, block, 0, st, y, w, pair_pos, k, H, out);
 }
 
+// y as 16-bit fixed point with a power-of-two exponent per row and 64-column
+// segment (the layer's down GEMM epilogue): a thread's 8 columns lie in one
+// segment, so each slot contributes w * 2^e * code.
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_fixed16_kernel(const int16_t *__restrict__ y16,
+                                                              const int8_t *__restrict__ y_exp,
+                                                              const float *__restrict__ w,
+                                                              const int32_t *__restrict__ pair_pos, int k, int64_t H,
+                                                              OT *__restrict__ out)
+{
+    const int64_t t = blockIdx.x;
+    const int64_t nseg = (H + 63) / 64;
+    for (int64_t c = (int64_t)threadIdx.x * 8; c < H; c += 256 * 8) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        constexpr int KMAX = 8;
+        uint4 v[KMAX];
+        float sc[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j < k) {
+                const int64_t row = pair_pos[t * k + j];
+                v[j] = *reinterpret_cast<const uint4 *>(y16 + row * H + c);
+                sc[j] = ldexpf(w[t * k + j], (int)y_exp[row * nseg + c / 64]);
+            }
+        }
+        for (int j0 = 0; j0 < k; j0 += KMAX) {
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                if (j0 + j >= k) break;
+                if (j0 > 0) {
+                    const int64_t row = pair_pos[t * k + j0 + j];
+                    v[j] = *reinterpret_cast<const uint4 *>(y16 + row * H + c);
+                    sc[j] = ldexpf(w[t * k + j0 + j], (int)y_exp[row * nseg + c / 64]);
+                }
+                const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = fmaf(sc[j], (float)(int16_t)(u[i] & 0xffffu), acc[2 * i]);
+                    acc[2 * i + 1] = fmaf(sc[j], (float)(int16_t)(u[i] >> 16), acc[2 * i + 1]);
+                }
+            }
+        }
+        store8(out + t * H + c, acc);
+    }
+}
+
+hipError_t launch_combine_fixed16(const int16_t *y16, const int8_t *y_exp, const float *w, const int32_t *pair_pos,
+                                  int64_t T, int k, int64_t H, void *out, int out_dtype, hipStream_t st)
+{
+    if (T == 0) return hipSuccess;
+    dim3 grid((unsigned)T), block(256);
+    if (out_dtype == 0)
+        hipLaunchKernelGGL(combine_fixed16_kernel<uint16_t>, grid, block, 0, st, y16, y_exp, w, pair_pos, k, H,
+                           (uint16_t *)out);
+    else
+        hipLaunchKernelGGL(combine_fixed16_kernel<float>, grid, block, 0, st, y16, y_exp, w, pair_pos, k, H,
+                           (float *)out);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T, int k,
                           int64_t H, void *out, int out_dtype, hipStream_t st)
 {

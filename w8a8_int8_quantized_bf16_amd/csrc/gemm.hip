@@ -59,6 +59,7 @@ struct GemmArgs {
     int64_t M_total, N, K;
     int64_t A_bytes;              // bytes of A addressable (rows * K)
     void *out;
+    int8_t *out_exp;              // EPI_FIXED16 only: [M][ceil(N/64)] power-of-two exponents
     const int32_t *tile_prefix;   // [G+1]: first tile of each group; [G] = total tiles
     const int4 *tiles;            // per launched block: {group, first grouped row, rows, column block}
     int nblocks_n;                // column blocks per group
@@ -110,6 +111,13 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restr
         if (row < N && k0 < K) v = *reinterpret_cast<const v4i *>(B + (g * N + row) * K + k0);
         *reinterpret_cast<v4i *>(P + i * 16) = v;
     }
+}
+
+// A lane's fp32 value moved by a DPP lane pattern (quad permutes, row mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
 // Buffer-resource loads: an offset at or beyond num_records returns zero
@@ -322,7 +330,9 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
     // one 32-row block and at most two 32-column fragments at a time, and
     // writes them back as 16-byte row segments (the MFMA layout gives a lane
     // one column of many rows; a store wants many columns of one row).
-    using ET = std::conditional_t<EPI == 0, int32_t, OutT>;
+    // staged element: the int32 accumulator, the output value, or (16-bit
+    // fixed point) the fp32 value before its segment scale is known
+    using ET = std::conditional_t<EPI == 0, int32_t, std::conditional_t<EPI == EPI_FIXED16, float, OutT>>;
     constexpr int NOF = EPI == 2 ? WN / 2 : WN;          // output fragments of 32 columns
     constexpr int FP = NOF < 2 ? NOF : 2;                 // fragments per pass
     constexpr int ROWB = 32 * FP * (int)sizeof(ET) + 16;  // padded staging row, bytes
@@ -349,6 +359,8 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
                         val = acc[mi][f][i];
                     } else if constexpr (EPI == 1) {
                         val = to_out<OutT>(((float)acc[mi][f][i] * sa) * bsc[f]);
+                    } else if constexpr (EPI == EPI_FIXED16) {
+                        val = ((float)acc[mi][f][i] * sa) * bsc[f];
                     } else {
                         const float gate = ((float)acc[mi][f][i] * sa) * bsc[f];
                         const float up = ((float)acc[mi][NOF + f][i] * sa) * bsc[NOF + f];
@@ -361,14 +373,50 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
                 }
             }
             __syncthreads();
+            if constexpr (EPI == EPI_FIXED16) {
+                // 16 lanes hold one row's 64 columns (4 each): the row's largest
+                // magnitude over them fixes a power-of-two scale 2^e that maps it
+                // into [2^13, 2^14); codes = rint(v * 2^-e) fit int16 with room.
+                static_assert(CPR == 16, "one 64-column segment per pass");
 #pragma unroll
-            for (int idx = lane; idx < 32 * CPR; idx += 64) {
-                const int rl = idx / CPR, ch = idx % CPR;
-                const int r = mi * 32 + rl;
-                const int ocol = ocol0 + 32 * f0 + ch * (16 / (int)sizeof(ET));
-                if (r < rows && ocol < ldo)
-                    *reinterpret_cast<uint4 *>(reinterpret_cast<ET *>(a.out) + (row0 + r) * ldo + ocol) =
-                        *reinterpret_cast<const uint4 *>(stage + rl * ROWB + ch * 16);
+                for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                    const int rl = idx / CPR, ch = idx % CPR;
+                    const int r = mi * 32 + rl;
+                    const int ocol = ocol0 + 32 * f0 + ch * 4;
+                    const float4 v = *reinterpret_cast<const float4 *>(stage + rl * ROWB + ch * 16);
+                    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+                    // max over the 16-lane row: lane swaps 1 and 2 within quads,
+                    // then mirrors within 8 and within 16 lanes
+                    m = fmaxf(m, dpp_f32<0xB1>(m));
+                    m = fmaxf(m, dpp_f32<0x4E>(m));
+                    m = fmaxf(m, dpp_f32<0x141>(m));
+                    m = fmaxf(m, dpp_f32<0x140>(m));
+                    int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 13 : 0;
+                    e = e < -126 ? -126 : e;
+                    const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+                    // rint(v * 2^-e) as an integer: adding 1.5 * 2^23 rounds the
+                    // (exact) product half-to-even into the mantissa
+                    const float vs[4] = {v.x, v.y, v.z, v.w};
+                    uint32_t q[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        q[u] = (uint32_t)(__float_as_int(fmaf(vs[u], sc, 12582912.0f)) - 0x4B400000) & 0xffffu;
+                    if (r < rows && ocol < ldo) {
+                        *reinterpret_cast<uint2 *>(reinterpret_cast<int16_t *>(a.out) + (row0 + r) * ldo + ocol) =
+                            make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
+                        if (ch == 0) a.out_exp[(row0 + r) * ((ldo + 63) / 64) + (ocol0 + 32 * f0) / 64] = (int8_t)e;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                    const int rl = idx / CPR, ch = idx % CPR;
+                    const int r = mi * 32 + rl;
+                    const int ocol = ocol0 + 32 * f0 + ch * (16 / (int)sizeof(ET));
+                    if (r < rows && ocol < ldo)
+                        *reinterpret_cast<uint4 *>(reinterpret_cast<ET *>(a.out) + (row0 + r) * ldo + ocol) =
+                            *reinterpret_cast<const uint4 *>(stage + rl * ROWB + ch * 16);
+                }
             }
             __syncthreads();
         }
@@ -384,11 +432,13 @@ struct TileCfg {
     int BM, WN;
 };
 
-TileCfg gemm_cfg(int64_t M_total, int G)
+TileCfg gemm_cfg(int64_t M_total, int G, int epilogue)
 {
     const double avg_rows = (double)M_total / (double)G;
     if (avg_rows <= 32.0) return {32, 2};
-    if (avg_rows <= 192.0) return {64, 2};
+    // the 16-bit fixed-point epilogue has more per-tile work: two blocks per
+    // CU (64-row tiles) overlap one block's epilogue with the other's MFMAs
+    if (avg_rows <= 192.0 || epilogue == EPI_FIXED16) return {64, 2};
     return {128, 4};
 }
 
@@ -401,11 +451,15 @@ int gemm_nblocks(int64_t N, int epilogue, int WN)
     return (int)((cols + per_block - 1) / per_block);
 }
 
+// upper bound of the tile count over every tile shape and epilogue
 int64_t gemm_max_tiles(int64_t M_total, int64_t N, int G)
 {
-    const TileCfg c = gemm_cfg(M_total, G);
-    const int nb = std::max(gemm_nblocks(N, 1, c.WN), gemm_nblocks(N, 2, c.WN));
-    return ((M_total + c.BM - 1) / c.BM + G) * nb;
+    int64_t most = 0;
+    for (const TileCfg c : {TileCfg{32, 2}, TileCfg{64, 2}, TileCfg{128, 4}}) {
+        const int nb = std::max(gemm_nblocks(N, 1, c.WN), gemm_nblocks(N, 2, c.WN));
+        most = std::max<int64_t>(most, ((M_total + c.BM - 1) / c.BM + G) * nb);
+    }
+    return most;
 }
 
 size_t prefix_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
@@ -421,6 +475,9 @@ hipError_t launch_main_layout(const GemmArgs &ga, int epilogue, int out_dtype, h
         hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, uint16_t, PACKED>), grid, block, 0, st, ga);
     else if (epilogue == 1)
         hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, float, PACKED>), grid, block, 0, st, ga);
+    else if (epilogue == EPI_FIXED16)
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, EPI_FIXED16, int16_t, PACKED>), grid, block, 0, st,
+                           ga);
     else if (out_dtype == 0)
         hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, uint16_t, PACKED>), grid, block, 0, st, ga);
     else
@@ -444,7 +501,7 @@ size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G)
 
 void gemm_tile_params(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n)
 {
-    const TileCfg c = gemm_cfg(M_total, G);
+    const TileCfg c = gemm_cfg(M_total, G, epilogue);
     *BM = c.BM;
     *nblocks_n = gemm_nblocks(N, epilogue, c.WN);
 }
@@ -455,7 +512,7 @@ hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, i
                                hipStream_t st)
 {
     if (M_total == 0) return hipSuccess;
-    const TileCfg c = gemm_cfg(M_total, G);
+    const TileCfg c = gemm_cfg(M_total, G, epilogue);
     const int64_t blocks = std::min<int64_t>((gemm_max_tiles(M_total, N, G) + 255) / 256, 64);
     hipLaunchKernelGGL(gemm_tilemap_kernel, dim3((unsigned)blocks), dim3(256), 0, st, offsets, G, c.BM,
                        gemm_nblocks(N, epilogue, c.WN), (int32_t *)ws, (int4 *)((char *)ws + prefix_bytes(G)));
@@ -465,10 +522,11 @@ hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, i
 hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                             int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                             const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                            int out_dtype, void *out, const void *ws, hipStream_t st)
+                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp)
 {
     if (M_total == 0) return hipSuccess;
     GemmArgs ga;
+    ga.out_exp = out_exp;
     ga.A = A;
     ga.a_scales = a_scales;
     ga.gather = gather;
@@ -485,7 +543,7 @@ hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scal
     ga.tiles = (const int4 *)((const char *)ws + prefix_bytes(G));
     ga.A_bytes = A_rows * K;
     ga.packed_b = b_packed;
-    const TileCfg c = gemm_cfg(M_total, G);
+    const TileCfg c = gemm_cfg(M_total, G, epilogue);
     ga.nblocks_n = gemm_nblocks(N, epilogue, c.WN);
     if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, epilogue, out_dtype, st);
     if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, epilogue, out_dtype, st);

@@ -29,10 +29,16 @@ void *gemm_tiles_ptr(void *ws, int G);
 // tile map of a grouped GEMM (into ws), then the GEMM itself reading that map
 hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
                                hipStream_t st);
+// Internal epilogue of the layer's down GEMM (not a public W8A8_EPI_* code):
+// the dequantised value v as 16-bit fixed point, out = rint(v * 2^-e) (int16)
+// with one exponent e per row and 64-column segment in out_exp
+// ([M][ceil(N/64)] int8), e chosen so the segment's largest |v| maps into
+// [2^13, 2^14).  Absolute error per element <= 2^-14 of the segment maximum.
+constexpr int EPI_FIXED16 = 3;
 hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                             int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                             const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                            int out_dtype, void *out, const void *ws, hipStream_t st);
+                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp = nullptr);
 hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                                int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                                const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
@@ -42,5 +48,8 @@ hipError_t launch_pack_weights(const int8_t *B, int64_t G, int64_t N, int64_t K,
 
 hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T,
                           int k, int64_t H, void *out, int out_dtype, hipStream_t st);
+// combine of y in the EPI_FIXED16 format: y16 [T*k][H] int16, y_exp [T*k][ceil(H/64)]
+hipError_t launch_combine_fixed16(const int16_t *y16, const int8_t *y_exp, const float *w, const int32_t *pair_pos,
+                                  int64_t T, int k, int64_t H, void *out, int out_dtype, hipStream_t st);
 
 }  // namespace w8a8
