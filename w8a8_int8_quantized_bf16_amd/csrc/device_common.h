@@ -24,6 +24,29 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// A lane's 32-bit value moved by a DPP lane pattern (quad permutes, row mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Maximum of a non-negative value over the wavefront, in every lane: DPP
+// swaps within each 16-lane row (xor 1, xor 2, mirror of 8, mirror of 16),
+// then the four row maxima read as scalars (non-negative floats order like
+// their bit patterns).
+__device__ __forceinline__ float wave_max_nonneg(float m)
+{
+    m = fmaxf(m, dpp_move<0xB1>(m));
+    m = fmaxf(m, dpp_move<0x4E>(m));
+    m = fmaxf(m, dpp_move<0x141>(m));
+    m = fmaxf(m, dpp_move<0x140>(m));
+    const uint32_t b = __float_as_uint(m);
+    const uint32_t r0 = __builtin_amdgcn_readlane(b, 0), r1 = __builtin_amdgcn_readlane(b, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(b, 32), r3 = __builtin_amdgcn_readlane(b, 48);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll

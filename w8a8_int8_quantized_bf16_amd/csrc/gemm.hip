@@ -113,13 +113,6 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restr
     }
 }
 
-// A lane's fp32 value moved by a DPP lane pattern (quad permutes, row mirrors).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
 // Buffer-resource loads: an offset at or beyond num_records returns zero
 // without touching memory, which masks ragged rows, column tails and the K
 // tail without branches (so the compiler's wait counters stay exact and the
@@ -387,10 +380,10 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
                     float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
                     // max over the 16-lane row: lane swaps 1 and 2 within quads,
                     // then mirrors within 8 and within 16 lanes
-                    m = fmaxf(m, dpp_f32<0xB1>(m));
-                    m = fmaxf(m, dpp_f32<0x4E>(m));
-                    m = fmaxf(m, dpp_f32<0x141>(m));
-                    m = fmaxf(m, dpp_f32<0x140>(m));
+                    m = fmaxf(m, dpp_move<0xB1>(m));
+                    m = fmaxf(m, dpp_move<0x4E>(m));
+                    m = fmaxf(m, dpp_move<0x141>(m));
+                    m = fmaxf(m, dpp_move<0x140>(m));
                     int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 13 : 0;
                     e = e < -126 ? -126 : e;
                     const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact

@@ -7,23 +7,57 @@
 // divide, round half to even), clamped to [-127, 127]; an all-zero row has
 // scale 0 and codes 0.
 //
-// One 64-lane wavefront per row.  Each lane owns 8 consecutive elements of
-// every 512-element stripe (16-byte loads of bf16, 32 bytes of fp32), so a
-// wave reads 1 KiB of bf16 per instruction, fully coalesced.  Rows of up to
-// 512 * MAXC elements are read once and held in registers (all loads issued
-// before the max reduction); longer rows are read twice (max pass, then code
-// pass; the second read hits L2).
+// One 64-lane wavefront handles R rows at once (all their loads are issued
+// before any reduction, so short rows still keep enough bytes in flight).
+// Each lane owns 8 consecutive elements of every 512-element stripe (16-byte
+// loads of bf16, 32 bytes of fp32), a wave reading 1 KiB of bf16 per
+// instruction, fully coalesced.  Rows of up to 512 * MAXC elements are held in
+// registers; longer rows are read twice (max pass, then code pass; the second
+// read hits L2).  The row maximum is a DPP reduction inside 16-lane rows plus
+// four lane reads.
+//
+// x / s is the IEEE quotient: with y = 1/s correctly rounded (one IEEE divide
+// per row), q0 = x*y, r = x - s*q0 (exact, by fma) and q = q0 + r*y (one fma)
+// give the correctly rounded x/s whenever no intermediate is subnormal
+// (Markstein's theorem).  That holds when s >= 2^-100: a subnormal x then has
+// |x/s| < 2^-26 and code 0 either way.  Rows with a smaller scale use the
+// divide itself.
 #include "device_common.h"
 #include "launch.h"
 
 namespace w8a8 {
 
-__device__ __forceinline__ uint32_t quant_code(float v, float s)
+__device__ __forceinline__ uint32_t clamp_code(float q)
 {
-    float c = rintf(v / s);
+    float c = rintf(q);
     c = fminf(fmaxf(c, -127.0f), 127.0f);
     return (uint32_t)((int32_t)c) & 0xffu;
 }
+
+__device__ __forceinline__ uint32_t quant_code(float v, float s) { return clamp_code(v / s); }
+
+// fl(v / s) from the correctly rounded reciprocal y (see above)
+__device__ __forceinline__ uint32_t quant_code_fma(float v, float s, float y)
+{
+    const float q0 = v * y;
+    const float r = fmaf(-s, q0, v);
+    return clamp_code(fmaf(r, y, q0));
+}
+
+__device__ __forceinline__ uint2 pack8(const float v[8], float s, float y, bool fast)
+{
+    uint32_t c[8];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = quant_code_fma(v[i], s, y);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = quant_code(v[i], s);
+    }
+    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+constexpr float QUANT_FAST_MIN_SCALE = 0x1p-100f;
 
 template <typename T>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T *__restrict__ x, int64_t rows, int64_t cols,
@@ -41,8 +75,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T *__restrict__ x
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     }
-    amax = wave_max(amax);
+    amax = wave_max_nonneg(amax);
     const float s = amax / 127.0f;
+    const float y = s > 0.0f ? 1.0f / s : 0.0f;
+    const bool fast = s >= QUANT_FAST_MIN_SCALE;
     if (lane == 0) scales[r] = s;
     int8_t *qr = q + r * cols;
     for (int64_t c = (int64_t)lane * 8; c < cols; c += 512) {
@@ -50,54 +86,53 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const T *__restrict__ x
         if (s != 0.0f) {
             float v[8];
             load8_f32(xr + c, v);
-            packed.x = quant_code(v[0], s) | (quant_code(v[1], s) << 8) | (quant_code(v[2], s) << 16) |
-                       (quant_code(v[3], s) << 24);
-            packed.y = quant_code(v[4], s) | (quant_code(v[5], s) << 8) | (quant_code(v[6], s) << 16) |
-                       (quant_code(v[7], s) << 24);
+            packed = pack8(v, s, y, fast);
         }
         *reinterpret_cast<uint2 *>(qr + c) = packed;
     }
 }
 
-template <typename T, int MAXC>
+template <typename T, int MAXC, int R>
 __global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T *__restrict__ x, int64_t rows, int64_t cols,
                                                              int64_t ld, int8_t *__restrict__ q,
                                                              float *__restrict__ scales)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= rows) return;
-    const T *xr = x + r * ld;
-    float v[MAXC][8];
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+    if (r0 >= rows) return;
+    float v[R][MAXC][8];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        const int64_t col = (int64_t)lane * 8 + 512 * c;
-        if (col < cols) load8_f32(xr + col, v[c]);
-        else
+    for (int j = 0; j < R; ++j)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
-    }
-    float amax = 0.0f;
+        for (int c = 0; c < MAXC; ++c) {
+            const int64_t col = (int64_t)lane * 8 + 512 * c;
+            if (r0 + j < rows && col < cols) load8_f32(x + (r0 + j) * ld + col, v[j][c]);
+            else
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
-    amax = wave_max(amax);
-    const float s = amax / 127.0f;
-    if (lane == 0) scales[r] = s;
-    int8_t *qr = q + r * cols;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-        const int64_t col = (int64_t)lane * 8 + 512 * c;
-        if (col >= cols) break;
-        uint2 packed = make_uint2(0u, 0u);
-        if (s != 0.0f) {
-            packed.x = quant_code(v[c][0], s) | (quant_code(v[c][1], s) << 8) | (quant_code(v[c][2], s) << 16) |
-                       (quant_code(v[c][3], s) << 24);
-            packed.y = quant_code(v[c][4], s) | (quant_code(v[c][5], s) << 8) | (quant_code(v[c][6], s) << 16) |
-                       (quant_code(v[c][7], s) << 24);
+                for (int i = 0; i < 8; ++i) v[j][c][i] = 0.0f;
         }
-        *reinterpret_cast<uint2 *>(qr + col) = packed;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t r = r0 + j;
+        if (r >= rows) break;
+        float amax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][c][i]));
+        amax = wave_max_nonneg(amax);
+        const float s = amax / 127.0f;
+        const float y = s > 0.0f ? 1.0f / s : 0.0f;
+        const bool fast = s >= QUANT_FAST_MIN_SCALE;
+        if (lane == 0) scales[r] = s;
+        int8_t *qr = q + r * cols;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int64_t col = (int64_t)lane * 8 + 512 * c;
+            if (col >= cols) break;
+            const uint2 packed = s != 0.0f ? pack8(v[j][c], s, y, fast) : make_uint2(0u, 0u);
+            *reinterpret_cast<uint2 *>(qr + col) = packed;
+        }
     }
 }
 
@@ -105,13 +140,14 @@ template <typename T>
 static void launch_typed(const T *x, int64_t rows, int64_t cols, int64_t ld, int8_t *q, float *scales,
                          hipStream_t st)
 {
-    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    dim3 block(256);
     const int64_t nc = (cols + 511) / 512;
-    if (nc <= 1) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 1>), grid, block, 0, st, x, rows, cols, ld, q, scales);
-    else if (nc <= 2) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 2>), grid, block, 0, st, x, rows, cols, ld, q, scales);
-    else if (nc <= 4) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 4>), grid, block, 0, st, x, rows, cols, ld, q, scales);
-    else if (nc <= 8) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8>), grid, block, 0, st, x, rows, cols, ld, q, scales);
-    else hipLaunchKernelGGL(quant_rows_kernel<T>, grid, block, 0, st, x, rows, cols, ld, q, scales);
+    auto grid = [&](int R) { return dim3((unsigned)((rows + 4 * R - 1) / (4 * R))); };
+    if (nc <= 1) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 1, 4>), grid(4), block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 2) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 2, 2>), grid(2), block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 4) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 4, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 8) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
+    else hipLaunchKernelGGL(quant_rows_kernel<T>, grid(1), block, 0, st, x, rows, cols, ld, q, scales);
 }
 
 hipError_t launch_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld, int8_t *q,
