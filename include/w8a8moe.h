@@ -110,6 +110,14 @@ int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T
                    float *logits_out, void *stream);
 
 /*
+ * The router weight widened once to fp32 for the layer (w8a8_moe_weights
+ * .w_gate_f32): w_gate_f32[i] = w_gate[i] exactly (a bf16 value is the upper
+ * half of an fp32).  w_gate device [E][H] bf16; w_gate_f32 device [E][H] fp32,
+ * written.  H % 16 == 0.
+ */
+int moe_router_widen(const uint16_t *w_gate, int E, int64_t H, float *w_gate_f32, void *stream);
+
+/*
  * Group the routed pairs by expert (the packed MoE grouped matmul,
  * "Qwen3-Next-80B-A3B-Instruct in AMCT" case, section 6).  Pair p = t*k + j is
  * routed to expert topk_ids[p]; pairs are stably sorted by (expert, p).
@@ -189,6 +197,9 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
  *   s_gate_up [E][2I]   fp32 per-output-channel scales
  *   w_down    int8 down_proj codes [E][H][I], packed the same way
  *   s_down    [E][H]    fp32
+ *   w_gate_f32 [E][H]   fp32: w_gate widened by moe_router_widen (exact), or
+ *             NULL.  When given, the router stages it as is instead of
+ *             widening w_gate inside every call; the scores are identical.
  * H % 16 == 0, I % 32 == 0.
  */
 typedef struct {
@@ -199,6 +210,7 @@ typedef struct {
     const float *s_gate_up;
     const int8_t *w_down;
     const float *s_down;
+    const float *w_gate_f32;
 } w8a8_moe_weights;
 
 /*

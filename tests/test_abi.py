@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
               "w8a8_moe_layer"):
         assert n in names
@@ -116,6 +116,14 @@ def test_pack_rejects(L):
     assert L.w8a8_pack_weights(None, 1, 48, 64, FAKE, s) == INVALID
 
 
+def test_router_widen_rejects(L):
+    s = None
+    assert L.moe_router_widen(FAKE, 8, 72, FAKE, s) == SHAPE
+    assert L.moe_router_widen(FAKE, 0, 64, FAKE, s) == INVALID
+    assert L.moe_router_widen(None, 8, 64, FAKE, s) == INVALID
+    assert L.moe_router_widen(FAKE, 8, 64, MIS, s) == ALIGN
+
+
 def test_combine_rejects(L):
     s = None
     assert L.moe_combine(FAKE, 0, FAKE, FAKE, 16, 2, 72, FAKE, 0, s) == SHAPE
@@ -126,7 +134,7 @@ def test_combine_rejects(L):
 
 
 def _weights(E=8, k=2, H=64, I=32, ptr=FAKE):
-    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value)
+    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value, None)
 
 
 def test_layer_rejects_and_sizes_workspace(L):
@@ -143,6 +151,9 @@ def test_layer_rejects_and_sizes_workspace(L):
     assert L.w8a8_moe_layer(ctypes.byref(_weights(k=9)), FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
     assert L.w8a8_moe_layer(ctypes.byref(_weights(E=257, k=2)), FAKE, 1, 16, FAKE, FAKE, need, s) == SHAPE
     assert L.w8a8_moe_layer(ctypes.byref(_weights(ptr=MIS)), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN
+    Wf = _weights()
+    Wf.w_gate_f32 = MIS.value
+    assert L.w8a8_moe_layer(ctypes.byref(Wf), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN
     assert L.w8a8_moe_layer(None, FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
     assert L.w8a8_moe_layer(ctypes.byref(W), None, 1, 0, None, None, 0, s) == OK
     # intermediates are laid out inside the workspace, in order, without overlap

@@ -489,6 +489,24 @@ def test_layer_determinism_and_token_shuffle():
     assert torch.equal(out_s.view(torch.int16), out1[:37].view(torch.int16))
 
 
+def test_router_widen_and_both_router_inputs():
+    """The fp32 router weight is the exact widening of the bf16 one, and the
+    layer gives bit-identical results whether the router stages that copy or
+    widens the bf16 weight itself."""
+    case = get_case("moe_30b_prefill_T4096")
+    wf = w8.router_widen(case.W.w_gate)
+    want = torch.from_numpy(synth.bf16_bits_to_f32(case.wg)).to(DEV)
+    assert torch.equal(wf.view(torch.int32), want.view(torch.int32))
+    out1, _, _ = case.run_layer()
+    saved = case.W.c.w_gate_f32
+    try:
+        case.W.c.w_gate_f32 = None
+        out2 = w8.moe_layer(case.W, case.xd)
+    finally:
+        case.W.c.w_gate_f32 = saved
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
 def test_layer_edge_cases():
     case = get_case("moe_30b_prefill_T4096")
     out1, _, _ = case.run_layer()

@@ -36,7 +36,7 @@ class W8A8Error(RuntimeError):
 class _Weights(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int), ("k", ctypes.c_int), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("w_gate", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("w_gate_f32", ctypes.c_void_p)]
 
 
 _lib = None
@@ -55,6 +55,7 @@ def lib():
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_quant_act.argtypes = [P, i32, i64, i64, i64, P, P, P]
     L.moe_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, P]
+    L.moe_router_widen.argtypes = [P, i32, i64, P, P]
     L.moe_permute_workspace_size.argtypes = [i64, i32, i32]
     L.moe_permute_workspace_size.restype = sz
     L.moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P, sz, P]
@@ -225,6 +226,15 @@ def combine(y, w, pair_pos, out_dtype=None):
 
 # ------------------------------------------------------------------- layer ---
 
+def router_widen(w_gate):
+    """The bf16 router weight widened to fp32 (exact) by the library."""
+    _need(w_gate, "w_gate", torch.bfloat16, 2)
+    E, H = w_gate.shape
+    out = torch.empty((E, H), dtype=torch.float32, device=w_gate.device)
+    _check(lib().moe_router_widen(_p(w_gate), E, H, _p(out), _stream()), "moe_router_widen")
+    return out
+
+
 class MoEWeights:
     """Device tensors of one layer.
     w_gate [E,H] bf16; w_gate_up [E,2I,H] int8 codes (gate rows, then up rows);
@@ -243,8 +253,9 @@ class MoEWeights:
         self.w_gate, self.w_gate_up, self.s_gate_up, self.w_down, self.s_down = self.tensors
         self.p_gate_up = pack_weights(w_gate_up)
         self.p_down = pack_weights(w_down)
+        self.w_gate_f32 = router_widen(w_gate)
         self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), self.p_gate_up.data_ptr(), s_gate_up.data_ptr(),
-                          self.p_down.data_ptr(), s_down.data_ptr())
+                          self.p_down.data_ptr(), s_down.data_ptr(), self.w_gate_f32.data_ptr())
 
     @classmethod
     def quantize(cls, w_gate, gate_up_f32, down_f32, k):

@@ -87,7 +87,7 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
     if (!W->w_gate || !W->w_gate_up || !W->s_gate_up || !W->w_down || !W->s_down) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!x || !out)) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(W->w_gate) || !aligned16(W->w_gate_up) || !aligned16(W->s_gate_up) || !aligned16(W->w_down) ||
-        !aligned16(W->s_down))
+        !aligned16(W->s_down) || (W->w_gate_f32 && !aligned16(W->w_gate_f32)))
         return W8A8_ERR_ALIGNMENT;
     if (T > 0 && (!aligned16(x) || !aligned16(out))) return W8A8_ERR_ALIGNMENT;
     return W8A8_OK;
@@ -133,7 +133,8 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     hipError_t e;
     if ((e = mark()) != hipSuccess) return hip_status(e);
     // 1 route
-    if ((e = launch_route_topk(x, x_dtype, W->w_gate, T, H, E, k, 1, ids, w, nullptr, st)) != hipSuccess ||
+    if ((e = launch_route_topk(x, x_dtype, W->w_gate, W->w_gate_f32, T, H, E, k, 1, ids, w, nullptr, st)) !=
+            hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 2 quantise x once per token (before the permutation: one scale per token
@@ -205,8 +206,17 @@ int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T
     int rc = check_route(x, x_dtype, w_gate, T, H, E, k, topk_ids, topk_w, logits_out);
     if (rc) return rc;
     if (T == 0) return W8A8_OK;
-    return hip_status(launch_route_topk(x, x_dtype, w_gate, T, H, E, k, renormalize, topk_ids, topk_w, logits_out,
+    return hip_status(launch_route_topk(x, x_dtype, w_gate, nullptr, T, H, E, k, renormalize, topk_ids, topk_w,
+                                        logits_out,
                                         (hipStream_t)stream));
+}
+
+int moe_router_widen(const uint16_t *w_gate, int E, int64_t H, float *w_gate_f32, void *stream)
+{
+    if (E <= 0 || H <= 0 || !w_gate || !w_gate_f32) return W8A8_ERR_INVALID_ARG;
+    if (H % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(w_gate) || !aligned16(w_gate_f32)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_widen_bf16(w_gate, (int64_t)E * H, w_gate_f32, (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_size(int64_t T, int k, int E)

@@ -9,8 +9,13 @@ namespace w8a8 {
 hipError_t launch_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                              int8_t *q, float *scales, hipStream_t st);
 
-hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H, int E,
-                             int k, int renormalize, int32_t *ids, float *w, float *logits, hipStream_t st);
+// wg_f32: the same router weight widened to fp32, or nullptr (then the
+// kernel widens wg while staging it)
+hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
+                             int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
+                             hipStream_t st);
+// n bf16 values (n % 8 == 0, 16-byte aligned) widened to fp32
+hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStream_t st);
 
 size_t permute_ws_bytes(int64_t T, int k, int E);
 // Tile tables the permutation builds for grouped GEMMs over its groups.

@@ -16,6 +16,8 @@
 // hidden dimension.
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -255,16 +257,18 @@ constexpr int RM_ROW = RM_KC * 4 + 16;     // padded fp32 LDS row, bytes
 constexpr int RM_STAGES = 3;               // slices in flight (registers)
 }
 
-template <int S>   // 64-expert slices (E <= 64 S), S in {1, 2, 4}
+// WF32: W_g is given already widened to fp32 ([E][H]), staged by plain copies.
+template <int S, bool WF32>   // 64-expert slices (E <= 64 S), S in {1, 2, 4}
 __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restrict__ x,
-                                                         const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
+                                                         const void *__restrict__ wg, int64_t T_, int64_t H,
                                                          int E, int k, int renorm, int32_t *__restrict__ ids,
                                                          float *__restrict__ wout, float *__restrict__ logits_out)
 {
     constexpr int NT = 512;                                    // threads
     constexpr int TC = 8 / S;                                  // 4-token chunks per block
     constexpr int WROWS = 64 * S, XROWS = 4 * TC;
-    constexpr int WPIECES = WROWS * 4, XPIECES = XROWS * 4;   // 16-byte bf16 pieces per slice
+    constexpr int WPR = WF32 ? 8 : 4;                          // 16-byte pieces per W_g row slice
+    constexpr int WPIECES = WROWS * WPR, XPIECES = XROWS * 4;   // 16-byte pieces per slice
     constexpr int WPT = (WPIECES + NT - 1) / NT, XPT = (XPIECES + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) unsigned char wl[2][WROWS * RM_ROW];
     __shared__ __attribute__((aligned(16))) unsigned char xl[2][XROWS * RM_ROW];
@@ -278,14 +282,13 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     // buffer resources: an out-of-range offset reads zero without a branch
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, 0x7ffffff0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, 0x7ffffff0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(wg), 0, 0x7ffffff0, 0x00020000);
     // staging assignment: piece p = row * 4 + c holds hidden 8c..8c+7 of the slice
     int woff[WPT], xoff[XPT];
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
-        const int p = tid + j * NT, row = p >> 2, c = p & 3;
-        woff[j] = (p < WPIECES && row < E) ? (int)((int64_t)row * H * 2) + 16 * c : 0x7fffffff;
+        const int p = tid + j * NT, row = p / WPR, c = p % WPR;
+        woff[j] = (p < WPIECES && row < E) ? (int)((int64_t)row * H * (WF32 ? 4 : 2)) + 16 * c : 0x7fffffff;
     }
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
@@ -296,10 +299,11 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     auto load = [&](int st, int slc) {
 #pragma unroll
         for (int j = 0; j < WPT; ++j) {
-            const int c = (tid + j * NT) & 3;
-            const bool ok = woff[j] != 0x7fffffff && slc * RM_KC + 8 * c < H;
+            const int c = (tid + j * NT) % WPR;
+            const bool ok = woff[j] != 0x7fffffff && slc * RM_KC + (WF32 ? 4 : 8) * c < H;
             wr[st][j] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ok ? woff[j] + slc * RM_KC * 2 : 0x7fffffff, 0, 0));
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rw, ok ? woff[j] + slc * RM_KC * (WF32 ? 4 : 2) : 0x7fffffff, 0, 0));
         }
 #pragma unroll
         for (int j = 0; j < XPT; ++j) {
@@ -324,7 +328,12 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     auto stage_item = [&](int item, int st, int buf) {
         if (item < WPT) {
             const int p = tid + item * NT;
-            if (p < WPIECES) put(wl[buf], p, wr[st][item]);
+            if constexpr (WF32) {
+                if (p < WPIECES)
+                    *reinterpret_cast<uint4 *>(wl[buf] + (p / WPR) * RM_ROW + 16 * (p % WPR)) = wr[st][item];
+            } else {
+                if (p < WPIECES) put(wl[buf], p, wr[st][item]);
+            }
         } else {
             const int p = tid + (item - WPT) * NT;
             if (p < XPIECES) put(xl[buf], p, xr[st][item - WPT]);
@@ -389,19 +398,41 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     }
 }
 
-hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H, int E, int k,
-                             int renormalize, int32_t *ids, float *w, float *logits, hipStream_t st)
+// W_g widened to fp32 once (exact): the bf16 pattern becomes the upper half.
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t *__restrict__ src, int64_t n,
+                                                         float *__restrict__ dst)
+{
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (int64_t)gridDim.x * 256 * 8) {
+        float v[8];
+        load8_f32(src + i, v);
+        store8(dst + i, v);
+    }
+}
+
+hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n / 8 + 255) / 256, 4096);
+    hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, n, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
+                             int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
+                             hipStream_t st)
 {
     if (T == 0) return hipSuccess;
     if (dtype == 0) {
         const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
         dim3 g((unsigned)((T + 32 / S - 1) / (32 / S))), b(512);
         const uint16_t *xb = (const uint16_t *)x;
-        switch (S) {
-        case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
-        case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
-        default: hipLaunchKernelGGL(route_mfma_kernel<4>, g, b, 0, st, xb, wg, T, H, E, k, renormalize, ids, w, logits); break;
-        }
+        const void *wp = wg_f32 ? (const void *)wg_f32 : (const void *)wg;
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, g, b, 0, st, xb, wp, T, H, E, k, renormalize, ids, w, logits);
+        };
+        if (S == 1) wg_f32 ? go(route_mfma_kernel<1, true>) : go(route_mfma_kernel<1, false>);
+        else if (S == 2) wg_f32 ? go(route_mfma_kernel<2, true>) : go(route_mfma_kernel<2, false>);
+        else wg_f32 ? go(route_mfma_kernel<4, true>) : go(route_mfma_kernel<4, false>);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((T + RT_TOK - 1) / RT_TOK)), block(256);
