@@ -133,8 +133,11 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 // BM rows x (4 waves x WN fragments of 32 columns); DEPTH K steps of B in flight.
+// Tiles of up to 128 x 256 run two blocks per CU (two waves per SIMD, at most
+// 256 registers per lane, accumulators in VGPRs); 128 x 512 tiles run one.
 template <int BM, int WN, int DEPTH, int EPI, typename OutT, bool PACKED>
-__global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
+__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(BM * WN <= 256 ? 2 : 1, 8)))
+void grouped_gemm_kernel(GemmArgs a)
 {
     static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH and alternates two LDS buffers");
     static_assert(EPI != 2 || WN % 2 == 0, "SwiGLU pairs gate and up fragments");
@@ -417,10 +420,11 @@ __global__ __launch_bounds__(G_THREADS) void grouped_gemm_kernel(GemmArgs a)
 }
 
 namespace {
-// Tile shapes: decode-like groups (a few rows per expert) use 32 x 256 tiles,
-// mid-sized groups 64 x 256, prefill-sized groups (over 192 rows per group on
-// average) 128 x 512 tiles that reuse each weight byte over more rows and each
-// activation row over more columns.
+// Tile shapes by the average rows per group: decode-like groups (<= 32 rows)
+// use 32 x 256 tiles, then 64 x 256 (<= 192), 128 x 256 (<= 384) and 128 x 512
+// tiles that reuse each weight byte over more rows and each activation row
+// over more columns; the 16-bit fixed-point epilogue stays at 64 x 256 up to
+// 384 rows and 128 x 256 above.
 struct TileCfg {
     int BM, WN;
 };
@@ -429,9 +433,11 @@ TileCfg gemm_cfg(int64_t M_total, int G, int epilogue)
 {
     const double avg_rows = (double)M_total / (double)G;
     if (avg_rows <= 32.0) return {32, 2};
-    // the 16-bit fixed-point epilogue has more per-tile work: two blocks per
-    // CU (64-row tiles) overlap one block's epilogue with the other's MFMAs
-    if (avg_rows <= 192.0 || epilogue == EPI_FIXED16) return {64, 2};
+    if (avg_rows <= 192.0) return {64, 2};
+    // the 16-bit fixed-point epilogue does more work per tile: smaller tiles
+    // keep it short next to the other block's MFMAs
+    if (epilogue == EPI_FIXED16) return avg_rows <= 384.0 ? TileCfg{64, 2} : TileCfg{128, 2};
+    if (avg_rows <= 384.0) return {128, 2};
     return {128, 4};
 }
 
@@ -448,7 +454,7 @@ int gemm_nblocks(int64_t N, int epilogue, int WN)
 int64_t gemm_max_tiles(int64_t M_total, int64_t N, int G)
 {
     int64_t most = 0;
-    for (const TileCfg c : {TileCfg{32, 2}, TileCfg{64, 2}, TileCfg{128, 4}}) {
+    for (const TileCfg c : {TileCfg{32, 2}, TileCfg{64, 2}, TileCfg{128, 2}, TileCfg{128, 4}}) {
         const int nb = std::max(gemm_nblocks(N, 1, c.WN), gemm_nblocks(N, 2, c.WN));
         most = std::max<int64_t>(most, ((M_total + c.BM - 1) / c.BM + G) * nb);
     }
@@ -540,6 +546,7 @@ hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scal
     ga.nblocks_n = gemm_nblocks(N, epilogue, c.WN);
     if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, epilogue, out_dtype, st);
     if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, epilogue, out_dtype, st);
+    if (c.WN == 2) return launch_main_cfg<128, 2, 2>(ga, epilogue, out_dtype, st);
     return launch_main_cfg<128, 4, 2>(ga, epilogue, out_dtype, st);
 }
 
