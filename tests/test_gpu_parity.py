@@ -221,7 +221,7 @@ def test_route_full_size(name):
 @pytest.mark.parametrize("T,k,E,mode", [
     (1, 1, 1, "rand"), (16, 2, 8, "rand"), (37, 8, 128, "rand"), (4096, 8, 128, "rand"),
     (8192, 8, 128, "zipf"), (300, 4, 256, "rand"), (1000, 2, 8, "one"), (2049, 1, 3, "rand"),
-    (513, 8, 16, "rand")])
+    (513, 8, 16, "rand"), (512, 8, 128, "rand"), (4097, 1, 64, "rand"), (4096, 1, 256, "zipf")])
 def test_permute_bit_exact(T, k, E, mode):
     rng = np.random.default_rng(T + k + E)
     if mode == "one":

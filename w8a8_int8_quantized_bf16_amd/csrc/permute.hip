@@ -6,6 +6,7 @@
 //   1. count:   one block per chunk of 512 pairs -> per-chunk histograms
 //   2. scan:    one block; per expert an exclusive scan over the chunks, then
 //               an exclusive scan over experts -> offsets[E+1]
+//   (up to 4096 pairs one block does all three steps in a single launch)
 //   3. scatter: one block per chunk; pairs are ranked in pair order, 256 at a
 //               time: equal experts inside a wavefront are matched with eight
 //               ballots (one per bit of the id), waves are ordered through LDS.
@@ -22,6 +23,7 @@ constexpr int PM_THREADS = 256;
 constexpr int PM_PER_THREAD = 2;
 constexpr int PM_CHUNK = PM_THREADS * PM_PER_THREAD;   // pairs per chunk
 constexpr int PM_MAX_E = 256;
+constexpr int64_t PM_SMALL_P = 4096;   // up to this many pairs: one block does everything
 
 inline int64_t pm_chunks(int64_t P) { return (P + PM_CHUNK - 1) / PM_CHUNK; }
 }  // namespace
@@ -82,46 +84,22 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__res
     if (tid == 0) offsets[E] = (int32_t)P;
 }
 
-// The tile tables of up to two grouped GEMMs over the expert groups: every
-// block forms the tile prefixes from the offsets, block 0 stores them, and the
-// blocks of the scatter grid share the descriptor writes.
-struct ScanTables {
-    TileTableReq r[2];
-    int n;
-};
-
-__global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
-                                                                     int E, const int32_t *__restrict__ chunk_base,
-                                                                     const int32_t *__restrict__ offsets,
-                                                                     int32_t *__restrict__ sorted_pair,
-                                                                     int32_t *__restrict__ pair_pos, ScanTables tt)
+// Stable placement of the pairs p = first + 256 r + tid (r < rounds, p < P):
+// pairs are ranked in pair order, 256 at a time; equal experts inside a
+// wavefront are matched with eight ballots (one per bit of the id), waves are
+// ordered through LDS.  base[e] (LDS) holds expert e's next free row and is
+// advanced; wcnt is LDS scratch.
+__device__ inline void scatter_rounds(const int32_t *__restrict__ ids, int64_t P, int64_t first, int rounds, int E,
+                                      int32_t *base, int32_t (*wcnt)[PM_MAX_E], int32_t *__restrict__ sorted_pair,
+                                      int32_t *__restrict__ pair_pos)
 {
-    __shared__ int32_t base[PM_MAX_E];     // next free row of each expert inside this chunk
-    __shared__ int32_t wcnt[4][PM_MAX_E];  // per-wave counts of the current round
-    __shared__ int32_t off_l[PM_MAX_E + 1];
-    __shared__ int32_t pre[PM_MAX_E + 1];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-
-    // ---- tile tables
-    for (int g = tid; g <= E; g += PM_THREADS) off_l[g] = offsets[g];
-    __syncthreads();
-    for (int j = 0; j < tt.n; ++j) {
-        const int total = tile_table_prefix(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, &wcnt[0][0]);
-        if (blockIdx.x == 0)
-            for (int g = tid; g <= E; g += PM_THREADS) tt.r[j].prefix[g] = pre[g];
-        tile_fill(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, total, tt.r[j].tiles,
-                  blockIdx.x * PM_THREADS + tid, gridDim.x * PM_THREADS);
-        __syncthreads();
-    }
-
-    // ---- scatter
-    if (tid < E) base[tid] = off_l[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int round = 0; round < PM_PER_THREAD; ++round) {
+    for (int round = 0; round < rounds; ++round) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
         __syncthreads();
-        const int64_t p = (int64_t)blockIdx.x * PM_CHUNK + (int64_t)round * PM_THREADS + tid;
+        const int64_t p = first + (int64_t)round * PM_THREADS + tid;
         const bool valid = p < P;
         const int e = valid ? ids[p] : 0;
         // lanes of this wave holding the same expert id
@@ -147,6 +125,83 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32
     }
 }
 
+// The tile tables of up to two grouped GEMMs over the expert groups: every
+// block forms the tile prefixes from the offsets, block 0 stores them, and the
+// blocks of the scatter grid share the descriptor writes.
+struct ScanTables {
+    TileTableReq r[2];
+    int n;
+};
+
+__global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
+                                                                     int E, const int32_t *__restrict__ chunk_base,
+                                                                     const int32_t *__restrict__ offsets,
+                                                                     int32_t *__restrict__ sorted_pair,
+                                                                     int32_t *__restrict__ pair_pos, ScanTables tt)
+{
+    __shared__ int32_t base[PM_MAX_E];     // next free row of each expert inside this chunk
+    __shared__ int32_t wcnt[4][PM_MAX_E];  // per-wave counts of the current round
+    __shared__ int32_t off_l[PM_MAX_E + 1];
+    __shared__ int32_t pre[PM_MAX_E + 1];
+    const int tid = threadIdx.x;
+
+    // ---- tile tables
+    for (int g = tid; g <= E; g += PM_THREADS) off_l[g] = offsets[g];
+    __syncthreads();
+    for (int j = 0; j < tt.n; ++j) {
+        const int total = tile_table_prefix(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, &wcnt[0][0]);
+        if (blockIdx.x == 0)
+            for (int g = tid; g <= E; g += PM_THREADS) tt.r[j].prefix[g] = pre[g];
+        tile_fill(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, total, tt.r[j].tiles,
+                  blockIdx.x * PM_THREADS + tid, gridDim.x * PM_THREADS);
+        __syncthreads();
+    }
+
+    // ---- scatter
+    if (tid < E) base[tid] = off_l[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
+    scatter_rounds(ids, P, (int64_t)blockIdx.x * PM_CHUNK, PM_PER_THREAD, E, base, wcnt, sorted_pair, pair_pos);
+}
+
+// P <= PM_SMALL_P: the whole permutation (histogram, offsets, tile tables,
+// stable scatter) in one block, one launch.
+__global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t *__restrict__ ids, int64_t P, int E,
+                                                                   int32_t *__restrict__ offsets,
+                                                                   int32_t *__restrict__ sorted_pair,
+                                                                   int32_t *__restrict__ pair_pos, ScanTables tt)
+{
+    __shared__ int32_t base[PM_MAX_E];
+    __shared__ int32_t wcnt[4][PM_MAX_E];
+    __shared__ int32_t off_l[PM_MAX_E + 1];
+    __shared__ int32_t pre[PM_MAX_E + 1];
+    const int tid = threadIdx.x;
+    int32_t *hist = &wcnt[0][0];
+    hist[tid] = 0;
+    __syncthreads();
+    for (int64_t p = tid; p < P; p += PM_THREADS) atomicAdd(&hist[ids[p]], 1);   // counts only
+    __syncthreads();
+    int32_t *sc = &wcnt[1][0];
+    const int32_t cnt = tid < E ? hist[tid] : 0;
+    sc[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < PM_THREADS; d <<= 1) {   // inclusive scan over 256 entries
+        const int32_t v = tid >= d ? sc[tid - d] : 0;
+        __syncthreads();
+        sc[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) off_l[tid] = offsets[tid] = sc[tid] - cnt;
+    if (tid == 0) off_l[E] = offsets[E] = (int32_t)P;
+    __syncthreads();
+    for (int j = 0; j < tt.n; ++j) {
+        const int total = tile_table_prefix(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, &wcnt[2][0]);
+        for (int g = tid; g <= E; g += PM_THREADS) tt.r[j].prefix[g] = pre[g];
+        tile_fill(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, total, tt.r[j].tiles, tid, PM_THREADS);
+        __syncthreads();
+    }
+    if (tid < E) base[tid] = off_l[tid];
+    scatter_rounds(ids, P, 0, (int)((P + PM_THREADS - 1) / PM_THREADS), E, base, wcnt, sorted_pair, pair_pos);
+}
+
 size_t permute_ws_bytes(int64_t T, int k, int E) { return (size_t)pm_chunks(T * k) * (size_t)E * sizeof(int32_t); }
 
 hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets, int32_t *sorted_pair,
@@ -156,6 +211,11 @@ hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *
     tt.n = nreq < 2 ? nreq : 2;
     for (int j = 0; j < tt.n; ++j) tt.r[j] = req[j];
     const int64_t P = T * k;
+    if (P > 0 && P <= PM_SMALL_P) {
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PM_THREADS), 0, st, ids, P, E, offsets, sorted_pair,
+                           pair_pos, tt);
+        return hipGetLastError();
+    }
     const int64_t nch = pm_chunks(P);
     int32_t *cc = (int32_t *)ws;
     // with P == 0 only the scan runs: it writes all-zero offsets (and no tile
