@@ -185,11 +185,16 @@ def test_route_ties_lower_index_first():
 
 @pytest.mark.parametrize("T,H,E,k", [(1, 16, 1, 1), (5, 48, 8, 2), (37, 2048, 63, 8), (9, 64, 64, 64),
                                      (17, 128, 65, 3), (33, 256, 96, 8), (12, 4096, 128, 8), (7, 80, 200, 11),
-                                     (40, 32, 256, 16)])
+                                     (40, 32, 256, 16), (256, 2064, 128, 8), (128, 112, 200, 8),
+                                     (257, 2064, 128, 8), (520, 2064, 63, 8), (300, 80, 200, 11),
+                                     (700, 32, 256, 16), (600, 48, 8, 2)])
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
 def test_route_shapes(T, H, E, k, xdt):
     """Expert counts that fill 1..4 slices of 64 (ragged ones included), odd
-    token counts, short and long hidden sizes; bf16 and fp32 activations."""
+    token counts, short and long hidden sizes; bf16 and fp32 activations.
+    With bf16 activations up to 512 (token, expert-slice) pairs take the
+    vector-ALU router, more take the matrix-core one: both sides of that
+    switch are here, with hidden sizes that leave a tail of W_g steps."""
     rng = np.random.default_rng(T * 1000 + E)
     x = rng.standard_t(4, (T, H)).astype(np.float32)
     xa = synth.f32_to_bf16_bits(x) if xdt == "bf16" else x

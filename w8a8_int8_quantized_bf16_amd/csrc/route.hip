@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -398,6 +399,134 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     }
 }
 
+// Vector-ALU router for few tokens.  A wavefront owns TPW tokens and one
+// slice of 64 experts: lane l runs the TPW fma chains of expert 64 sl + l
+// (v_fma_f32 is exactly the chain's fmaf), so every W_g value a lane loads
+// feeds TPW chains.  The block first widens its tokens' rows of x into LDS
+// (fp32); the chains then take them as broadcast LDS reads issued XP steps
+// ahead, while each lane streams its expert's bf16 W_g row D steps of 8
+// values ahead and widens it in registers.  The S waves of a block cover all
+// experts of the same tokens.  With few tokens the router is bound by one
+// wave's issue of its H-long chain, so a step holds as few instructions as it
+// can: 8 fmas, 8 widening ops, one W load at a fixed offset from the row
+// base, two LDS reads.  (The fp32 copy of W_g would double the load
+// instructions; the bf16 rows are faster here.)
+template <int S, int TPW>
+__global__ __launch_bounds__(64 * S) void route_valu_kernel(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ wg, int64_t T_,
+                                                            int64_t H, int E, int k, int renorm,
+                                                            int32_t *__restrict__ ids, float *__restrict__ wout,
+                                                            float *__restrict__ logits_out)
+{
+    constexpr int D = 16;   // W_g steps (8 values each) in flight per lane
+    constexpr int XP = 2;   // x steps read ahead from LDS
+    // [TPW][H] fp32, plus the XP * 8 floats that the read-ahead past the last row touches
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+    __shared__ float lg[TPW][64 * S + 1];
+    __shared__ __attribute__((aligned(16))) uint32_t tk_scr[S][512];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int e = 64 * wave + lane;
+    const int64_t tb = (int64_t)blockIdx.x * TPW;
+    // the resource spans W_g exactly: a read past its end (the look-ahead of
+    // the last rows, the lanes past E) returns zeros
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, (int)(E * H * 2), 0x00020000);
+    const uint32_t wrow = e < E ? (uint32_t)((int64_t)e * H * 2) : 0x80000000u;
+    const int nst = (int)(H / 8);
+
+    uint4 wr[D];
+    // step st of the row; within a pass the offset is the pass base plus an immediate
+    auto load_w = [&](int slot, uint32_t base, int imm) {
+        wr[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, base, imm, 0));
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_w(d, wrow, 16 * d);
+    // x rows into LDS (a token past T stages zeros; its result is never stored)
+    for (int64_t i = (int64_t)tid * 8; i < TPW * H; i += 64 * S * 8) {
+        const int t = (int)(i / H);
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (tb + t < T_) load8_f32(x + (tb + t) * H + (i - (int64_t)t * H), v);
+        *reinterpret_cast<float4 *>(xs + i) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(xs + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __syncthreads();
+
+    auto widen_w = [&](int slot, float w8[8]) {
+        const uint32_t u[4] = {wr[slot].x, wr[slot].y, wr[slot].z, wr[slot].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w8[2 * i] = __uint_as_float(u[i] << 16);
+            w8[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    };
+    float4 xr[XP][TPW][2];
+    auto load_x = [&](int slot, int st) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            xr[slot][t][0] = *reinterpret_cast<const float4 *>(xs + t * H + st * 8);
+            xr[slot][t][1] = *reinterpret_cast<const float4 *>(xs + t * H + st * 8 + 4);
+        }
+    };
+    auto chain8 = [&](const float4 (&xv)[TPW][2], const float w8[8], float acc[TPW]) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const float x8[8] = {xv[t][0].x, xv[t][0].y, xv[t][0].z, xv[t][0].w,
+                                 xv[t][1].x, xv[t][1].y, xv[t][1].z, xv[t][1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[t] = fmaf(x8[i], w8[i], acc[t]);
+        }
+    };
+    float acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < XP; ++p) load_x(p, p);
+    const int nmain = nst / D * D;
+    for (int st0 = 0; st0 < nmain; st0 += D) {
+        const uint32_t base = wrow + (uint32_t)(st0 + D) * 16u;   // the next pass's steps
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            float w8[8];
+            widen_w(d, w8);
+            float4 xv[TPW][2];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) xv[t][0] = xr[d % XP][t][0], xv[t][1] = xr[d % XP][t][1];
+            load_x(d % XP, st0 + d + XP);   // past the rows it reads the pad (unused)
+            chain8(xv, w8, acc);
+            load_w(d, base, 16 * d);   // after the fmas: the slot's registers are free again
+            // keep each step's loads in place: the scheduler would otherwise batch
+            // them at the end of the body, and every pass would wait for them all
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // tail: the last nst - nmain (< D) steps; slot d holds step nmain + d
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (nmain + d < nst) {
+            float w8[8];
+            widen_w(d, w8);
+            float4 xv[TPW][2];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                xv[t][0] = *reinterpret_cast<const float4 *>(xs + t * H + (nmain + d) * 8);
+                xv[t][1] = *reinterpret_cast<const float4 *>(xs + t * H + (nmain + d) * 8 + 4);
+            }
+            chain8(xv, w8, acc);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) lg[t][e] = acc[t];
+    __syncthreads();
+    for (int tt = wave; tt < TPW; tt += S) {
+        const int64_t t = tb + tt;
+        if (t >= T_) break;
+        float l4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? lg[tt][lane + 64 * j] : 0.0f;
+        select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
+    }
+}
+
 // W_g widened to fp32 once (exact): the bf16 pattern becomes the upper half.
 __global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t *__restrict__ src, int64_t n,
                                                          float *__restrict__ dst)
@@ -424,9 +553,25 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
     if (T == 0) return hipSuccess;
     if (dtype == 0) {
         const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
-        dim3 g((unsigned)((T + 32 / S - 1) / (32 / S))), b(512);
         const uint16_t *xb = (const uint16_t *)x;
         const void *wp = wg_f32 ? (const void *)wg_f32 : (const void *)wg;
+#ifndef RV_LIM
+#define RV_LIM 512
+#endif
+        if (T * S <= RV_LIM && H <= 8192) {
+            // few tokens: vector-ALU chains over the bf16 W_g, one token per wave
+            constexpr int TP = 1;
+            const size_t lds = ((size_t)TP * H + 16) * sizeof(float);
+            auto go = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3((unsigned)((T + TP - 1) / TP)), dim3(64 * S), lds, st, xb, wg, T, H, E,
+                                   k, renormalize, ids, w, logits);
+            };
+            if (S == 1) go(route_valu_kernel<1, TP>);
+            else if (S == 2) go(route_valu_kernel<2, TP>);
+            else go(route_valu_kernel<4, TP>);
+            return hipGetLastError();
+        }
+        dim3 g((unsigned)((T + 32 / S - 1) / (32 / S))), b(512);
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, g, b, 0, st, xb, wp, T, H, E, k, renormalize, ids, w, logits);
         };
