@@ -228,7 +228,9 @@ int w8a8_moe_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_
  * The same layer, recording `n_events` (<= W8A8_LAYER_STAGES + 1) hipEvent_t
  * handles on `stream`: events[0] before the first stage and events[i] after
  * stage i, stages in the order route, quantise x, permute, gate_up GEMM,
- * quantise h, down GEMM, combine.  Used to time the stages from the host.
+ * quantise h, down GEMM, combine.  A null entry skips that mark, so a caller
+ * can bracket one stage without adding records between the others.  Used to
+ * time the stages from the host.
  */
 #define W8A8_LAYER_STAGES 7
 int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T,

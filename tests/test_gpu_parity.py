@@ -494,6 +494,25 @@ def test_layer_determinism_and_token_shuffle():
     assert torch.equal(out_s.view(torch.int16), out1[:37].view(torch.int16))
 
 
+def test_layer_with_stage_events():
+    """The timing entry point records its events (all, or only the non-null
+    ones) and computes the same layer bit for bit."""
+    case = get_case("moe_30b_decode_T64")
+    out1, _, _ = case.run_layer()
+    n = w8.LAYER_STAGES + 1
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    o_all = w8.moe_layer(case.W, case.xd, events=evs)
+    sel = [e if j in (3, 4) else None for j, e in enumerate(evs)]
+    o_sel = w8.moe_layer(case.W, case.xd, events=sel)
+    torch.cuda.synchronize()
+    assert evs[3].elapsed_time(evs[4]) > 0.0
+    assert torch.equal(o_all.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(o_sel.view(torch.int16), out1.view(torch.int16))
+
+
 def test_router_widen_and_both_router_inputs():
     """The fp32 router weight is the exact widening of the bf16 one, and the
     layer gives bit-identical results whether the router stages that copy or

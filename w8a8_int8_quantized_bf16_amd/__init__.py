@@ -287,9 +287,12 @@ def moe_layer(W: MoEWeights, x, ws=None, out=None, events=None):
     if events is None:
         rc = lib().w8a8_moe_layer(ctypes.byref(W.c), _p(x), dt, T, _p(out), _p(ws), ws.numel(), _stream(x.device))
     else:
-        if any(e.cuda_event == 0 for e in events):
+        # None skips a mark; a torch event must have been recorded once (torch
+        # creates the HIP event lazily)
+        if any(e is not None and e.cuda_event == 0 for e in events):
             raise ValueError("events must have been recorded once (torch creates the HIP event lazily)")
-        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(None if e is None else e.cuda_event)
+                                                  for e in events])
         rc = lib().w8a8_moe_layer_events(ctypes.byref(W.c), _p(x), dt, T, _p(out), _p(ws), ws.numel(),
                                          _stream(x.device), arr, len(events))
     _check(rc, "w8a8_moe_layer")

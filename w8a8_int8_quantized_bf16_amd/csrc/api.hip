@@ -127,19 +127,22 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
 
     int ev = 0;
     auto mark = [&]() -> hipError_t {
-        if (ev < n_events) return hipEventRecord((hipEvent_t)events[ev++], st);
-        return hipSuccess;
+        if (ev >= n_events) return hipSuccess;
+        void *h = events[ev++];
+        return h ? hipEventRecord((hipEvent_t)h, st) : hipSuccess;   // a null entry skips the mark
     };
     hipError_t e;
     if ((e = mark()) != hipSuccess) return hip_status(e);
-    // 1 route
-    if ((e = launch_route_topk(x, x_dtype, W->w_gate, W->w_gate_f32, T, H, E, k, 1, ids, w, nullptr, st)) !=
-            hipSuccess ||
+    // 1 route; with few tokens the router also quantises them (stage 2 is then empty)
+    const bool fused_q = route_fuses_quant(x_dtype, T, H, E);
+    if ((e = launch_route_topk(x, x_dtype, W->w_gate, W->w_gate_f32, T, H, E, k, 1, ids, w, nullptr, st,
+                               fused_q ? xq : nullptr, fused_q ? sx : nullptr)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 2 quantise x once per token (before the permutation: one scale per token
     //   serves all k experts)
-    if ((e = launch_quant_rows(x, x_dtype, T, H, H, xq, sx, st)) != hipSuccess || (e = mark()) != hipSuccess)
+    if ((!fused_q && (e = launch_quant_rows(x, x_dtype, T, H, H, xq, sx, st)) != hipSuccess) ||
+        (e = mark()) != hipSuccess)
         return hip_status(e);
     // 3 permute; its scan also builds the tile tables of both grouped GEMMs
     TileTableReq req[2];

@@ -55,6 +55,35 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 // Load 8 consecutive elements (16-byte aligned) widened to fp32.
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the 256 threads of a block (all must call it);
+// *total gets the sum of all 256 values.  sc: 4 ints of LDS scratch, free
+// again when the call returns.
+__device__ __forceinline__ int block_excl_scan256(int v, int *sc, int *total)
+{
+    const int wave = threadIdx.x >> 6;
+    const int inc = wave_incl_scan(v);
+    if ((threadIdx.x & 63) == 63) sc[wave] = inc;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) before += w < wave ? sc[w] : 0;
+    *total = sc[0] + sc[1] + sc[2] + sc[3];
+    __syncthreads();
+    return before + inc - v;
+}
+
 __device__ __forceinline__ void load8_f32(const uint16_t *p, float v[8])
 {
     uint4 u = *reinterpret_cast<const uint4 *>(p);

@@ -10,10 +10,13 @@ hipError_t launch_quant_rows(const void *x, int dtype, int64_t rows, int64_t col
                              int8_t *q, float *scales, hipStream_t st);
 
 // wg_f32: the same router weight widened to fp32, or nullptr (then the
-// kernel widens wg while staging it)
+// kernel widens wg while staging it).  xq/sx: when route_fuses_quant() holds,
+// the router may also write the tokens' int8 codes [T,H] and scales [T]
+// (pass nullptr otherwise; non-null where it does not hold is an error).
+bool route_fuses_quant(int dtype, int64_t T, int64_t H, int E);
 hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
                              int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
-                             hipStream_t st);
+                             hipStream_t st, int8_t *xq = nullptr, float *sx = nullptr);
 // n bf16 values (n % 8 == 0, 16-byte aligned) widened to fp32
 hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStream_t st);
 

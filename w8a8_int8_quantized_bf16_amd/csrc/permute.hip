@@ -71,16 +71,9 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__res
             run += v;
         }
     }
-    tot[tid] = (tid < E) ? run : 0;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over 256 entries
-    for (int d = 1; d < PM_THREADS; d <<= 1) {
-        const int32_t v = (tid >= d) ? tot[tid - d] : 0;
-        __syncthreads();
-        tot[tid] += v;
-        __syncthreads();
-    }
-    if (tid < E) offsets[tid] = tot[tid] - run;
+    int all;
+    const int32_t ex = block_excl_scan256(tid < E ? run : 0, tot, &all);
+    if (tid < E) offsets[tid] = ex;
     if (tid == 0) offsets[E] = (int32_t)P;
 }
 
@@ -173,23 +166,27 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t
     __shared__ int32_t wcnt[4][PM_MAX_E];
     __shared__ int32_t off_l[PM_MAX_E + 1];
     __shared__ int32_t pre[PM_MAX_E + 1];
+    __shared__ int32_t ids_l[PM_SMALL_P];
     const int tid = threadIdx.x;
     int32_t *hist = &wcnt[0][0];
     hist[tid] = 0;
-    __syncthreads();
-    for (int64_t p = tid; p < P; p += PM_THREADS) atomicAdd(&hist[ids[p]], 1);   // counts only
-    __syncthreads();
-    int32_t *sc = &wcnt[1][0];
-    const int32_t cnt = tid < E ? hist[tid] : 0;
-    sc[tid] = cnt;
-    __syncthreads();
-    for (int d = 1; d < PM_THREADS; d <<= 1) {   // inclusive scan over 256 entries
-        const int32_t v = tid >= d ? sc[tid - d] : 0;
-        __syncthreads();
-        sc[tid] += v;
-        __syncthreads();
+    // the ids into LDS, up to 16 loads per thread in flight
+    constexpr int PER = (int)(PM_SMALL_P / PM_THREADS);
+    int32_t v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int p = u * PM_THREADS + tid;
+        v[u] = p < P ? ids[p] : 0;
     }
-    if (tid < E) off_l[tid] = offsets[tid] = sc[tid] - cnt;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+        if (u * PM_THREADS + tid < P) ids_l[u * PM_THREADS + tid] = v[u];
+    __syncthreads();
+    for (int p = tid; p < P; p += PM_THREADS) atomicAdd(&hist[ids_l[p]], 1);   // counts only
+    __syncthreads();
+    int all;
+    const int32_t ex = block_excl_scan256(tid < E ? hist[tid] : 0, &wcnt[1][0], &all);
+    if (tid < E) off_l[tid] = offsets[tid] = ex;
     if (tid == 0) off_l[E] = offsets[E] = (int32_t)P;
     __syncthreads();
     for (int j = 0; j < tt.n; ++j) {
@@ -199,7 +196,7 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t
         __syncthreads();
     }
     if (tid < E) base[tid] = off_l[tid];
-    scatter_rounds(ids, P, 0, (int)((P + PM_THREADS - 1) / PM_THREADS), E, base, wcnt, sorted_pair, pair_pos);
+    scatter_rounds(ids_l, P, 0, (int)((P + PM_THREADS - 1) / PM_THREADS), E, base, wcnt, sorted_pair, pair_pos);
 }
 
 size_t permute_ws_bytes(int64_t T, int k, int E) { return (size_t)pm_chunks(T * k) * (size_t)E * sizeof(int32_t); }

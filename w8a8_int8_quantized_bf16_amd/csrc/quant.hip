@@ -14,50 +14,13 @@
 // instruction, fully coalesced.  Rows of up to 512 * MAXC elements are held in
 // registers; longer rows are read twice (max pass, then code pass; the second
 // read hits L2).  The row maximum is a DPP reduction inside 16-lane rows plus
-// four lane reads.
-//
-// x / s is the IEEE quotient: with y = 1/s correctly rounded (one IEEE divide
-// per row), q0 = x*y, r = x - s*q0 (exact, by fma) and q = q0 + r*y (one fma)
-// give the correctly rounded x/s whenever no intermediate is subnormal
-// (Markstein's theorem).  That holds when s >= 2^-100: a subnormal x then has
-// |x/s| < 2^-26 and code 0 either way.  Rows with a smaller scale use the
-// divide itself.
+// four lane reads.  The per-element code (and the division behind it) is in
+// quant_common.h.
 #include "device_common.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace w8a8 {
-
-__device__ __forceinline__ uint32_t clamp_code(float q)
-{
-    float c = rintf(q);
-    c = fminf(fmaxf(c, -127.0f), 127.0f);
-    return (uint32_t)((int32_t)c) & 0xffu;
-}
-
-__device__ __forceinline__ uint32_t quant_code(float v, float s) { return clamp_code(v / s); }
-
-// fl(v / s) from the correctly rounded reciprocal y (see above)
-__device__ __forceinline__ uint32_t quant_code_fma(float v, float s, float y)
-{
-    const float q0 = v * y;
-    const float r = fmaf(-s, q0, v);
-    return clamp_code(fmaf(r, y, q0));
-}
-
-__device__ __forceinline__ uint2 pack8(const float v[8], float s, float y, bool fast)
-{
-    uint32_t c[8];
-    if (fast) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = quant_code_fma(v[i], s, y);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = quant_code(v[i], s);
-    }
-    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-}
-
-constexpr float QUANT_FAST_MIN_SCALE = 0x1p-100f;
 
 template <typename T>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const T *__restrict__ x, int64_t rows, int64_t cols,

@@ -21,6 +21,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace w8a8 {
 
@@ -411,12 +412,17 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
 // can: 8 fmas, 8 widening ops, one W load at a fixed offset from the row
 // base, two LDS reads.  (The fp32 copy of W_g would double the load
 // instructions; the bf16 rows are faster here.)
+//
+// With xq != nullptr the block has one more wave, which quantises the staged
+// token rows (per-token int8 codes and scale, the same arithmetic as the
+// quantisation kernels) while the other waves run their chains.
 template <int S, int TPW>
-__global__ __launch_bounds__(64 * S) void route_valu_kernel(const uint16_t *__restrict__ x,
-                                                            const uint16_t *__restrict__ wg, int64_t T_,
-                                                            int64_t H, int E, int k, int renorm,
-                                                            int32_t *__restrict__ ids, float *__restrict__ wout,
-                                                            float *__restrict__ logits_out)
+__global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t *__restrict__ x,
+                                                                  const uint16_t *__restrict__ wg, int64_t T_,
+                                                                  int64_t H, int E, int k, int renorm,
+                                                                  int32_t *__restrict__ ids, float *__restrict__ wout,
+                                                                  float *__restrict__ logits_out,
+                                                                  int8_t *__restrict__ xq, float *__restrict__ sx)
 {
     constexpr int D = 16;   // W_g steps (8 values each) in flight per lane
     constexpr int XP = 2;   // x steps read ahead from LDS
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(64 * S) void route_valu_kernel(const uint16_t *__re
 #pragma unroll
     for (int d = 0; d < D; ++d) load_w(d, wrow, 16 * d);
     // x rows into LDS (a token past T stages zeros; its result is never stored)
-    for (int64_t i = (int64_t)tid * 8; i < TPW * H; i += 64 * S * 8) {
+    for (int64_t i = (int64_t)tid * 8; i < TPW * H; i += (int64_t)blockDim.x * 8) {
         const int t = (int)(i / H);
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (tb + t < T_) load8_f32(x + (tb + t) * H + (i - (int64_t)t * H), v);
@@ -450,6 +456,35 @@ __global__ __launch_bounds__(64 * S) void route_valu_kernel(const uint16_t *__re
         *reinterpret_cast<float4 *>(xs + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
     __syncthreads();
+
+    if (wave == S) {   // the quantisation wave (present only when xq is given)
+        for (int t = 0; t < TPW && tb + t < T_; ++t) {
+            const float *xr = xs + t * H;
+            float amax = 0.0f;
+            for (int64_t c = (int64_t)lane * 8; c < H; c += 512) {
+                const float4 a = *reinterpret_cast<const float4 *>(xr + c);
+                const float4 b = *reinterpret_cast<const float4 *>(xr + c + 4);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+            }
+            amax = wave_max_nonneg(amax);
+            const float s = amax / 127.0f;
+            const float y = s > 0.0f ? 1.0f / s : 0.0f;
+            const bool fast = s >= QUANT_FAST_MIN_SCALE;
+            if (lane == 0) sx[tb + t] = s;
+            int8_t *qr = xq + (tb + t) * H;
+            for (int64_t c = (int64_t)lane * 8; c < H; c += 512) {
+                const float4 a = *reinterpret_cast<const float4 *>(xr + c);
+                const float4 b = *reinterpret_cast<const float4 *>(xr + c + 4);
+                const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                *reinterpret_cast<uint2 *>(qr + c) = s != 0.0f ? pack8(v, s, y, fast) : make_uint2(0u, 0u);
+            }
+        }
+    }
+    if (wave >= S) {   // no chain: meet the chain waves at the barrier before the top-k
+        __syncthreads();
+        return;
+    }
 
     auto widen_w = [&](int slot, float w8[8]) {
         const uint32_t u[4] = {wr[slot].x, wr[slot].y, wr[slot].z, wr[slot].w};
@@ -546,31 +581,38 @@ hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStre
     return hipGetLastError();
 }
 
+// Up to 512 (token, 64-expert slice) pairs and H <= 8192 (the token row in
+// LDS) the vector-ALU router runs; it can also quantise the tokens.
+bool route_fuses_quant(int dtype, int64_t T, int64_t H, int E)
+{
+    const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
+    return dtype == 0 && T * S <= 512 && H <= 8192;
+}
+
 hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
                              int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
-                             hipStream_t st)
+                             hipStream_t st, int8_t *xq, float *sx)
 {
     if (T == 0) return hipSuccess;
     if (dtype == 0) {
         const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
         const uint16_t *xb = (const uint16_t *)x;
         const void *wp = wg_f32 ? (const void *)wg_f32 : (const void *)wg;
-#ifndef RV_LIM
-#define RV_LIM 512
-#endif
-        if (T * S <= RV_LIM && H <= 8192) {
-            // few tokens: vector-ALU chains over the bf16 W_g, one token per wave
+        if (route_fuses_quant(dtype, T, H, E)) {
+            // few tokens: vector-ALU chains over the bf16 W_g, one token per block
             constexpr int TP = 1;
             const size_t lds = ((size_t)TP * H + 16) * sizeof(float);
+            const dim3 blk(64 * (S + (xq ? 1 : 0)));
             auto go = [&](auto kern) {
-                hipLaunchKernelGGL(kern, dim3((unsigned)((T + TP - 1) / TP)), dim3(64 * S), lds, st, xb, wg, T, H, E,
-                                   k, renormalize, ids, w, logits);
+                hipLaunchKernelGGL(kern, dim3((unsigned)((T + TP - 1) / TP)), blk, lds, st, xb, wg, T, H, E, k,
+                                   renormalize, ids, w, logits, xq, sx);
             };
             if (S == 1) go(route_valu_kernel<1, TP>);
             else if (S == 2) go(route_valu_kernel<2, TP>);
             else go(route_valu_kernel<4, TP>);
             return hipGetLastError();
         }
+        if (xq) return hipErrorInvalidValue;   // the caller quantises separately here
         dim3 g((unsigned)((T + 32 / S - 1) / (32 / S))), b(512);
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, g, b, 0, st, xb, wp, T, H, E, k, renormalize, ids, w, logits);

@@ -17,7 +17,7 @@ constexpr int TILES_MAX_G = 4096;   // groups a tile table supports (LDS prefix)
 
 // Exclusive prefix of the tile counts over the groups into pre[0..G] (LDS);
 // returns the total.  Called by all 256 threads of a block; sc is LDS scratch
-// of 256 ints.  offsets may be in LDS or global memory.
+// of at least 4 ints.  offsets may be in LDS or global memory.
 __device__ inline int tile_table_prefix(const int32_t *offsets, int G, int BM, int nbn, int32_t *pre, int32_t *sc)
 {
     const int tid = threadIdx.x;
@@ -25,17 +25,10 @@ __device__ inline int tile_table_prefix(const int32_t *offsets, int G, int BM, i
     for (int g0 = 0; g0 < G; g0 += 256) {
         const int g = g0 + tid;
         const int32_t cnt = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM * nbn : 0;
-        sc[tid] = cnt;
-        __syncthreads();
-        for (int d = 1; d < 256; d <<= 1) {
-            const int32_t v = tid >= d ? sc[tid - d] : 0;
-            __syncthreads();
-            sc[tid] += v;
-            __syncthreads();
-        }
-        if (g < G) pre[g] = carry + sc[tid] - cnt;
-        carry += sc[255];
-        __syncthreads();
+        int tot;
+        const int ex = block_excl_scan256(cnt, sc, &tot);
+        if (g < G) pre[g] = carry + ex;
+        carry += tot;
     }
     if (tid == 0) pre[G] = carry;
     __syncthreads();
@@ -43,22 +36,35 @@ __device__ inline int tile_table_prefix(const int32_t *offsets, int G, int BM, i
 }
 
 // Writes the descriptors {group, first grouped row, rows, column block} of
-// the tiles v = first, first + stride, ... below total, each at its dispatch
-// slot (see above).
+// the tiles, each at its dispatch slot (see above).  Thread `first` of
+// `stride` threads writes one contiguous run of tile numbers: it finds the
+// group of the run's first tile by bisection over pre and then walks the
+// groups forward.
 __device__ inline void tile_fill(const int32_t *offsets, int G, int BM, int nbn, const int32_t *pre, int total,
                                  int4 *__restrict__ tiles, int first, int stride)
 {
     const int q = total >> 3, r = total & 7;
-    for (int v = first; v < total; v += stride) {
-        int lo = 0, hi = G;   // largest g with pre[g] <= v
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (pre[mid] <= v) lo = mid;
-            else hi = mid;
+    const int chunk = (total + stride - 1) / stride;
+    int v = first * chunk;
+    const int vend = min(total, v + chunk);
+    if (v >= vend) return;
+    int lo = 0, hi = G;   // largest g with pre[g] <= v
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= v) lo = mid;
+        else hi = mid;
+    }
+    int g = lo, gend = pre[g + 1];
+    int32_t row_begin = offsets[g], rows_g = offsets[g + 1] - row_begin;
+    int mt_g = (rows_g + BM - 1) / BM;
+    for (; v < vend; ++v) {
+        while (v >= gend) {   // next non-empty group
+            ++g;
+            gend = pre[g + 1];
+            row_begin = offsets[g];
+            rows_g = offsets[g + 1] - row_begin;
+            mt_g = (rows_g + BM - 1) / BM;
         }
-        const int g = lo;
-        const int32_t row_begin = offsets[g], rows_g = offsets[g + 1] - row_begin;
-        const int mt_g = (rows_g + BM - 1) / BM;
         const int local = v - pre[g];
         const int nb = local / mt_g, mt = local - nb * mt_g;
         int x = 7;   // XCD x owns v in [x*q + min(x, r), (x+1)*q + min(x+1, r))
