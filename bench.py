@@ -48,9 +48,12 @@ def kernel_model(cfg, E_hit):
                              bytes=E_hit * 2 * I * H + E_hit * 2 * I * 4 + T * H + T * 4 + P * 4 + (E + 1) * 4
                              + P * I * 2)
     m["quant_h"] = dict(ops=0, bytes=P * I * 2 + P * I + P * 4)
+    # y (the per-pair expert outputs) is 16-bit fixed point with one exponent
+    # byte per row and 64 columns
+    ybytes = P * H * 2 + P * ((H + 63) // 64)
     m["down_gemm"] = dict(ops=2 * P * H * I, bytes=E_hit * H * I + E_hit * H * 4 + P * I + P * 4 + (E + 1) * 4
-                          + P * H * 4)
-    m["combine"] = dict(ops=0, bytes=P * H * 4 + P * 8 + T * H * xb)
+                          + ybytes)
+    m["combine"] = dict(ops=0, bytes=ybytes + P * 8 + T * H * xb)
     return m
 
 
@@ -157,6 +160,112 @@ def cpu_baseline(case, target_s):
                       "weights quantised by the oracle beforehand, untimed" % (n, cfg.T, cfg.name, dt)}
 
 
+def bench_dense(args, cfg):
+    """The dense W8A8 linear: one step = quantise x per token + one-group GEMM
+    with the dequantising epilogue (bf16 out); W quantised and packed once."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_int8_quantized_bf16_amd as w8
+    M, K, N = cfg.M, cfg.K, cfg.N
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    xb, Wf = synth.dense_inputs(cfg)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    qw, sw = w8.quant_act(torch.from_numpy(Wf).to(dev))
+    wbytes = N * K
+    copies = args.copies or max(1, min(4, (1 << 30) // wbytes + 1))
+    packs = [w8.pack_weights(qw.view(1, N, K)) for _ in range(copies)]
+    qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    nws = max(int(w8.lib().w8a8_grouped_gemm_workspace_size(M, N, 1)), 256)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    L, st = w8.lib(), w8._stream(x.device)
+    P = w8._p
+
+    def step(i, e0=None, e1=None):
+        rc = L.w8a8_quant_act(P(x), w8.BF16, M, K, K, P(qx), P(sx), st)
+        if rc:
+            raise SystemExit("w8a8_quant_act: %s" % w8.status_string(rc))
+        if e0 is not None:
+            e0.record()
+        rc = L.w8a8_grouped_gemm(P(qx), M, P(sx), None, 1, P(packs[i % copies]), w8.B_PACKED, P(sw), P(off), 1,
+                                 M, N, K, w8.EPI_DEQUANT, w8.BF16, P(out), P(ws), nws, st)
+        if rc:
+            raise SystemExit("w8a8_grouped_gemm: %s" % w8.status_string(rc))
+        if e1 is not None:
+            e1.record()
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, *evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gemm_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / args.steps
+    ops = 2 * M * N * K
+    byts = N * K + N * 4 + M * K + M * 4 + 8 + M * N * 2   # W codes + scales, x codes + scales, offsets, out
+    mfma_bound = ops / byts > RIDGE
+    if mfma_bound:
+        achieved, peak, unit = ops / (gemm_us * 1e-6) / 1e12, INT8_PEAK_TOPS, "TOP/s"
+    else:
+        achieved, peak, unit = byts / (gemm_us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    t_step = elapsed / args.steps
+    lbytes = N * K + N * 4 + M * K * 2 + M * N * 2   # W codes + scales, x in (bf16), out (bf16)
+    roof_t = max(ops / (INT8_PEAK_TOPS * 1e12), lbytes / (HBM_PEAK_GBS * 1e9))
+    result = {
+        "metric": "W8A8 linear tokens/s; int8 TOPS as % of MI355X roofline",
+        "value": M / t_step, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": M, "in_features": K, "out_features": N, "x_dtype": "bf16",
+                   "weight_copies_rotated": copies},
+        "roofline": {"kernel": "dense_gemm", "bound": "mfma" if mfma_bound else "hbm", "achieved": achieved,
+                     "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": None, "avg_launch_us": gemm_us,
+                     "alg_bytes_per_launch": byts, "int8_ops_per_launch": ops},
+        "layer": {"int8_tops": ops / t_step / 1e12, "int8_tops_frac": ops / t_step / 1e12 / INT8_PEAK_TOPS,
+                  "roof_time_us": roof_t * 1e6, "roofline_frac": roof_t / t_step,
+                  "stage_us": {"quant_x": round(t_step * 1e6 - gemm_us, 2), "gemm": round(gemm_us, 2)}},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_dense(cfg, xb, Wf, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_dense(cfg, xb, Wf, target_s):
+    """The CPU oracle, as is, on a bounded sample of the linear's rows."""
+    import numpy as np
+
+    import oracle
+    t0 = time.time()
+    qw, sw = oracle.quant_rows(Wf)
+    log("oracle weight quantisation (untimed setup): %.1f s" % (time.time() - t0))
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = np.sort(rng.choice(cfg.M, n, replace=False))
+        t0 = time.perf_counter()
+        qx, sx = oracle.quant_rows(np.ascontiguousarray(xb[rows]))
+        oracle.grouped_gemm(qx, sx, None, 1, qw[None], sw[None], np.array([0, n], np.int32), oracle.DEQUANT,
+                            oracle.BF16)
+        return time.perf_counter() - t0
+
+    n = 16
+    dt = run(n)
+    n2 = int(min(cfg.M, max(n, n * target_s / max(dt, 1e-6))))
+    if n2 > n:
+        n, dt = n2, run(n2)
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of the %d rows of %s (rows are independent), %.1f s of CPU time; weights quantised by "
+                      "the oracle beforehand, untimed" % (n, cfg.M, cfg.name, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,7 +280,7 @@ def main():
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_<stage>_<workload>.json from rocprofv3 counter files and exit")
     ap.add_argument("--traffic-kernel", nargs=3, metavar=("STAGE", "KERNEL_PREFIX", "SOURCE"),
-                    default=["gate_up_gemm", "void w8a8::grouped_gemm_kernel<64, 2, 2, 2, unsigned short, true>",
+                    default=["gate_up_gemm", "void w8a8::grouped_gemm_kernel<128, 2, 2, 2, unsigned short, true>",
                              "gemm.hip"])
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
@@ -193,6 +302,8 @@ def main():
     import synth
     import w8a8_int8_quantized_bf16_amd as w8
 
+    if args.workload in synth.DENSE_CONFIGS:
+        return bench_dense(args, synth.DENSE_CONFIGS[args.workload])
     cfg = synth.MOE_CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
