@@ -133,7 +133,7 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     };
     hipError_t e;
     if ((e = mark()) != hipSuccess) return hip_status(e);
-    // 1 route; with few tokens the router also quantises them (stage 2 is then empty)
+    // 1 route; with bf16 tokens the router also quantises them (stage 2 is then empty)
     const bool fused_q = route_fuses_quant(x_dtype, T, H, E);
     if ((e = launch_route_topk(x, x_dtype, W->w_gate, W->w_gate_f32, T, H, E, k, 1, ids, w, nullptr, st,
                                fused_q ? xq : nullptr, fused_q ? sx : nullptr)) != hipSuccess ||

@@ -247,37 +247,47 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x
 // A block is 8 wavefronts (two per SIMD, so that one wave's staging work and
 // LDS waits overlap the other's matrix work); each owns one slice of 64
 // experts (S slices) and one chunk of 4 tokens (8 / S chunks per block).
-// x and W_g are staged through LDS in 32-wide
+// x and W_g are staged through LDS in 32- or 64-wide
 // hidden slices, widened to fp32 once when staged (so the inner loop is LDS
-// reads and MFMAs only), rows padded to 144 bytes (the 16-byte reads of 16
-// consecutive rows hit distinct bank groups), three slices in flight in
+// reads and MFMAs only), rows padded to an odd number of 16-byte units (144
+// or 272 bytes: the 16-byte reads of 16 consecutive rows hit distinct bank
+// groups), three slices in flight in
 // registers.  Zero padding beyond H or E adds +0 * 0 terms, which leave every
 // chain unchanged.
 namespace {
-constexpr int RM_KC = 32;                  // hidden indices per staged slice
-constexpr int RM_ROW = RM_KC * 4 + 16;     // padded fp32 LDS row, bytes
 constexpr int RM_STAGES = 3;               // slices in flight (registers)
 }
 
 // WF32: W_g is given already widened to fp32 ([E][H]), staged by plain copies.
-template <int S, bool WF32>   // 64-expert slices (E <= 64 S), S in {1, 2, 4}
+// KC: hidden indices per staged slice, 32 or 64 (64 halves the barriers and
+// staging rounds of the chain; its LDS allows one block per CU, and 256
+// experts do not fit).
+template <int S, bool WF32, int KC>   // 64-expert slices (E <= 64 S), S in {1, 2, 4}
 __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restrict__ x,
                                                          const void *__restrict__ wg, int64_t T_, int64_t H,
                                                          int E, int k, int renorm, int32_t *__restrict__ ids,
-                                                         float *__restrict__ wout, float *__restrict__ logits_out)
+                                                         float *__restrict__ wout, float *__restrict__ logits_out,
+                                                         int8_t *__restrict__ xq, float *__restrict__ sx)
 {
+    static_assert(KC == 32 || (KC == 64 && S <= 2), "slice width");
+    constexpr int RM_KC = KC;
+    constexpr int RM_ROW = RM_KC * 4 + 16;   // padded fp32 LDS row, bytes (an odd number of 16-byte units)
+    constexpr int RM_PPR = RM_KC / 8;        // 16-byte bf16 pieces per row slice
     constexpr int NT = 512;                                    // threads
     constexpr int TC = 8 / S;                                  // 4-token chunks per block
     constexpr int WROWS = 64 * S, XROWS = 4 * TC;
-    constexpr int WPR = WF32 ? 8 : 4;                          // 16-byte pieces per W_g row slice
-    constexpr int WPIECES = WROWS * WPR, XPIECES = XROWS * 4;   // 16-byte pieces per slice
+    constexpr int WPR = WF32 ? 2 * RM_PPR : RM_PPR;            // 16-byte pieces per W_g row slice
+    constexpr int WPIECES = WROWS * WPR, XPIECES = XROWS * RM_PPR;   // 16-byte pieces per slice
     constexpr int WPT = (WPIECES + NT - 1) / NT, XPT = (XPIECES + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) unsigned char wl[2][WROWS * RM_ROW];
     __shared__ __attribute__((aligned(16))) unsigned char xl[2][XROWS * RM_ROW];
     __shared__ float lg[XROWS][WROWS + 1];
     __shared__ __attribute__((aligned(16))) uint32_t tk_scr[8][512];
+    __shared__ float qmax[XROWS];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int sl = wave % S, ch = wave / S;
+    static_assert(XPT == 1, "one x piece per thread and slice");
+    float xmax = 0.0f;   // largest |x| of the pieces this thread stages (one token row)
     const int64_t tb = (int64_t)blockIdx.x * XROWS;
     const int nsl = (int)((H + RM_KC - 1) / RM_KC);
 
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     }
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-        const int p = tid + j * NT, row = p >> 2, c = p & 3;
+        const int p = tid + j * NT, row = p / RM_PPR, c = p % RM_PPR;
         xoff[j] = (p < XPIECES && tb + row < T_) ? (int)((tb + row) * H * 2) + 16 * c : 0x7fffffff;
     }
     uint4 wr[RM_STAGES][WPT], xr[RM_STAGES][XPT];
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
         }
 #pragma unroll
         for (int j = 0; j < XPT; ++j) {
-            const int c = (tid + j * NT) & 3;
+            const int c = (tid + j * NT) % RM_PPR;
             const bool ok = xoff[j] != 0x7fffffff && slc * RM_KC + 8 * c < H;
             xr[st][j] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? xoff[j] + slc * RM_KC * 2 : 0x7fffffff, 0, 0));
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
         uint4 lo, hi;
         lo.x = u[0] << 16; lo.y = u[0] & 0xffff0000u; lo.z = u[1] << 16; lo.w = u[1] & 0xffff0000u;
         hi.x = u[2] << 16; hi.y = u[2] & 0xffff0000u; hi.z = u[3] << 16; hi.w = u[3] & 0xffff0000u;
-        unsigned char *d = base + (p >> 2) * RM_ROW + 32 * (p & 3);
+        unsigned char *d = base + (p / RM_PPR) * RM_ROW + 32 * (p % RM_PPR);
         *reinterpret_cast<uint4 *>(d) = lo;
         *reinterpret_cast<uint4 *>(d + 16) = hi;
     };
@@ -338,7 +348,15 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
             }
         } else {
             const int p = tid + (item - WPT) * NT;
-            if (p < XPIECES) put(xl[buf], p, xr[st][item - WPT]);
+            if (p < XPIECES) {
+                const uint4 v = xr[st][item - WPT];
+                put(xl[buf], p, v);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xmax = fmaxf(xmax, fmaxf(__uint_as_float((u[i] << 16) & 0x7fffffffu),
+                                             __uint_as_float(u[i] & 0x7fff0000u)));
+            }
         }
     };
 
@@ -397,6 +415,34 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
 #pragma unroll
         for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? lg[tt][lane + 64 * j] : 0.0f;
         select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
+    }
+
+    // Per-token int8 codes of the block's tokens, when asked for: every x
+    // element passed through this block's staging, whose pieces of one token
+    // row are staged by RM_PPR consecutive lanes, so the row maxima are a
+    // reduction over those lanes; the codes then take a second (L2-resident)
+    // read of the rows, with the quantisation kernels' arithmetic.
+    if (xq) {
+        float m = xmax;
+#pragma unroll
+        for (int o = 1; o < RM_PPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (tid < XPIECES && tid % RM_PPR == 0) qmax[tid / RM_PPR] = m;
+        __syncthreads();
+        constexpr int TPR = NT / XROWS;   // threads per token row
+        const int row = tid / TPR, t8 = tid % TPR;
+        const int64_t t = tb + row;
+        if (t < T_) {
+            const float amax = qmax[row];
+            const float s = amax / 127.0f;
+            const float y = s > 0.0f ? 1.0f / s : 0.0f;
+            const bool fast = s >= QUANT_FAST_MIN_SCALE;
+            if (t8 == 0) sx[t] = s;
+            for (int64_t c = (int64_t)t8 * 8; c < H; c += TPR * 8) {
+                float v[8];
+                load8_f32(x + t * H + c, v);
+                *reinterpret_cast<uint2 *>(xq + t * H + c) = s != 0.0f ? pack8(v, s, y, fast) : make_uint2(0u, 0u);
+            }
+        }
     }
 }
 
@@ -582,12 +628,15 @@ hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStre
 }
 
 // Up to 512 (token, 64-expert slice) pairs and H <= 8192 (the token row in
-// LDS) the vector-ALU router runs; it can also quantise the tokens.
-bool route_fuses_quant(int dtype, int64_t T, int64_t H, int E)
+// LDS) the vector-ALU router runs, above that the matrix-core one; with bf16
+// tokens both can also quantise them.
+static bool route_valu_path(int64_t T, int64_t H, int E)
 {
     const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
-    return dtype == 0 && T * S <= 512 && H <= 8192;
+    return T * S <= 512 && H <= 8192;
 }
+
+bool route_fuses_quant(int dtype, int64_t, int64_t, int) { return dtype == 0; }
 
 hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
                              int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
@@ -598,7 +647,7 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
         const int S = E <= 64 ? 1 : (E <= 128 ? 2 : 4);
         const uint16_t *xb = (const uint16_t *)x;
         const void *wp = wg_f32 ? (const void *)wg_f32 : (const void *)wg;
-        if (route_fuses_quant(dtype, T, H, E)) {
+        if (route_valu_path(T, H, E)) {
             // few tokens: vector-ALU chains over the bf16 W_g, one token per block
             constexpr int TP = 1;
             const size_t lds = ((size_t)TP * H + 16) * sizeof(float);
@@ -612,14 +661,19 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
             else go(route_valu_kernel<4, TP>);
             return hipGetLastError();
         }
-        if (xq) return hipErrorInvalidValue;   // the caller quantises separately here
-        dim3 g((unsigned)((T + 32 / S - 1) / (32 / S))), b(512);
+        const int64_t nblk = (T + 32 / S - 1) / (32 / S);
+        dim3 g((unsigned)nblk), b(512);
         auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, g, b, 0, st, xb, wp, T, H, E, k, renormalize, ids, w, logits);
+            hipLaunchKernelGGL(kern, g, b, 0, st, xb, wp, T, H, E, k, renormalize, ids, w, logits, xq, sx);
         };
-        if (S == 1) wg_f32 ? go(route_mfma_kernel<1, true>) : go(route_mfma_kernel<1, false>);
-        else if (S == 2) wg_f32 ? go(route_mfma_kernel<2, true>) : go(route_mfma_kernel<2, false>);
-        else wg_f32 ? go(route_mfma_kernel<4, true>) : go(route_mfma_kernel<4, false>);
+        // 64-wide slices while the blocks fit one per CU; 32-wide (two blocks
+        // per CU) beyond
+        const bool wide = S <= 2 && nblk <= 256;
+        if (S == 1 && wide) wg_f32 ? go(route_mfma_kernel<1, true, 64>) : go(route_mfma_kernel<1, false, 64>);
+        else if (S == 1) wg_f32 ? go(route_mfma_kernel<1, true, 32>) : go(route_mfma_kernel<1, false, 32>);
+        else if (S == 2 && wide) wg_f32 ? go(route_mfma_kernel<2, true, 64>) : go(route_mfma_kernel<2, false, 64>);
+        else if (S == 2) wg_f32 ? go(route_mfma_kernel<2, true, 32>) : go(route_mfma_kernel<2, false, 32>);
+        else wg_f32 ? go(route_mfma_kernel<4, true, 32>) : go(route_mfma_kernel<4, false, 32>);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((T + RT_TOK - 1) / RT_TOK)), block(256);
