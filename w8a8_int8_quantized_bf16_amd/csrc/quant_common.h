@@ -16,11 +16,15 @@
 
 namespace w8a8 {
 
+// clamp(rint(q), -127, 127) as a byte.  The bounds are integers, so clamping
+// first and rounding after gives the same integer (NaN clamps to -127 either
+// way); adding 1.5 * 2^23 rounds the clamped value half-to-even into the low
+// mantissa bits, whose low byte is then the two's-complement code.
+// (the byte is the low byte of the returned word; the other bits are junk)
 __device__ __forceinline__ uint32_t clamp_code(float q)
 {
-    float c = rintf(q);
-    c = fminf(fmaxf(c, -127.0f), 127.0f);
-    return (uint32_t)((int32_t)c) & 0xffu;
+    const float c = fminf(fmaxf(q, -127.0f), 127.0f);
+    return __float_as_uint(c + 12582912.0f);
 }
 
 __device__ __forceinline__ uint32_t quant_code(float v, float s) { return clamp_code(v / s); }
@@ -33,6 +37,14 @@ __device__ __forceinline__ uint32_t quant_code_fma(float v, float s, float y)
     return clamp_code(fmaf(r, y, q0));
 }
 
+// the low bytes of four words, in order, as one word (three byte permutes)
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3)
+{
+    const uint32_t p01 = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);   // [c0.b0, c1.b0, 0, 0]
+    const uint32_t p23 = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);   // [c2.b0, c3.b0, 0, 0]
+    return __builtin_amdgcn_perm(p23, p01, 0x05040100u);              // [c0, c1, c2, c3]
+}
+
 __device__ __forceinline__ uint2 pack8(const float v[8], float s, float y, bool fast)
 {
     uint32_t c[8];
@@ -43,7 +55,7 @@ __device__ __forceinline__ uint2 pack8(const float v[8], float s, float y, bool 
 #pragma unroll
         for (int i = 0; i < 8; ++i) c[i] = quant_code(v[i], s);
     }
-    return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+    return make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]), pack_low_bytes(c[4], c[5], c[6], c[7]));
 }
 
 constexpr float QUANT_FAST_MIN_SCALE = 0x1p-100f;
