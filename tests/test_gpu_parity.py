@@ -494,6 +494,26 @@ def test_layer_determinism_and_token_shuffle():
     assert torch.equal(out_s.view(torch.int16), out1[:37].view(torch.int16))
 
 
+@pytest.mark.parametrize("T", [1, 255, 256, 257, 1000])
+def test_layer_router_quantises_tokens(T):
+    """With bf16 tokens the router also writes their int8 codes and scales
+    (the vector-ALU router up to 256 tokens here, the matrix-core one above,
+    ragged last blocks included): ids, weights, codes and scales bit-exact."""
+    case = get_case("moe_30b_prefill_T4096")
+    cfg = case.cfg
+    xd = case.xd[:T].contiguous()
+    ws = w8.moe_layer_workspace(case.W, T, w8.BF16)
+    w8.moe_layer(case.W, xd, ws=ws)
+    torch.cuda.synchronize()
+    inter = w8.moe_layer_intermediates(case.W, T, ws, w8.BF16)
+    x = case.x[:T]
+    oids, ow, _ = oracle.route_topk(x, case.wg, cfg.k)
+    assert np.array_equal(to_host(inter["ids"]), oids)
+    assert np.abs(to_host(inter["w"]) - ow).max() <= 2e-6
+    oxq, osx = oracle.quant_rows(x)
+    assert np.array_equal(to_host(inter["xq"]), oxq) and np.array_equal(to_host(inter["sx"]), osx)
+
+
 def test_layer_with_stage_events():
     """The timing entry point records its events (all, or only the non-null
     ones) and computes the same layer bit for bit."""
