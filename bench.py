@@ -266,6 +266,83 @@ def cpu_baseline_dense(cfg, xb, Wf, target_s):
                       "the oracle beforehand, untimed" % (n, cfg.M, cfg.name, dt)}
 
 
+def bench_ep_shares(args, cfg, ngpu):
+    """One GPU's share under ngpu-way expert parallelism, at its real shape:
+    the routed, quantised pairs of experts [g*E/ngpu, (g+1)*E/ngpu) (taken
+    from a full layer run on this GPU, as an all-to-all would deliver them)
+    through gate_up GEMM + SwiGLU, h quantisation and the down GEMM, for every
+    g.  The layer would run at the pace of the slowest share; the exchanges
+    themselves are not part of this (one GPU)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w8a8_int8_quantized_bf16_amd as w8
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    if E % ngpu:
+        raise SystemExit("%d experts do not split over %d GPUs" % (E, ngpu))
+    x, wg, gu, dn = synth.moe_inputs(cfg)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    wgd = torch.from_numpy(wg.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = w8.MoEWeights.quantize(wgd, torch.from_numpy(gu).to(dev), torch.from_numpy(dn).to(dev), k)
+    del gu, dn
+    ws = w8.moe_layer_workspace(W, T, w8.BF16, dev)
+    w8.moe_layer(W, xd, ws=ws)
+    torch.cuda.synchronize()
+    inter = w8.moe_layer_intermediates(W, T, ws, w8.BF16)
+    off = inter["offsets"].cpu().numpy().astype(np.int64)
+    per = E // ngpu
+    gbu = int(w8.lib().w8a8_packed_weights_size(1, 2 * I, H))
+    gbd = int(w8.lib().w8a8_packed_weights_size(1, H, I))
+    shares = []
+    for g in range(ngpu):
+        e0, e1 = g * per, (g + 1) * per
+        r0, r1 = int(off[e0]), int(off[e1])
+        rows = r1 - r0
+        loc_off = torch.from_numpy((off[e0:e1 + 1] - r0).astype(np.int32)).to(dev)
+        sp = inter["sorted_pair"][r0:r1].clone()   # its own (16-byte aligned) buffer
+        Bgu, sgu = W.p_gate_up[e0 * gbu:e1 * gbu], W.s_gate_up[e0:e1]
+        Bd, sd = W.p_down[e0 * gbd:e1 * gbd], W.s_down[e0:e1]
+
+        def step():
+            h = w8.grouped_gemm(inter["xq"], inter["sx"], sp, k, Bgu, sgu, loc_off, w8.EPI_DEQUANT_SWIGLU, w8.BF16,
+                                M_total=rows, b_shape=(per, 2 * I, H))
+            hq, sh = w8.quant_act(h)
+            w8.grouped_gemm(hq, sh, None, 1, Bd, sd, loc_off, w8.EPI_DEQUANT, w8.BF16, M_total=rows,
+                            b_shape=(per, H, I))
+
+        for _ in range(args.warmup):
+            step()
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record()
+        for _ in range(args.steps):
+            step()
+        e_b.record()
+        torch.cuda.synchronize()
+        us = e_a.elapsed_time(e_b) * 1e3 / args.steps
+        ops = 2 * rows * 3 * H * I
+        wbytes = per * 3 * H * I
+        shares.append({"gpu": g, "experts": [e0, e1], "rows": rows, "us": round(us, 2),
+                       "int8_tops": ops / us / 1e6, "weight_gbs": wbytes / us / 1e3})
+        log("share %d: experts %d..%d, %d rows, %.1f us" % (g, e0, e1 - 1, rows, us))
+    slow = max(shares, key=lambda r: r["us"])
+    result = {
+        "metric": "W8A8 MoE expert compute of one GPU's share under %d-way expert parallelism "
+                  "(tokens/s of the layer at the pace of the slowest share; all-to-all not included)" % ngpu,
+        "value": T / (slow["us"] * 1e-6), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": slow["us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": cfg.name + "_ep%d_share" % ngpu, "tokens": T, "hidden": H, "experts": E,
+                   "experts_per_gpu": per, "top_k": k, "expert_intermediate": I,
+                   "placement": "contiguous expert indices"},
+        "roofline": None,
+        "shares": shares,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +351,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ep-share", type=int, default=0, metavar="G",
+                    help="time each GPU's share of the workload's experts under G-way expert parallelism")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of MIB MiB (counter calibration) and exit")
@@ -304,6 +383,8 @@ def main():
 
     if args.workload in synth.DENSE_CONFIGS:
         return bench_dense(args, synth.DENSE_CONFIGS[args.workload])
+    if args.ep_share:
+        return bench_ep_shares(args, synth.MOE_CONFIGS[args.workload], args.ep_share)
     cfg = synth.MOE_CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
