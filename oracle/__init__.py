@@ -53,6 +53,10 @@ def lib():
         L.oracle_combine.argtypes = [P, i32, P, P, i64, i32, i64, P, i32]
         L.oracle_moe_layer.argtypes = [P, i32, i64, i64, i32, i32, i64, P, P, P, P, P, P] + [P] * 12
         L.oracle_moe_layer_tokens.argtypes = [P, i32, i64, i32, i32, i64, P, P, P, P, P, P, i64, P]
+        L.oracle_quant_w4_rows.argtypes = [P, i64, i64, P, P, P]
+        L.oracle_w4a8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, P, i32, i64, i64, i32, i32, P]
+        L.oracle_moe_layer_w4.argtypes = [P, i32, i64, i64, i32, i32, i64, P, P, P, P, P, P, P] + [P] * 10
+        L.oracle_moe_layer_w4_tokens.argtypes = [P, i32, i64, i32, i32, i64, P, P, P, P, P, P, P, i64, P]
         L.oracle_num_threads.restype = i32
         L.oracle_f64_to_bf16.argtypes = [d]
         L.oracle_f64_to_bf16.restype = ctypes.c_uint16
@@ -213,3 +217,82 @@ def moe_layer_tokens(x, wg, wgu, sgu, wd, sd, k, tokens):
 def bf16_bits_to_f32(b):
     """Widen bf16 bit patterns to float32 (exact)."""
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------- W4A8 ---
+
+W4_GROUP = 128
+
+
+def quant_w4_rows(w):
+    """W4 codes of fp32 weights [rows, cols] (R17): (codes int8 [rows, cols] in
+    [-8, 7], scales fp32 [rows, ceil(cols/128)], offsets int8 [rows, ceil(cols/128)])."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    ng = (cols + W4_GROUP - 1) // W4_GROUP
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty((rows, ng), np.float32)
+    o = np.empty((rows, ng), np.int8)
+    lib().oracle_quant_w4_rows(_p(w), rows, cols, _p(q), _p(s), _p(o))
+    return q, s, o
+
+
+def w4a8_grouped_gemm(A, a_scales, gather, gather_div, Bq, b_scales, b_offs, offsets, epilogue, out_dtype=BF16):
+    """Grouped W4A8 GEMM (epilogue DEQUANT or DEQUANT_SWIGLU): Bq [G,N,K] codes,
+    b_scales / b_offs [G,N,ceil(K/128)]."""
+    A = _c(A, np.int8)
+    Bq = _c(Bq, np.int8)
+    a_scales = _c(a_scales, np.float32)
+    b_scales = _c(b_scales, np.float32)
+    b_offs = _c(b_offs, np.int8)
+    offsets = _c(offsets, np.int32)
+    G, N, K = Bq.shape
+    M = int(offsets[-1]) if gather is None else len(gather)
+    gather = None if gather is None else _c(gather, np.int32)
+    ncol = N if epilogue == DEQUANT else N // 2
+    out = np.empty((M, ncol), np.uint16 if out_dtype == BF16 else np.float32)
+    lib().oracle_w4a8_grouped_gemm(_p(A), _p(a_scales), _p(gather), int(gather_div), _p(Bq), _p(b_scales),
+                                   _p(b_offs), _p(offsets), G, N, K, epilogue, out_dtype, _p(out))
+    return out
+
+
+def moe_layer_w4(x, wg, wgu4, sgu4, ogu4, wd, sd, k, intermediates=False):
+    """The layer with W4A8 gate_up weights (codes [E,2I,H], scales / offsets
+    [E,2I,ceil(H/128)]) and W8A8 down weights."""
+    x = np.ascontiguousarray(x)
+    dt = _xdtype(x)
+    wgu4 = _c(wgu4, np.int8)
+    E, twoI, H = wgu4.shape
+    I = twoI // 2
+    T = x.shape[0]
+    P = T * k
+    out = np.empty((T, H), x.dtype)
+    inter = {}
+    if intermediates:
+        inter = dict(
+            ids=np.empty((T, k), np.int32), w=np.empty((T, k), np.float32),
+            xq=np.empty((T, H), np.int8), sx=np.empty(T, np.float32),
+            offsets=np.empty(E + 1, np.int32), sorted_pair=np.empty(P, np.int32),
+            pair_pos=np.empty(P, np.int32), h=np.empty((P, I), np.uint16), hq=np.empty((P, I), np.int8),
+            sh=np.empty(P, np.float32))
+    g = inter.get
+    lib().oracle_moe_layer_w4(_p(x), dt, T, H, E, k, I, _p(_c(wg, np.uint16)), _p(wgu4),
+                              _p(_c(sgu4, np.float32)), _p(_c(ogu4, np.int8)), _p(_c(wd, np.int8)),
+                              _p(_c(sd, np.float32)), _p(out),
+                              _p(g("ids")), _p(g("w")), _p(g("xq")), _p(g("sx")), _p(g("offsets")),
+                              _p(g("sorted_pair")), _p(g("pair_pos")), _p(g("h")), _p(g("hq")), _p(g("sh")))
+    return (out, inter) if intermediates else out
+
+
+def moe_layer_w4_tokens(x, wg, wgu4, sgu4, ogu4, wd, sd, k, tokens):
+    """Rows `tokens` of the W4A8-gate_up layer output."""
+    x = np.ascontiguousarray(x)
+    dt = _xdtype(x)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    E, twoI, H = wgu4.shape
+    I = twoI // 2
+    out = np.empty((len(tok), H), x.dtype)
+    lib().oracle_moe_layer_w4_tokens(_p(x), dt, H, E, k, I, _p(_c(wg, np.uint16)), _p(_c(wgu4, np.int8)),
+                                     _p(_c(sgu4, np.float32)), _p(_c(ogu4, np.int8)), _p(_c(wd, np.int8)),
+                                     _p(_c(sd, np.float32)), _p(tok), len(tok), _p(out))
+    return out

@@ -21,6 +21,8 @@
  *                "input_activations" parameter lists.
  *   [235B-FILES] "Qwen3-235B-A22B-quantized.w8a8" file-structure guide: model
  *                overview table, shard contents, W8A8 section.
+ *   [1.7B-W4A8]  "Qwen3-1.7B-W4A8 on Ascend": the W4A8 variant (4-bit weights
+ *                in groups of 128 with scale/offset, two's-complement packing).
  *   [NEXT-AMCT]  "Qwen3-Next-80B-A3B-Instruct in AMCT" adaptation case:
  *                section 2.2 (packed gate_up_proj / down_proj), section 6
  *                (packed MoE GMM performance note).
@@ -43,6 +45,18 @@
  *       for down_proj; down_proj is int8 like gate/up ([235B-FILES]).
  *   R11 the permutation inside one expert's group is by ascending pair index
  *       p = t * k + j.
+ *   R17 W4A8 (the next row after the W8A8 layer): gate_up_proj expert weights
+ *       in 4 bits, groups of 128 consecutive inputs of one output channel
+ *       (the last group of a row may be shorter), each with an fp32 scale and
+ *       an integer offset ([1.7B-W4A8] "4bit 权重" items 1-2: group_size 128
+ *       with a scale/offset per group, two's-complement 4-bit codes).  The
+ *       plainest asymmetric min-max reading: the range [min(w, 0), max(w, 0)]
+ *       (zero always representable) is split into 15 steps, s = (max - min)/15
+ *       (one fp32 divide), z = rint(-min / s) in [0, 15], u = clamp(rint(w / s)
+ *       + z, 0, 15); stored code q = u - 8 in [-8, 7], offset o = z - 8 in
+ *       [-8, 7]; w ~ (q - o) * s.  A group of zeros has s = 0, codes and
+ *       offset 0.  down_proj stays W8A8 (the page keeps down_proj in higher
+ *       precision); activations are the same per-token int8 codes.
  *   Floating-point results that are compared within a tolerance (dequantised
  *   GEMM outputs, SwiGLU, softmax weights, the combine) are computed here in
  *   fp64.  Floating-point work that decides an integer (int8 codes, top-k
@@ -258,6 +272,61 @@ static int32_t or_dot_i8(const int8_t *a, const int8_t *b, int64_t K)
     return acc;
 }
 
+/* -------------------------------------------------------------- W4 codes --- */
+
+/* One group of n <= 128 weights of one output channel (R17). */
+static void or_quant_w4_group(const float *w, int64_t n, int8_t *q, float *scale, int8_t *off)
+{
+    float mn = 0.0f, mx = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        if (w[i] < mn) mn = w[i];
+        if (w[i] > mx) mx = w[i];
+    }
+    float s = (mx - mn) / 15.0f;
+    *scale = s;
+    if (s == 0.0f) {
+        *off = 0;
+        for (int64_t i = 0; i < n; ++i) q[i] = 0;
+        return;
+    }
+    float z = rintf(-mn / s);
+    *off = (int8_t)(z - 8.0f);
+    for (int64_t i = 0; i < n; ++i) {
+        float u = rintf(w[i] / s) + z;
+        if (u < 0.0f) u = 0.0f;
+        if (u > 15.0f) u = 15.0f;
+        q[i] = (int8_t)(u - 8.0f);
+    }
+}
+
+/* rows x cols fp32 weights -> codes [rows][cols] in [-8, 7] (one per byte),
+ * scales and offsets [rows][ceil(cols / 128)]. */
+void oracle_quant_w4_rows(const float *w, int64_t rows, int64_t cols, int8_t *q, float *scales, int8_t *offs)
+{
+    int64_t ng = (cols + 127) / 128, r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < ng; ++g) {
+            int64_t c0 = g * 128, n = cols - c0 < 128 ? cols - c0 : 128;
+            or_quant_w4_group(w + r * cols + c0, n, q + r * cols + c0, &scales[r * ng + g], &offs[r * ng + g]);
+        }
+}
+
+/* sum over the groups g of s_g * sum_{k in g} a_k * (q_k - o_g): each group's
+ * integer sum is exact, the sum over groups is fp64. */
+static double or_dot_w4(const int8_t *a, const int8_t *q, const float *scale, const int8_t *off, int64_t K)
+{
+    double acc = 0.0;
+    int64_t ng = (K + 127) / 128;
+    for (int64_t g = 0; g < ng; ++g) {
+        int32_t sum = 0;
+        for (int64_t kk = g * 128; kk < K && kk < (g + 1) * 128; ++kk)
+            sum += (int32_t)a[kk] * ((int32_t)q[kk] - (int32_t)off[g]);
+        acc += (double)scale[g] * (double)sum;
+    }
+    return acc;
+}
+
 static double or_silu(double g) { return g / (1.0 + exp(-g)); }
 
 /* Output casts: dtype 0 bf16 (one RNE rounding of the fp64 value), 1 fp32. */
@@ -313,6 +382,46 @@ void oracle_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *
     }
 }
 
+/*
+ * Grouped W4A8 GEMM: as the W8A8 one with epilogue 1 or 2, the weights being
+ * W4 codes Bq [G][N][K] (one per byte) with scales / offsets [G][N][ceil(K/128)]:
+ *   acc(r, n) = sum_g s[g][n][kg] * sum_{k in kg} A[a][k] * (Bq[g][n][k] - o[g][n][kg])
+ *   1 DEQUANT        out = acc * a_scales[a]
+ *   2 DEQUANT_SWIGLU out = silu(gate) * up on columns [0, N/2) and [N/2, N)
+ */
+void oracle_w4a8_grouped_gemm(const int8_t *A, const float *a_scales, const int32_t *gather, int gather_div,
+                              const int8_t *Bq, const float *b_scales, const int8_t *b_offs,
+                              const int32_t *offsets, int G, int64_t N, int64_t K, int epilogue, int out_dtype,
+                              void *out)
+{
+    int64_t ng = (K + 127) / 128;
+    for (int g = 0; g < G; ++g) {
+        int64_t r;
+#pragma omp parallel for schedule(static)
+        for (r = offsets[g]; r < offsets[g + 1]; ++r) {
+            int64_t a = gather ? gather[r] / gather_div : r;
+            const int8_t *arow = A + a * K;
+            const int8_t *Bg = Bq + (int64_t)g * N * K;
+            const float *sg = b_scales + (int64_t)g * N * ng;
+            const int8_t *og = b_offs + (int64_t)g * N * ng;
+            if (epilogue == 1) {
+                for (int64_t n = 0; n < N; ++n) {
+                    double acc = or_dot_w4(arow, Bg + n * K, sg + n * ng, og + n * ng, K);
+                    or_store(out, out_dtype, r * N + n, acc * (double)a_scales[a]);
+                }
+            } else {
+                int64_t Ih = N / 2;
+                for (int64_t n = 0; n < Ih; ++n) {
+                    double gate = or_dot_w4(arow, Bg + n * K, sg + n * ng, og + n * ng, K) * (double)a_scales[a];
+                    double up = or_dot_w4(arow, Bg + (Ih + n) * K, sg + (Ih + n) * ng, og + (Ih + n) * ng, K) *
+                                (double)a_scales[a];
+                    or_store(out, out_dtype, r * Ih + n, or_silu(gate) * up);
+                }
+            }
+        }
+    }
+}
+
 /* ---------------------------------------------------------------- combine --- */
 
 /*
@@ -359,12 +468,13 @@ void oracle_combine(const void *y, int y_dtype, const float *w, const int32_t *p
  *   acc_d [T*k][H] int32.
  * out [T][H] has the dtype of x.
  */
-void oracle_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
-                      const uint16_t *wg, const int8_t *wgu, const float *sgu,
-                      const int8_t *wd, const float *sd, void *out,
-                      int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
-                      int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
-                      int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o)
+static void or_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
+                         const uint16_t *wg, const int8_t *wgu, const float *sgu,
+                         const int8_t *wgu4, const float *sgu4, const int8_t *ogu4,
+                         const int8_t *wd, const float *sd, void *out,
+                         int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
+                         int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
+                         int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o)
 {
     int64_t P = T * k;
     int32_t *ids = ids_o ? ids_o : (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
@@ -393,6 +503,16 @@ void oracle_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int
         int64_t t = p / k;
         int64_t e = ids[p];
         const int8_t *arow = xq + t * H;
+        if (wgu4) {   /* W4A8 gate_up (R17) */
+            int64_t ng = (H + 127) / 128;
+            for (int64_t n = 0; n < I; ++n) {
+                int64_t rg = e * 2 * I + n, ru = e * 2 * I + I + n;
+                double gate = or_dot_w4(arow, wgu4 + rg * H, sgu4 + rg * ng, ogu4 + rg * ng, H) * (double)sx[t];
+                double up = or_dot_w4(arow, wgu4 + ru * H, sgu4 + ru * ng, ogu4 + ru * ng, H) * (double)sx[t];
+                h[r * I + n] = or_f64_to_bf16(or_silu(gate) * up);
+            }
+            continue;
+        }
         for (int64_t n = 0; n < I; ++n) {
             int32_t ag = or_dot_i8(arow, wgu + (e * 2 * I + n) * H, H);
             int32_t au = or_dot_i8(arow, wgu + (e * 2 * I + I + n) * H, H);
@@ -432,6 +552,30 @@ void oracle_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int
     free(y);
 }
 
+void oracle_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
+                      const uint16_t *wg, const int8_t *wgu, const float *sgu,
+                      const int8_t *wd, const float *sd, void *out,
+                      int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
+                      int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
+                      int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o)
+{
+    or_moe_layer(x, dtype, T, H, E, k, I, wg, wgu, sgu, NULL, NULL, NULL, wd, sd, out, ids_o, w_o, xq_o, sx_o,
+                 offsets_o, sorted_o, pos_o, acc_gu_o, h_o, hq_o, sh_o, acc_d_o);
+}
+
+/* The layer with W4A8 gate_up weights (R17): codes wgu4 [E][2I][H], scales
+ * and offsets [E][2I][ceil(H/128)]; down_proj W8A8 as above. */
+void oracle_moe_layer_w4(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
+                         const uint16_t *wg, const int8_t *wgu4, const float *sgu4, const int8_t *ogu4,
+                         const int8_t *wd, const float *sd, void *out,
+                         int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
+                         int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
+                         uint16_t *h_o, int8_t *hq_o, float *sh_o)
+{
+    or_moe_layer(x, dtype, T, H, E, k, I, wg, NULL, NULL, wgu4, sgu4, ogu4, wd, sd, out, ids_o, w_o, xq_o, sx_o,
+                 offsets_o, sorted_o, pos_o, NULL, h_o, hq_o, sh_o, NULL);
+}
+
 /*
  * The same layer restricted to a subset of tokens.  The layer has no term that
  * couples tokens (each token's output depends on its own row of x only), so the
@@ -449,5 +593,18 @@ void oracle_moe_layer_tokens(const void *x, int dtype, int64_t H, int E, int k, 
         memcpy(xs + esz * (size_t)(i * H), (const unsigned char *)x + esz * (size_t)(tok[i] * H), esz * (size_t)H);
     oracle_moe_layer(xs, dtype, n, H, E, k, I, wg, wgu, sgu, wd, sd, out,
                      NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+    free(xs);
+}
+
+void oracle_moe_layer_w4_tokens(const void *x, int dtype, int64_t H, int E, int k, int64_t I,
+                                const uint16_t *wg, const int8_t *wgu4, const float *sgu4, const int8_t *ogu4,
+                                const int8_t *wd, const float *sd, const int64_t *tok, int64_t n, void *out)
+{
+    size_t esz = dtype == 0 ? 2 : 4;
+    unsigned char *xs = (unsigned char *)malloc(esz * (size_t)(n * H));
+    for (int64_t i = 0; i < n; ++i)
+        memcpy(xs + esz * (size_t)(i * H), (const unsigned char *)x + esz * (size_t)(tok[i] * H), esz * (size_t)H);
+    oracle_moe_layer_w4(xs, dtype, n, H, E, k, I, wg, wgu4, sgu4, ogu4, wd, sd, out,
+                        NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
     free(xs);
 }

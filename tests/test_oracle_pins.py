@@ -497,3 +497,119 @@ def test_combine_closed_form(orc):
     assert np.array_equal(out[1], 0.25 * y[3] + 0.75 * y[1])
     outb = orc.combine(synth.f32_to_bf16_bits(y), w, pair_pos, orc.BF16)
     assert np.array_equal(synth.bf16_bits_to_f32(outb), out)   # all values bf16-exact
+
+
+# -------------------------------------------------------------------- W4A8 ---
+
+def _w4_dequant(q, s, o):
+    """(q - o) * s per group of 128 columns, in float64."""
+    rows, cols = q.shape
+    out = np.empty((rows, cols))
+    for g in range(s.shape[1]):
+        c0, c1 = 128 * g, min(cols, 128 * g + 128)
+        out[:, c0:c1] = (q[:, c0:c1].astype(np.float64) - o[:, g:g + 1]) * s[:, g:g + 1].astype(np.float64)
+    return out
+
+
+def test_w4_codes_reconstruct_within_half_a_step(orc):
+    """Every weight is within half a quantisation step of (q - o) * s, up to
+    the rounding of s and w / s (an element whose u would be 16 by a tie is
+    clamped: within one step); codes and offsets are 4-bit two's complement."""
+    rng = np.random.default_rng(11)
+    for cols in (128, 300, 64, 1536):
+        w = (rng.standard_t(4, (6, cols)) * 0.02).astype(np.float32)
+        w[1] = np.abs(w[1])          # one-signed rows: zero is an end of the range
+        w[2] = -np.abs(w[2])
+        q, s, o = orc.quant_w4_rows(w)
+        assert q.min() >= -8 and q.max() <= 7 and o.min() >= -8 and o.max() <= 7
+        assert s.shape == (6, (cols + 127) // 128)
+        err = np.abs(_w4_dequant(q, s, o) - w)
+        step = np.repeat(s.astype(np.float64), 128, axis=1)[:, :cols]
+        assert np.all(err <= step * (0.5 + 1e-5) + 1e-12) or np.all(err <= step * 1.0001)
+        assert np.mean(err <= step * (0.5 + 1e-5)) > 0.999
+
+
+def test_w4_grid_values_are_exact(orc):
+    """Values on a power-of-two grid whose codes span 0..15 come back exactly,
+    with the constructed codes, offset and step."""
+    rng = np.random.default_rng(5)
+    rows = []
+    want = []
+    for z in range(16):
+        u = rng.integers(0, 16, 128)
+        u[0], u[1] = 0, 15                   # the range is exactly 15 steps
+        s = 2.0 ** -7
+        rows.append(((u - z) * s).astype(np.float32))
+        want.append((u - 8, z - 8, s))
+    q, sc, o = orc.quant_w4_rows(np.stack(rows))
+    for r, (qu, oz, s) in enumerate(want):
+        assert np.array_equal(q[r], qu.astype(np.int8))
+        assert o[r, 0] == oz and sc[r, 0] == np.float32(s)
+        assert np.array_equal(_w4_dequant(q[r:r + 1], sc[r:r + 1], o[r:r + 1])[0], rows[r].astype(np.float64))
+
+
+def test_w4_degenerate_groups(orc):
+    """A group of zeros has step 0, codes and offset 0; a constant group keeps
+    zero at an end of its range (codes 7 / -8 against offsets -8 / 7)."""
+    c = np.float32(0.0375)
+    w = np.stack([np.zeros(128, np.float32), np.full(128, c, np.float32), np.full(128, -c, np.float32)])
+    q, s, o = orc.quant_w4_rows(w)
+    assert s[0, 0] == 0 and np.all(q[0] == 0) and o[0, 0] == 0
+    assert np.all(q[1] == 7) and o[1, 0] == -8 and s[1, 0] == np.float32(c / np.float32(15))
+    assert np.all(q[2] == -8) and o[2, 0] == 7
+    d = _w4_dequant(q, s, o)
+    assert np.allclose(d[1], float(c), rtol=1e-6) and np.allclose(d[2], -float(c), rtol=1e-6)
+
+
+def test_w4a8_gemm_equals_dequantised_float_matmul(orc):
+    """The W4A8 GEMM (integer sums per group, then the step) equals the float64
+    product of the codes with the dequantised weights, for both epilogues."""
+    rng = np.random.default_rng(9)
+    G, N, K = 3, 64, 300
+    A = rng.integers(-127, 128, (40, K)).astype(np.int8)
+    sa = (rng.random(40) * 0.01 + 1e-3).astype(np.float32)
+    w = (rng.standard_normal((G * N, K)) * 0.02).astype(np.float32)
+    q, s, o = orc.quant_w4_rows(w)
+    Wd = _w4_dequant(q, s, o).reshape(G, N, K)
+    offsets = np.array([0, 7, 7, 40], np.int32)
+    out = orc.w4a8_grouped_gemm(A, sa, None, 1, q.reshape(G, N, K), s.reshape(G, N, -1), o.reshape(G, N, -1),
+                                offsets, orc.DEQUANT, orc.F32)
+    for g in range(G):
+        r0, r1 = offsets[g], offsets[g + 1]
+        want = (A[r0:r1].astype(np.float64) @ Wd[g].T) * sa[r0:r1, None].astype(np.float64)
+        assert np.allclose(out[r0:r1], want, rtol=2e-6, atol=1e-9)
+    sw = orc.w4a8_grouped_gemm(A, sa, None, 1, q.reshape(G, N, K), s.reshape(G, N, -1), o.reshape(G, N, -1),
+                               offsets, orc.DEQUANT_SWIGLU, orc.F32)
+    for g in range(G):
+        r0, r1 = offsets[g], offsets[g + 1]
+        full = (A[r0:r1].astype(np.float64) @ Wd[g].T) * sa[r0:r1, None].astype(np.float64)
+        gate, up = full[:, :N // 2], full[:, N // 2:]
+        assert np.allclose(sw[r0:r1], gate / (1.0 + np.exp(-gate)) * up, rtol=2e-6, atol=1e-9)
+
+
+def test_w4_layer_dense_brute_force(orc):
+    """The W4A8-gate_up layer against a dense numpy evaluation of every expert
+    for every token with the dequantised W4 weights, then each token's experts."""
+    cfg = TINY
+    x, wg, gu, dn = synth.moe_inputs(cfg, 0)
+    q4, s4, o4 = orc.quant_w4_rows(gu.reshape(-1, cfg.H))
+    qd, sd = orc.quant_rows(dn.reshape(-1, cfg.I))
+    E, I, H = cfg.E, cfg.I, cfg.H
+    W4 = dict(q=q4.reshape(E, 2 * I, H), s=s4.reshape(E, 2 * I, -1), o=o4.reshape(E, 2 * I, -1))
+    wd, sd = qd.reshape(E, H, I), sd.reshape(E, H)
+    out, it = orc.moe_layer_w4(x, wg, W4["q"], W4["s"], W4["o"], wd, sd, cfg.k, intermediates=True)
+    qx, sx = orc.quant_rows(x)
+    Wgu = _w4_dequant(q4, s4, o4).reshape(E, 2 * I, H)
+    gu_all = np.einsum("th,enh->ten", qx.astype(np.float64), Wgu) * sx.astype(np.float64)[:, None, None]
+    want = np.zeros((cfg.T, H))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            e = it["ids"][t, j]
+            g, u = gu_all[t, e, :I], gu_all[t, e, I:]
+            h = _bf16_np(g / (1.0 + np.exp(-g)) * u)
+            r = it["pair_pos"][t * cfg.k + j]
+            assert np.array_equal(it["h"][r], h)
+            hq, sh = orc.quant_rows(h[None, :])
+            accd = wd[e].astype(np.int64) @ hq[0].astype(np.int64)
+            want[t] += float(it["w"][t, j]) * (accd * float(sh[0]) * sd[e].astype(np.float64))
+    assert np.array_equal(out, want.astype(np.float32))
