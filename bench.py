@@ -35,7 +35,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_model(cfg, E_hit):
+def gate_up_weight_bytes(cfg, E_hit, w4):
+    """gate_up_proj weights of the experts hit: int8 codes and one fp32 scale
+    per channel, or (W4A8) half a byte per code and an fp32 scale and an int8
+    offset per channel and group of 128 inputs."""
+    H, I = cfg.H, cfg.I
+    if w4:
+        return E_hit * 2 * I * (H // 2 + ((H + 127) // 128) * 5)
+    return E_hit * 2 * I * (H + 4)
+
+
+def kernel_model(cfg, E_hit, w4=False):
     """Algorithmic int8 ops and HBM bytes per launch of each stage kernel."""
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
     P = T * k
@@ -45,7 +55,7 @@ def kernel_model(cfg, E_hit):
     m["quant_x"] = dict(ops=0, bytes=T * H * xb + T * H + T * 4)
     m["permute"] = dict(ops=0, bytes=P * 4 * 3 + (E + 1) * 4)
     m["gate_up_gemm"] = dict(ops=2 * P * 2 * I * H,
-                             bytes=E_hit * 2 * I * H + E_hit * 2 * I * 4 + T * H + T * 4 + P * 4 + (E + 1) * 4
+                             bytes=gate_up_weight_bytes(cfg, E_hit, w4) + T * H + T * 4 + P * 4 + (E + 1) * 4
                              + P * I * 2)
     m["quant_h"] = dict(ops=0, bytes=P * I * 2 + P * I + P * 4)
     # y (the per-pair expert outputs) is 16-bit fixed point with one exponent
@@ -57,13 +67,13 @@ def kernel_model(cfg, E_hit):
     return m
 
 
-def layer_model(cfg, E_hit):
+def layer_model(cfg, E_hit, w4=False):
     """Whole-layer algorithmic work: int8 ops, and the bytes the method must
-    move: int8 weights and scales of the experts hit, the router, x in, out."""
+    move: quantised weights and scales of the experts hit, the router, x in, out."""
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
     xb = 2 if cfg.x_dtype == "bf16" else 4
     ops = 2 * T * k * 3 * H * I
-    byts = E_hit * 3 * H * I + E_hit * (2 * I + H) * 4 + E * H * 2 + 2 * T * H * xb
+    byts = gate_up_weight_bytes(cfg, E_hit, w4) + E_hit * H * (I + 4) + E * H * 2 + 2 * T * H * xb
     return ops, byts
 
 
@@ -351,6 +361,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--w4", action="store_true",
+                    help="W4A8 gate_up_proj weights (4-bit codes, groups of 128 with scale and offset)")
     ap.add_argument("--ep-share", type=int, default=0, metavar="G",
                     help="time each GPU's share of the workload's experts under G-way expert parallelism")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -395,10 +407,17 @@ def main():
     if x.dtype == np.uint16:
         xd = xd.view(torch.bfloat16)
     wgd = torch.from_numpy(wg.view(np.int16)).to(dev).view(torch.bfloat16)
-    W0 = w8.MoEWeights.quantize(wgd, torch.from_numpy(gu).to(dev), torch.from_numpy(dn).to(dev), cfg.k)
-    wbytes = cfg.E * 3 * cfg.H * cfg.I
+    W0 = w8.MoEWeights.quantize(wgd, torch.from_numpy(gu).to(dev), torch.from_numpy(dn).to(dev), cfg.k,
+                                w4=args.w4)
+    wbytes = cfg.E * cfg.H * cfg.I * (2 if args.w4 else 3)   # W4 gate_up: half a byte per weight
+
+    def clone_weights(W):
+        cl = lambda t: None if t is None else t.clone()
+        return w8.MoEWeights(*[cl(t) for t in W.tensors], k=cfg.k,
+                             w4=None if W.w4 is None else tuple(t.clone() for t in W.w4))
+
     copies = args.copies or max(1, min(4, (1 << 30) // max(wbytes, 1) + 1))
-    Ws = [W0] + [w8.MoEWeights(*[t.clone() for t in W0.tensors], k=cfg.k) for _ in range(copies - 1)]
+    Ws = [W0] + [clone_weights(W0) for _ in range(copies - 1)]
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     ws = w8.moe_layer_workspace(W0, cfg.T, w8.BF16 if x.dtype == np.uint16 else w8.F32, dev)
@@ -440,7 +459,7 @@ def main():
     inter = w8.moe_layer_intermediates(W0, cfg.T, ws, w8.BF16 if x.dtype == np.uint16 else w8.F32)
     counts = np.diff(inter["offsets"].cpu().numpy())
     E_hit = int(np.sum(counts > 0))
-    km = kernel_model(cfg, E_hit)
+    km = kernel_model(cfg, E_hit, args.w4)
     name = w8.STAGE_NAMES[dom]
     t_dom = dom_us * 1e-6
     ops, byts = km[name]["ops"], km[name]["bytes"]
@@ -450,7 +469,7 @@ def main():
     else:
         achieved, peak, unit = byts / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
     ms_per_step = elapsed * 1e3 / args.steps
-    lops, lbytes = layer_model(cfg, E_hit)
+    lops, lbytes = layer_model(cfg, E_hit, args.w4)
     t_step = elapsed / args.steps
     roof_t = max(lops / (INT8_PEAK_TOPS * 1e12), lbytes / (HBM_PEAK_GBS * 1e9))
     result = {
@@ -466,11 +485,12 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E, "top_k": cfg.k,
+        "config": {"workload": cfg.name + ("_w4a8" if args.w4 else ""), "tokens": cfg.T, "hidden": cfg.H,
+                   "experts": cfg.E, "top_k": cfg.k, "gate_up_weights": "w4a8" if args.w4 else "w8a8",
                    "expert_intermediate": cfg.I, "x_dtype": cfg.x_dtype, "experts_hit": E_hit,
                    "weight_copies_rotated": copies},
         "roofline": {"kernel": name, "bound": "mfma" if mfma_bound else "hbm", "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": traffic_for(name, cfg.name),
+                     "unit": unit, "frac": achieved / peak, "traffic": None if args.w4 else traffic_for(name, cfg.name),
                      "avg_launch_us": dom_us, "alg_bytes_per_launch": byts, "int8_ops_per_launch": ops},
         "layer": {"int8_tops": lops / t_step / 1e12, "int8_tops_frac": lops / t_step / 1e12 / INT8_PEAK_TOPS,
                   "alg_gbs": lbytes / t_step / 1e9, "alg_gbs_frac": lbytes / t_step / 1e9 / HBM_PEAK_GBS,

@@ -180,6 +180,49 @@ int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
                       size_t ws_bytes, void *stream);
 
 /*
+ * W4A8 weights ("Qwen3-1.7B-W4A8 on Ascend", section on 4bit weights, items 1
+ * and 2: groups of 128 weights share a scale and an offset; 4-bit codes in
+ * two's complement).  Per output channel (row of w) and group of 128
+ * consecutive inputs (the last group of a row may be shorter), over the range
+ * [min(w, 0), max(w, 0)]: s = (max - min) / 15, z = rint(-min / s),
+ * u = clamp(rint(w / s) + z, 0, 15) (IEEE fp32 divides, round half to even);
+ * code u - 8 and offset z - 8, both in [-8, 7]; w ~ (code - offset) * s.  A
+ * group of zeros has s = 0, codes and offset 0.
+ *   w        device [rows][cols] fp32 (cols % 16 == 0)
+ *   q        device [rows][cols] int8 codes (one per byte)
+ *   scales   device [rows][ceil(cols / 128)] fp32;  offsets the same, int8
+ */
+int w4a8_quant_weights(const float *w, int64_t rows, int64_t cols, int8_t *q, float *scales,
+                       int8_t *offsets, void *stream);
+
+/*
+ * W4 codes [G][N][K] (one per byte) packed two per byte for the W4A8 GEMM:
+ * for group g, 32-row block nb and 128-column step ks, a 2 KiB chunk at byte
+ * ((g * NB + nb) * KS + ks) * 2048 holds at l * 32 + 16 * p + 4 * j + i
+ * (l = 0..63, p = 0..1, j, i = 0..3) the code of column
+ * 128 ks + 64 (l / 32) + 32 p + 4 j + i of row 32 nb + l % 32 in the low
+ * nibble and the code 16 columns further in the high nibble; zero padding.
+ * NB = ceil(N / 32), KS = ceil(K / 128).
+ */
+size_t w4a8_packed_weights_size(int G, int64_t N, int64_t K);
+int w4a8_pack_weights(const int8_t *q, int G, int64_t N, int64_t K, uint8_t *packed, void *stream);
+
+/*
+ * Grouped W4A8 GEMM: as w8a8_grouped_gemm with epilogue DEQUANT or
+ * DEQUANT_SWIGLU, B the packed W4 codes of w4a8_pack_weights with per-group
+ * scales and offsets [G][N][ceil(K/128)]:
+ *   acc[r][n] = sum_kg s[g][n][kg] * sum_{k in kg} A[a][k] * (q[g][n][k] - o[g][n][kg])
+ *   DEQUANT out = acc * a_scales[a];  DEQUANT_SWIGLU out = silu(gate) * up
+ * The workspace is w8a8_grouped_gemm_workspace_size(M_total, N, G).  Same
+ * limits as w8a8_grouped_gemm.
+ */
+int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
+                      const int32_t *a_row_gather, int gather_div, const uint8_t *B_packed,
+                      const float *b_scales, const int8_t *b_offsets, const int32_t *group_offsets,
+                      int G, int64_t M_total, int64_t N, int64_t K, int epilogue, int out_dtype,
+                      void *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Weighted combine of the expert outputs:
  *   out[t][n] = sum_{j<k} topk_w[t][j] * y[pair_pos[t*k+j]][n]
  * accumulated in fp32 in slot order, then rounded once to out_dtype.
@@ -200,6 +243,11 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
  *   w_gate_f32 [E][H]   fp32: w_gate widened by moe_router_widen (exact), or
  *             NULL.  When given, the router stages it as is instead of
  *             widening w_gate inside every call; the scores are identical.
+ *   w4_gate_up W4A8 gate_up_proj: packed W4 codes of [E][2I][H]
+ *             (w4a8_pack_weights), or NULL.  When given, gate_up runs as the
+ *             W4A8 GEMM with w4_s_gate_up / w4_o_gate_up [E][2I][ceil(H/128)]
+ *             (fp32 / int8) and w_gate_up, s_gate_up may be NULL; down_proj
+ *             stays W8A8.
  * H % 16 == 0, I % 32 == 0.
  */
 typedef struct {
@@ -211,6 +259,9 @@ typedef struct {
     const int8_t *w_down;
     const float *s_down;
     const float *w_gate_f32;
+    const uint8_t *w4_gate_up;
+    const float *w4_s_gate_up;
+    const int8_t *w4_o_gate_up;
 } w8a8_moe_weights;
 
 /*

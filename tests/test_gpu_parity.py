@@ -593,3 +593,97 @@ def test_dense_linear_sampled():
     acc = w8.grouped_gemm(qx, None, None, 1, qw.view(1, cfg.N, cfg.K), None, off, w8.EPI_RAW_I32)
     r = rows[:8]
     assert np.array_equal(to_host(acc)[r].astype(np.float64), oqx[r].astype(np.float64) @ oqw.astype(np.float64).T)
+
+
+# ------------------------------------------------------------------- W4A8 ---
+
+@pytest.mark.parametrize("rows,cols", [(5, 64), (7, 304), (33, 2048), (3, 16)])
+def test_w4_quant_bit_exact(rows, cols):
+    """W4 codes, scales and offsets equal the oracle's, including one-signed
+    rows, a zero row, short last groups and values on the quantisation grid."""
+    rng = np.random.default_rng(rows * 31 + cols)
+    w = (rng.standard_t(4, (rows, cols)) * 0.02).astype(np.float32)
+    w[0] = 0.0
+    if rows > 2:
+        w[1] = np.abs(w[1])
+        w[2] = -np.abs(w[2])
+    if rows > 3:
+        w[3] = (rng.integers(-7, 8, cols) * 2.0 ** -8).astype(np.float32)
+    q, s, o = w8.w4a8_quant_weights(to_dev(w))
+    oq, os_, oo = oracle.quant_w4_rows(w)
+    assert np.array_equal(to_host(q), oq)
+    assert np.array_equal(to_host(s), os_)
+    assert np.array_equal(to_host(o), oo)
+
+
+def _w4_problem(G, N, K, counts, seed, A_rows=None):
+    rng = np.random.default_rng(seed)
+    M = int(sum(counts))
+    A_rows = A_rows or M
+    A = rng.integers(-127, 128, (A_rows, K)).astype(np.int8)
+    sa = (rng.random(A_rows) * 0.02 + 1e-3).astype(np.float32)
+    w = (rng.standard_normal((G * N, K)) * 0.02).astype(np.float32)
+    q, s, o = oracle.quant_w4_rows(w)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return A, sa, q.reshape(G, N, K), s.reshape(G, N, -1), o.reshape(G, N, -1), off
+
+
+@pytest.mark.parametrize("G,N,K,counts,gather,epi,od", [
+    (3, 64, 304, [7, 0, 33], False, 1, "f32"), (3, 128, 256, [5, 70, 1], True, 2, "bf16"),
+    (2, 64, 64, [16, 16], False, 2, "f32"), (16, 1536, 2048, [128] * 16, True, 2, "bf16"),
+    (128, 1536, 2048, [4] * 128, True, 2, "bf16"), (8, 2048, 768, [40] * 8, False, 1, "bf16")])
+def test_w4a8_grouped_gemm(G, N, K, counts, gather, epi, od):
+    """The W4A8 GEMM through the C ABI against the oracle (32- and 64-row
+    tiles, ragged and empty groups, gathered rows, both epilogues)."""
+    M = int(sum(counts))
+    k = 4
+    A, sa, q, s, o, off = _w4_problem(G, N, K, counts, G + N + K, A_rows=(M + k - 1) // k if gather else M)
+    gat = (np.random.default_rng(1).permutation(M) % (A.shape[0] * k)).astype(np.int32) if gather else None
+    if gather:
+        gat = np.minimum(gat, A.shape[0] * k - 1).astype(np.int32)
+    odc = w8.BF16 if od == "bf16" else w8.F32
+    Bp = w8.w4a8_pack_weights(to_dev(q))
+    got = w8.w4a8_grouped_gemm(to_dev(A), to_dev(sa), None if gat is None else to_dev(gat), k if gather else 1, Bp,
+                               to_dev(s), to_dev(o), to_dev(off), epi, odc, M_total=M, b_shape=(G, N, K))
+    want = oracle.w4a8_grouped_gemm(A, sa, gat, k if gather else 1, q, s, o, off, epi,
+                                    oracle.BF16 if od == "bf16" else oracle.F32)
+    tol_check(to_host(got), want, "w4a8 gemm G%d N%d K%d epi %d" % (G, N, K, epi))
+
+
+@pytest.mark.parametrize("name", ["moe_tiny_T16_H64_E8_k2_I32", "moe_30b_decode_T64", "moe_30b_prefill_T4096"])
+def test_w4_layer(name):
+    """The layer with W4A8 gate_up weights (quantised on the GPU, bit-exact with
+    the oracle's codes) against the oracle's W4 layer: ids and x codes bit-exact,
+    h codes of the GPU's own h bit-exact, the output within tolerance (all
+    tokens for tiny and decode, a sample for prefill)."""
+    cfg = synth.MOE_CONFIGS[name]
+    x, wg, gu, dn = synth.moe_inputs(cfg)
+    E, I, H = cfg.E, cfg.I, cfg.H
+    W = w8.MoEWeights.quantize(dev_bf16(wg), to_dev(gu), to_dev(dn), cfg.k, w4=True)
+    q4, s4, o4 = oracle.quant_w4_rows(gu.reshape(-1, H))
+    assert np.array_equal(to_host(W.w4[0]).reshape(-1, H), q4)
+    assert np.array_equal(to_host(W.w4[1]).reshape(q4.shape[0], -1), s4)
+    assert np.array_equal(to_host(W.w4[2]).reshape(q4.shape[0], -1), o4)
+    qd, sd = oracle.quant_rows(dn.reshape(-1, I))
+    args = (wg, q4.reshape(E, 2 * I, H), s4.reshape(E, 2 * I, -1), o4.reshape(E, 2 * I, -1), qd.reshape(E, H, I),
+            sd.reshape(E, H), cfg.k)
+    xd = to_dev(x)
+    dt = w8.BF16 if x.dtype == np.uint16 else w8.F32
+    ws = w8.moe_layer_workspace(W, cfg.T, dt)
+    out = w8.moe_layer(W, xd, ws=ws)
+    torch.cuda.synchronize()
+    inter = w8.moe_layer_intermediates(W, cfg.T, ws, dt)
+    if cfg.T <= 64:
+        want, it = oracle.moe_layer_w4(x, *args, intermediates=True)
+        assert np.array_equal(to_host(inter["ids"]), it["ids"])
+        assert np.array_equal(to_host(inter["xq"]), it["xq"])
+        tol_check(to_host(inter["h"]), it["h"], "%s w4 h" % name)
+        tol_check(to_host(out), want, "%s w4 layer" % name)
+    else:
+        tok = np.sort(np.random.default_rng(3).choice(cfg.T, 96, replace=False))
+        want = oracle.moe_layer_w4_tokens(x, *args, tok)
+        tol_check(to_host(out)[tok], want, "%s w4 layer (sampled tokens)" % name)
+    h = to_host(inter["h"])
+    rows = np.random.default_rng(4).choice(h.shape[0], min(64, h.shape[0]), replace=False)
+    oq, os_ = oracle.quant_rows(h[rows])
+    assert np.array_equal(to_host(inter["hq"])[rows], oq) and np.array_equal(to_host(inter["sh"])[rows], os_)

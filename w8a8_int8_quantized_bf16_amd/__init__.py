@@ -36,7 +36,9 @@ class W8A8Error(RuntimeError):
 class _Weights(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int), ("k", ctypes.c_int), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("w_gate", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("w_gate_f32", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("w_gate_f32", ctypes.c_void_p),
+                ("w4_gate_up", ctypes.c_void_p), ("w4_s_gate_up", ctypes.c_void_p),
+                ("w4_o_gate_up", ctypes.c_void_p)]
 
 
 _lib = None
@@ -66,6 +68,11 @@ def lib():
     L.w8a8_packed_weights_size.restype = sz
     L.w8a8_pack_weights.argtypes = [P, i32, i64, i64, P, P]
     L.moe_combine.argtypes = [P, i32, P, P, i64, i32, i64, P, i32, P]
+    L.w4a8_quant_weights.argtypes = [P, i64, i64, P, P, P, P]
+    L.w4a8_packed_weights_size.argtypes = [i32, i64, i64]
+    L.w4a8_packed_weights_size.restype = sz
+    L.w4a8_pack_weights.argtypes = [P, i32, i64, i64, P, P]
+    L.w4a8_grouped_gemm.argtypes = [P, i64, P, P, i32, P, P, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
     WP = ctypes.POINTER(_Weights)
     L.w8a8_moe_layer_workspace_size.argtypes = [WP, i64, i32]
     L.w8a8_moe_layer_workspace_size.restype = sz
@@ -73,7 +80,7 @@ def lib():
     L.w8a8_moe_layer_events.argtypes = [WP, P, i32, i64, P, P, sz, P, ctypes.POINTER(P), i32]
     L.w8a8_moe_layer_intermediates.argtypes = [WP, i64, i32, P, ctypes.POINTER(P)]
     for name in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
-                 "w8a8_pack_weights",
+                 "w8a8_pack_weights", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm",
                  "w8a8_moe_layer", "w8a8_moe_layer_events", "w8a8_moe_layer_intermediates"):
         getattr(L, name).restype = i32
     _lib = L
@@ -84,7 +91,7 @@ def header_functions():
     """Names of the functions declared in include/w8a8moe.h."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w8a8_\w+|moe_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w8a8_\w+|w4a8_\w+|moe_\w+)\s*\(", text)))
 
 
 def status_string(status):
@@ -210,6 +217,52 @@ def grouped_gemm(A, a_scales, gather, gather_div, B, b_scales, offsets, epilogue
     return out
 
 
+W4_GROUP = 128
+
+
+def w4a8_quant_weights(w):
+    """W4 codes of fp32 weights [rows, cols]: (codes int8 [rows, cols] in [-8, 7],
+    scales fp32 [rows, ceil(cols/128)], offsets int8 [rows, ceil(cols/128)])."""
+    _need(w, "w", torch.float32, 2)
+    rows, cols = w.shape
+    ng = (cols + W4_GROUP - 1) // W4_GROUP
+    q = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    s = torch.empty((rows, ng), dtype=torch.float32, device=w.device)
+    o = torch.empty((rows, ng), dtype=torch.int8, device=w.device)
+    _check(lib().w4a8_quant_weights(_p(w), rows, cols, _p(q), _p(s), _p(o), _stream(w.device)), "w4a8_quant_weights")
+    return q, s, o
+
+
+def w4a8_pack_weights(q):
+    """Pack W4 codes [G, N, K] two per byte in the W4A8 GEMM layout (uint8 bytes)."""
+    _need(q, "q", torch.int8, 3)
+    G, N, K = q.shape
+    n = int(lib().w4a8_packed_weights_size(G, N, K))
+    out = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(lib().w4a8_pack_weights(_p(q), G, N, K, _p(out), _stream(q.device)), "w4a8_pack_weights")
+    return out
+
+
+def w4a8_grouped_gemm(A, a_scales, gather, gather_div, B_packed, b_scales, b_offsets, offsets, epilogue,
+                      out_dtype=BF16, M_total=None, b_shape=None):
+    """Grouped W4A8 GEMM: B_packed from w4a8_pack_weights of codes of shape
+    b_shape = (G, N, K); b_scales / b_offsets [G, N, ceil(K/128)]."""
+    _need(A, "A", torch.int8, 2)
+    _need(B_packed, "B_packed", torch.uint8, 1)
+    _need(offsets, "offsets", torch.int32, 1)
+    G, N, K = b_shape
+    if M_total is None:
+        M_total = gather.shape[0] if gather is not None else A.shape[0]
+    ncol = N if epilogue == EPI_DEQUANT else N // 2
+    out = torch.empty((M_total, ncol), dtype=_torch_dtype(out_dtype), device=A.device)
+    nws = int(lib().w8a8_grouped_gemm_workspace_size(M_total, N, G))
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=A.device)
+    _check(lib().w4a8_grouped_gemm(_p(A), A.shape[0], _p(a_scales), _p(gather), int(gather_div), _p(B_packed),
+                                   _p(b_scales), _p(b_offsets), _p(offsets), G, M_total, N, K, epilogue, out_dtype,
+                                   _p(out), _p(ws), ws.numel(), _stream(A.device)), "w4a8_grouped_gemm")
+    return out
+
+
 def combine(y, w, pair_pos, out_dtype=None):
     """out[t] = sum_j w[t,j] * y[pair_pos[t*k+j]]."""
     _need(y, "y", dim=2)
@@ -241,29 +294,45 @@ class MoEWeights:
     s_gate_up [E,2I] fp32; w_down [E,H,I] int8 codes; s_down [E,H] fp32.
     The layer reads the codes in the packed layout (pack_weights), built here."""
 
-    def __init__(self, w_gate, w_gate_up, s_gate_up, w_down, s_down, k):
+    def __init__(self, w_gate, w_gate_up, s_gate_up, w_down, s_down, k, w4=None):
+        """w4: optional W4A8 gate_up_proj (codes [E,2I,H], scales and offsets
+        [E,2I,ceil(H/128)]), used instead of w_gate_up / s_gate_up (which may
+        then be None)."""
         _need(w_gate, "w_gate", torch.bfloat16, 2)
-        _need(w_gate_up, "w_gate_up", torch.int8, 3)
-        _need(s_gate_up, "s_gate_up", torch.float32, 2)
         _need(w_down, "w_down", torch.int8, 3)
         _need(s_down, "s_down", torch.float32, 2)
-        E, twoI, H = w_gate_up.shape
+        if w4 is None:
+            _need(w_gate_up, "w_gate_up", torch.int8, 3)
+            _need(s_gate_up, "s_gate_up", torch.float32, 2)
+            E, twoI, H = w_gate_up.shape
+        else:
+            _need(w4[0], "w4 codes", torch.int8, 3)
+            E, twoI, H = w4[0].shape
         self.E, self.H, self.I, self.k = E, H, twoI // 2, int(k)
         self.tensors = (w_gate, w_gate_up, s_gate_up, w_down, s_down)
         self.w_gate, self.w_gate_up, self.s_gate_up, self.w_down, self.s_down = self.tensors
-        self.p_gate_up = pack_weights(w_gate_up)
+        self.w4 = w4
+        self.p_gate_up = pack_weights(w_gate_up) if w_gate_up is not None else None
         self.p_down = pack_weights(w_down)
         self.w_gate_f32 = router_widen(w_gate)
-        self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), self.p_gate_up.data_ptr(), s_gate_up.data_ptr(),
-                          self.p_down.data_ptr(), s_down.data_ptr(), self.w_gate_f32.data_ptr())
+        self.p4_gate_up = w4a8_pack_weights(w4[0]) if w4 is not None else None
+        ptr = lambda t: None if t is None else t.data_ptr()
+        self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), ptr(self.p_gate_up), ptr(s_gate_up),
+                          self.p_down.data_ptr(), s_down.data_ptr(), self.w_gate_f32.data_ptr(),
+                          ptr(self.p4_gate_up), ptr(w4[1]) if w4 else None, ptr(w4[2]) if w4 else None)
 
     @classmethod
-    def quantize(cls, w_gate, gate_up_f32, down_f32, k):
-        """Static per-output-channel int8 quantisation of fp32 expert weights on
-        the GPU (the same row quantisation kernel as the activations)."""
+    def quantize(cls, w_gate, gate_up_f32, down_f32, k, w4=False):
+        """Static quantisation of fp32 expert weights on the GPU: per output
+        channel int8 (the same row kernel as the activations), or with w4=True
+        W4A8 gate_up_proj (groups of 128) and int8 down_proj."""
         E, twoI, H = gate_up_f32.shape
-        qgu, sgu = quant_act(gate_up_f32.reshape(E * twoI, H))
         qd, sd = quant_act(down_f32.reshape(E * H, twoI // 2))
+        if w4:
+            q4, s4, o4 = w4a8_quant_weights(gate_up_f32.reshape(E * twoI, H))
+            return cls(w_gate, None, None, qd.view(E, H, twoI // 2), sd.view(E, H), k,
+                       w4=(q4.view(E, twoI, H), s4.view(E, twoI, -1), o4.view(E, twoI, -1)))
+        qgu, sgu = quant_act(gate_up_f32.reshape(E * twoI, H))
         return cls(w_gate, qgu.view(E, twoI, H), sgu.view(E, twoI), qd.view(E, H, twoI // 2), sd.view(E, H), k)
 
 

@@ -84,10 +84,18 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
         (int64_t)packed_weights_bytes(1, W->H, W->I) > INT32_MAX - 256 || T * W->k * W->I > INT32_MAX - 256 ||
         T * W->H > INT32_MAX - 256)
         return W8A8_ERR_UNSUPPORTED_SHAPE;
-    if (!W->w_gate || !W->w_gate_up || !W->s_gate_up || !W->w_down || !W->s_down) return W8A8_ERR_INVALID_ARG;
+    const bool w4 = W->w4_gate_up != nullptr;
+    if (w4 && ((int64_t)packed_w4_bytes(1, 2 * W->I, W->H) > INT32_MAX - 256 ||
+               2 * W->I * ((W->H + 127) / 128) * 4 > INT32_MAX - 256))
+        return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!W->w_gate || !W->w_down || !W->s_down) return W8A8_ERR_INVALID_ARG;
+    if (w4 ? (!W->w4_s_gate_up || !W->w4_o_gate_up) : (!W->w_gate_up || !W->s_gate_up)) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!x || !out)) return W8A8_ERR_INVALID_ARG;
-    if (!aligned16(W->w_gate) || !aligned16(W->w_gate_up) || !aligned16(W->s_gate_up) || !aligned16(W->w_down) ||
-        !aligned16(W->s_down) || (W->w_gate_f32 && !aligned16(W->w_gate_f32)))
+    if (!aligned16(W->w_gate) || !aligned16(W->w_down) || !aligned16(W->s_down) ||
+        (W->w_gate_f32 && !aligned16(W->w_gate_f32)))
+        return W8A8_ERR_ALIGNMENT;
+    if (w4 ? (!aligned16(W->w4_gate_up) || !aligned16(W->w4_s_gate_up) || !aligned16(W->w4_o_gate_up))
+           : (!aligned16(W->w_gate_up) || !aligned16(W->s_gate_up)))
         return W8A8_ERR_ALIGNMENT;
     if (T > 0 && (!aligned16(x) || !aligned16(out))) return W8A8_ERR_ALIGNMENT;
     return W8A8_OK;
@@ -146,7 +154,9 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
         return hip_status(e);
     // 3 permute; its scan also builds the tile tables of both grouped GEMMs
     TileTableReq req[2];
-    gemm_tile_params(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
+    const bool w4 = W->w4_gate_up != nullptr;
+    if (w4) gemm_tile_params_w4(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
+    else gemm_tile_params(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
     gemm_tile_params(P, H, E, EPI_FIXED16, &req[1].BM, &req[1].nblocks_n);
     req[0].prefix = (int32_t *)gws1;
     req[0].tiles = (int4 *)gemm_tiles_ptr(gws1, E);
@@ -155,11 +165,12 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     if ((e = launch_permute(ids, T, k, E, offsets, sorted, pos, perm, st, req, 2)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
-    // 4a gate_up GEMM + SwiGLU -> h (bf16)
-    if ((e = launch_gemm_main(xq, T, sx, sorted, k, W->w_gate_up, 1, W->s_gate_up, offsets, E, P, 2 * I, H,
-                              W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)) != hipSuccess ||
-        (e = mark()) != hipSuccess)
-        return hip_status(e);
+    // 4a gate_up GEMM + SwiGLU -> h (bf16), W8A8 or W4A8 weights
+    e = w4 ? launch_gemm_w4_main(xq, T, sx, sorted, k, W->w4_gate_up, W->w4_s_gate_up, W->w4_o_gate_up, offsets, E,
+                                 P, 2 * I, H, W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)
+           : launch_gemm_main(xq, T, sx, sorted, k, W->w_gate_up, 1, W->s_gate_up, offsets, E, P, 2 * I, H,
+                              W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st);
+    if (e != hipSuccess || (e = mark()) != hipSuccess) return hip_status(e);
     // quantise h per grouped row
     if ((e = launch_quant_rows(h, W8A8_BF16, P, I, I, hq, sh, st)) != hipSuccess || (e = mark()) != hipSuccess)
         return hip_status(e);
@@ -290,6 +301,57 @@ int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, co
     return hip_status(launch_grouped_gemm(A, A_rows, a_scales, a_row_gather, gather_div, B, b_layout, b_scales,
                                           group_offsets, G, M_total, N, K, epilogue, out_dtype, out, ws,
                                           (hipStream_t)stream));
+}
+
+int w4a8_quant_weights(const float *w, int64_t rows, int64_t cols, int8_t *q, float *scales, int8_t *offsets,
+                       void *stream)
+{
+    if (rows < 0 || cols <= 0) return W8A8_ERR_INVALID_ARG;
+    if (cols % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (rows == 0) return W8A8_OK;
+    if (!w || !q || !scales || !offsets) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(q) || ((uintptr_t)scales & 3u)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_quant_w4(w, rows, cols, q, scales, offsets, (hipStream_t)stream));
+}
+
+size_t w4a8_packed_weights_size(int G, int64_t N, int64_t K)
+{
+    if (G <= 0 || N <= 0 || K <= 0) return 0;
+    return packed_w4_bytes(G, N, K);
+}
+
+int w4a8_pack_weights(const int8_t *q, int G, int64_t N, int64_t K, uint8_t *packed, void *stream)
+{
+    if (G <= 0 || N <= 0 || K <= 0 || !q || !packed) return W8A8_ERR_INVALID_ARG;
+    if (N % 16 || K % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(q) || !aligned16(packed)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_pack_w4(q, G, N, K, packed, (hipStream_t)stream));
+}
+
+int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *a_row_gather,
+                      int gather_div, const uint8_t *B_packed, const float *b_scales, const int8_t *b_offsets,
+                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                      int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (M_total < 0 || A_rows < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
+    if (G > 4096) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (epilogue != W8A8_EPI_DEQUANT && epilogue != W8A8_EPI_DEQUANT_SWIGLU) return W8A8_ERR_INVALID_ARG;
+    if (!act_dtype_ok(out_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (a_row_gather && gather_div <= 0) return W8A8_ERR_INVALID_ARG;
+    if (K % 16 || N % 16 || (epilogue == W8A8_EPI_DEQUANT_SWIGLU && N % 64)) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (A_rows * K > INT32_MAX - 256 || (int64_t)packed_w4_bytes(1, N, K) > INT32_MAX - 256 ||
+        N * ((K + 127) / 128) * 4 > INT32_MAX - 256)
+        return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!B_packed || !b_scales || !b_offsets || !group_offsets || !ws) return W8A8_ERR_INVALID_ARG;
+    if (M_total > 0 && (!A || !out || !a_scales)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(B_packed) || !aligned16(out) || !aligned16(ws) || !aligned16(group_offsets) ||
+        (a_row_gather && !aligned16(a_row_gather)) || !aligned16(a_scales) || ((uintptr_t)b_scales & 3u))
+        return W8A8_ERR_ALIGNMENT;
+    if (ws_bytes < gemm_ws_bytes(M_total, N, G)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+    if (M_total == 0) return W8A8_OK;
+    return hip_status(launch_grouped_gemm_w4(A, A_rows, a_scales, a_row_gather, gather_div, B_packed, b_scales,
+                                             b_offsets, group_offsets, G, M_total, N, K, epilogue, out_dtype, out,
+                                             ws, (hipStream_t)stream));
 }
 
 int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *pair_pos, int64_t T, int k, int64_t H,

@@ -64,6 +64,8 @@ struct GemmArgs {
     const int4 *tiles;            // per launched block: {group, first grouped row, rows, column block}
     int nblocks_n;                // column blocks per group
     int packed_b;                 // B in the MFMA-fragment packed layout (see w8a8_pack_weights)
+    const float *b_gscales;       // W4: per (group, column, 128-step) scales [G][N][KS]
+    const int8_t *b_goffs;        //     and offsets [G][N][KS]
 };
 
 template <typename T>
@@ -113,6 +115,39 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const int8_t *__restr
     }
 }
 
+// Packed W4 layout: codes B [G][N][K] (one per byte, in [-8, 7]) re-laid so
+// that a lane's MFMA operands of one 128-column step are 32 contiguous bytes.
+// For group g, 32-row block nb and step ks, a 2 KiB chunk at
+// ((g * NB + nb) * KS + ks) * 2048 holds at l * 32 + 16 p + 4 j + i (lane l,
+// piece p, dword j, byte i) the code of sub-step 2p in the low nibble and of
+// sub-step 2p + 1 in the high nibble, both at index 4 j + i of lane l's 16
+// operand bytes (row 32 nb + l % 32, column 128 ks + 64 (l / 32) + 16 s + 4 j
+// + i).  A nibble moved to the top of its byte is 16 times the code as an
+// int8, so a shift and a mask unpack four operands at once.  Zero padded.
+__global__ __launch_bounds__(256) void pack_w4_kernel(const int8_t *__restrict__ B, int64_t G, int64_t N,
+                                                      int64_t K, uint32_t *__restrict__ P)
+{
+    const int64_t NB = (N + 31) / 32, KS = (K + 127) / 128;
+    const int64_t nd = G * NB * KS * 512;   // dwords
+    for (int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x; d < nd; d += (int64_t)gridDim.x * 256) {
+        const int64_t chunk = d >> 9;
+        const int within = (int)(d & 511);
+        const int l = within >> 3, pj = within & 7, p = pj >> 2, j = pj & 3;
+        const int64_t ks = chunk % KS, nbk = (chunk / KS) % NB, g = chunk / (KS * NB);
+        const int64_t row = nbk * 32 + (l & 31);
+        const int64_t k0 = ks * 128 + 64 * (l >> 5) + 4 * j;
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t klo = k0 + 16 * (2 * p) + i, khi = k0 + 16 * (2 * p + 1) + i;
+            const int lo = (row < N && klo < K) ? B[(g * N + row) * K + klo] : 0;
+            const int hi = (row < N && khi < K) ? B[(g * N + row) * K + khi] : 0;
+            word |= (uint32_t)((lo & 0xf) | ((hi & 0xf) << 4)) << (8 * i);
+        }
+        P[d] = word;
+    }
+}
+
 // Buffer-resource loads: an offset at or beyond num_records returns zero
 // without touching memory, which masks ragged rows, column tails and the K
 // tail without branches (so the compiler's wait counters stay exact and the
@@ -130,6 +165,126 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off
 {
     const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return __builtin_bit_cast(v4i, v);
+}
+
+// Epilogue of one tile.  Each wave stages its results through its own LDS
+// region (stage_base + wave * 32 * ROWB, see gemm_stage_bytes), one 32-row
+// block and at most two 32-column fragments at a time, and writes them back
+// as 16-byte row segments (the MFMA layout gives a lane one column of many
+// rows; a store wants many columns of one row).  ascale: the tile's
+// activation scales (LDS); bsc: this lane's column scales.  FACC: acc holds
+// fp32 bit patterns already scaled per column (W4A8), bsc all ones.
+template <int EPI, typename OutT>
+struct EpiTypes {
+    // staged element: the int32 accumulator, the output value, or (16-bit
+    // fixed point) the fp32 value before its segment scale is known
+    using ET = std::conditional_t<EPI == 0, int32_t, std::conditional_t<EPI == EPI_FIXED16, float, OutT>>;
+};
+template <int WN, int EPI, typename OutT>
+constexpr int gemm_stage_bytes()
+{
+    using ET = typename EpiTypes<EPI, OutT>::ET;
+    constexpr int NOF = EPI == 2 ? WN / 2 : WN;
+    constexpr int FP = NOF < 2 ? NOF : 2;
+    return 4 * 32 * (32 * FP * (int)sizeof(ET) + 16);
+}
+
+template <int BM, int WN, int EPI, typename OutT, bool FACC = false>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, v16i (&acc)[BM / 32][WN], const float *ascale,
+                                              const float (&bsc)[WN], unsigned char *stage_base, int rows,
+                                              int64_t row0, int nb, int N)
+{
+    constexpr int MI = BM / 32;
+    constexpr int WCOLS = 32 * WN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    auto accv = [](int32_t v) -> float { return FACC ? __int_as_float(v) : (float)v; };
+    using ET = typename EpiTypes<EPI, OutT>::ET;
+    constexpr int NOF = EPI == 2 ? WN / 2 : WN;          // output fragments of 32 columns
+    constexpr int FP = NOF < 2 ? NOF : 2;                 // fragments per pass
+    constexpr int ROWB = 32 * FP * (int)sizeof(ET) + 16;  // padded staging row, bytes
+    constexpr int CPR = 32 * FP * (int)sizeof(ET) / 16;   // 16-byte chunks per staged row
+    unsigned char *stage = stage_base + wave * 32 * ROWB;
+    const int ldo = EPI == 2 ? (N >> 1) : N;
+    // first output column of this wave's fragment f is ocol0 + 32 f
+    const int ocol0 = EPI == 2 ? nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) : nb * (4 * WCOLS) + wave * WCOLS;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int f0 = 0; f0 < NOF; f0 += FP) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rl = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                const float sa = ascale[mi * 32 + rl];
+#pragma unroll
+                for (int ff = 0; ff < FP; ++ff) {
+                    const int f = f0 + ff;
+                    ET val;
+                    if constexpr (EPI == 0) {
+                        val = acc[mi][f][i];
+                    } else if constexpr (EPI == 1) {
+                        val = to_out<OutT>((accv(acc[mi][f][i]) * sa) * bsc[f]);
+                    } else if constexpr (EPI == EPI_FIXED16) {
+                        val = (accv(acc[mi][f][i]) * sa) * bsc[f];
+                    } else {
+                        const float gate = (accv(acc[mi][f][i]) * sa) * bsc[f];
+                        const float up = (accv(acc[mi][NOF + f][i]) * sa) * bsc[NOF + f];
+                        // silu(g) = g / (1 + e^-g); the result is rounded to bf16 (or
+                        // compared within a tolerance), so the hardware exp and
+                        // reciprocal are accurate enough
+                        val = to_out<OutT>(gate * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)));
+                    }
+                    *reinterpret_cast<ET *>(stage + rl * ROWB + (32 * ff + (lane & 31)) * (int)sizeof(ET)) = val;
+                }
+            }
+            __syncthreads();
+            if constexpr (EPI == EPI_FIXED16) {
+                // 16 lanes hold one row's 64 columns (4 each): the row's largest
+                // magnitude over them fixes a power-of-two scale 2^e that maps it
+                // into [2^13, 2^14); codes = rint(v * 2^-e) fit int16 with room.
+                static_assert(CPR == 16, "one 64-column segment per pass");
+#pragma unroll
+                for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                    const int rl = idx / CPR, ch = idx % CPR;
+                    const int r = mi * 32 + rl;
+                    const int ocol = ocol0 + 32 * f0 + ch * 4;
+                    const float4 v = *reinterpret_cast<const float4 *>(stage + rl * ROWB + ch * 16);
+                    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+                    // max over the 16-lane row: lane swaps 1 and 2 within quads,
+                    // then mirrors within 8 and within 16 lanes
+                    m = fmaxf(m, dpp_move<0xB1>(m));
+                    m = fmaxf(m, dpp_move<0x4E>(m));
+                    m = fmaxf(m, dpp_move<0x141>(m));
+                    m = fmaxf(m, dpp_move<0x140>(m));
+                    int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 13 : 0;
+                    e = e < -126 ? -126 : e;
+                    const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
+                    // rint(v * 2^-e) as an integer: adding 1.5 * 2^23 rounds the
+                    // (exact) product half-to-even into the mantissa
+                    const float vs[4] = {v.x, v.y, v.z, v.w};
+                    uint32_t q[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        q[u] = (uint32_t)(__float_as_int(fmaf(vs[u], sc, 12582912.0f)) - 0x4B400000) & 0xffffu;
+                    if (r < rows && ocol < ldo) {
+                        *reinterpret_cast<uint2 *>(reinterpret_cast<int16_t *>(a.out) + (row0 + r) * ldo + ocol) =
+                            make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
+                        if (ch == 0) a.out_exp[(row0 + r) * ((ldo + 63) / 64) + (ocol0 + 32 * f0) / 64] = (int8_t)e;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int idx = lane; idx < 32 * CPR; idx += 64) {
+                    const int rl = idx / CPR, ch = idx % CPR;
+                    const int r = mi * 32 + rl;
+                    const int ocol = ocol0 + 32 * f0 + ch * (16 / (int)sizeof(ET));
+                    if (r < rows && ocol < ldo)
+                        *reinterpret_cast<uint4 *>(reinterpret_cast<ET *>(a.out) + (row0 + r) * ldo + ocol) =
+                            *reinterpret_cast<const uint4 *>(stage + rl * ROWB + ch * 16);
+                }
+            }
+            __syncthreads();
+        }
+    }
 }
 
 // BM rows x (4 waves x WN fragments of 32 columns); DEPTH K steps of B in flight.
@@ -322,101 +477,225 @@ void grouped_gemm_kernel(GemmArgs a)
         }
     }
 
-    // ---- epilogue.  Each wave stages its results through its own LDS region,
-    // one 32-row block and at most two 32-column fragments at a time, and
-    // writes them back as 16-byte row segments (the MFMA layout gives a lane
-    // one column of many rows; a store wants many columns of one row).
-    // staged element: the int32 accumulator, the output value, or (16-bit
-    // fixed point) the fp32 value before its segment scale is known
-    using ET = std::conditional_t<EPI == 0, int32_t, std::conditional_t<EPI == EPI_FIXED16, float, OutT>>;
-    constexpr int NOF = EPI == 2 ? WN / 2 : WN;          // output fragments of 32 columns
-    constexpr int FP = NOF < 2 ? NOF : 2;                 // fragments per pass
-    constexpr int ROWB = 32 * FP * (int)sizeof(ET) + 16;  // padded staging row, bytes
-    constexpr int CPR = 32 * FP * (int)sizeof(ET) / 16;   // 16-byte chunks per staged row
-    static_assert(4 * 32 * ROWB <= (int)sizeof(smem), "epilogue staging exceeds the LDS buffer");
-    unsigned char *stage = smem + wave * 32 * ROWB;
-    const int ldo = EPI == 2 ? (N >> 1) : N;
-    // first output column of this wave's fragment f is ocol0 + 32 f
-    const int ocol0 = EPI == 2 ? nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) : nb * (4 * WCOLS) + wave * WCOLS;
     __syncthreads();   // every wave is done with the A buffers
+    static_assert(gemm_stage_bytes<WN, EPI, OutT>() <= (int)sizeof(smem), "epilogue staging exceeds the LDS buffer");
+    gemm_epilogue<BM, WN, EPI, OutT>(a, acc, ascale, bsc, smem, rows, row0, nb, N);
+}
+
+// Grouped W4A8 GEMM ("Qwen3-1.7B-W4A8 on Ascend", 4bit weights items 1-2):
+// the same tiles and A path as grouped_gemm_kernel, B in the packed W4 layout
+// (pack_w4_kernel).  A lane loads 32 bytes of codes per fragment and step and
+// unpacks them with a shift and a mask into operands worth 16 times the
+// codes; the int32 sum of one 128-column step, which is exactly one group of
+// the weights, is folded into fp32 accumulators as
+//   acc += (s / 16) * sum16 - (s * o) * xsum,
+// s and o the group's scale and offset of the lane's column, xsum the sum of
+// the row's A codes over the step (formed by the threads that stage the A
+// tile, so no pass of its own).  Columns are scaled per group here; the
+// epilogue applies the per-token scale (and SwiGLU).
+template <int BM, int WN, int DEPTH, int EPI, typename OutT>
+__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(BM <= 32 ? 2 : 1, 8)))
+void grouped_gemm_w4_kernel(GemmArgs a)
+{
+    static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH and alternates two LDS buffers");
+    static_assert(EPI == 1 || EPI == 2, "dequantising epilogues only");
+    static_assert(EPI != 2 || WN % 2 == 0, "SwiGLU pairs gate and up fragments");
+    constexpr int MI = BM / 32;
+    constexpr int APASS = BM / 32;
+    constexpr int WCOLS = 32 * WN;
+    constexpr int SMEM = 2 * BM * G_BK > gemm_stage_bytes<WN, EPI, OutT>() ? 2 * BM * G_BK
+                                                                            : gemm_stage_bytes<WN, EPI, OutT>();
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    int8_t(*As)[BM * G_BK] = reinterpret_cast<int8_t(*)[BM * G_BK]>(smem);
+    __shared__ int32_t arow[BM];
+    __shared__ float ascale[BM];
+    __shared__ __attribute__((aligned(16))) float xs[2][BM];   // row sums of the staged A codes
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int bid = blockIdx.x;
+    if (bid >= a.tile_prefix[a.G]) return;
+    const int4 tinfo = a.tiles[bid];
+    const int g = tinfo.x, rows = tinfo.z, nb = tinfo.w;
+    const int64_t row0 = tinfo.y;
+    const int N = (int)a.N, K = (int)a.K;
+    const int nk = (K + G_BK - 1) / G_BK;
+
+    int col[WN];
+    bool cvalid[WN];
+    if constexpr (EPI == 2) {
+        const int Nh = N >> 1;
+        const int hc0 = nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) + (lane & 31);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+        for (int f = 0; f < WN / 2; ++f) {
+            col[f] = hc0 + 32 * f;
+            col[WN / 2 + f] = Nh + hc0 + 32 * f;
+            cvalid[f] = cvalid[WN / 2 + f] = hc0 + 32 * f < Nh;
+        }
+    } else {
+        const int c0 = nb * (4 * WCOLS) + wave * WCOLS + (lane & 31);
 #pragma unroll
-        for (int f0 = 0; f0 < NOF; f0 += FP) {
+        for (int f = 0; f < WN; ++f) {
+            col[f] = c0 + 32 * f;
+            cvalid[f] = col[f] < N;
+        }
+    }
+    const int64_t b_bytes = (int64_t)((N + 31) / 32) * nk * 2048;
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B + (int64_t)g * b_bytes, b_bytes);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.b_gscales + (int64_t)g * N * nk, (int64_t)N * nk * 4);
+    const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.b_goffs + (int64_t)g * N * nk, (int64_t)N * nk);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
+    // byte offsets of the column's codes, step-0 scale and step-0 offset
+    uint32_t boff[WN], soff[WN], ooff[WN];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rl = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                const float sa = ascale[mi * 32 + rl];
+    for (int f = 0; f < WN; ++f) {
+        boff[f] = cvalid[f] ? (uint32_t)((col[f] >> 5) * nk * 2048 + lane * 32) : OOB_BASE;
+        soff[f] = cvalid[f] ? (uint32_t)(col[f] * nk * 4) : OOB_BASE;
+        ooff[f] = cvalid[f] ? (uint32_t)(col[f] * nk) : OOB_BASE;
+    }
+    float ones[WN];
 #pragma unroll
-                for (int ff = 0; ff < FP; ++ff) {
-                    const int f = f0 + ff;
-                    ET val;
-                    if constexpr (EPI == 0) {
-                        val = acc[mi][f][i];
-                    } else if constexpr (EPI == 1) {
-                        val = to_out<OutT>(((float)acc[mi][f][i] * sa) * bsc[f]);
-                    } else if constexpr (EPI == EPI_FIXED16) {
-                        val = ((float)acc[mi][f][i] * sa) * bsc[f];
-                    } else {
-                        const float gate = ((float)acc[mi][f][i] * sa) * bsc[f];
-                        const float up = ((float)acc[mi][NOF + f][i] * sa) * bsc[NOF + f];
-                        // silu(g) = g / (1 + e^-g); the result is rounded to bf16 (or
-                        // compared within a tolerance), so the hardware exp and
-                        // reciprocal are accurate enough
-                        val = to_out<OutT>(gate * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)));
+    for (int f = 0; f < WN; ++f) ones[f] = 1.0f;
+
+    if (tid < BM) {
+        int32_t src = -1;
+        if (tid < rows) src = a.gather ? a.gather[row0 + tid] / a.gather_div : (int32_t)(row0 + tid);
+        arow[tid] = src;
+        ascale[tid] = src >= 0 ? a.a_scales[src] : 0.0f;
+    }
+    __syncthreads();
+    const int ac = tid & 7;
+    uint32_t aoff[APASS];
+    int arr[APASS];
+#pragma unroll
+    for (int j = 0; j < APASS; ++j) {
+        arr[j] = (tid >> 3) + 32 * j;
+        const int32_t sr = arow[arr[j]];
+        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + 16 * ac) : OOB_BASE;
+    }
+
+    v4i breg[DEPTH][WN][2];
+    float gsc[DEPTH][WN], gof[DEPTH][WN];
+    v4i areg[DEPTH][APASS];
+    v16f accf[MI][WN];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int f = 0; f < WN; ++f)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) accf[mi][f][i] = 0.0f;
+
+    auto load_b = [&](int slot, int it) {
+        const bool live = it < nk;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int f = 0; f < WN; ++f)
+                breg[slot][f][p] = buf_load16(rB, live ? boff[f] + it * 2048 + p * 16 : OOB_BASE);
+#pragma unroll
+        for (int f = 0; f < WN; ++f) {
+            gsc[slot][f] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rS, live ? soff[f] + it * 4 : OOB_BASE, 0, 0));
+            gof[slot][f] =
+                (float)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rO, live ? ooff[f] + it : OOB_BASE, 0, 0);
+        }
+    };
+    auto load_a = [&](int slot, int it) {
+        const bool live = it < nk;
+        const bool kin = it * G_BK + 16 * ac < K;
+#pragma unroll
+        for (int j = 0; j < APASS; ++j)
+            areg[slot][j] = buf_load16(rA, (live && kin) ? aoff[j] + it * G_BK : OOB_BASE);
+    };
+    // the A chunks into LDS, and each row's code sum over the step (its 8
+    // chunks are staged by 8 neighbouring lanes)
+    auto store_a = [&](int slot, int buf) {
+#pragma unroll
+        for (int j = 0; j < APASS; ++j) {
+            const v4i v = areg[slot][j];
+            *reinterpret_cast<v4i *>(&As[buf][arr[j] * G_BK + ((ac ^ (arr[j] & 7)) << 4)]) = v;
+            int sum = __builtin_amdgcn_sdot4(v[0], 0x01010101, 0, false);
+            sum = __builtin_amdgcn_sdot4(v[1], 0x01010101, sum, false);
+            sum = __builtin_amdgcn_sdot4(v[2], 0x01010101, sum, false);
+            sum = __builtin_amdgcn_sdot4(v[3], 0x01010101, sum, false);
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            if (ac == 0) xs[buf][arr[j]] = (float)sum;
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_a(d, d);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_b(d, d);
+    store_a(0, 0);
+    load_a(0, DEPTH);
+    __syncthreads();
+
+    const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
+    for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int it = it0 + d;
+            const int8_t *Ab = As[d & 1];
+            v16i acs[MI][WN];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                v4i bop[WN];
+#pragma unroll
+                for (int f = 0; f < WN; ++f) {
+                    const v4i P = breg[d][f][s >> 1];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        bop[f][q] = (s & 1) ? (int)((uint32_t)P[q] & 0xf0f0f0f0u)
+                                            : (int)(((uint32_t)P[q] << 4) & 0xf0f0f0f0u);
+                }
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int r = mi * 32 + (lane & 31);
+                    const int ch = 4 * (lane >> 5) + s;
+                    const v4i av = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
+#pragma unroll
+                    for (int f = 0; f < WN; ++f) {
+                        const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                        acs[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bop[f], s == 0 ? zero : acs[mi][f],
+                                                                           0, 0, 0);
                     }
-                    *reinterpret_cast<ET *>(stage + rl * ROWB + (32 * ff + (lane & 31)) * (int)sizeof(ET)) = val;
                 }
             }
-            __syncthreads();
-            if constexpr (EPI == EPI_FIXED16) {
-                // 16 lanes hold one row's 64 columns (4 each): the row's largest
-                // magnitude over them fixes a power-of-two scale 2^e that maps it
-                // into [2^13, 2^14); codes = rint(v * 2^-e) fit int16 with room.
-                static_assert(CPR == 16, "one 64-column segment per pass");
+            // fold the step (one weight group) into the fp32 accumulators
 #pragma unroll
-                for (int idx = lane; idx < 32 * CPR; idx += 64) {
-                    const int rl = idx / CPR, ch = idx % CPR;
-                    const int r = mi * 32 + rl;
-                    const int ocol = ocol0 + 32 * f0 + ch * 4;
-                    const float4 v = *reinterpret_cast<const float4 *>(stage + rl * ROWB + ch * 16);
-                    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-                    // max over the 16-lane row: lane swaps 1 and 2 within quads,
-                    // then mirrors within 8 and within 16 lanes
-                    m = fmaxf(m, dpp_move<0xB1>(m));
-                    m = fmaxf(m, dpp_move<0x4E>(m));
-                    m = fmaxf(m, dpp_move<0x141>(m));
-                    m = fmaxf(m, dpp_move<0x140>(m));
-                    int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 13 : 0;
-                    e = e < -126 ? -126 : e;
-                    const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-                    // rint(v * 2^-e) as an integer: adding 1.5 * 2^23 rounds the
-                    // (exact) product half-to-even into the mantissa
-                    const float vs[4] = {v.x, v.y, v.z, v.w};
-                    uint32_t q[4];
+            for (int f = 0; f < WN; ++f) {
+                const float sc = gsc[d][f] * 0.0625f, so = gsc[d][f] * gof[d][f];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        q[u] = (uint32_t)(__float_as_int(fmaf(vs[u], sc, 12582912.0f)) - 0x4B400000) & 0xffffu;
-                    if (r < rows && ocol < ldo) {
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<int16_t *>(a.out) + (row0 + r) * ldo + ocol) =
-                            make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
-                        if (ch == 0) a.out_exp[(row0 + r) * ((ldo + 63) / 64) + (ocol0 + 32 * f0) / 64] = (int8_t)e;
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const float4 xv =
+                            *reinterpret_cast<const float4 *>(&xs[d & 1][mi * 32 + 8 * q4 + 4 * (lane >> 5)]);
+                        const float x4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int i = 4 * q4 + u;
+                            accf[mi][f][i] = fmaf((float)acs[mi][f][i], sc, accf[mi][f][i]);
+                            accf[mi][f][i] = fmaf(-so, x4[u], accf[mi][f][i]);
+                        }
                     }
-                }
-            } else {
-#pragma unroll
-                for (int idx = lane; idx < 32 * CPR; idx += 64) {
-                    const int rl = idx / CPR, ch = idx % CPR;
-                    const int r = mi * 32 + rl;
-                    const int ocol = ocol0 + 32 * f0 + ch * (16 / (int)sizeof(ET));
-                    if (r < rows && ocol < ldo)
-                        *reinterpret_cast<uint4 *>(reinterpret_cast<ET *>(a.out) + (row0 + r) * ldo + ocol) =
-                            *reinterpret_cast<const uint4 *>(stage + rl * ROWB + ch * 16);
-                }
             }
+            load_b(d, it + DEPTH);
+            const int dn = (d + 1) % DEPTH;
+            store_a(dn, (d + 1) & 1);
+            load_a(dn, it + 1 + DEPTH);
             __syncthreads();
         }
     }
+    v16i accb[MI][WN];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int f = 0; f < WN; ++f) accb[mi][f] = __builtin_bit_cast(v16i, accf[mi][f]);
+    __syncthreads();   // every wave is done with the A buffers
+    gemm_epilogue<BM, WN, EPI, OutT, true>(a, accb, ascale, ones, smem, rows, row0, nb, N);
 }
 
 namespace {
@@ -507,15 +786,106 @@ void gemm_tile_params(int64_t M_total, int64_t N, int G, int epilogue, int *BM, 
 
 void *gemm_tiles_ptr(void *ws, int G) { return (char *)ws + prefix_bytes(G); }
 
-hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
-                               hipStream_t st)
+static hipError_t launch_tilemap_cfg(const int32_t *offsets, int G, int64_t M_total, int64_t N, TileCfg c,
+                                     int epilogue, void *ws, hipStream_t st)
 {
-    if (M_total == 0) return hipSuccess;
-    const TileCfg c = gemm_cfg(M_total, G, epilogue);
     const int64_t blocks = std::min<int64_t>((gemm_max_tiles(M_total, N, G) + 255) / 256, 64);
     hipLaunchKernelGGL(gemm_tilemap_kernel, dim3((unsigned)blocks), dim3(256), 0, st, offsets, G, c.BM,
                        gemm_nblocks(N, epilogue, c.WN), (int32_t *)ws, (int4 *)((char *)ws + prefix_bytes(G)));
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
+                               hipStream_t st)
+{
+    if (M_total == 0) return hipSuccess;
+    return launch_tilemap_cfg(offsets, G, M_total, N, gemm_cfg(M_total, G, epilogue), epilogue, ws, st);
+}
+
+// ---- W4A8
+// Tile shapes: 32 x 256 up to 32 rows per group on average, 64 x 256 above
+// (the fp32 accumulators and the step's int32 sums both stay in registers,
+// which 128-row tiles would not fit).
+static TileCfg gemm_cfg_w4(int64_t M_total, int G)
+{
+    return (double)M_total / (double)G <= 32.0 ? TileCfg{32, 2} : TileCfg{64, 2};
+}
+
+void gemm_tile_params_w4(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n)
+{
+    const TileCfg c = gemm_cfg_w4(M_total, G);
+    *BM = c.BM;
+    *nblocks_n = gemm_nblocks(N, epilogue, c.WN);
+}
+
+size_t packed_w4_bytes(int64_t G, int64_t N, int64_t K) { return (size_t)(G * ((N + 31) / 32) * ((K + 127) / 128) * 2048); }
+
+hipError_t launch_pack_w4(const int8_t *B, int64_t G, int64_t N, int64_t K, uint8_t *P, hipStream_t st)
+{
+    const int64_t nd = (int64_t)packed_w4_bytes(G, N, K) / 4;
+    if (nd == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((nd + 255) / 256, 65536);
+    hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, B, G, N, K, (uint32_t *)P);
+    return hipGetLastError();
+}
+
+template <int BM>
+static hipError_t launch_w4_bm(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
+{
+    const int64_t grid = ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
+    const dim3 g((unsigned)grid), b(G_THREADS);
+    if (epilogue == 1 && out_dtype == 0)
+        hipLaunchKernelGGL((grouped_gemm_w4_kernel<BM, 2, 2, 1, uint16_t>), g, b, 0, st, ga);
+    else if (epilogue == 1)
+        hipLaunchKernelGGL((grouped_gemm_w4_kernel<BM, 2, 2, 1, float>), g, b, 0, st, ga);
+    else if (out_dtype == 0)
+        hipLaunchKernelGGL((grouped_gemm_w4_kernel<BM, 2, 2, 2, uint16_t>), g, b, 0, st, ga);
+    else
+        hipLaunchKernelGGL((grouped_gemm_w4_kernel<BM, 2, 2, 2, float>), g, b, 0, st, ga);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                               int gather_div, const uint8_t *Bp, const float *gscales, const int8_t *goffs,
+                               const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                               int out_dtype, void *out, const void *ws, hipStream_t st)
+{
+    if (M_total == 0) return hipSuccess;
+    GemmArgs ga{};
+    ga.A = A;
+    ga.a_scales = a_scales;
+    ga.gather = gather;
+    ga.gather_div = gather_div > 0 ? gather_div : 1;
+    ga.B = (const int8_t *)Bp;
+    ga.b_scales = nullptr;
+    ga.b_gscales = gscales;
+    ga.b_goffs = goffs;
+    ga.offsets = offsets;
+    ga.G = G;
+    ga.M_total = M_total;
+    ga.N = N;
+    ga.K = K;
+    ga.out = out;
+    ga.out_exp = nullptr;
+    ga.tile_prefix = (const int32_t *)ws;
+    ga.tiles = (const int4 *)((const char *)ws + prefix_bytes(G));
+    ga.A_bytes = A_rows * K;
+    ga.packed_b = 1;
+    const TileCfg c = gemm_cfg_w4(M_total, G);
+    ga.nblocks_n = gemm_nblocks(N, epilogue, c.WN);
+    return c.BM == 32 ? launch_w4_bm<32>(ga, epilogue, out_dtype, st) : launch_w4_bm<64>(ga, epilogue, out_dtype, st);
+}
+
+hipError_t launch_grouped_gemm_w4(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                                  int gather_div, const uint8_t *Bp, const float *gscales, const int8_t *goffs,
+                                  const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K,
+                                  int epilogue, int out_dtype, void *out, void *ws, hipStream_t st)
+{
+    if (M_total == 0) return hipSuccess;
+    hipError_t e = launch_tilemap_cfg(offsets, G, M_total, N, gemm_cfg_w4(M_total, G), epilogue, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_gemm_w4_main(A, A_rows, a_scales, gather, gather_div, Bp, gscales, goffs, offsets, G, M_total, N,
+                               K, epilogue, out_dtype, out, ws, st);
 }
 
 hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,

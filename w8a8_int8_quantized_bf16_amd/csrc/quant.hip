@@ -113,6 +113,57 @@ static void launch_typed(const T *x, int64_t rows, int64_t cols, int64_t ld, int
     else hipLaunchKernelGGL(quant_rows_kernel<T>, grid(1), block, 0, st, x, rows, cols, ld, q, scales);
 }
 
+// W4 codes of fp32 weights ("Qwen3-1.7B-W4A8 on Ascend", 4bit weights items
+// 1-2: groups of 128 inputs with a scale and an offset, 4-bit two's
+// complement).  Per group of one row, over the range [min(w, 0), max(w, 0)]
+// (zero stays representable): s = (max - min) / 15, z = rint(-min / s),
+// u = clamp(rint(w / s) + z, 0, 15); code u - 8 and offset z - 8, both in
+// [-8, 7] (a group of zeros: s = 0, codes and offset 0).  Every division is
+// the IEEE fp32 quotient.  One wavefront per (row, group), two columns per
+// lane; a short last group reads zeros past the row, which leave the range
+// (it always holds 0) unchanged.
+__global__ __launch_bounds__(256) void quant_w4_kernel(const float *__restrict__ w, int64_t rows, int64_t cols,
+                                                       int8_t *__restrict__ q, float *__restrict__ scales,
+                                                       int8_t *__restrict__ offs)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t ng = (cols + 127) / 128;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (unit >= rows * ng) return;
+    const int64_t r = unit / ng, g = unit % ng;
+    const int64_t c = g * 128 + 2 * lane;   // cols is even: c < cols covers both columns
+    float2 v = make_float2(0.0f, 0.0f);
+    if (c < cols) v = *reinterpret_cast<const float2 *>(w + r * cols + c);
+    const float mx = wave_max_nonneg(fmaxf(fmaxf(v.x, v.y), 0.0f));
+    const float nmn = wave_max_nonneg(fmaxf(fmaxf(-v.x, -v.y), 0.0f));   // -min(w, 0)
+    const float s = (mx + nmn) / 15.0f;
+    int q0 = 0, q1 = 0, o = 0;
+    if (s != 0.0f) {
+        const float z = rintf(nmn / s);
+        const float u0 = fminf(fmaxf(rintf(v.x / s) + z, 0.0f), 15.0f);
+        const float u1 = fminf(fmaxf(rintf(v.y / s) + z, 0.0f), 15.0f);
+        q0 = (int)u0 - 8;
+        q1 = (int)u1 - 8;
+        o = (int)z - 8;
+    }
+    if (c < cols)
+        *reinterpret_cast<uint16_t *>(q + r * cols + c) = (uint16_t)((q0 & 0xff) | ((q1 & 0xff) << 8));
+    if (lane == 0) {
+        scales[r * ng + g] = s;
+        offs[r * ng + g] = (int8_t)o;
+    }
+}
+
+hipError_t launch_quant_w4(const float *w, int64_t rows, int64_t cols, int8_t *q, float *scales, int8_t *offs,
+                           hipStream_t st)
+{
+    const int64_t units = rows * ((cols + 127) / 128);
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_w4_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, w, rows, cols, q,
+                       scales, offs);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ld, int8_t *q,
                              float *scales, hipStream_t st)
 {
