@@ -486,15 +486,20 @@ void grouped_gemm_kernel(GemmArgs a)
 // the same tiles and A path as grouped_gemm_kernel, B in the packed W4 layout
 // (pack_w4_kernel).  A lane loads 32 bytes of codes per fragment and step and
 // unpacks them with a shift and a mask into operands worth 16 times the
-// codes; the int32 sum of one 128-column step, which is exactly one group of
-// the weights, is folded into fp32 accumulators as
-//   acc += (s / 16) * sum16 - (s * o) * xsum,
-// s and o the group's scale and offset of the lane's column, xsum the sum of
-// the row's A codes over the step (formed by the threads that stage the A
-// tile, so no pass of its own).  Columns are scaled per group here; the
+// codes.  One 128-column step is exactly one group of the weights, and the
+// row r, column c result is
+//   sum_g s_g * (sum16_g / 16) - sum_g (s_g * o_g) * xsum_g[r],
+// sum16_g the int32 MFMA sum of the step, s_g and o_g the group's scale and
+// offset of column c, xsum_g the sum of row r's A codes over the step.  The
+// first term is folded into fp32 accumulators after every step (a convert and
+// one fma per value); the second is a contraction over the groups, which
+// v_mfma_f32_32x32x2_f32 adds into the same accumulators two groups at a
+// time (row sums as the A operand, -s*o of the lane's column as B), so it
+// costs matrix-core cycles instead of vector ones.  The row sums are formed by
+// the threads that stage the A tile.  Columns are scaled per group here; the
 // epilogue applies the per-token scale (and SwiGLU).
 template <int BM, int WN, int DEPTH, int EPI, typename OutT>
-__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(BM <= 32 ? 2 : 1, 8)))
+__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void grouped_gemm_w4_kernel(GemmArgs a)
 {
     static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH and alternates two LDS buffers");
@@ -509,7 +514,7 @@ void grouped_gemm_w4_kernel(GemmArgs a)
     int8_t(*As)[BM * G_BK] = reinterpret_cast<int8_t(*)[BM * G_BK]>(smem);
     __shared__ int32_t arow[BM];
     __shared__ float ascale[BM];
-    __shared__ __attribute__((aligned(16))) float xs[2][BM];   // row sums of the staged A codes
+    __shared__ float xs[4][BM];   // row sums of the staged A codes, a ring of four steps
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int bid = blockIdx.x;
@@ -606,9 +611,9 @@ void grouped_gemm_w4_kernel(GemmArgs a)
         for (int j = 0; j < APASS; ++j)
             areg[slot][j] = buf_load16(rA, (live && kin) ? aoff[j] + it * G_BK : OOB_BASE);
     };
-    // the A chunks into LDS, and each row's code sum over the step (its 8
+    // the A chunks into LDS, and each row's code sum over step `it` (its 8
     // chunks are staged by 8 neighbouring lanes)
-    auto store_a = [&](int slot, int buf) {
+    auto store_a = [&](int slot, int buf, int it) {
 #pragma unroll
         for (int j = 0; j < APASS; ++j) {
             const v4i v = areg[slot][j];
@@ -620,7 +625,7 @@ void grouped_gemm_w4_kernel(GemmArgs a)
             sum += __shfl_xor(sum, 1, 64);
             sum += __shfl_xor(sum, 2, 64);
             sum += __shfl_xor(sum, 4, 64);
-            if (ac == 0) xs[buf][arr[j]] = (float)sum;
+            if (ac == 0) xs[it & 3][arr[j]] = (float)sum;
         }
     };
 
@@ -628,11 +633,12 @@ void grouped_gemm_w4_kernel(GemmArgs a)
     for (int d = 0; d < DEPTH; ++d) load_a(d, d);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_b(d, d);
-    store_a(0, 0);
+    store_a(0, 0, 0);
     load_a(0, DEPTH);
     __syncthreads();
 
     const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
+    float so_even[WN];   // -s*o of the even step of the current pair
     for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
@@ -663,28 +669,35 @@ void grouped_gemm_w4_kernel(GemmArgs a)
                     }
                 }
             }
-            // fold the step (one weight group) into the fp32 accumulators
+            // fold the step's sums (one weight group) into the fp32 accumulators
 #pragma unroll
             for (int f = 0; f < WN; ++f) {
-                const float sc = gsc[d][f] * 0.0625f, so = gsc[d][f] * gof[d][f];
+                const float sc = gsc[d][f] * 0.0625f;
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const float4 xv =
-                            *reinterpret_cast<const float4 *>(&xs[d & 1][mi * 32 + 8 * q4 + 4 * (lane >> 5)]);
-                        const float x4[4] = {xv.x, xv.y, xv.z, xv.w};
+                    for (int i = 0; i < 16; ++i) accf[mi][f][i] = fmaf((float)acs[mi][f][i], sc, accf[mi][f][i]);
+            }
+            if ((d & 1) == 0) {
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int i = 4 * q4 + u;
-                            accf[mi][f][i] = fmaf((float)acs[mi][f][i], sc, accf[mi][f][i]);
-                            accf[mi][f][i] = fmaf(-so, x4[u], accf[mi][f][i]);
-                        }
+                for (int f = 0; f < WN; ++f) so_even[f] = -gsc[d][f] * gof[d][f];
+            } else {
+                // offsets of the pair of groups (it - 1, it): lanes 0-31 carry
+                // the even group's row sums and -s*o, lanes 32-63 the odd one's
+                const int gl = it - 1 + (lane >> 5);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const float xa = xs[gl & 3][mi * 32 + (lane & 31)];
+#pragma unroll
+                    for (int f = 0; f < WN; ++f) {
+                        const float ob = lane < 32 ? so_even[f] : -gsc[d][f] * gof[d][f];
+                        accf[mi][f] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa, ob, accf[mi][f], 0, 0, 0);
                     }
+                }
             }
             load_b(d, it + DEPTH);
             const int dn = (d + 1) % DEPTH;
-            store_a(dn, (d + 1) & 1);
+            store_a(dn, (d + 1) & 1, it + 1);
             load_a(dn, it + 1 + DEPTH);
             __syncthreads();
         }
