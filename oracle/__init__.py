@@ -57,6 +57,10 @@ def lib():
         L.oracle_w4a8_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, P, i32, i64, i64, i32, i32, P]
         L.oracle_moe_layer_w4.argtypes = [P, i32, i64, i64, i32, i32, i64, P, P, P, P, P, P, P] + [P] * 10
         L.oracle_moe_layer_w4_tokens.argtypes = [P, i32, i64, i32, i32, i64, P, P, P, P, P, P, P, i64, P]
+        L.oracle_moe_layer_shared.argtypes = ([P, i32, i64, i64, i32, i32, i64, P, P, P, P, P, i64, P, P, P, P, P, P]
+                                              + [P] * 15)
+        L.oracle_moe_layer_shared_tokens.argtypes = [P, i32, i64, i32, i32, i64, P, P, P, P, P, i64, P, P, P, P, P,
+                                                     P, i64, P]
         L.oracle_num_threads.restype = i32
         L.oracle_f64_to_bf16.argtypes = [d]
         L.oracle_f64_to_bf16.restype = ctypes.c_uint16
@@ -295,4 +299,65 @@ def moe_layer_w4_tokens(x, wg, wgu4, sgu4, ogu4, wd, sd, k, tokens):
     lib().oracle_moe_layer_w4_tokens(_p(x), dt, H, E, k, I, _p(_c(wg, np.uint16)), _p(_c(wgu4, np.int8)),
                                      _p(_c(sgu4, np.float32)), _p(_c(ogu4, np.int8)), _p(_c(wd, np.int8)),
                                      _p(_c(sd, np.float32)), _p(tok), len(tok), _p(out))
+    return out
+
+
+# ---------------------------------------------------------- shared expert ---
+
+
+def _shared_args(se, H):
+    """(Is, codes/scales of gate_up and down, gate bits) of a shared expert dict
+    {wgu [2Is,H] int8, sgu [2Is] fp32, wd [H,Is] int8, sd [H] fp32, wsg [H] bf16 bits}."""
+    wgu = _c(se["wgu"], np.int8)
+    twoIs, H2 = wgu.shape
+    Is = twoIs // 2
+    wd = _c(se["wd"], np.int8)
+    assert H2 == H and wd.shape == (H, Is) and np.shape(se["wsg"]) == (H,)
+    return Is, (wgu, _c(se["sgu"], np.float32), wd, _c(se["sd"], np.float32), _c(se["wsg"], np.uint16))
+
+
+def moe_layer_shared(x, wg, wgu, sgu, wd, sd, k, shared, intermediates=False):
+    """The layer with a shared expert (R18, R19); `shared` as in _shared_args.
+    Intermediates: the routed ones (ids, w, xq, sx, offsets, sorted_pair,
+    pair_pos, h, hq, sh) and the shared expert's gate [T] (fp64 sigmoid), hs
+    [T,Is] bf16, hqs [T,Is], shs [T], accs_d [T,H] int32."""
+    x = np.ascontiguousarray(x)
+    dt = _xdtype(x)
+    wgu = _c(wgu, np.int8)
+    E, twoI, H = wgu.shape
+    I = twoI // 2
+    T = x.shape[0]
+    P = T * k
+    Is, sa = _shared_args(shared, H)
+    out = np.empty((T, H), x.dtype)
+    inter = {}
+    if intermediates:
+        inter = dict(
+            ids=np.empty((T, k), np.int32), w=np.empty((T, k), np.float32),
+            xq=np.empty((T, H), np.int8), sx=np.empty(T, np.float32),
+            offsets=np.empty(E + 1, np.int32), sorted_pair=np.empty(P, np.int32),
+            pair_pos=np.empty(P, np.int32), h=np.empty((P, I), np.uint16), hq=np.empty((P, I), np.int8),
+            sh=np.empty(P, np.float32), gate=np.empty(T, np.float64), hs=np.empty((T, Is), np.uint16),
+            hqs=np.empty((T, Is), np.int8), shs=np.empty(T, np.float32), accs_d=np.empty((T, H), np.int32))
+    g = inter.get
+    lib().oracle_moe_layer_shared(_p(x), dt, T, H, E, k, I, _p(_c(wg, np.uint16)), _p(wgu), _p(_c(sgu, np.float32)),
+                                  _p(_c(wd, np.int8)), _p(_c(sd, np.float32)), Is, *[_p(a) for a in sa], _p(out),
+                                  _p(g("ids")), _p(g("w")), _p(g("xq")), _p(g("sx")), _p(g("offsets")),
+                                  _p(g("sorted_pair")), _p(g("pair_pos")), _p(g("h")), _p(g("hq")), _p(g("sh")),
+                                  _p(g("gate")), _p(g("hs")), _p(g("hqs")), _p(g("shs")), _p(g("accs_d")))
+    return (out, inter) if intermediates else out
+
+
+def moe_layer_shared_tokens(x, wg, wgu, sgu, wd, sd, k, shared, tokens):
+    """Rows `tokens` of the shared-expert layer's output (no term couples tokens)."""
+    x = np.ascontiguousarray(x)
+    dt = _xdtype(x)
+    tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    E, twoI, H = wgu.shape
+    I = twoI // 2
+    Is, sa = _shared_args(shared, H)
+    out = np.empty((len(tok), H), x.dtype)
+    lib().oracle_moe_layer_shared_tokens(_p(x), dt, H, E, k, I, _p(_c(wg, np.uint16)), _p(_c(wgu, np.int8)),
+                                         _p(_c(sgu, np.float32)), _p(_c(wd, np.int8)), _p(_c(sd, np.float32)), Is,
+                                         *[_p(a) for a in sa], _p(tok), len(tok), _p(out))
     return out

@@ -57,6 +57,20 @@
  *       [-8, 7]; w ~ (q - o) * s.  A group of zeros has s = 0, codes and
  *       offset 0.  down_proj stays W8A8 (the page keeps down_proj in higher
  *       precision); activations are the same per-token int8 codes.
+ *   R18 shared expert (the next row after W4A8): the layers of the pages'
+ *       Qwen3.6 and Qwen3-Next models add an always-on shared expert whose
+ *       Linears are W8A8 like a routed expert's ([NEXT-AMCT] 2.2: the shared
+ *       expert is a dense path quantised directly) while shared_expert_gate
+ *       stays bf16 ([3.6-CFG] ignore list).  The plainest reading of the
+ *       pair: the shared expert is a SwiGLU FFN of its own intermediate size
+ *       Is over every token's int8 codes from step 2, with the steps of a
+ *       routed expert (h rounded to bf16, quantised per row, int8 down_proj),
+ *       and the gate is one bf16 Linear [H] -> 1 whose sigmoid weights the
+ *       shared output: out = sum_j w_j y_j + sigmoid(x . w_sg) * z.
+ *   R19 the gate logit x . w_sg is not a decision (no integer depends on
+ *       it), so here it is the exact fp64 sum of the products (bf16 x bf16 and
+ *       fp32 x bf16 products are exact in fp64); the shared term is added after
+ *       the k routed slots.
  *   Floating-point results that are compared within a tolerance (dequantised
  *   GEMM outputs, SwiGLU, softmax weights, the combine) are computed here in
  *   fp64.  Floating-point work that decides an integer (int8 codes, top-k
@@ -468,13 +482,31 @@ void oracle_combine(const void *y, int y_dtype, const float *w, const int32_t *p
  *   acc_d [T*k][H] int32.
  * out [T][H] has the dtype of x.
  */
+/* The shared expert of R18 (NULL when the layer has none); the *_o members
+ * are optional outputs: gate [T] (the sigmoid), h [T][Is] bf16, hq [T][Is]
+ * with scales sh [T], and the down_proj int32 sums acc_d [T][H]. */
+typedef struct {
+    int64_t Is;
+    const int8_t *wgu;   /* [2Is][H] codes, gate rows then up rows */
+    const float *sgu;    /* [2Is] */
+    const int8_t *wd;    /* [H][Is] */
+    const float *sd;     /* [H] */
+    const uint16_t *wsg; /* [H] bf16, shared_expert_gate */
+    double *gate_o;
+    uint16_t *h_o;
+    int8_t *hq_o;
+    float *sh_o;
+    int32_t *acc_d_o;
+} or_shared_t;
+
 static void or_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
                          const uint16_t *wg, const int8_t *wgu, const float *sgu,
                          const int8_t *wgu4, const float *sgu4, const int8_t *ogu4,
                          const int8_t *wd, const float *sd, void *out,
                          int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
                          int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
-                         int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o)
+                         int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o,
+                         const or_shared_t *se)
 {
     int64_t P = T * k;
     int32_t *ids = ids_o ? ids_o : (int32_t *)malloc(sizeof(int32_t) * (size_t)P);
@@ -537,7 +569,56 @@ static void or_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, 
         }
     }
     /* 5 */
-    oracle_combine(y, 2, w, pos, T, k, H, out, dtype);
+    if (!se) {
+        oracle_combine(y, 2, w, pos, T, k, H, out, dtype);
+    } else {
+        /* R18: the shared expert on every token, then its gated output is
+         * added after the routed slots */
+        int64_t Is = se->Is;
+        uint16_t *hs = se->h_o ? se->h_o : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * Is));
+        int8_t *hqs = se->hq_o ? se->hq_o : (int8_t *)malloc((size_t)(T * Is));
+        float *shs = se->sh_o ? se->sh_o : (float *)malloc(sizeof(float) * (size_t)T);
+        double *z = (double *)malloc(sizeof(double) * (size_t)(T * H));
+        double *sig = (double *)malloc(sizeof(double) * (size_t)T);
+        int64_t t;
+#pragma omp parallel for schedule(static)
+        for (t = 0; t < T; ++t) {
+            for (int64_t n = 0; n < Is; ++n) {
+                double gate = (double)or_dot_i8(xq + t * H, se->wgu + n * H, H) * (double)sx[t] * (double)se->sgu[n];
+                double up = (double)or_dot_i8(xq + t * H, se->wgu + (Is + n) * H, H) * (double)sx[t] *
+                            (double)se->sgu[Is + n];
+                hs[t * Is + n] = or_f64_to_bf16(or_silu(gate) * up);
+            }
+        }
+        oracle_quant_rows(hs, 0, T, Is, Is, hqs, shs);
+#pragma omp parallel for schedule(static)
+        for (t = 0; t < T; ++t) {
+            for (int64_t n = 0; n < H; ++n) {
+                int32_t ad = or_dot_i8(hqs + t * Is, se->wd + n * Is, Is);
+                if (se->acc_d_o) se->acc_d_o[t * H + n] = ad;
+                z[t * H + n] = (double)ad * (double)shs[t] * (double)se->sd[n];
+            }
+            double g = 0.0; /* R19 */
+            for (int64_t c = 0; c < H; ++c)
+                g += (double)or_load(x, dtype, t * H + c) * (double)or_bf16_to_f32(se->wsg[c]);
+            sig[t] = 1.0 / (1.0 + exp(-g));
+            if (se->gate_o) se->gate_o[t] = sig[t];
+        }
+#pragma omp parallel for schedule(static)
+        for (t = 0; t < T; ++t) {
+            for (int64_t n = 0; n < H; ++n) {
+                double acc = 0.0;
+                for (int j = 0; j < k; ++j) acc += (double)w[t * k + j] * y[(int64_t)pos[t * k + j] * H + n];
+                acc += sig[t] * z[t * H + n];
+                or_store(out, dtype, t * H + n, acc);
+            }
+        }
+        if (!se->h_o) free(hs);
+        if (!se->hq_o) free(hqs);
+        if (!se->sh_o) free(shs);
+        free(z);
+        free(sig);
+    }
 
     if (!ids_o) free(ids);
     if (!w_o) free(w);
@@ -560,7 +641,7 @@ void oracle_moe_layer(const void *x, int dtype, int64_t T, int64_t H, int E, int
                       int32_t *acc_gu_o, uint16_t *h_o, int8_t *hq_o, float *sh_o, int32_t *acc_d_o)
 {
     or_moe_layer(x, dtype, T, H, E, k, I, wg, wgu, sgu, NULL, NULL, NULL, wd, sd, out, ids_o, w_o, xq_o, sx_o,
-                 offsets_o, sorted_o, pos_o, acc_gu_o, h_o, hq_o, sh_o, acc_d_o);
+                 offsets_o, sorted_o, pos_o, acc_gu_o, h_o, hq_o, sh_o, acc_d_o, NULL);
 }
 
 /* The layer with W4A8 gate_up weights (R17): codes wgu4 [E][2I][H], scales
@@ -573,7 +654,27 @@ void oracle_moe_layer_w4(const void *x, int dtype, int64_t T, int64_t H, int E, 
                          uint16_t *h_o, int8_t *hq_o, float *sh_o)
 {
     or_moe_layer(x, dtype, T, H, E, k, I, wg, NULL, NULL, wgu4, sgu4, ogu4, wd, sd, out, ids_o, w_o, xq_o, sx_o,
-                 offsets_o, sorted_o, pos_o, NULL, h_o, hq_o, sh_o, NULL);
+                 offsets_o, sorted_o, pos_o, NULL, h_o, hq_o, sh_o, NULL, NULL);
+}
+
+/* The layer with a shared expert (R18, R19): wsgu [2Is][H] int8 + ssgu [2Is],
+ * wsd [H][Is] int8 + ssd [H], wsg [H] bf16.  The routed intermediates are the
+ * same optional outputs as oracle_moe_layer's; gate_o [T] (fp64 sigmoid),
+ * hs_o [T][Is] bf16, hqs_o [T][Is] + shs_o [T], accs_d_o [T][H] those of the
+ * shared expert. */
+void oracle_moe_layer_shared(const void *x, int dtype, int64_t T, int64_t H, int E, int k, int64_t I,
+                             const uint16_t *wg, const int8_t *wgu, const float *sgu,
+                             const int8_t *wd, const float *sd,
+                             int64_t Is, const int8_t *wsgu, const float *ssgu, const int8_t *wsd, const float *ssd,
+                             const uint16_t *wsg, void *out,
+                             int32_t *ids_o, float *w_o, int8_t *xq_o, float *sx_o,
+                             int32_t *offsets_o, int32_t *sorted_o, int32_t *pos_o,
+                             uint16_t *h_o, int8_t *hq_o, float *sh_o,
+                             double *gate_o, uint16_t *hs_o, int8_t *hqs_o, float *shs_o, int32_t *accs_d_o)
+{
+    or_shared_t se = {Is, wsgu, ssgu, wsd, ssd, wsg, gate_o, hs_o, hqs_o, shs_o, accs_d_o};
+    or_moe_layer(x, dtype, T, H, E, k, I, wg, wgu, sgu, NULL, NULL, NULL, wd, sd, out, ids_o, w_o, xq_o, sx_o,
+                 offsets_o, sorted_o, pos_o, NULL, h_o, hq_o, sh_o, NULL, &se);
 }
 
 /*
@@ -606,5 +707,21 @@ void oracle_moe_layer_w4_tokens(const void *x, int dtype, int64_t H, int E, int 
         memcpy(xs + esz * (size_t)(i * H), (const unsigned char *)x + esz * (size_t)(tok[i] * H), esz * (size_t)H);
     oracle_moe_layer_w4(xs, dtype, n, H, E, k, I, wg, wgu4, sgu4, ogu4, wd, sd, out,
                         NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+    free(xs);
+}
+
+void oracle_moe_layer_shared_tokens(const void *x, int dtype, int64_t H, int E, int k, int64_t I,
+                                    const uint16_t *wg, const int8_t *wgu, const float *sgu,
+                                    const int8_t *wd, const float *sd,
+                                    int64_t Is, const int8_t *wsgu, const float *ssgu, const int8_t *wsd,
+                                    const float *ssd, const uint16_t *wsg,
+                                    const int64_t *tok, int64_t n, void *out)
+{
+    size_t esz = dtype == 0 ? 2 : 4;
+    unsigned char *xs = (unsigned char *)malloc(esz * (size_t)(n * H));
+    for (int64_t i = 0; i < n; ++i)
+        memcpy(xs + esz * (size_t)(i * H), (const unsigned char *)x + esz * (size_t)(tok[i] * H), esz * (size_t)H);
+    oracle_moe_layer_shared(xs, dtype, n, H, E, k, I, wg, wgu, sgu, wd, sd, Is, wsgu, ssgu, wsd, ssd, wsg, out,
+                            NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
     free(xs);
 }

@@ -14,6 +14,10 @@ a fixed order:
     3 + 3e + 0   expert e gate_proj   [I][H]
     3 + 3e + 1   expert e up_proj     [I][H]
     3 + 3e + 2   expert e down_proj   [H][I]
+    3 + 3E + 0   shared expert gate_proj  [Is][H]   (layers with a shared expert)
+    3 + 3E + 1   shared expert up_proj    [Is][H]
+    3 + 3E + 2   shared expert down_proj  [H][Is]
+    3 + 3E + 3   shared_expert_gate       [H] (bf16)
 
 Workloads (shapes of the pages' models; all values synthetic):
   moe_tiny_T16_H64_E8_k2_I32      x fp32 N(0,1)
@@ -27,8 +31,16 @@ Workloads (shapes of the pages' models; all values synthetic):
                                   k=8, I=1536; x as above, shifted so that the
                                   router's scores carry a bias -1.1*ln(rank_e):
                                   Zipf(1.1)-skewed expert loads
+  moe_tiny_shared_T16_H64_E8_k2_I32_Is64   the tiny layer plus a shared expert
+                                  of intermediate size 64
+  moe_30b_shared_prefill_T4096    the 30B-shaped prefill layer plus an always-on
+                                  shared expert of intermediate size 768 and its
+                                  bf16 sigmoid gate
+  moe_30b_shared_decode_T64       the same with T=64
 Weights: router W_g N(0, 0.02) in bf16; expert weights N(0, 0.02) in fp32 (they
-are quantised to int8 per output channel by whichever side uses them).
+are quantised to int8 per output channel by whichever side uses them); the
+shared expert's weights N(0, 0.02) in fp32 and its gate vector N(0, 0.02) in
+bf16.
 """
 from __future__ import annotations
 
@@ -50,6 +62,7 @@ class MoEConfig:
     x_dist: str           # "normal" or "student_t4"
     n_outlier: int        # outlier channels scaled by 20
     zipf_s: float = 0.0   # > 0: bias the router towards Zipf(zipf_s) loads
+    Is: int = 0           # > 0: an always-on shared expert of this intermediate size
 
     @property
     def P(self):
@@ -71,6 +84,9 @@ MOE_CONFIGS = {
         MoEConfig("moe_30b_prefill_T4096", 4096, 2048, 128, 8, 768, "bf16", "student_t4", 8),
         MoEConfig("moe_30b_decode_T64", 64, 2048, 128, 8, 768, "bf16", "student_t4", 8),
         MoEConfig("moe_235b_zipf_T8192", 8192, 4096, 128, 8, 1536, "bf16", "student_t4", 8, zipf_s=1.1),
+        MoEConfig("moe_tiny_shared_T16_H64_E8_k2_I32_Is64", 16, 64, 8, 2, 32, "f32", "normal", 0, Is=64),
+        MoEConfig("moe_30b_shared_prefill_T4096", 4096, 2048, 128, 8, 768, "bf16", "student_t4", 8, Is=768),
+        MoEConfig("moe_30b_shared_decode_T64", 64, 2048, 128, 8, 768, "bf16", "student_t4", 8, Is=768),
     ]
 }
 DENSE_CONFIGS = {c.name: c for c in [DenseConfig("dense_M4096_K2048_N4096", 4096, 2048, 4096, 20)]}
@@ -162,6 +178,20 @@ def moe_inputs(cfg: MoEConfig, seed=0, threads=8):
     x = moe_x(cfg, seed, wg)
     gu, dn = moe_expert_weights(cfg, seed, threads)
     return x, wg, gu, dn
+
+
+def shared_expert(cfg: MoEConfig, seed=0):
+    """The shared expert of a layer with cfg.Is > 0: fp32 gate_up [2Is][H]
+    (gate rows then up rows), fp32 down [H][Is] and the bf16 bits of the
+    shared_expert_gate vector [H]."""
+    assert cfg.Is > 0
+    st = [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(3 + 3 * cfg.E + 4)][3 + 3 * cfg.E:]
+    gu = np.empty((2 * cfg.Is, cfg.H), np.float32)
+    gu[:cfg.Is] = st[0].standard_normal((cfg.Is, cfg.H), dtype=np.float32) * np.float32(W_STD)
+    gu[cfg.Is:] = st[1].standard_normal((cfg.Is, cfg.H), dtype=np.float32) * np.float32(W_STD)
+    dn = st[2].standard_normal((cfg.H, cfg.Is), dtype=np.float32) * np.float32(W_STD)
+    wsg = f32_to_bf16_bits(st[3].standard_normal(cfg.H, dtype=np.float32) * np.float32(W_STD))
+    return gu, dn, wsg
 
 
 def dense_inputs(cfg: DenseConfig, seed=0):

@@ -613,3 +613,103 @@ def test_w4_layer_dense_brute_force(orc):
             accd = wd[e].astype(np.int64) @ hq[0].astype(np.int64)
             want[t] += float(it["w"][t, j]) * (accd * float(sh[0]) * sd[e].astype(np.float64))
     assert np.array_equal(out, want.astype(np.float32))
+
+
+# ---------------------------------------------------------- shared expert ---
+
+TINY_SE = synth.MOE_CONFIGS["moe_tiny_shared_T16_H64_E8_k2_I32_Is64"]
+
+
+def _tiny_shared(orc, wsg=None):
+    x, W = _tiny_layer(orc, TINY_SE)
+    gu, dn, wsg0 = synth.shared_expert(TINY_SE)
+    qs, ss = orc.quant_rows(gu)
+    qd, sd = orc.quant_rows(dn)
+    se = dict(wgu=qs, sgu=ss, wd=qd, sd=sd, wsg=wsg0 if wsg is None else wsg)
+    return x, W, se
+
+
+def _one_expert_layer(orc, x, se):
+    """The shared expert run as the only expert of a routed layer with k = 1:
+    its renormalised routing weight is exactly 1, so the layer returns the
+    expert's output through the routed path (router, permute, combine)."""
+    wg1 = np.zeros((1, x.shape[1]), np.uint16)
+    return orc.moe_layer(x, wg1, se["wgu"][None], se["sgu"][None], se["wd"][None], se["sd"][None], 1)
+
+
+def _routed(orc, x, W, k):
+    return orc.moe_layer(x, W["wg"], W["wgu"], W["sgu"], W["wd"], W["sd"], k)
+
+
+def test_shared_expert_with_zero_gate_adds_half_a_one_expert_layer(orc):
+    """w_sg = 0 gives a logit of 0 and a sigmoid of exactly 1/2: the layer is
+    the routed layer plus half of the shared expert, which equals a one-expert
+    routed layer with the shared weights (a different code path)."""
+    x, W, se = _tiny_shared(orc, wsg=np.zeros(TINY_SE.H, np.uint16))
+    out, it = orc.moe_layer_shared(x, W["wg"], W["wgu"], W["sgu"], W["wd"], W["sd"], TINY_SE.k, se,
+                                   intermediates=True)
+    assert np.all(it["gate"] == 0.5)
+    want = _routed(orc, x, W, TINY_SE.k).astype(np.float64) + 0.5 * _one_expert_layer(orc, x, se)
+    np.testing.assert_allclose(out, want, rtol=2e-6, atol=1e-7)
+    assert not np.allclose(out, _routed(orc, x, W, TINY_SE.k), rtol=1e-3, atol=1e-5)
+
+
+def test_shared_gate_saturates_to_zero_and_one(orc):
+    """A logit of -1000 gives a sigmoid of exactly 0 (the shared expert drops out
+    bit for bit), +1000 exactly 1 (the full shared output is added)."""
+    x, W, se = _tiny_shared(orc)
+    x = x.copy()
+    sign = np.where(np.arange(TINY_SE.T) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    x[:, 0] = sign
+    wsg = np.zeros(TINY_SE.H, np.uint16)
+    wsg[0] = synth.f32_to_bf16_bits(np.float32([1000.0]))[0]   # 1000 is a bf16 value
+    se["wsg"] = wsg
+    out, it = orc.moe_layer_shared(x, W["wg"], W["wgu"], W["sgu"], W["wd"], W["sd"], TINY_SE.k, se,
+                                   intermediates=True)
+    assert np.array_equal(it["gate"], np.where(sign > 0, 1.0, 0.0))
+    routed = _routed(orc, x, W, TINY_SE.k)
+    neg = sign < 0
+    assert np.array_equal(out[neg], routed[neg])
+    want = routed.astype(np.float64) + _one_expert_layer(orc, x, se)
+    np.testing.assert_allclose(out[~neg], want[~neg], rtol=2e-6, atol=1e-7)
+
+
+def test_shared_expert_brute_force(orc):
+    """The shared expert and its gate evaluated by hand: int64 matmuls of the
+    codes, SwiGLU in fp64, bf16 by exact rationals, the gate logit as the fp64
+    sum of x times the bf16 gate vector over the hidden index (from x, not its
+    int8 codes), sigmoid with libm's exp."""
+    x, W, se = _tiny_shared(orc)
+    cfg = TINY_SE
+    out, it = orc.moe_layer_shared(x, W["wg"], W["wgu"], W["sgu"], W["wd"], W["sd"], cfg.k, se,
+                                   intermediates=True)
+    qx, sx = orc.quant_rows(x)
+    Is = cfg.Is
+    acc = qx.astype(np.int64) @ se["wgu"].astype(np.int64).T
+    g = acc[:, :Is] * sx.astype(np.float64)[:, None] * se["sgu"][:Is].astype(np.float64)
+    u = acc[:, Is:] * sx.astype(np.float64)[:, None] * se["sgu"][Is:].astype(np.float64)
+    hs = _bf16_np(g / (1.0 + np.exp(-g)) * u)
+    assert np.array_equal(it["hs"], hs)
+    hqs, shs = orc.quant_rows(hs)
+    assert np.array_equal(it["hqs"], hqs) and np.array_equal(it["shs"], shs)
+    accd = hqs.astype(np.int64) @ se["wd"].astype(np.int64).T
+    assert np.array_equal(it["accs_d"], accd)
+    wsg = synth.bf16_bits_to_f32(se["wsg"]).astype(np.float64)
+    for t in range(cfg.T):
+        lg = 0.0
+        for c in range(cfg.H):
+            lg += float(x[t, c]) * float(wsg[c])
+        assert it["gate"][t] == 1.0 / (1.0 + math.exp(-lg))
+    z = accd * shs.astype(np.float64)[:, None] * se["sd"].astype(np.float64)
+    want = _routed(orc, x, W, cfg.k).astype(np.float64) + it["gate"][:, None] * z
+    np.testing.assert_allclose(out, want, rtol=2e-6, atol=1e-7)
+    # the gates span a real range, not a constant
+    assert it["gate"].min() < 0.5 < it["gate"].max()
+
+
+def test_shared_layer_token_subset(orc):
+    x, W, se = _tiny_shared(orc)
+    args = (W["wg"], W["wgu"], W["sgu"], W["wd"], W["sd"], TINY_SE.k, se)
+    out = orc.moe_layer_shared(x, *args)
+    sub = [5, 0, 15]
+    assert np.array_equal(orc.moe_layer_shared_tokens(x, *args, sub), out[sub])
