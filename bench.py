@@ -64,6 +64,17 @@ def kernel_model(cfg, E_hit, w4=False):
     m["down_gemm"] = dict(ops=2 * P * H * I, bytes=E_hit * H * I + E_hit * H * 4 + P * I + P * 4 + (E + 1) * 4
                           + ybytes)
     m["combine"] = dict(ops=0, bytes=ybytes + P * 8 + T * H * xb)
+    Is = cfg.Is
+    if Is:
+        # the shared expert's launches sit in the same stages: one group of T
+        # rows (no gather), its gate read by the combine with x
+        ys = T * H * 2 + T * ((H + 63) // 64)
+        m["gate_up_gemm"]["ops"] += 2 * T * 2 * Is * H
+        m["gate_up_gemm"]["bytes"] += 2 * Is * (H + 4) + T * Is * 2
+        m["quant_h"]["bytes"] += T * Is * 3 + T * 4
+        m["down_gemm"]["ops"] += 2 * T * H * Is
+        m["down_gemm"]["bytes"] += H * (Is + 4) + T * Is + T * 4 + ys
+        m["combine"]["bytes"] += ys + H * 2 + T * H * xb
     return m
 
 
@@ -74,6 +85,9 @@ def layer_model(cfg, E_hit, w4=False):
     xb = 2 if cfg.x_dtype == "bf16" else 4
     ops = 2 * T * k * 3 * H * I
     byts = gate_up_weight_bytes(cfg, E_hit, w4) + E_hit * H * (I + 4) + E * H * 2 + 2 * T * H * xb
+    if cfg.Is:   # the shared expert on every token, its int8 weights and bf16 gate
+        ops += 2 * T * 3 * H * cfg.Is
+        byts += 2 * cfg.Is * (H + 4) + H * (cfg.Is + 4) + H * 2
     return ops, byts
 
 
@@ -150,18 +164,25 @@ def cpu_baseline(case, target_s):
     qd, sd = oracle.quant_rows(case["dn"].reshape(-1, cfg.I))
     wq = (case["wg"], qgu.reshape(case["gu"].shape), sgu.reshape(cfg.E, -1), qd.reshape(case["dn"].shape),
           sd.reshape(cfg.E, -1), cfg.k)
+    layer_tokens = oracle.moe_layer_tokens
+    if cfg.Is:
+        sgu_f, sdn_f, wsg = case["shared"]
+        qs, ss = oracle.quant_rows(sgu_f)
+        qsd, ssd = oracle.quant_rows(sdn_f)
+        wq = wq + (dict(wgu=qs, sgu=ss, wd=qsd, sd=ssd, wsg=wsg),)
+        layer_tokens = oracle.moe_layer_shared_tokens
     log("oracle weight quantisation (untimed setup): %.1f s" % (time.time() - t0))
     rng = np.random.default_rng(0)
     n = min(32, cfg.T)
     tok = np.sort(rng.choice(cfg.T, n, replace=False))
     t0 = time.perf_counter()
-    oracle.moe_layer_tokens(case["x"], *wq, tok)
+    layer_tokens(case["x"], *wq, tok)
     dt = time.perf_counter() - t0
     n2 = int(min(cfg.T, max(n, n * target_s / max(dt, 1e-6))))
     if n2 > n:
         tok = np.sort(rng.choice(cfg.T, n2, replace=False))
         t0 = time.perf_counter()
-        oracle.moe_layer_tokens(case["x"], *wq, tok)
+        layer_tokens(case["x"], *wq, tok)
         dt = time.perf_counter() - t0
         n = n2
     del synth
@@ -407,14 +428,22 @@ def main():
     if x.dtype == np.uint16:
         xd = xd.view(torch.bfloat16)
     wgd = torch.from_numpy(wg.view(np.int16)).to(dev).view(torch.bfloat16)
+    shared = synth.shared_expert(cfg) if cfg.Is else None
+    shared_d = None
+    if shared is not None:
+        shared_d = (torch.from_numpy(shared[0]).to(dev), torch.from_numpy(shared[1]).to(dev),
+                    torch.from_numpy(shared[2].view(np.int16)).to(dev).view(torch.bfloat16))
     W0 = w8.MoEWeights.quantize(wgd, torch.from_numpy(gu).to(dev), torch.from_numpy(dn).to(dev), cfg.k,
-                                w4=args.w4)
-    wbytes = cfg.E * cfg.H * cfg.I * (2 if args.w4 else 3)   # W4 gate_up: half a byte per weight
+                                w4=args.w4, shared=shared_d)
+    del shared_d
+    # W4 gate_up: half a byte per weight
+    wbytes = cfg.E * cfg.H * cfg.I * (2 if args.w4 else 3) + 3 * cfg.H * cfg.Is
 
     def clone_weights(W):
         cl = lambda t: None if t is None else t.clone()
         return w8.MoEWeights(*[cl(t) for t in W.tensors], k=cfg.k,
-                             w4=None if W.w4 is None else tuple(t.clone() for t in W.w4))
+                             w4=None if W.w4 is None else tuple(t.clone() for t in W.w4),
+                             shared=None if W.shared is None else tuple(t.clone() for t in W.shared))
 
     copies = args.copies or max(1, min(4, (1 << 30) // max(wbytes, 1) + 1))
     Ws = [W0] + [clone_weights(W0) for _ in range(copies - 1)]
@@ -490,7 +519,8 @@ def main():
                    "expert_intermediate": cfg.I, "x_dtype": cfg.x_dtype, "experts_hit": E_hit,
                    "weight_copies_rotated": copies},
         "roofline": {"kernel": name, "bound": "mfma" if mfma_bound else "hbm", "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": None if args.w4 else traffic_for(name, cfg.name),
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": None if args.w4 or cfg.Is else traffic_for(name, cfg.name),
                      "avg_launch_us": dom_us, "alg_bytes_per_launch": byts, "int8_ops_per_launch": ops},
         "layer": {"int8_tops": lops / t_step / 1e12, "int8_tops_frac": lops / t_step / 1e12 / INT8_PEAK_TOPS,
                   "alg_gbs": lbytes / t_step / 1e9, "alg_gbs_frac": lbytes / t_step / 1e9 / HBM_PEAK_GBS,
@@ -498,8 +528,13 @@ def main():
                   "stage_us": dict(zip(w8.STAGE_NAMES, [round(v, 2) for v in stage_us])),
                   "expert_rows_min_max": [int(counts.min()), int(counts.max())]},
     }
+    if cfg.Is:
+        result["config"]["shared_expert_intermediate"] = cfg.Is
+        # the stage's time covers the routed and the shared expert's launches
+        result["roofline"]["kernel"] = name + " (routed and shared-expert launches)"
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(dict(cfg=cfg, x=x, wg=wg, gu=gu, dn=dn), args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(dict(cfg=cfg, x=x, wg=wg, gu=gu, dn=dn, shared=shared),
+                                              args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -248,6 +248,20 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
  *             W4A8 GEMM with w4_s_gate_up / w4_o_gate_up [E][2I][ceil(H/128)]
  *             (fp32 / int8) and w_gate_up, s_gate_up may be NULL; down_proj
  *             stays W8A8.
+ *   Shared expert ("Qwen3-Next-80B-A3B-Instruct in AMCT" section 2.2: the
+ *   shared expert is a dense path quantised like the other Linears; the
+ *   "Qwen3.6-35B-A3B-w8a8" recipe keeps shared_expert_gate out of the
+ *   quantisation), all NULL / I_shared = 0 for a layer without one:
+ *   I_shared  its intermediate size (multiple of 32)
+ *   w_shared_gate_up  int8 codes [2*I_shared][H] (gate rows then up rows),
+ *             packed by w8a8_pack_weights as one group;  s_shared_gate_up [2*I_shared]
+ *   w_shared_down     int8 codes [H][I_shared], packed;  s_shared_down [H]
+ *   w_shared_gate     [H] bf16 shared_expert_gate (not quantised)
+ *   Every token runs through the shared expert with its int8 codes (the
+ *   steps of a routed expert) and the layer adds sigmoid(x . w_shared_gate)
+ *   times its output after the k routed slots; the logit is an fp32 sum.
+ *   A shared expert with W4A8 routed gate_up weights is not supported
+ *   (W8A8_ERR_UNSUPPORTED_SHAPE).
  * H % 16 == 0, I % 32 == 0.
  */
 typedef struct {
@@ -262,11 +276,19 @@ typedef struct {
     const uint8_t *w4_gate_up;
     const float *w4_s_gate_up;
     const int8_t *w4_o_gate_up;
+    int64_t I_shared;
+    const int8_t *w_shared_gate_up;
+    const float *s_shared_gate_up;
+    const int8_t *w_shared_down;
+    const float *s_shared_down;
+    const uint16_t *w_shared_gate;
 } w8a8_moe_weights;
 
 /*
  * The whole layer: route -> quantise x -> permute -> gate_up GEMM + SwiGLU ->
- * quantise h -> down GEMM -> combine, all launched on `stream`.
+ * quantise h -> down GEMM -> combine, all launched on `stream` (with a shared
+ * expert, its GEMMs and h quantisation run in the same stages as the routed
+ * ones and the combine adds its gated output).
  *   x   device [T][H] x_dtype (W8A8_BF16 or W8A8_F32);  out device [T][H] x_dtype
  *   ws  device scratch of at least w8a8_moe_layer_workspace_size() bytes
  * Returns 0 (also for T = 0) or a negative status.
@@ -297,9 +319,14 @@ int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype,
  * output (grouped row order) as 16-bit fixed point, value = y * 2^y_exp of its
  * row and 64-column segment, the exponent chosen so that the segment's largest
  * magnitude lies in [2^13, 2^14) (absolute error at most 2^-14 of it).
+ * With a shared expert y and y_exp have T*k + T rows, rows T*k + t holding
+ * the shared expert's output for token t, and four more entries follow:
+ * hs [T][I_shared] bf16, hqs [T][I_shared] i8, shs [T] f32 (its h, codes and
+ * scales) and gate [T] f32 (the sigmoid of each token's gate logit); without
+ * one they point at zero-sized parts.
  * Index order of `ptrs`: as listed.  For inspection and stage-by-stage checks.
  */
-#define W8A8_LAYER_INTERMEDIATES 12
+#define W8A8_LAYER_INTERMEDIATES 16
 int w8a8_moe_layer_intermediates(const w8a8_moe_weights *W, int64_t T, int x_dtype, void *ws,
                                  void **ptrs);
 

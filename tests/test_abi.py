@@ -134,7 +134,14 @@ def test_combine_rejects(L):
 
 
 def _weights(E=8, k=2, H=64, I=32, ptr=FAKE):
-    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value, None, None, None, None)
+    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value, None, None, None, None,
+                       0, None, None, None, None, None)
+
+
+def _with_shared(W, Is=64, ptr=FAKE):
+    W.I_shared = Is
+    W.w_shared_gate_up = W.s_shared_gate_up = W.w_shared_down = W.s_shared_down = W.w_shared_gate = ptr.value
+    return W
 
 
 def test_layer_rejects_and_sizes_workspace(L):
@@ -164,12 +171,33 @@ def test_layer_rejects_and_sizes_workspace(L):
     assert L.w8a8_moe_layer(ctypes.byref(W4), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN
     W4.w4_o_gate_up = FAKE.value
     assert L.w8a8_moe_layer(ctypes.byref(W4), FAKE, 1, 16, FAKE, FAKE, need - 1, s) == WS_SMALL
+    # shared expert: all of its weights or none, I_shared a multiple of 32
+    needs = L.w8a8_moe_layer_workspace_size(ctypes.byref(_with_shared(_weights())), 16, 1)
+    # + hs, hqs, shs, gate and the shared expert's 16 rows of y
+    assert needs >= need + 16 * 64 * 3 + 16 * 8 + 16 * 64 * 2
+    Ws = _with_shared(_weights())
+    assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs - 1, s) == WS_SMALL
+    Ws.w_shared_gate = None
+    assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == INVALID
+    Ws = _with_shared(_weights(), Is=0)
+    assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == INVALID
+    Ws = _with_shared(_weights(), Is=48)
+    assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == SHAPE
+    Ws = _with_shared(_weights(), ptr=MIS)
+    assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == ALIGN
+    Ws = _with_shared(_weights())
+    Ws.w4_gate_up = Ws.w4_s_gate_up = Ws.w4_o_gate_up = FAKE.value
+    assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == SHAPE
     # intermediates are laid out inside the workspace, in order, without overlap
-    ptrs = (ctypes.c_void_p * 12)()
+    ptrs = (ctypes.c_void_p * 16)()
     base = 1 << 30
     assert L.w8a8_moe_layer_intermediates(ctypes.byref(W), 16, 1, ctypes.c_void_p(base), ptrs) == OK
-    offs = [p - base for p in ptrs]
+    offs = [p - base for p in ptrs][:12]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and offs[-1] < need
+    Ws = _with_shared(_weights())
+    assert L.w8a8_moe_layer_intermediates(ctypes.byref(Ws), 16, 1, ctypes.c_void_p(base), ptrs) == OK
+    offs = [p - base for p in ptrs]
+    assert all(a < b for a, b in zip(offs, offs[1:])) and all(o % 256 == 0 for o in offs) and offs[-1] < needs
     big = _weights(E=128, k=8, H=4096, I=1536)
     assert L.w8a8_moe_layer_workspace_size(ctypes.byref(big), 8192, 0) > 8192 * 8 * 4096 * 2
 

@@ -687,3 +687,100 @@ def test_w4_layer(name):
     rows = np.random.default_rng(4).choice(h.shape[0], min(64, h.shape[0]), replace=False)
     oq, os_ = oracle.quant_rows(h[rows])
     assert np.array_equal(to_host(inter["hq"])[rows], oq) and np.array_equal(to_host(inter["sh"])[rows], os_)
+
+
+# ---------------------------------------------------------- shared expert ---
+
+@pytest.mark.parametrize("name", ["moe_tiny_shared_T16_H64_E8_k2_I32_Is64", "moe_30b_shared_decode_T64",
+                                  "moe_30b_shared_prefill_T4096"])
+def test_shared_expert_layer(name):
+    """The layer with a shared expert and its bf16 sigmoid gate: the shared
+    weights' codes bit-exact, each shared stage checked on the GPU's own inputs
+    to it (h within tolerance, h codes bit-exact, the down output within the
+    16-bit fixed-point bound of the exact dequantised sums), the gate within
+    1e-5 of the oracle's sigmoid, and the output within tolerance (every token
+    for tiny and decode, a sample for prefill)."""
+    cfg = synth.MOE_CONFIGS[name]
+    say("shared expert layer", name)
+    x, wg, gu, dn = synth.moe_inputs(cfg)
+    sgu, sdn, wsg = synth.shared_expert(cfg)
+    T, H, Is, k = cfg.T, cfg.H, cfg.Is, cfg.k
+    W = w8.MoEWeights.quantize(dev_bf16(wg), to_dev(gu), to_dev(dn), k,
+                               shared=(to_dev(sgu), to_dev(sdn), dev_bf16(wsg)))
+    oq = oracle_quant_w(gu, dn)
+    del gu, dn
+    oqs, oss = oracle.quant_rows(sgu)
+    oqsd, ossd = oracle.quant_rows(sdn)
+    for got, want in zip(W.shared[:4], (oqs, oss, oqsd, ossd)):
+        assert np.array_equal(to_host(got), want)
+    se = dict(wgu=oqs, sgu=oss, wd=oqsd, sd=ossd, wsg=wsg)
+    xd = to_dev(x)
+    dt = w8.BF16 if x.dtype == np.uint16 else w8.F32
+    ws = w8.moe_layer_workspace(W, T, dt)
+    out = w8.moe_layer(W, xd, ws=ws)
+    torch.cuda.synchronize()
+    inter = w8.moe_layer_intermediates(W, T, ws, dt)
+    P = T * k
+    xq, sx = to_host(inter["xq"]), to_host(inter["sx"])
+    oxq, osx = oracle.quant_rows(x)
+    assert np.array_equal(xq, oxq) and np.array_equal(sx, osx)
+    # shared gate_up + SwiGLU on the GPU's codes
+    rows = np.arange(T) if T <= 64 else np.sort(np.random.default_rng(5).choice(T, 64, replace=False))
+    hs = to_host(inter["hs"])
+    want_hs = oracle.grouped_gemm(xq[rows], sx[rows], None, 1, oqs[None], oss[None], np.array([0, len(rows)], np.int32),
+                                  oracle.DEQUANT_SWIGLU, oracle.BF16)
+    tol_check(hs[rows], want_hs, "%s shared h" % name)
+    # h codes of the GPU's own h, bit-exact
+    hqs, shs = to_host(inter["hqs"]), to_host(inter["shs"])
+    q_, s_ = oracle.quant_rows(hs[rows])
+    assert np.array_equal(hqs[rows], q_) and np.array_equal(shs[rows], s_)
+    # down output rows P + t: 16-bit fixed point within 2^-14 of the segment max
+    y16 = to_host(inter["y"])[P + rows].astype(np.float64)
+    yexp = to_host(inter["y_exp"])[P + rows].astype(np.int64)
+    ref = (hqs[rows].astype(np.float64) @ oqsd.astype(np.float64).T) * shs[rows].astype(np.float64)[:, None] \
+        * ossd.astype(np.float64)
+    got = y16 * np.exp2(np.repeat(yexp, 64, axis=1)[:, :H])
+    for sg in range((H + 63) // 64):
+        cols = slice(64 * sg, min(H, 64 * sg + 64))
+        m = np.abs(ref[:, cols]).max(axis=1, keepdims=True)
+        assert np.all(np.abs(got[:, cols] - ref[:, cols]) <= 2.0 ** -14 * m * 1.0001 + 1e-30)
+    # the layer output, and the gate
+    oargs = (wg, oq[0], oq[1], oq[2], oq[3], k, se)
+    gate = to_host(inter["gate"]).astype(np.float64)
+    if T <= 64:
+        want, it = oracle.moe_layer_shared(x, *oargs, intermediates=True)
+        assert np.abs(gate - it["gate"]).max() <= 1e-5
+        say("%s: gates in [%.3f, %.3f]" % (name, gate.min(), gate.max()))
+        tol_check(to_host(out), want, "%s layer" % name)
+    else:
+        tok = np.sort(np.random.default_rng(3).choice(T, 48, replace=False))
+        want = oracle.moe_layer_shared_tokens(x, *oargs, tok)
+        _, it = oracle.moe_layer_shared(x[tok], *oargs, intermediates=True)
+        assert np.abs(gate[tok] - it["gate"]).max() <= 1e-5
+        tol_check(to_host(out)[tok], want, "%s layer (sampled tokens)" % name)
+    # the routed part is unchanged by the shared expert: same ids and codes as the plain layer
+    assert np.array_equal(to_host(inter["ids"]), oracle.route_topk(x, wg, k)[0])
+
+
+@pytest.mark.parametrize("Is", [64, 32])
+def test_shared_expert_edge_cases(Is):
+    """T = 0 launches nothing; one and three tokens, fp32 activations; a shared
+    expert wider than the routed ones (GEMMs of its own) and one as wide (an
+    extra group of the routed GEMMs)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.MOE_CONFIGS["moe_tiny_shared_T16_H64_E8_k2_I32_Is64"], Is=Is)
+    x, wg, gu, dn = synth.moe_inputs(cfg)
+    sgu, sdn, wsg = synth.shared_expert(cfg)
+    W = w8.MoEWeights.quantize(dev_bf16(wg), to_dev(gu), to_dev(dn), cfg.k,
+                               shared=(to_dev(sgu), to_dev(sdn), dev_bf16(wsg)))
+    oq = oracle_quant_w(gu, dn)
+    oqs, oss = oracle.quant_rows(sgu)
+    oqsd, ossd = oracle.quant_rows(sdn)
+    se = dict(wgu=oqs, sgu=oss, wd=oqsd, sd=ossd, wsg=wsg)
+    empty = torch.empty((0, cfg.H), dtype=torch.float32, device=DEV)
+    assert w8.moe_layer(W, empty).shape == (0, cfg.H)
+    for T in (1, 3, 16):
+        out = w8.moe_layer(W, to_dev(x[:T]))
+        torch.cuda.synchronize()
+        want = oracle.moe_layer_shared(x[:T], wg, oq[0], oq[1], oq[2], oq[3], cfg.k, se)
+        tol_check(to_host(out), want, "shared Is=%d T=%d" % (Is, T))

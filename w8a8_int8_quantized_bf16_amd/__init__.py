@@ -24,7 +24,8 @@ B_ROWMAJOR, B_PACKED = 0, 1
 EPI_RAW_I32, EPI_DEQUANT, EPI_DEQUANT_SWIGLU = 0, 1, 2
 LAYER_STAGES = 7
 STAGE_NAMES = ("route", "quant_x", "permute", "gate_up_gemm", "quant_h", "down_gemm", "combine")
-INTERMEDIATES = ("ids", "w", "xq", "sx", "offsets", "sorted_pair", "pair_pos", "h", "hq", "sh", "y", "y_exp")
+INTERMEDIATES = ("ids", "w", "xq", "sx", "offsets", "sorted_pair", "pair_pos", "h", "hq", "sh", "y", "y_exp",
+                 "hs", "hqs", "shs", "gate")
 
 
 class W8A8Error(RuntimeError):
@@ -38,7 +39,10 @@ class _Weights(ctypes.Structure):
                 ("w_gate", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("w_gate_f32", ctypes.c_void_p),
                 ("w4_gate_up", ctypes.c_void_p), ("w4_s_gate_up", ctypes.c_void_p),
-                ("w4_o_gate_up", ctypes.c_void_p)]
+                ("w4_o_gate_up", ctypes.c_void_p), ("I_shared", ctypes.c_int64),
+                ("w_shared_gate_up", ctypes.c_void_p), ("s_shared_gate_up", ctypes.c_void_p),
+                ("w_shared_down", ctypes.c_void_p), ("s_shared_down", ctypes.c_void_p),
+                ("w_shared_gate", ctypes.c_void_p)]
 
 
 _lib = None
@@ -294,10 +298,12 @@ class MoEWeights:
     s_gate_up [E,2I] fp32; w_down [E,H,I] int8 codes; s_down [E,H] fp32.
     The layer reads the codes in the packed layout (pack_weights), built here."""
 
-    def __init__(self, w_gate, w_gate_up, s_gate_up, w_down, s_down, k, w4=None):
+    def __init__(self, w_gate, w_gate_up, s_gate_up, w_down, s_down, k, w4=None, shared=None):
         """w4: optional W4A8 gate_up_proj (codes [E,2I,H], scales and offsets
         [E,2I,ceil(H/128)]), used instead of w_gate_up / s_gate_up (which may
-        then be None)."""
+        then be None).  shared: optional shared expert, a tuple (gate_up codes
+        [2Is,H] int8, scales [2Is] fp32, down codes [H,Is] int8, scales [H]
+        fp32, shared_expert_gate [H] bf16)."""
         _need(w_gate, "w_gate", torch.bfloat16, 2)
         _need(w_down, "w_down", torch.int8, 3)
         _need(s_down, "s_down", torch.float32, 2)
@@ -316,24 +322,47 @@ class MoEWeights:
         self.p_down = pack_weights(w_down)
         self.w_gate_f32 = router_widen(w_gate)
         self.p4_gate_up = w4a8_pack_weights(w4[0]) if w4 is not None else None
+        self.shared = shared
+        self.Is = 0
+        sp = (None,) * 5
+        if shared is not None:
+            sgu, ssgu, sdn, ssd, wsg = shared
+            _need(sgu, "shared gate_up", torch.int8, 2)
+            _need(ssgu, "shared gate_up scales", torch.float32, 1)
+            _need(sdn, "shared down", torch.int8, 2)
+            _need(ssd, "shared down scales", torch.float32, 1)
+            _need(wsg, "shared_expert_gate", torch.bfloat16, 1)
+            self.Is = sgu.shape[0] // 2
+            self.p_shared = (pack_weights(sgu[None]), pack_weights(sdn[None]))
+            sp = (self.p_shared[0], ssgu, self.p_shared[1], ssd, wsg)
         ptr = lambda t: None if t is None else t.data_ptr()
         self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), ptr(self.p_gate_up), ptr(s_gate_up),
                           self.p_down.data_ptr(), s_down.data_ptr(), self.w_gate_f32.data_ptr(),
-                          ptr(self.p4_gate_up), ptr(w4[1]) if w4 else None, ptr(w4[2]) if w4 else None)
+                          ptr(self.p4_gate_up), ptr(w4[1]) if w4 else None, ptr(w4[2]) if w4 else None,
+                          self.Is, *[ptr(t) for t in sp])
 
     @classmethod
-    def quantize(cls, w_gate, gate_up_f32, down_f32, k, w4=False):
+    def quantize(cls, w_gate, gate_up_f32, down_f32, k, w4=False, shared=None):
         """Static quantisation of fp32 expert weights on the GPU: per output
         channel int8 (the same row kernel as the activations), or with w4=True
-        W4A8 gate_up_proj (groups of 128) and int8 down_proj."""
+        W4A8 gate_up_proj (groups of 128) and int8 down_proj.  shared: optional
+        (gate_up fp32 [2Is,H], down fp32 [H,Is], shared_expert_gate bf16 [H]),
+        quantised per output channel to int8 (the gate stays bf16)."""
         E, twoI, H = gate_up_f32.shape
         qd, sd = quant_act(down_f32.reshape(E * H, twoI // 2))
+        se = None
+        if shared is not None:
+            sgu_f, sdn_f, wsg = shared
+            qsgu, ssgu = quant_act(sgu_f)
+            qsdn, ssdn = quant_act(sdn_f)
+            se = (qsgu, ssgu, qsdn, ssdn, wsg)
         if w4:
             q4, s4, o4 = w4a8_quant_weights(gate_up_f32.reshape(E * twoI, H))
             return cls(w_gate, None, None, qd.view(E, H, twoI // 2), sd.view(E, H), k,
-                       w4=(q4.view(E, twoI, H), s4.view(E, twoI, -1), o4.view(E, twoI, -1)))
+                       w4=(q4.view(E, twoI, H), s4.view(E, twoI, -1), o4.view(E, twoI, -1)), shared=se)
         qgu, sgu = quant_act(gate_up_f32.reshape(E * twoI, H))
-        return cls(w_gate, qgu.view(E, twoI, H), sgu.view(E, twoI), qd.view(E, H, twoI // 2), sd.view(E, H), k)
+        return cls(w_gate, qgu.view(E, twoI, H), sgu.view(E, twoI), qd.view(E, H, twoI // 2), sd.view(E, H), k,
+                   shared=se)
 
 
 def moe_layer_workspace_size(W: MoEWeights, T, x_dtype=BF16):
@@ -374,10 +403,13 @@ def moe_layer_intermediates(W: MoEWeights, T, ws, x_dtype=BF16):
     _check(lib().w8a8_moe_layer_intermediates(ctypes.byref(W.c), T, x_dtype, _p(ws), ptrs),
            "w8a8_moe_layer_intermediates")
     P, E, H, I = T * W.k, W.E, W.H, W.I
+    Ts, Is = (T, W.Is) if W.Is else (0, 0)
     spec = dict(ids=((T, W.k), torch.int32), w=((T, W.k), torch.float32), xq=((T, H), torch.int8),
                 sx=((T,), torch.float32), offsets=((E + 1,), torch.int32), sorted_pair=((P,), torch.int32),
                 pair_pos=((P,), torch.int32), h=((P, I), torch.bfloat16), hq=((P, I), torch.int8),
-                sh=((P,), torch.float32), y=((P, H), torch.int16), y_exp=((P, (H + 63) // 64), torch.int8))
+                sh=((P,), torch.float32), y=((P + Ts, H), torch.int16),
+                y_exp=((P + Ts, (H + 63) // 64), torch.int8), hs=((Ts, Is), torch.bfloat16),
+                hqs=((Ts, Is), torch.int8), shs=((Ts,), torch.float32), gate=((Ts,), torch.float32))
     base = ws.data_ptr()
     out = {}
     for name, p in zip(INTERMEDIATES, ptrs):

@@ -40,8 +40,19 @@ int check_route(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, i
 
 // Layer workspace layout (every part 256-byte aligned).
 struct LayerWs {
-    size_t ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y, yexp, perm, gemm1, gemm2, total;
+    size_t ids, w, xq, sx, offsets, sorted, pos, h, hq, sh, y, yexp, perm, gemm1, gemm2;
+    size_t hs, hqs, shs, sgate, gemm3, gemm4;   // shared expert (zero-sized without one)
+    size_t total;
 };
+
+inline bool has_shared(const w8a8_moe_weights *W) { return W->I_shared > 0; }
+// A shared expert as wide as the routed ones, with int8 gate_up weights, runs
+// as one extra group of the routed grouped GEMMs (rows P .. P+T of the
+// grouped order, each token once); otherwise as GEMMs of its own.
+inline bool shared_in_groups(const w8a8_moe_weights *W)
+{
+    return has_shared(W) && W->I_shared == W->I && W->w4_gate_up == nullptr;
+}
 
 LayerWs layer_ws(const w8a8_moe_weights *W, int64_t T, int x_dtype)
 {
@@ -57,18 +68,35 @@ LayerWs layer_ws(const w8a8_moe_weights *W, int64_t T, int x_dtype)
     L.w = take(sizeof(float) * P);
     L.xq = take((size_t)(T * W->H));
     L.sx = take(sizeof(float) * T);
+    // a shared expert's rows follow the P routed ones: in the grouped rows
+    // (sorted_pair, h, hq, sh) when it runs as an extra group, and in y always
+    const int64_t Ts = has_shared(W) ? T : 0, Is = has_shared(W) ? W->I_shared : 0;
+    const int64_t Tg = shared_in_groups(W) ? T : 0;   // extra grouped rows
+    const int Gx = shared_in_groups(W) ? 1 : 0;
     L.offsets = take(sizeof(int32_t) * (W->E + 1));
-    L.sorted = take(sizeof(int32_t) * P);
+    L.sorted = take(sizeof(int32_t) * (P + Tg));
     L.pos = take(sizeof(int32_t) * P);
-    L.h = take(2 * (size_t)(P * W->I));
-    L.hq = take((size_t)(P * W->I));
-    L.sh = take(sizeof(float) * P);
+    L.h = take(2 * (size_t)((P + Tg) * W->I));
+    L.hq = take((size_t)((P + Tg) * W->I));
+    L.sh = take(sizeof(float) * (P + Tg));
     // y: 16-bit fixed point with a power-of-two exponent per row and 64 columns
-    L.y = take(sizeof(int16_t) * (size_t)(P * W->H));
-    L.yexp = take((size_t)(P * ((W->H + 63) / 64)));
+    L.y = take(sizeof(int16_t) * (size_t)((P + Ts) * W->H));
+    L.yexp = take((size_t)((P + Ts) * ((W->H + 63) / 64)));
     L.perm = take(permute_ws_bytes(T, W->k, W->E));
-    L.gemm1 = take(gemm_ws_bytes(P, 2 * W->I, W->E));
-    L.gemm2 = take(gemm_ws_bytes(P, W->H, W->E));
+    L.gemm1 = take(gemm_ws_bytes(P + Tg, 2 * W->I, W->E + Gx));
+    L.gemm2 = take(gemm_ws_bytes(P + Tg, W->H, W->E + Gx));
+    if (Gx) {   // the shared expert's h, codes and scales are the extra group's rows
+        L.hs = L.h + 2 * (size_t)(P * W->I);
+        L.hqs = L.hq + (size_t)(P * W->I);
+        L.shs = L.sh + sizeof(float) * P;
+    } else {
+        L.hs = take(2 * (size_t)(Ts * Is));
+        L.hqs = take((size_t)(Ts * Is));
+        L.shs = take(sizeof(float) * (size_t)Ts);
+    }
+    L.sgate = take(sizeof(float) * (size_t)Ts);
+    L.gemm3 = Ts && !Gx ? take(gemm_ws_bytes(Ts, 2 * Is, 1)) : o;
+    L.gemm4 = Ts && !Gx ? take(gemm_ws_bytes(Ts, W->H, 1)) : o;
     L.total = o;
     return L;
 }
@@ -98,6 +126,22 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
            : (!aligned16(W->w_gate_up) || !aligned16(W->s_gate_up)))
         return W8A8_ERR_ALIGNMENT;
     if (T > 0 && (!aligned16(x) || !aligned16(out))) return W8A8_ERR_ALIGNMENT;
+    // shared expert: all of its weights, or none
+    const bool any_shared = W->I_shared != 0 || W->w_shared_gate_up || W->s_shared_gate_up || W->w_shared_down ||
+                            W->s_shared_down || W->w_shared_gate;
+    if (any_shared) {
+        if (W->I_shared <= 0 || !W->w_shared_gate_up || !W->s_shared_gate_up || !W->w_shared_down ||
+            !W->s_shared_down || !W->w_shared_gate)
+            return W8A8_ERR_INVALID_ARG;
+        if (W->I_shared % 32 || w4) return W8A8_ERR_UNSUPPORTED_SHAPE;   // with W4A8 routed weights: not built
+        if ((int64_t)packed_weights_bytes(1, 2 * W->I_shared, W->H) > INT32_MAX - 256 ||
+            (int64_t)packed_weights_bytes(1, W->H, W->I_shared) > INT32_MAX - 256 ||
+            T * W->I_shared > INT32_MAX - 256)
+            return W8A8_ERR_UNSUPPORTED_SHAPE;
+        if (!aligned16(W->w_shared_gate_up) || !aligned16(W->s_shared_gate_up) || !aligned16(W->w_shared_down) ||
+            !aligned16(W->s_shared_down) || !aligned16(W->w_shared_gate))
+            return W8A8_ERR_ALIGNMENT;
+    }
     return W8A8_OK;
 }
 
@@ -132,6 +176,14 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     const int64_t P = T * W->k;
     const int E = W->E, k = W->k;
     const int64_t H = W->H, I = W->I;
+    const bool shared = has_shared(W);
+    const int64_t Is = W->I_shared;
+    uint16_t *hs = (uint16_t *)(base + L.hs);
+    int8_t *hqs = (int8_t *)(base + L.hqs);
+    float *shs = (float *)(base + L.shs);
+    float *sgate = (float *)(base + L.sgate);
+    void *gws3 = base + L.gemm3;
+    void *gws4 = base + L.gemm4;
 
     int ev = 0;
     auto mark = [&]() -> hipError_t {
@@ -152,35 +204,68 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     if ((!fused_q && (e = launch_quant_rows(x, x_dtype, T, H, H, xq, sx, st)) != hipSuccess) ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
-    // 3 permute; its scan also builds the tile tables of both grouped GEMMs
-    TileTableReq req[2];
+    // 3 permute; its scan also builds the tile tables of the grouped GEMMs
+    //   (over E groups, or E + 1 with the shared expert as the extra group;
+    //   one-group tables for a shared expert with GEMMs of its own)
     const bool w4 = W->w4_gate_up != nullptr;
-    if (w4) gemm_tile_params_w4(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
-    else gemm_tile_params(P, 2 * I, E, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
-    gemm_tile_params(P, H, E, EPI_FIXED16, &req[1].BM, &req[1].nblocks_n);
+    const bool sg = shared_in_groups(W);
+    const int Gg = sg ? E + 1 : E;         // groups of the grouped GEMMs
+    const int64_t Pg = sg ? P + T : P;     // their rows
+    TileTableReq req[4] = {};
+    if (w4) gemm_tile_params_w4(Pg, 2 * I, Gg, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
+    else gemm_tile_params(Pg, 2 * I, Gg, W8A8_EPI_DEQUANT_SWIGLU, &req[0].BM, &req[0].nblocks_n);
+    gemm_tile_params(Pg, H, Gg, EPI_FIXED16, &req[1].BM, &req[1].nblocks_n);
     req[0].prefix = (int32_t *)gws1;
-    req[0].tiles = (int4 *)gemm_tiles_ptr(gws1, E);
+    req[0].tiles = (int4 *)gemm_tiles_ptr(gws1, Gg);
     req[1].prefix = (int32_t *)gws2;
-    req[1].tiles = (int4 *)gemm_tiles_ptr(gws2, E);
-    if ((e = launch_permute(ids, T, k, E, offsets, sorted, pos, perm, st, req, 2)) != hipSuccess ||
+    req[1].tiles = (int4 *)gemm_tiles_ptr(gws2, Gg);
+    int nreq = 2;
+    if (shared && !sg) {
+        gemm_tile_params(T, 2 * Is, 1, W8A8_EPI_DEQUANT_SWIGLU, &req[2].BM, &req[2].nblocks_n);
+        gemm_tile_params(T, H, 1, EPI_FIXED16, &req[3].BM, &req[3].nblocks_n);
+        req[2].prefix = (int32_t *)gws3;
+        req[2].tiles = (int4 *)gemm_tiles_ptr(gws3, 1);
+        req[3].prefix = (int32_t *)gws4;
+        req[3].tiles = (int4 *)gemm_tiles_ptr(gws4, 1);
+        req[2].dense_rows = req[3].dense_rows = (int32_t)T;
+        nreq = 4;
+    }
+    if ((e = launch_permute(ids, T, k, E, offsets, sorted, pos, perm, st, req, nreq, sg ? (int32_t)T : 0)) !=
+            hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 4a gate_up GEMM + SwiGLU -> h (bf16), W8A8 or W4A8 weights
     e = w4 ? launch_gemm_w4_main(xq, T, sx, sorted, k, W->w4_gate_up, W->w4_s_gate_up, W->w4_o_gate_up, offsets, E,
                                  P, 2 * I, H, W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)
-           : launch_gemm_main(xq, T, sx, sorted, k, W->w_gate_up, 1, W->s_gate_up, offsets, E, P, 2 * I, H,
-                              W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st);
-    if (e != hipSuccess || (e = mark()) != hipSuccess) return hip_status(e);
-    // quantise h per grouped row
-    if ((e = launch_quant_rows(h, W8A8_BF16, P, I, I, hq, sh, st)) != hipSuccess || (e = mark()) != hipSuccess)
+           : launch_gemm_main(xq, T, sx, sorted, k, W->w_gate_up, 1, W->s_gate_up, offsets, Gg, Pg, 2 * I, H,
+                              W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st, nullptr,
+                              sg ? W->w_shared_gate_up : nullptr, sg ? W->s_shared_gate_up : nullptr);
+    if (e != hipSuccess) return hip_status(e);
+    // a shared expert with GEMMs of its own, on every token's codes (no gather)
+    if (shared && !sg &&
+        (e = launch_gemm_main(xq, T, sx, nullptr, 1, W->w_shared_gate_up, 1, W->s_shared_gate_up, nullptr, 1, T,
+                              2 * Is, H, W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, hs, gws3, st)) != hipSuccess)
         return hip_status(e);
-    // 4b down GEMM -> y (16-bit fixed point + exponents)
-    if ((e = launch_gemm_main(hq, P, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, E, P, H, I, EPI_FIXED16,
-                              W8A8_F32, y, gws2, st, yexp)) != hipSuccess ||
+    if ((e = mark()) != hipSuccess) return hip_status(e);
+    // quantise h per grouped row (and a separate shared expert's h per token)
+    if ((e = launch_quant_rows(h, W8A8_BF16, Pg, I, I, hq, sh, st)) != hipSuccess ||
+        (shared && !sg && (e = launch_quant_rows(hs, W8A8_BF16, T, Is, Is, hqs, shs, st)) != hipSuccess) ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
-    // 5 combine
-    if ((e = launch_combine_fixed16(y, yexp, w, pos, T, k, H, out, x_dtype, st)) != hipSuccess ||
+    // 4b down GEMM -> y (16-bit fixed point + exponents); the shared expert's
+    //    rows follow the routed ones
+    const int64_t nseg = (H + 63) / 64;
+    if ((e = launch_gemm_main(hq, Pg, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, Gg, Pg, H, I, EPI_FIXED16,
+                              W8A8_F32, y, gws2, st, yexp, sg ? W->w_shared_down : nullptr,
+                              sg ? W->s_shared_down : nullptr)) != hipSuccess ||
+        (shared && !sg &&
+         (e = launch_gemm_main(hqs, T, shs, nullptr, 1, W->w_shared_down, 1, W->s_shared_down, nullptr, 1, T, H, Is,
+                               EPI_FIXED16, W8A8_F32, y + P * H, gws4, st, yexp + P * nseg)) != hipSuccess) ||
+        (e = mark()) != hipSuccess)
+        return hip_status(e);
+    // 5 combine (with the shared expert's gated output)
+    if ((e = launch_combine_fixed16(y, yexp, w, pos, T, k, H, out, x_dtype, st, shared ? x : nullptr,
+                                    shared ? W->w_shared_gate : nullptr, shared ? sgate : nullptr)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     return W8A8_OK;
@@ -388,8 +473,8 @@ int w8a8_moe_layer_intermediates(const w8a8_moe_weights *W, int64_t T, int x_dty
     if (!W || !ws || !ptrs || T < 0 || !act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
     const LayerWs L = layer_ws(W, T, x_dtype);
     char *b = (char *)ws;
-    const size_t offs[W8A8_LAYER_INTERMEDIATES] = {L.ids, L.w, L.xq, L.sx, L.offsets, L.sorted,
-                                                   L.pos, L.h, L.hq, L.sh, L.y, L.yexp};
+    const size_t offs[W8A8_LAYER_INTERMEDIATES] = {L.ids, L.w,  L.xq, L.sx,   L.offsets, L.sorted, L.pos, L.h,
+                                                   L.hq,  L.sh, L.y,  L.yexp, L.hs,      L.hqs,    L.shs, L.sgate};
     for (int i = 0; i < W8A8_LAYER_INTERMEDIATES; ++i) ptrs[i] = b + offs[i];
     return W8A8_OK;
 }

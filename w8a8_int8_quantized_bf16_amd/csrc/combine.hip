@@ -63,15 +63,41 @@ static void launch_typed(const YT *y, const float *w, const int32_t *pair_pos, i
 // y as 16-bit fixed point with a power-of-two exponent per row and 64-column
 // segment (the layer's down GEMM epilogue): a thread's 8 columns lie in one
 // segment, so each slot contributes w * 2^e * code.
-template <typename OT>
+//
+// SHARED: the layer's shared expert ("Qwen3-Next-80B-A3B-Instruct in AMCT"
+// section 2.2; its gate stays bf16 in the "Qwen3.6-35B-A3B-w8a8" recipe).
+// The block first forms the token's gate logit x . w_sg (fp32 fmas over its
+// columns, then a wave and a block sum), takes its sigmoid, and after the k
+// routed slots adds sigmoid * y of row shared_row0 + t.
+template <typename OT, typename XT, bool SHARED>
 __global__ __launch_bounds__(256) void combine_fixed16_kernel(const int16_t *__restrict__ y16,
                                                               const int8_t *__restrict__ y_exp,
                                                               const float *__restrict__ w,
                                                               const int32_t *__restrict__ pair_pos, int k, int64_t H,
-                                                              OT *__restrict__ out)
+                                                              OT *__restrict__ out, const XT *__restrict__ x,
+                                                              const uint16_t *__restrict__ w_sg, int64_t shared_row0,
+                                                              float *__restrict__ gate_out)
 {
     const int64_t t = blockIdx.x;
     const int64_t nseg = (H + 63) / 64;
+    float sig = 0.0f;
+    if constexpr (SHARED) {
+        __shared__ float part_l[4];
+        float part = 0.0f;
+        for (int64_t c = (int64_t)threadIdx.x * 8; c < H; c += 256 * 8) {
+            float xv[8], gv[8];
+            load8_f32(x + t * H + c, xv);
+            load8_f32(w_sg + c, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part = fmaf(xv[i], gv[i], part);
+        }
+        part = wave_sum(part);
+        if ((threadIdx.x & 63) == 0) part_l[threadIdx.x >> 6] = part;
+        __syncthreads();
+        const float logit = (part_l[0] + part_l[1]) + (part_l[2] + part_l[3]);
+        sig = 1.0f / (1.0f + expf(-logit));
+        if (threadIdx.x == 0) gate_out[t] = sig;
+    }
     for (int64_t c = (int64_t)threadIdx.x * 8; c < H; c += 256 * 8) {
         float acc[8];
 #pragma unroll
@@ -86,6 +112,13 @@ __global__ __launch_bounds__(256) void combine_fixed16_kernel(const int16_t *__r
                 v[j] = *reinterpret_cast<const uint4 *>(y16 + row * H + c);
                 sc[j] = ldexpf(w[t * k + j], (int)y_exp[row * nseg + c / 64]);
             }
+        }
+        uint4 vs;
+        float ss = 0.0f;
+        if constexpr (SHARED) {
+            const int64_t row = shared_row0 + t;
+            vs = *reinterpret_cast<const uint4 *>(y16 + row * H + c);
+            ss = ldexpf(sig, (int)y_exp[row * nseg + c / 64]);
         }
         for (int j0 = 0; j0 < k; j0 += KMAX) {
 #pragma unroll
@@ -104,21 +137,47 @@ __global__ __launch_bounds__(256) void combine_fixed16_kernel(const int16_t *__r
                 }
             }
         }
+        if constexpr (SHARED) {
+            const uint32_t u[4] = {vs.x, vs.y, vs.z, vs.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = fmaf(ss, (float)(int16_t)(u[i] & 0xffffu), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(ss, (float)(int16_t)(u[i] >> 16), acc[2 * i + 1]);
+            }
+        }
         store8(out + t * H + c, acc);
     }
 }
 
+template <typename OT, typename XT, bool SHARED>
+static void launch_fixed16(const int16_t *y16, const int8_t *y_exp, const float *w, const int32_t *pair_pos,
+                           int64_t T, int k, int64_t H, OT *out, const XT *x, const uint16_t *w_sg,
+                           int64_t shared_row0, float *gate_out, hipStream_t st)
+{
+    hipLaunchKernelGGL((combine_fixed16_kernel<OT, XT, SHARED>), dim3((unsigned)T), dim3(256), 0, st, y16, y_exp, w,
+                       pair_pos, k, H, out, x, w_sg, shared_row0, gate_out);
+}
+
 hipError_t launch_combine_fixed16(const int16_t *y16, const int8_t *y_exp, const float *w, const int32_t *pair_pos,
-                                  int64_t T, int k, int64_t H, void *out, int out_dtype, hipStream_t st)
+                                  int64_t T, int k, int64_t H, void *out, int out_dtype, hipStream_t st,
+                                  const void *x, const uint16_t *w_sg, float *gate_out)
 {
     if (T == 0) return hipSuccess;
-    dim3 grid((unsigned)T), block(256);
-    if (out_dtype == 0)
-        hipLaunchKernelGGL(combine_fixed16_kernel<uint16_t>, grid, block, 0, st, y16, y_exp, w, pair_pos, k, H,
-                           (uint16_t *)out);
-    else
-        hipLaunchKernelGGL(combine_fixed16_kernel<float>, grid, block, 0, st, y16, y_exp, w, pair_pos, k, H,
-                           (float *)out);
+    const int64_t r0 = T * k;   // the shared expert's rows follow the routed ones
+    if (!w_sg) {
+        if (out_dtype == 0)
+            launch_fixed16<uint16_t, uint16_t, false>(y16, y_exp, w, pair_pos, T, k, H, (uint16_t *)out, nullptr,
+                                                      nullptr, 0, nullptr, st);
+        else
+            launch_fixed16<float, float, false>(y16, y_exp, w, pair_pos, T, k, H, (float *)out, nullptr, nullptr, 0,
+                                                nullptr, st);
+    } else if (out_dtype == 0) {
+        launch_fixed16<uint16_t, uint16_t, true>(y16, y_exp, w, pair_pos, T, k, H, (uint16_t *)out,
+                                                 (const uint16_t *)x, w_sg, r0, gate_out, st);
+    } else {
+        launch_fixed16<float, float, true>(y16, y_exp, w, pair_pos, T, k, H, (float *)out, (const float *)x, w_sg,
+                                           r0, gate_out, st);
+    }
     return hipGetLastError();
 }
 

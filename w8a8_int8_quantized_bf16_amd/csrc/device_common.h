@@ -55,7 +55,6 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Load 8 consecutive elements (16-byte aligned) widened to fp32.
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_incl_scan(int v)
 {
@@ -85,6 +84,7 @@ __device__ __forceinline__ int block_excl_scan256(int v, int *sc, int *total)
     return before + inc - v;
 }
 
+// Load 8 consecutive elements (16-byte aligned) widened to fp32.
 __device__ __forceinline__ void load8_f32(const uint16_t *p, float v[8])
 {
     uint4 u = *reinterpret_cast<const uint4 *>(p);

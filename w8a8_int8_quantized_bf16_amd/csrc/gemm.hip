@@ -66,6 +66,9 @@ struct GemmArgs {
     int packed_b;                 // B in the MFMA-fragment packed layout (see w8a8_pack_weights)
     const float *b_gscales;       // W4: per (group, column, 128-step) scales [G][N][KS]
     const int8_t *b_goffs;        //     and offsets [G][N][KS]
+    int G_routed;                 // groups g >= G_routed take their weights from
+    const int8_t *B_extra;        //   B_extra / b_extra_scales (one group's worth,
+    const float *b_extra_scales;  //   same layout) instead of B and b_scales
 };
 
 template <typename T>
@@ -78,13 +81,22 @@ __device__ __forceinline__ uint16_t to_out<uint16_t>(float v) { return (uint16_t
 
 // Stand-alone tile map of one grouped GEMM (see tiles.h): every block forms
 // the tile prefix from the offsets, block 0 stores it, and the blocks share
-// the descriptor writes.
+// the descriptor writes.  offsets == nullptr: one group of dense_rows rows.
 __global__ __launch_bounds__(256) void gemm_tilemap_kernel(const int32_t *__restrict__ offsets, int G, int BM,
                                                            int nblocks_n, int32_t *__restrict__ tile_prefix,
-                                                           int4 *__restrict__ tiles)
+                                                           int4 *__restrict__ tiles, int32_t dense_rows)
 {
     __shared__ int32_t pre[TILES_MAX_G + 1];
     __shared__ int32_t sc[256];
+    __shared__ int32_t dense_off[2];
+    if (!offsets) {
+        if (threadIdx.x == 0) {
+            dense_off[0] = 0;
+            dense_off[1] = dense_rows;
+        }
+        __syncthreads();
+        offsets = dense_off;
+    }
     const int total = tile_table_prefix(offsets, G, BM, nblocks_n, pre, sc);
     if (blockIdx.x == 0)
         for (int g = threadIdx.x; g <= G; g += 256) tile_prefix[g] = pre[g];
@@ -344,7 +356,9 @@ void grouped_gemm_kernel(GemmArgs a)
     // OOB_BASE, above every resource size, and stays out of range as steps are
     // added, so its loads return zeros.
     const int64_t b_bytes = PACKED ? (int64_t)((N + 31) / 32) * nk * 4096 : (int64_t)N * K;
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B + (int64_t)g * b_bytes, b_bytes);
+    const bool xg = g >= a.G_routed;   // the extra group: weights of its own
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(xg ? a.B_extra : a.B + (int64_t)g * b_bytes, b_bytes);
+    const float *bsg = xg ? a.b_extra_scales : a.b_scales + (int64_t)g * N;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
     const int khalf = 64 * (lane >> 5);
     uint32_t boff[WN];
@@ -358,7 +372,7 @@ void grouped_gemm_kernel(GemmArgs a)
     // per-column weight scales, kept in registers for the epilogue
     float bsc[WN];
 #pragma unroll
-    for (int f = 0; f < WN; ++f) bsc[f] = (EPI != 0 && cvalid[f]) ? a.b_scales[(int64_t)g * N + col[f]] : 0.0f;
+    for (int f = 0; f < WN; ++f) bsc[f] = (EPI != 0 && cvalid[f]) ? bsg[col[f]] : 0.0f;
 
     // ---- activation rows of the tile and their scales
     if (tid < BM) {
@@ -721,7 +735,9 @@ struct TileCfg {
     int BM, WN;
 };
 
-TileCfg gemm_cfg(int64_t M_total, int G, int epilogue)
+int gemm_nblocks(int64_t N, int epilogue, int WN);
+
+TileCfg gemm_cfg_groups(int64_t M_total, int G, int epilogue)
 {
     const double avg_rows = (double)M_total / (double)G;
     if (avg_rows <= 32.0) return {32, 2};
@@ -731,6 +747,25 @@ TileCfg gemm_cfg(int64_t M_total, int G, int epilogue)
     if (epilogue == EPI_FIXED16) return avg_rows <= 384.0 ? TileCfg{64, 2} : TileCfg{128, 2};
     if (avg_rows <= 384.0) return {128, 2};
     return {128, 4};
+}
+
+// One group (a dense linear): step the tile down while the launch would have
+// fewer tiles than two per compute unit (tiles up to 128 x 256 run two blocks
+// per CU), keeping at least 64 rows per tile unless the GEMM has at most 256
+// rows (decode-sized, where the weight stream, not reuse, sets the time).
+TileCfg gemm_cfg(int64_t M_total, int64_t N, int G, int epilogue)
+{
+    TileCfg c = gemm_cfg_groups(M_total, G, epilogue);
+    if (G != 1) return c;
+    const TileCfg order[] = {{128, 4}, {128, 2}, {64, 2}, {32, 2}};
+    const int last = M_total <= 256 ? 3 : 2;
+    int i = 0;
+    while (order[i].BM != c.BM || order[i].WN != c.WN) ++i;
+    for (; i < last; ++i) {
+        const int64_t tiles = (M_total + order[i].BM - 1) / order[i].BM * gemm_nblocks(N, epilogue, order[i].WN);
+        if (tiles >= 512) break;
+    }
+    return order[i];
 }
 
 // column blocks per group: 4 waves x WN fragments of 32 B rows; with SwiGLU
@@ -792,7 +827,7 @@ size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G)
 
 void gemm_tile_params(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n)
 {
-    const TileCfg c = gemm_cfg(M_total, G, epilogue);
+    const TileCfg c = gemm_cfg(M_total, N, G, epilogue);
     *BM = c.BM;
     *nblocks_n = gemm_nblocks(N, epilogue, c.WN);
 }
@@ -804,7 +839,8 @@ static hipError_t launch_tilemap_cfg(const int32_t *offsets, int G, int64_t M_to
 {
     const int64_t blocks = std::min<int64_t>((gemm_max_tiles(M_total, N, G) + 255) / 256, 64);
     hipLaunchKernelGGL(gemm_tilemap_kernel, dim3((unsigned)blocks), dim3(256), 0, st, offsets, G, c.BM,
-                       gemm_nblocks(N, epilogue, c.WN), (int32_t *)ws, (int4 *)((char *)ws + prefix_bytes(G)));
+                       gemm_nblocks(N, epilogue, c.WN), (int32_t *)ws, (int4 *)((char *)ws + prefix_bytes(G)),
+                       (int32_t)M_total);
     return hipGetLastError();
 }
 
@@ -812,7 +848,7 @@ hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, i
                                hipStream_t st)
 {
     if (M_total == 0) return hipSuccess;
-    return launch_tilemap_cfg(offsets, G, M_total, N, gemm_cfg(M_total, G, epilogue), epilogue, ws, st);
+    return launch_tilemap_cfg(offsets, G, M_total, N, gemm_cfg(M_total, N, G, epilogue), epilogue, ws, st);
 }
 
 // ---- W4A8
@@ -865,6 +901,7 @@ hipError_t launch_gemm_w4_main(const int8_t *A, int64_t A_rows, const float *a_s
 {
     if (M_total == 0) return hipSuccess;
     GemmArgs ga{};
+    ga.G_routed = G;
     ga.A = A;
     ga.a_scales = a_scales;
     ga.gather = gather;
@@ -904,10 +941,14 @@ hipError_t launch_grouped_gemm_w4(const int8_t *A, int64_t A_rows, const float *
 hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                             int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                             const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp)
+                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp,
+                            const int8_t *B_extra, const float *b_extra_scales)
 {
     if (M_total == 0) return hipSuccess;
-    GemmArgs ga;
+    GemmArgs ga{};
+    ga.G_routed = B_extra ? G - 1 : G;
+    ga.B_extra = B_extra;
+    ga.b_extra_scales = b_extra_scales;
     ga.out_exp = out_exp;
     ga.A = A;
     ga.a_scales = a_scales;
@@ -925,7 +966,7 @@ hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scal
     ga.tiles = (const int4 *)((const char *)ws + prefix_bytes(G));
     ga.A_bytes = A_rows * K;
     ga.packed_b = b_packed;
-    const TileCfg c = gemm_cfg(M_total, G, epilogue);
+    const TileCfg c = gemm_cfg(M_total, N, G, epilogue);
     ga.nblocks_n = gemm_nblocks(N, epilogue, c.WN);
     if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, epilogue, out_dtype, st);
     if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, epilogue, out_dtype, st);

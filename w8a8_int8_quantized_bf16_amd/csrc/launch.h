@@ -25,20 +25,27 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
 hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStream_t st);
 
 size_t permute_ws_bytes(int64_t T, int k, int E);
-// Tile tables the permutation builds for grouped GEMMs over its groups.
+// Tile tables the permutation builds for grouped GEMMs (up to four): over its
+// E expert groups, plus one extra group of extra_rows rows after them when
+// launch_permute's extra_rows > 0; or, with dense_rows > 0, over one group of
+// dense_rows rows (a dense linear).
 struct TileTableReq {
     int BM, nblocks_n;
-    int32_t *prefix;   // [E+1]
+    int32_t *prefix;   // [groups + 1]
     int4 *tiles;
+    int32_t dense_rows;
 };
+// extra_rows > 0: also sorted_pair[T*k + t] = t*k for t < extra_rows (an
+// extra group that every token visits once, in token order).
 hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets,
                           int32_t *sorted_pair, int32_t *pair_pos, void *ws, hipStream_t st,
-                          const TileTableReq *req = nullptr, int nreq = 0);
+                          const TileTableReq *req = nullptr, int nreq = 0, int32_t extra_rows = 0);
 
 size_t gemm_ws_bytes(int64_t M_total, int64_t N, int G);
 void gemm_tile_params(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n);
 void *gemm_tiles_ptr(void *ws, int G);
 // tile map of a grouped GEMM (into ws), then the GEMM itself reading that map
+// (offsets == nullptr: one group of M_total rows, a dense linear)
 hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, int64_t N, int epilogue, void *ws,
                                hipStream_t st);
 // Internal epilogue of the layer's down GEMM (not a public W8A8_EPI_* code):
@@ -47,10 +54,13 @@ hipError_t launch_gemm_tilemap(const int32_t *offsets, int G, int64_t M_total, i
 // ([M][ceil(N/64)] int8), e chosen so the segment's largest |v| maps into
 // [2^13, 2^14).  Absolute error per element <= 2^-14 of the segment maximum.
 constexpr int EPI_FIXED16 = 3;
+// B_extra: the last of the G groups takes its weights (one group's worth, the
+// same layout) and scales from B_extra / b_extra_scales instead of B, b_scales.
 hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                             int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                             const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp = nullptr);
+                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp = nullptr,
+                            const int8_t *B_extra = nullptr, const float *b_extra_scales = nullptr);
 hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                                int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                                const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
@@ -75,8 +85,14 @@ hipError_t launch_grouped_gemm_w4(const int8_t *A, int64_t A_rows, const float *
 
 hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T,
                           int k, int64_t H, void *out, int out_dtype, hipStream_t st);
-// combine of y in the EPI_FIXED16 format: y16 [T*k][H] int16, y_exp [T*k][ceil(H/64)]
+// combine of y in the EPI_FIXED16 format: y16 [T*k][H] int16, y_exp [T*k][ceil(H/64)].
+// With a shared expert (w_sg non-null): y has T*k + T rows, row T*k + t the
+// shared expert's output for token t, added with weight sigmoid(x[t] . w_sg)
+// after the routed slots; x [T][H] has out's dtype, gate_out [T] receives the
+// sigmoids.
 hipError_t launch_combine_fixed16(const int16_t *y16, const int8_t *y_exp, const float *w, const int32_t *pair_pos,
-                                  int64_t T, int k, int64_t H, void *out, int out_dtype, hipStream_t st);
+                                  int64_t T, int k, int64_t H, void *out, int out_dtype, hipStream_t st,
+                                  const void *x = nullptr, const uint16_t *w_sg = nullptr,
+                                  float *gate_out = nullptr);
 
 }  // namespace w8a8

@@ -118,13 +118,42 @@ __device__ inline void scatter_rounds(const int32_t *__restrict__ ids, int64_t P
     }
 }
 
-// The tile tables of up to two grouped GEMMs over the expert groups: every
-// block forms the tile prefixes from the offsets, block 0 stores them, and the
-// blocks of the scatter grid share the descriptor writes.
+// The tile tables of up to four grouped GEMMs (TileTableReq): every block
+// forms the tile prefixes from the offsets, block 0 stores them, and the
+// blocks of the scatter grid share the descriptor writes.  extra > 0 appends
+// one group of `extra` rows after the E expert groups (rows P .. P + extra of
+// the grouped order, sorted_pair[P + t] = t * k: each token once, in order).
 struct ScanTables {
-    TileTableReq r[2];
+    TileTableReq r[4];
     int n;
+    int32_t extra;
+    int k;
 };
+
+// Tile table j from the expert offsets in LDS (off_l[0..E], and off_l[E + 1]
+// when tt.extra > 0); dn: LDS scratch of 2 ints.  All threads of the block
+// call it; `first` / `stride` split the descriptor writes.
+__device__ inline void build_table(const ScanTables &tt, int j, const int32_t *off_l, int E, int32_t *pre,
+                                   int32_t *sc, int32_t *dn, bool store_prefix, int first, int stride)
+{
+    const TileTableReq &r = tt.r[j];
+    const int32_t *offs = off_l;
+    int G = tt.extra > 0 ? E + 1 : E;
+    if (r.dense_rows > 0) {
+        if (threadIdx.x == 0) {
+            dn[0] = 0;
+            dn[1] = r.dense_rows;
+        }
+        __syncthreads();
+        offs = dn;
+        G = 1;
+    }
+    const int total = tile_table_prefix(offs, G, r.BM, r.nblocks_n, pre, sc);
+    if (store_prefix)
+        for (int g = threadIdx.x; g <= G; g += PM_THREADS) r.prefix[g] = pre[g];
+    tile_fill(offs, G, r.BM, r.nblocks_n, pre, total, r.tiles, first, stride);
+    __syncthreads();
+}
 
 __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
                                                                      int E, const int32_t *__restrict__ chunk_base,
@@ -134,21 +163,20 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32
 {
     __shared__ int32_t base[PM_MAX_E];     // next free row of each expert inside this chunk
     __shared__ int32_t wcnt[4][PM_MAX_E];  // per-wave counts of the current round
-    __shared__ int32_t off_l[PM_MAX_E + 1];
-    __shared__ int32_t pre[PM_MAX_E + 1];
+    __shared__ int32_t off_l[PM_MAX_E + 2];
+    __shared__ int32_t pre[PM_MAX_E + 2];
+    __shared__ int32_t dn[2];
     const int tid = threadIdx.x;
 
-    // ---- tile tables
+    // ---- tile tables (and the extra group's rows)
     for (int g = tid; g <= E; g += PM_THREADS) off_l[g] = offsets[g];
+    if (tid == 0) off_l[E + 1] = (int32_t)P + tt.extra;
+    for (int64_t t = (int64_t)blockIdx.x * PM_THREADS + tid; t < tt.extra; t += (int64_t)gridDim.x * PM_THREADS)
+        sorted_pair[P + t] = (int32_t)(t * tt.k);
     __syncthreads();
-    for (int j = 0; j < tt.n; ++j) {
-        const int total = tile_table_prefix(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, &wcnt[0][0]);
-        if (blockIdx.x == 0)
-            for (int g = tid; g <= E; g += PM_THREADS) tt.r[j].prefix[g] = pre[g];
-        tile_fill(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, total, tt.r[j].tiles,
-                  blockIdx.x * PM_THREADS + tid, gridDim.x * PM_THREADS);
-        __syncthreads();
-    }
+    for (int j = 0; j < tt.n; ++j)
+        build_table(tt, j, off_l, E, pre, &wcnt[0][0], dn, blockIdx.x == 0, blockIdx.x * PM_THREADS + tid,
+                    gridDim.x * PM_THREADS);
 
     // ---- scatter
     if (tid < E) base[tid] = off_l[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
@@ -164,8 +192,9 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t
 {
     __shared__ int32_t base[PM_MAX_E];
     __shared__ int32_t wcnt[4][PM_MAX_E];
-    __shared__ int32_t off_l[PM_MAX_E + 1];
-    __shared__ int32_t pre[PM_MAX_E + 1];
+    __shared__ int32_t off_l[PM_MAX_E + 2];
+    __shared__ int32_t pre[PM_MAX_E + 2];
+    __shared__ int32_t dn[2];
     __shared__ int32_t ids_l[PM_SMALL_P];
     const int tid = threadIdx.x;
     int32_t *hist = &wcnt[0][0];
@@ -187,14 +216,13 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t
     int all;
     const int32_t ex = block_excl_scan256(tid < E ? hist[tid] : 0, &wcnt[1][0], &all);
     if (tid < E) off_l[tid] = offsets[tid] = ex;
-    if (tid == 0) off_l[E] = offsets[E] = (int32_t)P;
-    __syncthreads();
-    for (int j = 0; j < tt.n; ++j) {
-        const int total = tile_table_prefix(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, &wcnt[2][0]);
-        for (int g = tid; g <= E; g += PM_THREADS) tt.r[j].prefix[g] = pre[g];
-        tile_fill(off_l, E, tt.r[j].BM, tt.r[j].nblocks_n, pre, total, tt.r[j].tiles, tid, PM_THREADS);
-        __syncthreads();
+    if (tid == 0) {
+        off_l[E] = offsets[E] = (int32_t)P;
+        off_l[E + 1] = (int32_t)P + tt.extra;
     }
+    for (int t = tid; t < tt.extra; t += PM_THREADS) sorted_pair[P + t] = t * tt.k;
+    __syncthreads();
+    for (int j = 0; j < tt.n; ++j) build_table(tt, j, off_l, E, pre, &wcnt[2][0], dn, true, tid, PM_THREADS);
     if (tid < E) base[tid] = off_l[tid];
     scatter_rounds(ids_l, P, 0, (int)((P + PM_THREADS - 1) / PM_THREADS), E, base, wcnt, sorted_pair, pair_pos);
 }
@@ -202,11 +230,14 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t
 size_t permute_ws_bytes(int64_t T, int k, int E) { return (size_t)pm_chunks(T * k) * (size_t)E * sizeof(int32_t); }
 
 hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *offsets, int32_t *sorted_pair,
-                          int32_t *pair_pos, void *ws, hipStream_t st, const TileTableReq *req, int nreq)
+                          int32_t *pair_pos, void *ws, hipStream_t st, const TileTableReq *req, int nreq,
+                          int32_t extra_rows)
 {
     ScanTables tt;
-    tt.n = nreq < 2 ? nreq : 2;
+    tt.n = nreq < 4 ? nreq : 4;
     for (int j = 0; j < tt.n; ++j) tt.r[j] = req[j];
+    tt.extra = extra_rows;
+    tt.k = k;
     const int64_t P = T * k;
     if (P > 0 && P <= PM_SMALL_P) {
         hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PM_THREADS), 0, st, ids, P, E, offsets, sorted_pair,
