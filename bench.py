@@ -211,22 +211,20 @@ def bench_dense(args, cfg):
     qx = torch.empty((M, K), dtype=torch.int8, device=dev)
     sx = torch.empty((M,), dtype=torch.float32, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    off = torch.tensor([0, M], dtype=torch.int32, device=dev)
-    nws = max(int(w8.lib().w8a8_grouped_gemm_workspace_size(M, N, 1)), 256)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     L, st = w8.lib(), w8._stream(x.device)
     P = w8._p
 
+    # w8a8_linear's two kernels, called as its two stages so that events can
+    # bracket the GEMM: the per-row quantisation, then w8a8_linear_q
     def step(i, e0=None, e1=None):
         rc = L.w8a8_quant_act(P(x), w8.BF16, M, K, K, P(qx), P(sx), st)
         if rc:
             raise SystemExit("w8a8_quant_act: %s" % w8.status_string(rc))
         if e0 is not None:
             e0.record()
-        rc = L.w8a8_grouped_gemm(P(qx), M, P(sx), None, 1, P(packs[i % copies]), w8.B_PACKED, P(sw), P(off), 1,
-                                 M, N, K, w8.EPI_DEQUANT, w8.BF16, P(out), P(ws), nws, st)
+        rc = L.w8a8_linear_q(P(qx), P(sx), M, K, P(packs[i % copies]), P(sw), N, P(out), w8.BF16, st)
         if rc:
-            raise SystemExit("w8a8_grouped_gemm: %s" % w8.status_string(rc))
+            raise SystemExit("w8a8_linear_q: %s" % w8.status_string(rc))
         if e1 is not None:
             e1.record()
 
@@ -241,7 +239,7 @@ def bench_dense(args, cfg):
     elapsed = time.perf_counter() - t0
     gemm_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / args.steps
     ops = 2 * M * N * K
-    byts = N * K + N * 4 + M * K + M * 4 + 8 + M * N * 2   # W codes + scales, x codes + scales, offsets, out
+    byts = N * K + N * 4 + M * K + M * 4 + M * N * 2   # W codes + scales, x codes + scales, out
     mfma_bound = ops / byts > RIDGE
     if mfma_bound:
         achieved, peak, unit = ops / (gemm_us * 1e-6) / 1e12, INT8_PEAK_TOPS, "TOP/s"
@@ -256,7 +254,8 @@ def bench_dense(args, cfg):
         "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": M, "in_features": K, "out_features": N, "x_dtype": "bf16",
-                   "weight_copies_rotated": copies},
+                   "weight_copies_rotated": copies,
+                   **({"fused_qkv_widths": list(cfg.split)} if cfg.split else {})},
         "roofline": {"kernel": "dense_gemm", "bound": "mfma" if mfma_bound else "hbm", "achieved": achieved,
                      "peak": peak, "unit": unit, "frac": achieved / peak, "traffic": None, "avg_launch_us": gemm_us,
                      "alg_bytes_per_launch": byts, "int8_ops_per_launch": ops},

@@ -223,6 +223,34 @@ int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
                       void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Dense W8A8 linear: the other Linears of the scheme, e.g. an attention
+ * block's q_proj / k_proj / v_proj / o_proj, which the "Qwen3-235B-A22B-
+ * quantized.w8a8" guide lists as INT8 next to the experts, and which the
+ * recipe's targets [Linear] cover ("Qwen3.6-35B-A3B-w8a8" recipe.yaml).
+ *   out[m][n] = (sum_k xq[m][k] * w[n][k]) * s_x[m] * w_scales[n]
+ * with xq, s_x the per-row int8 codes of x (as w8a8_quant_act).  A fused QKV
+ * projection is one call over the concatenated [q; k; v] weight rows: with
+ * per-output-channel scales its columns are exactly those of the three
+ * separate linears.
+ *   x        device [M][K] x_dtype (row-major, contiguous)
+ *   w_packed int8 codes [N][K] packed by w8a8_pack_weights (one group)
+ *   w_scales device [N] fp32;  out device [M][N] out_dtype (W8A8_BF16 or W8A8_F32)
+ *   ws       device scratch of w8a8_linear_workspace_size(M, K) bytes (the
+ *            codes and scales of x)
+ * K % 16 == 0, N % 16 == 0, 16-byte aligned pointers, M*K and the packed
+ * weight bytes below 2^31.  Returns 0 (also for M = 0) or a negative status;
+ * nothing is launched on error.
+ */
+size_t w8a8_linear_workspace_size(int64_t M, int64_t K);
+int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *w_packed,
+                const float *w_scales, int64_t N, void *out, int out_dtype, void *ws, size_t ws_bytes,
+                void *stream);
+/* The same GEMM on rows already quantised (xq [M][K] int8, x_scales [M] fp32,
+ * e.g. by w8a8_quant_act); needs no workspace. */
+int w8a8_linear_q(const int8_t *xq, const float *x_scales, int64_t M, int64_t K, const int8_t *w_packed,
+                  const float *w_scales, int64_t N, void *out, int out_dtype, void *stream);
+
+/*
  * Weighted combine of the expert outputs:
  *   out[t][n] = sum_{j<k} topk_w[t][j] * y[pair_pos[t*k+j]][n]
  * accumulated in fp32 in slot order, then rounded once to out_dtype.

@@ -361,3 +361,16 @@ def moe_layer_shared_tokens(x, wg, wgu, sgu, wd, sd, k, shared, tokens):
                                          _p(_c(sgu, np.float32)), _p(_c(wd, np.int8)), _p(_c(sd, np.float32)), Is,
                                          *[_p(a) for a in sa], _p(tok), len(tok), _p(out))
     return out
+
+
+# ------------------------------------------------------------ dense linear ---
+
+
+def linear(x, qw, sw, out_dtype=BF16):
+    """Dense W8A8 linear (the attention projections): x [M,K] quantised per row,
+    then the one-group GEMM with the dequantising epilogue against int8 codes
+    qw [N,K] and scales sw [N].  Returns out [M,N]."""
+    qx, sx = quant_rows(x)
+    M = qx.shape[0]
+    return grouped_gemm(qx, sx, None, 1, _c(qw, np.int8)[None], _c(sw, np.float32)[None],
+                        np.array([0, M], np.int32), DEQUANT, out_dtype)

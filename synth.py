@@ -37,6 +37,13 @@ Workloads (shapes of the pages' models; all values synthetic):
                                   shared expert of intermediate size 768 and its
                                   bf16 sigmoid gate
   moe_30b_shared_decode_T64       the same with T=64
+  attn_qkv_30b_T4096 / _T64       fused q/k/v projection of the 30B shape as one
+                                  W8A8 linear: K=2048, N=4096+512+512
+  attn_o_30b_T4096 / _T64         o_proj: K=4096, N=2048
+  attn_qkv_235b_T8192             K=4096, N=8192+512+512
+  attn_o_235b_T8192               K=8192, N=4096
+                                  (x as the dense linear's: N(0,1) with 1% of
+                                  the input channels scaled x20)
 Weights: router W_g N(0, 0.02) in bf16; expert weights N(0, 0.02) in fp32 (they
 are quantised to int8 per output channel by whichever side uses them); the
 shared expert's weights N(0, 0.02) in fp32 and its gate vector N(0, 0.02) in
@@ -76,6 +83,7 @@ class DenseConfig:
     K: int
     N: int
     n_outlier: int
+    split: tuple = ()     # fused q/k/v: the output widths of the three projections
 
 
 MOE_CONFIGS = {
@@ -89,7 +97,18 @@ MOE_CONFIGS = {
         MoEConfig("moe_30b_shared_decode_T64", 64, 2048, 128, 8, 768, "bf16", "student_t4", 8, Is=768),
     ]
 }
-DENSE_CONFIGS = {c.name: c for c in [DenseConfig("dense_M4096_K2048_N4096", 4096, 2048, 4096, 20)]}
+DENSE_CONFIGS = {c.name: c for c in [
+    DenseConfig("dense_M4096_K2048_N4096", 4096, 2048, 4096, 20),
+    # attention projections of the two layer shapes as dense W8A8 linears
+    # (fused q/k/v rows; 32 query and 4 key/value heads of 128 at hidden 2048,
+    # 64 and 4 at hidden 4096)
+    DenseConfig("attn_qkv_30b_T4096", 4096, 2048, 5120, 20, (4096, 512, 512)),
+    DenseConfig("attn_o_30b_T4096", 4096, 4096, 2048, 41),
+    DenseConfig("attn_qkv_30b_T64", 64, 2048, 5120, 20, (4096, 512, 512)),
+    DenseConfig("attn_o_30b_T64", 64, 4096, 2048, 41),
+    DenseConfig("attn_qkv_235b_T8192", 8192, 4096, 9216, 41, (8192, 512, 512)),
+    DenseConfig("attn_o_235b_T8192", 8192, 8192, 4096, 82),
+]}
 
 W_STD = 0.02
 OUTLIER_GAIN = 20.0

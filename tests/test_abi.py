@@ -24,9 +24,10 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 19
+    assert len(names) == 22
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
-              "w8a8_moe_layer", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm"):
+              "w8a8_moe_layer", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm", "w8a8_linear",
+              "w8a8_linear_q", "w8a8_linear_workspace_size"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -230,3 +231,29 @@ def test_w4a8_entry_points_reject_before_launch(L):
     assert call(args(A=MIS)) == ALIGN
     assert call(args(wsb=ws - 1)) == WS_SMALL
     assert call(args(M=0, A=None, out=None, a_scales=None)) == OK
+
+
+def test_linear_entry_points_reject_before_launch(L):
+    s = None
+    ws = L.w8a8_linear_workspace_size(64, 2048)
+    assert ws >= 64 * 2048 + 64 * 4
+    lin = lambda **kw: (lambda a: L.w8a8_linear(a["x"], a["xd"], a["M"], a["K"], a["W"], a["sw"], a["N"], a["out"],
+                                                a["od"], a["ws"], a["wsb"], s))(
+        dict(dict(x=FAKE, xd=0, M=64, K=2048, W=FAKE, sw=FAKE, N=5120, out=FAKE, od=0, ws=FAKE, wsb=ws), **kw))
+    assert lin(K=2040) == SHAPE
+    assert lin(N=5112) == SHAPE
+    assert lin(xd=3) == INVALID
+    assert lin(od=2) == INVALID
+    assert lin(W=None) == INVALID
+    assert lin(x=MIS) == ALIGN
+    assert lin(sw=MIS) == ALIGN
+    assert lin(wsb=ws - 1) == WS_SMALL
+    assert lin(M=0, x=None, out=None, ws=None, wsb=0) == OK
+    assert lin(M=1 << 20, K=4096) == SHAPE   # M*K beyond 32-bit byte offsets
+    q = lambda **kw: (lambda a: L.w8a8_linear_q(a["xq"], a["sx"], a["M"], a["K"], a["W"], a["sw"], a["N"], a["out"],
+                                                a["od"], s))(
+        dict(dict(xq=FAKE, sx=FAKE, M=64, K=2048, W=FAKE, sw=FAKE, N=5120, out=FAKE, od=1), **kw))
+    assert q(sx=None) == INVALID
+    assert q(xq=MIS) == ALIGN
+    assert q(K=8) == SHAPE
+    assert q(M=0, xq=None, sx=None, out=None) == OK

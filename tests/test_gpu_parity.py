@@ -784,3 +784,70 @@ def test_shared_expert_edge_cases(Is):
         torch.cuda.synchronize()
         want = oracle.moe_layer_shared(x[:T], wg, oq[0], oq[1], oq[2], oq[3], cfg.k, se)
         tol_check(to_host(out), want, "shared Is=%d T=%d" % (Is, T))
+
+
+# ---------------------------------------------- dense linear (attention) ---
+
+def _quant_pack_w(wf):
+    """GPU codes, scales and packed codes of fp32 weights [N,K]; the codes are
+    checked bit-exact against the oracle's."""
+    qw, sw = w8.quant_act(to_dev(wf))
+    oq, os_ = oracle.quant_rows(wf)
+    assert np.array_equal(to_host(qw), oq) and np.array_equal(to_host(sw), os_)
+    return qw, sw, w8.pack_weights(qw.view(1, *qw.shape)), oq, os_
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 48), (3, 2048, 5120), (64, 2048, 5120), (300, 4096, 2048),
+                                   (130, 96, 1040), (513, 128, 272)])
+@pytest.mark.parametrize("xdt,od", [("bf16", w8.BF16), ("f32", w8.F32)])
+def test_linear_matches_oracle(M, K, N, xdt, od):
+    """w8a8_linear (per-row quantisation + GEMM with tiles from the block index)
+    against the oracle's quantised linear; w8a8_linear_q on the GPU's own codes
+    returns the same bits."""
+    say("linear", M, K, N, xdt, od)
+    rng = np.random.default_rng(M * 7 + K + N)
+    x32 = rng.standard_normal((M, K)).astype(np.float32)
+    x32[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+    x = synth.f32_to_bf16_bits(x32) if xdt == "bf16" else x32
+    wf = rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02)
+    qw, sw, pw, oq, os_ = _quant_pack_w(wf)
+    out = w8.linear(to_dev(x), pw, sw, N, od)
+    xq, sx = w8.quant_act(to_dev(x))
+    out_q = w8.linear_q(xq, sx, pw, sw, N, od)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_q)
+    want = oracle.linear(x, oq, os_, oracle.BF16 if od == w8.BF16 else oracle.F32)
+    tol_check(to_host(out), want, "linear M%d K%d N%d" % (M, K, N))
+
+
+def test_linear_zero_rows():
+    wf = np.random.default_rng(1).standard_normal((64, 64)).astype(np.float32)
+    qw, sw, pw, _, _ = _quant_pack_w(wf)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    assert w8.linear(x, pw, sw, 64).shape == (0, 64)
+
+
+@pytest.mark.parametrize("name", ["attn_qkv_30b_T64", "attn_o_30b_T64", "attn_qkv_30b_T4096", "attn_o_30b_T4096",
+                                  "attn_qkv_235b_T8192", "attn_o_235b_T8192"])
+def test_attention_projection_workloads(name):
+    """The attention projections at the layer shapes: the whole linear on the
+    GPU, checked against the oracle on every row (decode) or a sample of rows
+    (rows are independent).  For the fused QKV shapes, the q, k and v column
+    ranges equal separate linears over their own weight rows, bit for bit."""
+    cfg = synth.DENSE_CONFIGS[name]
+    say("attention projection", name)
+    xb, wf = synth.dense_inputs(cfg)
+    qw, sw, pw, oq, os_ = _quant_pack_w(wf)
+    xd = to_dev(xb)
+    out = w8.linear(xd, pw, sw, cfg.N)
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.M) if cfg.M <= 64 else np.sort(np.random.default_rng(2).choice(cfg.M, 64, replace=False))
+    want = oracle.linear(xb[rows], oq, os_)
+    tol_check(to_host(out)[rows], want, name)
+    col = 0
+    for n in cfg.split:
+        part = w8.pack_weights(qw[col:col + n].contiguous().view(1, n, cfg.K))
+        sep = w8.linear(xd, part, sw[col:col + n].contiguous(), n)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, col:col + n], sep), (name, col, n)
+        col += n

@@ -713,3 +713,30 @@ def test_shared_layer_token_subset(orc):
     out = orc.moe_layer_shared(x, *args)
     sub = [5, 0, 15]
     assert np.array_equal(orc.moe_layer_shared_tokens(x, *args, sub), out[sub])
+
+
+
+# ------------------------------------------------------------ dense linear ---
+
+def test_fused_qkv_columns_equal_separate_linears(orc):
+    """With per-output-channel weight scales and per-token activation scales, a
+    fused QKV linear over the concatenated weight rows returns, column range
+    by column range, exactly the three separate linears (no quantity couples
+    output channels), and each equals the float64 product of the codes."""
+    rng = np.random.default_rng(11)
+    M, K, nq, nkv = 9, 96, 64, 16
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    parts = [rng.standard_normal((n, K)).astype(np.float32) * np.float32(0.02) for n in (nq, nkv, nkv)]
+    qs = [orc.quant_rows(w) for w in parts]
+    fused_q = np.concatenate([q for q, _ in qs])
+    fused_s = np.concatenate([s_ for _, s_ in qs])
+    out = orc.linear(x, fused_q, fused_s, orc.F32)
+    col = 0
+    for q, s_ in qs:
+        sep = orc.linear(x, q, s_, orc.F32)
+        assert np.array_equal(out[:, col:col + q.shape[0]], sep)
+        col += q.shape[0]
+    qx, sx = orc.quant_rows(x)
+    acc = qx.astype(np.float64) @ fused_q.astype(np.float64).T
+    want = (acc * sx.astype(np.float64)[:, None] * fused_s.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(out, want)

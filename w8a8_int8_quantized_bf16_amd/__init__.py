@@ -62,6 +62,10 @@ def lib():
     L.w8a8_quant_act.argtypes = [P, i32, i64, i64, i64, P, P, P]
     L.moe_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, P]
     L.moe_router_widen.argtypes = [P, i32, i64, P, P]
+    L.w8a8_linear_workspace_size.argtypes = [i64, i64]
+    L.w8a8_linear_workspace_size.restype = sz
+    L.w8a8_linear.argtypes = [P, i32, i64, i64, P, P, i64, P, i32, P, sz, P]
+    L.w8a8_linear_q.argtypes = [P, P, i64, i64, P, P, i64, P, i32, P]
     L.moe_permute_workspace_size.argtypes = [i64, i32, i32]
     L.moe_permute_workspace_size.restype = sz
     L.moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P, sz, P]
@@ -187,6 +191,35 @@ def pack_weights(B):
     n = int(lib().w8a8_packed_weights_size(G, N, K))
     out = torch.empty(n, dtype=torch.int8, device=B.device)
     _check(lib().w8a8_pack_weights(_p(B), G, N, K, _p(out), _stream(B.device)), "w8a8_pack_weights")
+    return out
+
+
+def linear(x, w_packed, w_scales, N, out_dtype=BF16, ws=None, out=None):
+    """Dense W8A8 linear: x [M,K] bf16/fp32 quantised per row, times the packed
+    int8 weights (pack_weights of [N,K] codes) with per-channel scales w_scales
+    [N]; out [M,N]."""
+    _need(x, "x", dim=2)
+    _need(w_packed, "w_packed", torch.int8)
+    _need(w_scales, "w_scales", torch.float32, 1)
+    M, K = x.shape
+    if ws is None:
+        ws = torch.empty(max(int(lib().w8a8_linear_workspace_size(M, K)), 256), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=x.device)
+    _check(lib().w8a8_linear(_p(x), _act_dtype(x), M, K, _p(w_packed), _p(w_scales), N, _p(out), out_dtype, _p(ws),
+                             ws.numel(), _stream(x.device)), "w8a8_linear")
+    return out
+
+
+def linear_q(xq, x_scales, w_packed, w_scales, N, out_dtype=BF16, out=None):
+    """The dense W8A8 linear on rows already quantised (xq int8 [M,K], x_scales [M])."""
+    _need(xq, "xq", torch.int8, 2)
+    _need(x_scales, "x_scales", torch.float32, 1)
+    M, K = xq.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=xq.device)
+    _check(lib().w8a8_linear_q(_p(xq), _p(x_scales), M, K, _p(w_packed), _p(w_scales), N, _p(out), out_dtype,
+                               _stream(xq.device)), "w8a8_linear_q")
     return out
 
 

@@ -439,6 +439,52 @@ int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, co
                                              ws, (hipStream_t)stream));
 }
 
+static int check_linear(int64_t M, int64_t K, int64_t N, const int8_t *w_packed, const float *w_scales, const void *out,
+                        int out_dtype)
+{
+    if (M < 0 || K <= 0 || N <= 0 || !act_dtype_ok(out_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (K % 16 || N % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (M * K > INT32_MAX - 256 || (int64_t)packed_weights_bytes(1, N, K) > INT32_MAX - 256 || M > INT32_MAX / 2)
+        return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (M > 0 && (!w_packed || !w_scales || !out)) return W8A8_ERR_INVALID_ARG;
+    if (M > 0 && (!aligned16(w_packed) || !aligned16(w_scales) || !aligned16(out))) return W8A8_ERR_ALIGNMENT;
+    return W8A8_OK;
+}
+
+size_t w8a8_linear_workspace_size(int64_t M, int64_t K)
+{
+    if (M < 0 || K <= 0) return 0;
+    return round256((size_t)(M * K)) + round256(sizeof(float) * (size_t)M);
+}
+
+int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *w_packed, const float *w_scales,
+                int64_t N, void *out, int out_dtype, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_linear(M, K, N, w_packed, w_scales, out, out_dtype);
+    if (rc) return rc;
+    if (!act_dtype_ok(x_dtype)) return W8A8_ERR_INVALID_ARG;
+    if (M == 0) return W8A8_OK;
+    if (!x || !ws) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(ws)) return W8A8_ERR_ALIGNMENT;
+    if (ws_bytes < w8a8_linear_workspace_size(M, K)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+    int8_t *xq = (int8_t *)ws;
+    float *sx = (float *)((char *)ws + round256((size_t)(M * K)));
+    hipError_t e = launch_quant_rows(x, x_dtype, M, K, K, xq, sx, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_linear(xq, sx, M, K, w_packed, w_scales, N, out_dtype, out, (hipStream_t)stream));
+}
+
+int w8a8_linear_q(const int8_t *xq, const float *x_scales, int64_t M, int64_t K, const int8_t *w_packed,
+                  const float *w_scales, int64_t N, void *out, int out_dtype, void *stream)
+{
+    int rc = check_linear(M, K, N, w_packed, w_scales, out, out_dtype);
+    if (rc) return rc;
+    if (M == 0) return W8A8_OK;
+    if (!xq || !x_scales) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(x_scales)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_linear(xq, x_scales, M, K, w_packed, w_scales, N, out_dtype, out, (hipStream_t)stream));
+}
+
 int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *pair_pos, int64_t T, int k, int64_t H,
                 void *out, int out_dtype, void *stream)
 {

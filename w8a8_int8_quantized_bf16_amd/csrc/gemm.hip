@@ -69,7 +69,25 @@ struct GemmArgs {
     int G_routed;                 // groups g >= G_routed take their weights from
     const int8_t *B_extra;        //   B_extra / b_extra_scales (one group's worth,
     const float *b_extra_scales;  //   same layout) instead of B and b_scales
+    int32_t dense_rows;           // > 0: one group of this many rows, tiles from
+                                  //   the block index (no tile table)
 };
+
+// The tile of block `bid` of a one-group GEMM without a table: the same
+// numbering and XCD split as tile_fill (column block, then row tile; XCD x =
+// bid % 8 runs one contiguous range of tile numbers).  False past the last tile.
+__device__ __forceinline__ bool dense_tile(int bid, int32_t M, int BM, int nbn, int4 *t)
+{
+    const int mt_n = (M + BM - 1) / BM;
+    const int total = mt_n * nbn;
+    if (bid >= total) return false;
+    const int q = total >> 3, r = total & 7;
+    const int x = bid & 7, slot = bid >> 3;
+    const int v = x * q + min(x, r) + slot;
+    const int nb = v / mt_n, mt = v - nb * mt_n;
+    *t = make_int4(0, mt * BM, min(BM, M - mt * BM), nb);
+    return true;
+}
 
 template <typename T>
 __device__ __forceinline__ T to_out(float v);
@@ -320,10 +338,15 @@ void grouped_gemm_kernel(GemmArgs a)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     __shared__ float ascale[BM];
 
-    // ---- which tile (one table load)
+    // ---- which tile (one table load, or from the block index)
     const int bid = blockIdx.x;
-    if (bid >= a.tile_prefix[a.G]) return;
-    const int4 tinfo = a.tiles[bid];
+    int4 tinfo;
+    if (a.dense_rows > 0) {
+        if (!dense_tile(bid, a.dense_rows, BM, a.nblocks_n, &tinfo)) return;
+    } else {
+        if (bid >= a.tile_prefix[a.G]) return;
+        tinfo = a.tiles[bid];
+    }
     const int g = tinfo.x, rows = tinfo.z, nb = tinfo.w;
     const int64_t row0 = tinfo.y;
     const int N = (int)a.N, K = (int)a.K;
@@ -793,7 +816,8 @@ size_t prefix_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) & 
 template <int BM, int WN, int DEPTH, bool PACKED>
 hipError_t launch_main_layout(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
 {
-    const int64_t max_tiles = ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
+    const int64_t max_tiles = ga.dense_rows > 0 ? (ga.M_total + BM - 1) / BM * ga.nblocks_n
+                                                : ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
     dim3 grid((unsigned)max_tiles), block(G_THREADS);
     if (epilogue == 0)
         hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 0, int32_t, PACKED>), grid, block, 0, st, ga);
@@ -983,6 +1007,33 @@ hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_s
     if (e != hipSuccess) return e;
     return launch_gemm_main(A, A_rows, a_scales, gather, gather_div, B, b_packed, b_scales, offsets, G, M_total, N,
                             K, epilogue, out_dtype, out, ws, st);
+}
+
+hipError_t launch_linear(const int8_t *xq, const float *sx, int64_t M, int64_t K, const int8_t *Bp,
+                         const float *b_scales, int64_t N, int out_dtype, void *out, hipStream_t st)
+{
+    if (M == 0) return hipSuccess;
+    GemmArgs ga{};
+    ga.A = xq;
+    ga.a_scales = sx;
+    ga.gather_div = 1;
+    ga.B = Bp;
+    ga.b_scales = b_scales;
+    ga.G = 1;
+    ga.G_routed = 1;
+    ga.M_total = M;
+    ga.N = N;
+    ga.K = K;
+    ga.out = out;
+    ga.A_bytes = M * K;
+    ga.packed_b = 1;
+    ga.dense_rows = (int32_t)M;
+    const TileCfg c = gemm_cfg(M, N, 1, 1);
+    ga.nblocks_n = gemm_nblocks(N, 1, c.WN);
+    if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, 1, out_dtype, st);
+    if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, 1, out_dtype, st);
+    if (c.WN == 2) return launch_main_cfg<128, 2, 2>(ga, 1, out_dtype, st);
+    return launch_main_cfg<128, 4, 2>(ga, 1, out_dtype, st);
 }
 
 size_t packed_weights_bytes(int64_t G, int64_t N, int64_t K) { return (size_t)(G * ((N + 31) / 32) * ((K + 127) / 128) * 4096); }
