@@ -320,13 +320,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, v16i (&acc)[BM 
 // BM rows x (4 waves x WN fragments of 32 columns); DEPTH K steps of B in flight.
 // Tiles of up to 128 x 256 run two blocks per CU (two waves per SIMD, at most
 // 256 registers per lane, accumulators in VGPRs); 128 x 512 tiles run one.
-// Waves per SIMD the kernel is compiled for: three for 64-row tiles (their
+// Waves per SIMD the kernel is compiled for: three for 64 x 256 tiles (their
 // registers fit 168 VGPRs: three blocks per CU overlap one block's start-up
 // and epilogue with the others' loops), except the variants that would spill
 // there; two for tiles up to 128 x 256; one above.
 constexpr int gemm_min_waves(int BM, int WN, int EPI, int out_bytes, bool packed)
 {
-    if (BM <= 64 && packed && !(EPI == 2 && out_bytes == 4)) return 3;
+    if (BM <= 64 && WN == 2 && packed && !(EPI == 2 && out_bytes == 4)) return 3;
     return BM * WN <= 256 ? 2 : 1;
 }
 
