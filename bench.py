@@ -213,16 +213,19 @@ def bench_dense(args, cfg):
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     L, st = w8.lib(), w8._stream(x.device)
     P = w8._p
+    nws = int(L.w8a8_linear_q_workspace_size(M, N, K))   # split-K partial sums (decode-sized linears)
+    lws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
 
-    # w8a8_linear's two kernels, called as its two stages so that events can
-    # bracket the GEMM: the per-row quantisation, then w8a8_linear_q
+    # w8a8_linear's kernels, called as its two stages so that events can
+    # bracket the GEMM: the per-row quantisation, then w8a8_linear_q (the
+    # GEMM, plus the sum of the K slices when K is split)
     def step(i, e0=None, e1=None):
         rc = L.w8a8_quant_act(P(x), w8.BF16, M, K, K, P(qx), P(sx), st)
         if rc:
             raise SystemExit("w8a8_quant_act: %s" % w8.status_string(rc))
         if e0 is not None:
             e0.record()
-        rc = L.w8a8_linear_q(P(qx), P(sx), M, K, P(packs[i % copies]), P(sw), N, P(out), w8.BF16, st)
+        rc = L.w8a8_linear_q(P(qx), P(sx), M, K, P(packs[i % copies]), P(sw), N, P(out), w8.BF16, P(lws), nws, st)
         if rc:
             raise SystemExit("w8a8_linear_q: %s" % w8.status_string(rc))
         if e1 is not None:

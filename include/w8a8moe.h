@@ -235,20 +235,27 @@ int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
  *   x        device [M][K] x_dtype (row-major, contiguous)
  *   w_packed int8 codes [N][K] packed by w8a8_pack_weights (one group)
  *   w_scales device [N] fp32;  out device [M][N] out_dtype (W8A8_BF16 or W8A8_F32)
- *   ws       device scratch of w8a8_linear_workspace_size(M, K) bytes (the
- *            codes and scales of x)
+ *   ws       device scratch of w8a8_linear_workspace_size(M, N, K) bytes (the
+ *            codes and scales of x; with few rows also the int32 partial sums
+ *            of slices of K: such a linear has too few output tiles for the
+ *            chip, so K is split and a second kernel adds the slices exactly
+ *            and dequantises, with the same result bit for bit)
  * K % 16 == 0, N % 16 == 0, 16-byte aligned pointers, M*K and the packed
  * weight bytes below 2^31.  Returns 0 (also for M = 0) or a negative status;
  * nothing is launched on error.
  */
-size_t w8a8_linear_workspace_size(int64_t M, int64_t K);
+size_t w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
 int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *w_packed,
                 const float *w_scales, int64_t N, void *out, int out_dtype, void *ws, size_t ws_bytes,
                 void *stream);
 /* The same GEMM on rows already quantised (xq [M][K] int8, x_scales [M] fp32,
- * e.g. by w8a8_quant_act); needs no workspace. */
+ * e.g. by w8a8_quant_act).  ws: w8a8_linear_q_workspace_size(M, N, K) bytes
+ * for the split of K (0 when the shape is not split), or NULL: then K is
+ * never split (same result, fewer tiles in flight). */
+size_t w8a8_linear_q_workspace_size(int64_t M, int64_t N, int64_t K);
 int w8a8_linear_q(const int8_t *xq, const float *x_scales, int64_t M, int64_t K, const int8_t *w_packed,
-                  const float *w_scales, int64_t N, void *out, int out_dtype, void *stream);
+                  const float *w_scales, int64_t N, void *out, int out_dtype, void *ws, size_t ws_bytes,
+                  void *stream);
 
 /*
  * Weighted combine of the expert outputs:

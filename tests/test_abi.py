@@ -24,10 +24,10 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
               "w8a8_moe_layer", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm", "w8a8_linear",
-              "w8a8_linear_q", "w8a8_linear_workspace_size"):
+              "w8a8_linear_q", "w8a8_linear_workspace_size", "w8a8_linear_q_workspace_size"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -235,8 +235,14 @@ def test_w4a8_entry_points_reject_before_launch(L):
 
 def test_linear_entry_points_reject_before_launch(L):
     s = None
-    ws = L.w8a8_linear_workspace_size(64, 2048)
+    ws = L.w8a8_linear_workspace_size(64, 5120, 2048)
     assert ws >= 64 * 2048 + 64 * 4
+    # a decode-sized linear with a long K splits it: int32 partial sums of the slices
+    assert L.w8a8_linear_q_workspace_size(64, 2048, 4096) >= 2 * 64 * 2048 * 4
+    assert L.w8a8_linear_q_workspace_size(64, 5120, 2048) == 0     # 16 steps: not worth a split
+    assert L.w8a8_linear_q_workspace_size(4096, 2048, 4096) == 0   # enough tiles: no split
+    assert L.w8a8_linear_workspace_size(64, 2048, 4096) >= 64 * 4096 + 64 * 4 + \
+        L.w8a8_linear_q_workspace_size(64, 2048, 4096)
     lin = lambda **kw: (lambda a: L.w8a8_linear(a["x"], a["xd"], a["M"], a["K"], a["W"], a["sw"], a["N"], a["out"],
                                                 a["od"], a["ws"], a["wsb"], s))(
         dict(dict(x=FAKE, xd=0, M=64, K=2048, W=FAKE, sw=FAKE, N=5120, out=FAKE, od=0, ws=FAKE, wsb=ws), **kw))
@@ -250,10 +256,13 @@ def test_linear_entry_points_reject_before_launch(L):
     assert lin(wsb=ws - 1) == WS_SMALL
     assert lin(M=0, x=None, out=None, ws=None, wsb=0) == OK
     assert lin(M=1 << 20, K=4096) == SHAPE   # M*K beyond 32-bit byte offsets
+    qws = L.w8a8_linear_q_workspace_size(64, 2048, 4096)
     q = lambda **kw: (lambda a: L.w8a8_linear_q(a["xq"], a["sx"], a["M"], a["K"], a["W"], a["sw"], a["N"], a["out"],
-                                                a["od"], s))(
-        dict(dict(xq=FAKE, sx=FAKE, M=64, K=2048, W=FAKE, sw=FAKE, N=5120, out=FAKE, od=1), **kw))
+                                                a["od"], a["ws"], a["wsb"], s))(
+        dict(dict(xq=FAKE, sx=FAKE, M=64, K=4096, W=FAKE, sw=FAKE, N=2048, out=FAKE, od=1, ws=FAKE, wsb=qws), **kw))
     assert q(sx=None) == INVALID
     assert q(xq=MIS) == ALIGN
+    assert q(ws=MIS) == ALIGN
+    assert q(wsb=qws - 1) == WS_SMALL
     assert q(K=8) == SHAPE
     assert q(M=0, xq=None, sx=None, out=None) == OK

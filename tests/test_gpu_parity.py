@@ -798,12 +798,13 @@ def _quant_pack_w(wf):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 64, 48), (3, 2048, 5120), (64, 2048, 5120), (300, 4096, 2048),
-                                   (130, 96, 1040), (513, 128, 272)])
+                                   (130, 96, 1040), (513, 128, 272), (64, 4096, 2048), (17, 3216, 528)])
 @pytest.mark.parametrize("xdt,od", [("bf16", w8.BF16), ("f32", w8.F32)])
 def test_linear_matches_oracle(M, K, N, xdt, od):
-    """w8a8_linear (per-row quantisation + GEMM with tiles from the block index)
-    against the oracle's quantised linear; w8a8_linear_q on the GPU's own codes
-    returns the same bits."""
+    """w8a8_linear (per-row quantisation + GEMM with tiles from the block index,
+    K split into slices when there are few rows) against the oracle's quantised
+    linear; w8a8_linear_q on the GPU's own codes returns the same bits, with
+    and without the split."""
     say("linear", M, K, N, xdt, od)
     rng = np.random.default_rng(M * 7 + K + N)
     x32 = rng.standard_normal((M, K)).astype(np.float32)
@@ -814,8 +815,11 @@ def test_linear_matches_oracle(M, K, N, xdt, od):
     out = w8.linear(to_dev(x), pw, sw, N, od)
     xq, sx = w8.quant_act(to_dev(x))
     out_q = w8.linear_q(xq, sx, pw, sw, N, od)
+    out_nosplit = w8.linear_q(xq, sx, pw, sw, N, od, split=False)
     torch.cuda.synchronize()
     assert torch.equal(out, out_q)
+    # K split into slices (few rows) adds int32 sums exactly: the same bits
+    assert torch.equal(out_q, out_nosplit)
     want = oracle.linear(x, oq, os_, oracle.BF16 if od == w8.BF16 else oracle.F32)
     tol_check(to_host(out), want, "linear M%d K%d N%d" % (M, K, N))
 

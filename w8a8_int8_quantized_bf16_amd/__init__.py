@@ -62,10 +62,12 @@ def lib():
     L.w8a8_quant_act.argtypes = [P, i32, i64, i64, i64, P, P, P]
     L.moe_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, P]
     L.moe_router_widen.argtypes = [P, i32, i64, P, P]
-    L.w8a8_linear_workspace_size.argtypes = [i64, i64]
+    L.w8a8_linear_workspace_size.argtypes = [i64, i64, i64]
     L.w8a8_linear_workspace_size.restype = sz
+    L.w8a8_linear_q_workspace_size.argtypes = [i64, i64, i64]
+    L.w8a8_linear_q_workspace_size.restype = sz
     L.w8a8_linear.argtypes = [P, i32, i64, i64, P, P, i64, P, i32, P, sz, P]
-    L.w8a8_linear_q.argtypes = [P, P, i64, i64, P, P, i64, P, i32, P]
+    L.w8a8_linear_q.argtypes = [P, P, i64, i64, P, P, i64, P, i32, P, sz, P]
     L.moe_permute_workspace_size.argtypes = [i64, i32, i32]
     L.moe_permute_workspace_size.restype = sz
     L.moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P, sz, P]
@@ -203,7 +205,8 @@ def linear(x, w_packed, w_scales, N, out_dtype=BF16, ws=None, out=None):
     _need(w_scales, "w_scales", torch.float32, 1)
     M, K = x.shape
     if ws is None:
-        ws = torch.empty(max(int(lib().w8a8_linear_workspace_size(M, K)), 256), dtype=torch.uint8, device=x.device)
+        ws = torch.empty(max(int(lib().w8a8_linear_workspace_size(M, N, K)), 256), dtype=torch.uint8,
+                         device=x.device)
     if out is None:
         out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=x.device)
     _check(lib().w8a8_linear(_p(x), _act_dtype(x), M, K, _p(w_packed), _p(w_scales), N, _p(out), out_dtype, _p(ws),
@@ -211,15 +214,18 @@ def linear(x, w_packed, w_scales, N, out_dtype=BF16, ws=None, out=None):
     return out
 
 
-def linear_q(xq, x_scales, w_packed, w_scales, N, out_dtype=BF16, out=None):
-    """The dense W8A8 linear on rows already quantised (xq int8 [M,K], x_scales [M])."""
+def linear_q(xq, x_scales, w_packed, w_scales, N, out_dtype=BF16, out=None, split=True):
+    """The dense W8A8 linear on rows already quantised (xq int8 [M,K], x_scales
+    [M]); split=False runs it without splitting K (no workspace)."""
     _need(xq, "xq", torch.int8, 2)
     _need(x_scales, "x_scales", torch.float32, 1)
     M, K = xq.shape
     if out is None:
         out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=xq.device)
+    nws = int(lib().w8a8_linear_q_workspace_size(M, N, K)) if split else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=xq.device) if nws else None
     _check(lib().w8a8_linear_q(_p(xq), _p(x_scales), M, K, _p(w_packed), _p(w_scales), N, _p(out), out_dtype,
-                               _stream(xq.device)), "w8a8_linear_q")
+                               _p(ws), nws, _stream(xq.device)), "w8a8_linear_q")
     return out
 
 

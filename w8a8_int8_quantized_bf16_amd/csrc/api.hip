@@ -451,10 +451,18 @@ static int check_linear(int64_t M, int64_t K, int64_t N, const int8_t *w_packed,
     return W8A8_OK;
 }
 
-size_t w8a8_linear_workspace_size(int64_t M, int64_t K)
+static bool linear_sizes_ok(int64_t M, int64_t N, int64_t K) { return M >= 0 && N > 0 && K > 0; }
+
+size_t w8a8_linear_q_workspace_size(int64_t M, int64_t N, int64_t K)
 {
-    if (M < 0 || K <= 0) return 0;
-    return round256((size_t)(M * K)) + round256(sizeof(float) * (size_t)M);
+    if (!linear_sizes_ok(M, N, K)) return 0;
+    return round256(linear_partials_bytes(M, N, K));
+}
+
+size_t w8a8_linear_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (!linear_sizes_ok(M, N, K)) return 0;
+    return round256((size_t)(M * K)) + round256(sizeof(float) * (size_t)M) + w8a8_linear_q_workspace_size(M, N, K);
 }
 
 int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *w_packed, const float *w_scales,
@@ -466,23 +474,29 @@ int w8a8_linear(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *
     if (M == 0) return W8A8_OK;
     if (!x || !ws) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(ws)) return W8A8_ERR_ALIGNMENT;
-    if (ws_bytes < w8a8_linear_workspace_size(M, K)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < w8a8_linear_workspace_size(M, N, K)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
     int8_t *xq = (int8_t *)ws;
     float *sx = (float *)((char *)ws + round256((size_t)(M * K)));
+    int32_t *part = (int32_t *)((char *)sx + round256(sizeof(float) * (size_t)M));
     hipError_t e = launch_quant_rows(x, x_dtype, M, K, K, xq, sx, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(launch_linear(xq, sx, M, K, w_packed, w_scales, N, out_dtype, out, (hipStream_t)stream));
+    return hip_status(launch_linear(xq, sx, M, K, w_packed, w_scales, N, out_dtype, out, (hipStream_t)stream,
+                                    linear_partials_bytes(M, N, K) ? part : nullptr));
 }
 
 int w8a8_linear_q(const int8_t *xq, const float *x_scales, int64_t M, int64_t K, const int8_t *w_packed,
-                  const float *w_scales, int64_t N, void *out, int out_dtype, void *stream)
+                  const float *w_scales, int64_t N, void *out, int out_dtype, void *ws, size_t ws_bytes,
+                  void *stream)
 {
     int rc = check_linear(M, K, N, w_packed, w_scales, out, out_dtype);
     if (rc) return rc;
     if (M == 0) return W8A8_OK;
     if (!xq || !x_scales) return W8A8_ERR_INVALID_ARG;
-    if (!aligned16(xq) || !aligned16(x_scales)) return W8A8_ERR_ALIGNMENT;
-    return hip_status(launch_linear(xq, x_scales, M, K, w_packed, w_scales, N, out_dtype, out, (hipStream_t)stream));
+    if (!aligned16(xq) || !aligned16(x_scales) || (ws && !aligned16(ws))) return W8A8_ERR_ALIGNMENT;
+    const size_t need = linear_partials_bytes(M, N, K);
+    if (ws && ws_bytes < need) return W8A8_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_linear(xq, x_scales, M, K, w_packed, w_scales, N, out_dtype, out, (hipStream_t)stream,
+                                    ws && need ? (int32_t *)ws : nullptr));
 }
 
 int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *pair_pos, int64_t T, int k, int64_t H,

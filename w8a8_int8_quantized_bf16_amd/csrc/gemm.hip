@@ -71,21 +71,27 @@ struct GemmArgs {
     const float *b_extra_scales;  //   same layout) instead of B and b_scales
     int32_t dense_rows;           // > 0: one group of this many rows, tiles from
                                   //   the block index (no tile table)
+    int ksplit, ksteps;           // dense: K in ksplit slices of ksteps 128-byte
+                                  //   steps, each writing int32 sums to out + slice * M * N
 };
 
 // The tile of block `bid` of a one-group GEMM without a table: the same
 // numbering and XCD split as tile_fill (column block, then row tile; XCD x =
 // bid % 8 runs one contiguous range of tile numbers).  False past the last tile.
-__device__ __forceinline__ bool dense_tile(int bid, int32_t M, int BM, int nbn, int4 *t)
+// With K split into ksplit slices the tiles are numbered slice-major (the
+// slice goes to the descriptor's group field).
+__device__ __forceinline__ bool dense_tile(int bid, int32_t M, int BM, int nbn, int ksplit, int4 *t)
 {
     const int mt_n = (M + BM - 1) / BM;
-    const int total = mt_n * nbn;
+    const int per = mt_n * nbn, total = per * ksplit;
     if (bid >= total) return false;
     const int q = total >> 3, r = total & 7;
     const int x = bid & 7, slot = bid >> 3;
-    const int v = x * q + min(x, r) + slot;
+    int v = x * q + min(x, r) + slot;
+    const int ks = v / per;
+    v -= ks * per;
     const int nb = v / mt_n, mt = v - nb * mt_n;
-    *t = make_int4(0, mt * BM, min(BM, M - mt * BM), nb);
+    *t = make_int4(ks, mt * BM, min(BM, M - mt * BM), nb);
     return true;
 }
 
@@ -351,8 +357,11 @@ void grouped_gemm_kernel(GemmArgs a)
     // ---- which tile (one table load, or from the block index)
     const int bid = blockIdx.x;
     int4 tinfo;
+    int kbeg = 0;   // first K step of this tile's slice (dense, split K)
     if (a.dense_rows > 0) {
-        if (!dense_tile(bid, a.dense_rows, BM, a.nblocks_n, &tinfo)) return;
+        if (!dense_tile(bid, a.dense_rows, BM, a.nblocks_n, a.ksplit, &tinfo)) return;
+        kbeg = tinfo.x * a.ksteps;
+        tinfo.x = 0;
     } else {
         if (bid >= a.tile_prefix[a.G]) return;
         tinfo = a.tiles[bid];
@@ -360,7 +369,10 @@ void grouped_gemm_kernel(GemmArgs a)
     const int g = tinfo.x, rows = tinfo.z, nb = tinfo.w;
     const int64_t row0 = tinfo.y;
     const int N = (int)a.N, K = (int)a.K;
-    const int nk = (K + G_BK - 1) / G_BK;
+    const int nk_all = (K + G_BK - 1) / G_BK;
+    // steps of this tile: all of K, or its slice (packed B only, so no K
+    // masking of A: bytes beyond K meet zero weights)
+    const int nk = a.ksplit > 1 ? min(nk_all - kbeg, a.ksteps) : nk_all;
 
     // ---- B rows (output columns) of this lane, one per fragment
     int col[WN];
@@ -388,7 +400,7 @@ void grouped_gemm_kernel(GemmArgs a)
     // padded in N and K.  Offsets are unsigned: an invalid lane starts at
     // OOB_BASE, above every resource size, and stays out of range as steps are
     // added, so its loads return zeros.
-    const int64_t b_bytes = PACKED ? (int64_t)((N + 31) / 32) * nk * 4096 : (int64_t)N * K;
+    const int64_t b_bytes = PACKED ? (int64_t)((N + 31) / 32) * nk_all * 4096 : (int64_t)N * K;
     const bool xg = g >= a.G_routed;   // the extra group: weights of its own
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(xg ? a.B_extra : a.B + (int64_t)g * b_bytes, b_bytes);
     const float *bsg = xg ? a.b_extra_scales : a.b_scales + (int64_t)g * N;
@@ -398,7 +410,7 @@ void grouped_gemm_kernel(GemmArgs a)
 #pragma unroll
     for (int f = 0; f < WN; ++f)
         boff[f] = !cvalid[f] ? OOB_BASE
-                             : (PACKED ? (uint32_t)((col[f] >> 5) * nk * 4096 + lane * 16)
+                             : (PACKED ? (uint32_t)(((col[f] >> 5) * nk_all + kbeg) * 4096 + lane * 16)
                                        : (uint32_t)(col[f] * K + khalf));
     constexpr uint32_t BSTEP = PACKED ? 4096 : G_BK, BSUB = PACKED ? 1024 : 16;
 
@@ -424,7 +436,7 @@ void grouped_gemm_kernel(GemmArgs a)
     for (int j = 0; j < APASS; ++j) {
         arr[j] = (tid >> 3) + 32 * j;
         const int32_t sr = arow[arr[j]];
-        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + 16 * ac) : OOB_BASE;
+        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ac) : OOB_BASE;
     }
 
     // Software pipeline over K steps of 128 bytes.  A ring of DEPTH register
@@ -526,6 +538,14 @@ void grouped_gemm_kernel(GemmArgs a)
 
     __syncthreads();   // every wave is done with the A buffers
     static_assert(gemm_stage_bytes<WN, EPI, OutT>() <= (int)sizeof(smem), "epilogue staging exceeds the LDS buffer");
+    if constexpr (EPI == 0) {
+        if (a.ksplit > 1) {   // this slice's int32 sums
+            GemmArgs as = a;
+            as.out = reinterpret_cast<int32_t *>(a.out) + (int64_t)(kbeg / a.ksteps) * a.M_total * N;
+            gemm_epilogue<BM, WN, EPI, OutT>(as, acc, ascale, bsc, smem, rows, row0, nb, N);
+            return;
+        }
+    }
     gemm_epilogue<BM, WN, EPI, OutT>(a, acc, ascale, bsc, smem, rows, row0, nb, N);
 }
 
@@ -826,7 +846,7 @@ size_t prefix_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) & 
 template <int BM, int WN, int DEPTH, bool PACKED>
 hipError_t launch_main_layout(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
 {
-    const int64_t max_tiles = ga.dense_rows > 0 ? (ga.M_total + BM - 1) / BM * ga.nblocks_n
+    const int64_t max_tiles = ga.dense_rows > 0 ? (ga.M_total + BM - 1) / BM * ga.nblocks_n * ga.ksplit
                                                 : ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
     dim3 grid((unsigned)max_tiles), block(G_THREADS);
     if (epilogue == 0)
@@ -980,6 +1000,7 @@ hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scal
 {
     if (M_total == 0) return hipSuccess;
     GemmArgs ga{};
+    ga.ksplit = 1;
     ga.G_routed = B_extra ? G - 1 : G;
     ga.B_extra = B_extra;
     ga.b_extra_scales = b_extra_scales;
@@ -1019,8 +1040,59 @@ hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_s
                             K, epilogue, out_dtype, out, ws, st);
 }
 
+// Split K for dense linears with fewer tiles than half the compute units: as
+// many slices of at least four steps as bring the tile count to about 128.  A
+// slice saves the weight stream of the steps it drops from a tile (about a
+// quarter of a microsecond per 32 KB step) and costs the sum kernel (a few
+// microseconds), so K is split only from 24 steps (3072 inputs) up.
+static int linear_ksplit(int64_t M, int64_t N, int64_t K, int *ksteps)
+{
+    const TileCfg c = gemm_cfg(M, N, 1, 1);
+    const int64_t tiles = (M + c.BM - 1) / c.BM * gemm_nblocks(N, 1, c.WN);
+    const int nk = (int)((K + G_BK - 1) / G_BK);
+    int S = 1;
+    if (tiles < 128 && nk >= 24) S = (int)std::min<int64_t>(nk / 4, (128 + tiles - 1) / tiles);
+    const int steps = (nk + S - 1) / S;
+    *ksteps = steps;
+    return (nk + steps - 1) / steps;
+}
+
+size_t linear_partials_bytes(int64_t M, int64_t N, int64_t K)
+{
+    int steps;
+    const int S = linear_ksplit(M, N, K, &steps);
+    return S > 1 ? (size_t)S * (size_t)(M * N) * sizeof(int32_t) : 0;
+}
+
+// out[m][n] = ((float)sum_s part[s][m][n] * sx[m]) * s_w[n]: the int32 sums of
+// the slices add exactly, so the result equals the unsplit GEMM's bit for bit.
+template <typename OT>
+__global__ __launch_bounds__(256) void linear_reduce_kernel(const int32_t *__restrict__ part, int S, int64_t M,
+                                                            int64_t N, const float *__restrict__ sx,
+                                                            const float *__restrict__ sw, OT *__restrict__ out)
+{
+    const int64_t n4 = M * N / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        int4 acc = reinterpret_cast<const int4 *>(part)[i];
+        for (int s = 1; s < S; ++s) {
+            const int4 v = reinterpret_cast<const int4 *>(part + (int64_t)s * M * N)[i];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        const int64_t m = (4 * i) / N, n = 4 * i - m * N;
+        const float sa = sx[m];
+        const float r[4] = {((float)acc.x * sa) * sw[n], ((float)acc.y * sa) * sw[n + 1],
+                            ((float)acc.z * sa) * sw[n + 2], ((float)acc.w * sa) * sw[n + 3]};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) out[4 * i + u] = to_out<OT>(r[u]);
+    }
+}
+
 hipError_t launch_linear(const int8_t *xq, const float *sx, int64_t M, int64_t K, const int8_t *Bp,
-                         const float *b_scales, int64_t N, int out_dtype, void *out, hipStream_t st)
+                         const float *b_scales, int64_t N, int out_dtype, void *out, hipStream_t st,
+                         int32_t *partials)
 {
     if (M == 0) return hipSuccess;
     GemmArgs ga{};
@@ -1038,12 +1110,25 @@ hipError_t launch_linear(const int8_t *xq, const float *sx, int64_t M, int64_t K
     ga.A_bytes = M * K;
     ga.packed_b = 1;
     ga.dense_rows = (int32_t)M;
+    ga.ksplit = partials ? linear_ksplit(M, N, K, &ga.ksteps) : 1;
+    const int epi = ga.ksplit > 1 ? 0 : 1;
+    if (ga.ksplit > 1) ga.out = partials;
     const TileCfg c = gemm_cfg(M, N, 1, 1);
     ga.nblocks_n = gemm_nblocks(N, 1, c.WN);
-    if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, 1, out_dtype, st);
-    if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, 1, out_dtype, st);
-    if (c.WN == 2) return launch_main_cfg<128, 2, 2>(ga, 1, out_dtype, st);
-    return launch_main_cfg<128, 4, 2>(ga, 1, out_dtype, st);
+    hipError_t e;
+    if (c.BM == 32) e = launch_main_cfg<32, 2, 2>(ga, epi, out_dtype, st);
+    else if (c.BM == 64) e = launch_main_cfg<64, 2, 2>(ga, epi, out_dtype, st);
+    else if (c.WN == 2) e = launch_main_cfg<128, 2, 2>(ga, epi, out_dtype, st);
+    else e = launch_main_cfg<128, 4, 2>(ga, epi, out_dtype, st);
+    if (e != hipSuccess || ga.ksplit == 1) return e;
+    const int64_t blocks = std::min<int64_t>((M * N / 4 + 255) / 256, 2048);
+    if (out_dtype == 0)
+        hipLaunchKernelGGL(linear_reduce_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, partials,
+                           ga.ksplit, M, N, sx, b_scales, (uint16_t *)out);
+    else
+        hipLaunchKernelGGL(linear_reduce_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, partials,
+                           ga.ksplit, M, N, sx, b_scales, (float *)out);
+    return hipGetLastError();
 }
 
 size_t packed_weights_bytes(int64_t G, int64_t N, int64_t K) { return (size_t)(G * ((N + 31) / 32) * ((K + 127) / 128) * 4096); }

@@ -66,9 +66,14 @@ hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_s
                                const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
                                int out_dtype, void *out, void *ws, hipStream_t st);
 // Dense W8A8 linear on quantised rows: out [M][N] = (xq . W^T) * sx[m] * s[n]
-// (packed weights, one group), tiles from the block index (no table).
+// (packed weights, one group), tiles from the block index (no table).  With
+// few tiles K is split into slices whose int32 sums go to `partials`
+// (linear_partials_bytes(M, N, K) bytes; 0: no split) and a second kernel adds
+// them and dequantises; partials == nullptr never splits.
+size_t linear_partials_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear(const int8_t *xq, const float *sx, int64_t M, int64_t K, const int8_t *Bp,
-                         const float *b_scales, int64_t N, int out_dtype, void *out, hipStream_t st);
+                         const float *b_scales, int64_t N, int out_dtype, void *out, hipStream_t st,
+                         int32_t *partials = nullptr);
 size_t packed_weights_bytes(int64_t G, int64_t N, int64_t K);
 hipError_t launch_pack_weights(const int8_t *B, int64_t G, int64_t N, int64_t K, int8_t *P, hipStream_t st);
 
