@@ -202,15 +202,22 @@ int w4a8_quant_weights(const float *w, int64_t rows, int64_t cols, int8_t *q, fl
  * (l = 0..63, p = 0..1, j, i = 0..3) the code of column
  * 128 ks + 64 (l / 32) + 32 p + 4 j + i of row 32 nb + l % 32 in the low
  * nibble and the code 16 columns further in the high nibble; zero padding.
- * NB = ceil(N / 32), KS = ceil(K / 128).
+ * NB = ceil(N / 32), KS = ceil(K / 128).  After the codes (at the next
+ * multiple of 256 bytes) the buffer holds the group scales re-laid step-major,
+ * [G][KS][N] fp32, then (256-byte aligned) the offsets [G][KS][N] int8: one
+ * 128-column step of a wave's 64 columns is then one contiguous read.
+ *   q        device [G][N][K] codes;  scales / offsets device [G][N][KS] (as
+ *            w4a8_quant_weights writes them, rows = G*N)
+ *   packed   device, w4a8_packed_weights_size(G, N, K) bytes
  */
 size_t w4a8_packed_weights_size(int G, int64_t N, int64_t K);
-int w4a8_pack_weights(const int8_t *q, int G, int64_t N, int64_t K, uint8_t *packed, void *stream);
+int w4a8_pack_weights(const int8_t *q, const float *scales, const int8_t *offsets, int G, int64_t N, int64_t K,
+                      uint8_t *packed, void *stream);
 
 /*
  * Grouped W4A8 GEMM: as w8a8_grouped_gemm with epilogue DEQUANT or
- * DEQUANT_SWIGLU, B the packed W4 codes of w4a8_pack_weights with per-group
- * scales and offsets [G][N][ceil(K/128)]:
+ * DEQUANT_SWIGLU, B the packed buffer of w4a8_pack_weights (codes q, group
+ * scales s and offsets o, groups of 128 inputs kg):
  *   acc[r][n] = sum_kg s[g][n][kg] * sum_{k in kg} A[a][k] * (q[g][n][k] - o[g][n][kg])
  *   DEQUANT out = acc * a_scales[a];  DEQUANT_SWIGLU out = silu(gate) * up
  * The workspace is w8a8_grouped_gemm_workspace_size(M_total, N, G).  Same
@@ -218,9 +225,8 @@ int w4a8_pack_weights(const int8_t *q, int G, int64_t N, int64_t K, uint8_t *pac
  */
 int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
                       const int32_t *a_row_gather, int gather_div, const uint8_t *B_packed,
-                      const float *b_scales, const int8_t *b_offsets, const int32_t *group_offsets,
-                      int G, int64_t M_total, int64_t N, int64_t K, int epilogue, int out_dtype,
-                      void *out, void *ws, size_t ws_bytes, void *stream);
+                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                      int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dense W8A8 linear: the other Linears of the scheme, e.g. an attention
@@ -278,11 +284,10 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
  *   w_gate_f32 [E][H]   fp32: w_gate widened by moe_router_widen (exact), or
  *             NULL.  When given, the router stages it as is instead of
  *             widening w_gate inside every call; the scores are identical.
- *   w4_gate_up W4A8 gate_up_proj: packed W4 codes of [E][2I][H]
- *             (w4a8_pack_weights), or NULL.  When given, gate_up runs as the
- *             W4A8 GEMM with w4_s_gate_up / w4_o_gate_up [E][2I][ceil(H/128)]
- *             (fp32 / int8) and w_gate_up, s_gate_up may be NULL; down_proj
- *             stays W8A8.
+ *   w4_gate_up W4A8 gate_up_proj: the w4a8_pack_weights buffer of its codes
+ *             [E][2I][H] with their scales and offsets, or NULL.  When given,
+ *             gate_up runs as the W4A8 GEMM and w_gate_up, s_gate_up may be
+ *             NULL; down_proj stays W8A8.
  *   Shared expert ("Qwen3-Next-80B-A3B-Instruct in AMCT" section 2.2: the
  *   shared expert is a dense path quantised like the other Linears; the
  *   "Qwen3.6-35B-A3B-w8a8" recipe keeps shared_expert_gate out of the
@@ -309,8 +314,6 @@ typedef struct {
     const float *s_down;
     const float *w_gate_f32;
     const uint8_t *w4_gate_up;
-    const float *w4_s_gate_up;
-    const int8_t *w4_o_gate_up;
     int64_t I_shared;
     const int8_t *w_shared_gate_up;
     const float *s_shared_gate_up;

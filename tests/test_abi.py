@@ -135,7 +135,7 @@ def test_combine_rejects(L):
 
 
 def _weights(E=8, k=2, H=64, I=32, ptr=FAKE):
-    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value, None, None, None, None,
+    return w8._Weights(E, k, H, I, ptr.value, ptr.value, ptr.value, ptr.value, ptr.value, None, None,
                        0, None, None, None, None, None)
 
 
@@ -164,14 +164,14 @@ def test_layer_rejects_and_sizes_workspace(L):
     assert L.w8a8_moe_layer(ctypes.byref(Wf), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN
     assert L.w8a8_moe_layer(None, FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
     assert L.w8a8_moe_layer(ctypes.byref(W), None, 1, 0, None, None, 0, s) == OK
-    # W4A8 gate_up: its scales and offsets are required, the int8 gate_up is not
+    # W4A8 gate_up: the packed W4 buffer (codes, scales, offsets) replaces the int8 gate_up
     W4 = _weights()
-    W4.w4_gate_up, W4.w_gate_up, W4.s_gate_up = FAKE.value, None, None
-    assert L.w8a8_moe_layer(ctypes.byref(W4), FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
-    W4.w4_s_gate_up, W4.w4_o_gate_up = FAKE.value, MIS.value
+    W4.w4_gate_up, W4.w_gate_up, W4.s_gate_up = MIS.value, None, None
     assert L.w8a8_moe_layer(ctypes.byref(W4), FAKE, 1, 16, FAKE, FAKE, need, s) == ALIGN
-    W4.w4_o_gate_up = FAKE.value
+    W4.w4_gate_up = FAKE.value
     assert L.w8a8_moe_layer(ctypes.byref(W4), FAKE, 1, 16, FAKE, FAKE, need - 1, s) == WS_SMALL
+    W4.w4_gate_up = None
+    assert L.w8a8_moe_layer(ctypes.byref(W4), FAKE, 1, 16, FAKE, FAKE, need, s) == INVALID
     # shared expert: all of its weights or none, I_shared a multiple of 32
     needs = L.w8a8_moe_layer_workspace_size(ctypes.byref(_with_shared(_weights())), 16, 1)
     # + hs, hqs, shs, gate and the shared expert's 16 rows of y
@@ -187,7 +187,7 @@ def test_layer_rejects_and_sizes_workspace(L):
     Ws = _with_shared(_weights(), ptr=MIS)
     assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == ALIGN
     Ws = _with_shared(_weights())
-    Ws.w4_gate_up = Ws.w4_s_gate_up = Ws.w4_o_gate_up = FAKE.value
+    Ws.w4_gate_up = FAKE.value
     assert L.w8a8_moe_layer(ctypes.byref(Ws), FAKE, 1, 16, FAKE, FAKE, needs, s) == SHAPE
     # intermediates are laid out inside the workspace, in order, without overlap
     ptrs = (ctypes.c_void_p * 16)()
@@ -216,18 +216,20 @@ def test_w4a8_entry_points_reject_before_launch(L):
     assert L.w4a8_quant_weights(FAKE, -1, 64, FAKE, FAKE, FAKE, s) == INVALID
     assert L.w4a8_quant_weights(MIS, 4, 64, FAKE, FAKE, FAKE, s) == ALIGN
     assert L.w4a8_quant_weights(FAKE, 0, 64, None, None, None, s) == OK
-    assert L.w4a8_packed_weights_size(2, 64, 300) == 2 * 2 * 3 * 2048
-    assert L.w4a8_pack_weights(FAKE, 1, 40, 64, FAKE, s) == SHAPE
-    assert L.w4a8_pack_weights(FAKE, 1, 64, 64, MIS, s) == ALIGN
+    # codes, then step-major scales and offsets, each part 256-byte aligned
+    assert L.w4a8_packed_weights_size(2, 64, 300) == 2 * 2 * 3 * 2048 + 2 * 3 * 64 * 4 + 512
+    assert L.w4a8_pack_weights(FAKE, FAKE, FAKE, 1, 40, 64, FAKE, s) == SHAPE
+    assert L.w4a8_pack_weights(FAKE, FAKE, FAKE, 1, 64, 64, MIS, s) == ALIGN
+    assert L.w4a8_pack_weights(FAKE, None, FAKE, 1, 64, 64, FAKE, s) == INVALID
     ws = L.w8a8_grouped_gemm_workspace_size(32, 64, 2)
-    args = lambda **kw: dict(dict(A=FAKE, A_rows=32, a_scales=FAKE, gather=None, div=1, B=FAKE, bs=FAKE, bo=FAKE,
+    args = lambda **kw: dict(dict(A=FAKE, A_rows=32, a_scales=FAKE, gather=None, div=1, B=FAKE,
                                   off=FAKE, G=2, M=32, N=64, K=128, epi=1, od=0, out=FAKE, ws=FAKE, wsb=ws), **kw)
-    call = lambda a: L.w4a8_grouped_gemm(a["A"], a["A_rows"], a["a_scales"], a["gather"], a["div"], a["B"], a["bs"],
-                                         a["bo"], a["off"], a["G"], a["M"], a["N"], a["K"], a["epi"], a["od"],
+    call = lambda a: L.w4a8_grouped_gemm(a["A"], a["A_rows"], a["a_scales"], a["gather"], a["div"], a["B"],
+                                         a["off"], a["G"], a["M"], a["N"], a["K"], a["epi"], a["od"],
                                          a["out"], a["ws"], a["wsb"], s)
     assert call(args(epi=0)) == INVALID            # no raw int32 sums across weight groups
     assert call(args(N=48, epi=2)) == SHAPE
-    assert call(args(bo=None)) == INVALID
+    assert call(args(B=None)) == INVALID
     assert call(args(A=MIS)) == ALIGN
     assert call(args(wsb=ws - 1)) == WS_SMALL
     assert call(args(M=0, A=None, out=None, a_scales=None)) == OK

@@ -642,9 +642,9 @@ def test_w4a8_grouped_gemm(G, N, K, counts, gather, epi, od):
     if gather:
         gat = np.minimum(gat, A.shape[0] * k - 1).astype(np.int32)
     odc = w8.BF16 if od == "bf16" else w8.F32
-    Bp = w8.w4a8_pack_weights(to_dev(q))
+    Bp = w8.w4a8_pack_weights(to_dev(q), to_dev(s), to_dev(o))
     got = w8.w4a8_grouped_gemm(to_dev(A), to_dev(sa), None if gat is None else to_dev(gat), k if gather else 1, Bp,
-                               to_dev(s), to_dev(o), to_dev(off), epi, odc, M_total=M, b_shape=(G, N, K))
+                               to_dev(off), epi, odc, M_total=M, b_shape=(G, N, K))
     want = oracle.w4a8_grouped_gemm(A, sa, gat, k if gather else 1, q, s, o, off, epi,
                                     oracle.BF16 if od == "bf16" else oracle.F32)
     tol_check(to_host(got), want, "w4a8 gemm G%d N%d K%d epi %d" % (G, N, K, epi))

@@ -38,8 +38,7 @@ class _Weights(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int), ("k", ctypes.c_int), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("w_gate", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p), ("w_gate_f32", ctypes.c_void_p),
-                ("w4_gate_up", ctypes.c_void_p), ("w4_s_gate_up", ctypes.c_void_p),
-                ("w4_o_gate_up", ctypes.c_void_p), ("I_shared", ctypes.c_int64),
+                ("w4_gate_up", ctypes.c_void_p), ("I_shared", ctypes.c_int64),
                 ("w_shared_gate_up", ctypes.c_void_p), ("s_shared_gate_up", ctypes.c_void_p),
                 ("w_shared_down", ctypes.c_void_p), ("s_shared_down", ctypes.c_void_p),
                 ("w_shared_gate", ctypes.c_void_p)]
@@ -81,8 +80,8 @@ def lib():
     L.w4a8_quant_weights.argtypes = [P, i64, i64, P, P, P, P]
     L.w4a8_packed_weights_size.argtypes = [i32, i64, i64]
     L.w4a8_packed_weights_size.restype = sz
-    L.w4a8_pack_weights.argtypes = [P, i32, i64, i64, P, P]
-    L.w4a8_grouped_gemm.argtypes = [P, i64, P, P, i32, P, P, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
+    L.w4a8_pack_weights.argtypes = [P, P, P, i32, i64, i64, P, P]
+    L.w4a8_grouped_gemm.argtypes = [P, i64, P, P, i32, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
     WP = ctypes.POINTER(_Weights)
     L.w8a8_moe_layer_workspace_size.argtypes = [WP, i64, i32]
     L.w8a8_moe_layer_workspace_size.restype = sz
@@ -276,20 +275,25 @@ def w4a8_quant_weights(w):
     return q, s, o
 
 
-def w4a8_pack_weights(q):
-    """Pack W4 codes [G, N, K] two per byte in the W4A8 GEMM layout (uint8 bytes)."""
+def w4a8_pack_weights(q, scales, offsets):
+    """Pack W4 codes [G, N, K] two per byte in the W4A8 GEMM layout, followed
+    by their group scales and offsets ([G, N, ceil(K/128)]) re-laid step-major
+    (uint8 bytes)."""
     _need(q, "q", torch.int8, 3)
+    _need(scales, "scales", torch.float32)
+    _need(offsets, "offsets", torch.int8)
     G, N, K = q.shape
     n = int(lib().w4a8_packed_weights_size(G, N, K))
     out = torch.empty(n, dtype=torch.uint8, device=q.device)
-    _check(lib().w4a8_pack_weights(_p(q), G, N, K, _p(out), _stream(q.device)), "w4a8_pack_weights")
+    _check(lib().w4a8_pack_weights(_p(q), _p(scales), _p(offsets), G, N, K, _p(out), _stream(q.device)),
+           "w4a8_pack_weights")
     return out
 
 
-def w4a8_grouped_gemm(A, a_scales, gather, gather_div, B_packed, b_scales, b_offsets, offsets, epilogue,
-                      out_dtype=BF16, M_total=None, b_shape=None):
+def w4a8_grouped_gemm(A, a_scales, gather, gather_div, B_packed, offsets, epilogue, out_dtype=BF16, M_total=None,
+                      b_shape=None):
     """Grouped W4A8 GEMM: B_packed from w4a8_pack_weights of codes of shape
-    b_shape = (G, N, K); b_scales / b_offsets [G, N, ceil(K/128)]."""
+    b_shape = (G, N, K) with their scales and offsets."""
     _need(A, "A", torch.int8, 2)
     _need(B_packed, "B_packed", torch.uint8, 1)
     _need(offsets, "offsets", torch.int32, 1)
@@ -301,8 +305,8 @@ def w4a8_grouped_gemm(A, a_scales, gather, gather_div, B_packed, b_scales, b_off
     nws = int(lib().w8a8_grouped_gemm_workspace_size(M_total, N, G))
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=A.device)
     _check(lib().w4a8_grouped_gemm(_p(A), A.shape[0], _p(a_scales), _p(gather), int(gather_div), _p(B_packed),
-                                   _p(b_scales), _p(b_offsets), _p(offsets), G, M_total, N, K, epilogue, out_dtype,
-                                   _p(out), _p(ws), ws.numel(), _stream(A.device)), "w4a8_grouped_gemm")
+                                   _p(offsets), G, M_total, N, K, epilogue, out_dtype, _p(out), _p(ws), ws.numel(),
+                                   _stream(A.device)), "w4a8_grouped_gemm")
     return out
 
 
@@ -360,7 +364,7 @@ class MoEWeights:
         self.p_gate_up = pack_weights(w_gate_up) if w_gate_up is not None else None
         self.p_down = pack_weights(w_down)
         self.w_gate_f32 = router_widen(w_gate)
-        self.p4_gate_up = w4a8_pack_weights(w4[0]) if w4 is not None else None
+        self.p4_gate_up = w4a8_pack_weights(*w4) if w4 is not None else None
         self.shared = shared
         self.Is = 0
         sp = (None,) * 5
@@ -377,8 +381,7 @@ class MoEWeights:
         ptr = lambda t: None if t is None else t.data_ptr()
         self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), ptr(self.p_gate_up), ptr(s_gate_up),
                           self.p_down.data_ptr(), s_down.data_ptr(), self.w_gate_f32.data_ptr(),
-                          ptr(self.p4_gate_up), ptr(w4[1]) if w4 else None, ptr(w4[2]) if w4 else None,
-                          self.Is, *[ptr(t) for t in sp])
+                          ptr(self.p4_gate_up), self.Is, *[ptr(t) for t in sp])
 
     @classmethod
     def quantize(cls, w_gate, gate_up_f32, down_f32, k, w4=False, shared=None):

@@ -117,13 +117,12 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
                2 * W->I * ((W->H + 127) / 128) * 4 > INT32_MAX - 256))
         return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (!W->w_gate || !W->w_down || !W->s_down) return W8A8_ERR_INVALID_ARG;
-    if (w4 ? (!W->w4_s_gate_up || !W->w4_o_gate_up) : (!W->w_gate_up || !W->s_gate_up)) return W8A8_ERR_INVALID_ARG;
+    if (!w4 && (!W->w_gate_up || !W->s_gate_up)) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!x || !out)) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(W->w_gate) || !aligned16(W->w_down) || !aligned16(W->s_down) ||
         (W->w_gate_f32 && !aligned16(W->w_gate_f32)))
         return W8A8_ERR_ALIGNMENT;
-    if (w4 ? (!aligned16(W->w4_gate_up) || !aligned16(W->w4_s_gate_up) || !aligned16(W->w4_o_gate_up))
-           : (!aligned16(W->w_gate_up) || !aligned16(W->s_gate_up)))
+    if (w4 ? !aligned16(W->w4_gate_up) : (!aligned16(W->w_gate_up) || !aligned16(W->s_gate_up)))
         return W8A8_ERR_ALIGNMENT;
     if (T > 0 && (!aligned16(x) || !aligned16(out))) return W8A8_ERR_ALIGNMENT;
     // shared expert: all of its weights, or none
@@ -235,8 +234,8 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 4a gate_up GEMM + SwiGLU -> h (bf16), W8A8 or W4A8 weights
-    e = w4 ? launch_gemm_w4_main(xq, T, sx, sorted, k, W->w4_gate_up, W->w4_s_gate_up, W->w4_o_gate_up, offsets, E,
-                                 P, 2 * I, H, W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)
+    e = w4 ? launch_gemm_w4_main(xq, T, sx, sorted, k, W->w4_gate_up, offsets, E, P, 2 * I, H,
+                                 W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st)
            : launch_gemm_main(xq, T, sx, sorted, k, W->w_gate_up, 1, W->s_gate_up, offsets, Gg, Pg, 2 * I, H,
                               W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, h, gws1, st, nullptr,
                               sg ? W->w_shared_gate_up : nullptr, sg ? W->s_shared_gate_up : nullptr);
@@ -405,18 +404,19 @@ size_t w4a8_packed_weights_size(int G, int64_t N, int64_t K)
     return packed_w4_bytes(G, N, K);
 }
 
-int w4a8_pack_weights(const int8_t *q, int G, int64_t N, int64_t K, uint8_t *packed, void *stream)
+int w4a8_pack_weights(const int8_t *q, const float *scales, const int8_t *offsets, int G, int64_t N, int64_t K,
+                      uint8_t *packed, void *stream)
 {
-    if (G <= 0 || N <= 0 || K <= 0 || !q || !packed) return W8A8_ERR_INVALID_ARG;
+    if (G <= 0 || N <= 0 || K <= 0 || !q || !scales || !offsets || !packed) return W8A8_ERR_INVALID_ARG;
     if (N % 16 || K % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
-    if (!aligned16(q) || !aligned16(packed)) return W8A8_ERR_ALIGNMENT;
-    return hip_status(launch_pack_w4(q, G, N, K, packed, (hipStream_t)stream));
+    if (!aligned16(q) || !aligned16(packed) || ((uintptr_t)scales & 3u)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_pack_w4(q, scales, offsets, G, N, K, packed, (hipStream_t)stream));
 }
 
 int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *a_row_gather,
-                      int gather_div, const uint8_t *B_packed, const float *b_scales, const int8_t *b_offsets,
-                      const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                      int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream)
+                      int gather_div, const uint8_t *B_packed, const int32_t *group_offsets, int G, int64_t M_total,
+                      int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws, size_t ws_bytes,
+                      void *stream)
 {
     if (M_total < 0 || A_rows < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
     if (G > 4096) return W8A8_ERR_UNSUPPORTED_SHAPE;
@@ -427,16 +427,15 @@ int w4a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, co
     if (A_rows * K > INT32_MAX - 256 || (int64_t)packed_w4_bytes(1, N, K) > INT32_MAX - 256 ||
         N * ((K + 127) / 128) * 4 > INT32_MAX - 256)
         return W8A8_ERR_UNSUPPORTED_SHAPE;
-    if (!B_packed || !b_scales || !b_offsets || !group_offsets || !ws) return W8A8_ERR_INVALID_ARG;
+    if (!B_packed || !group_offsets || !ws) return W8A8_ERR_INVALID_ARG;
     if (M_total > 0 && (!A || !out || !a_scales)) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(A) || !aligned16(B_packed) || !aligned16(out) || !aligned16(ws) || !aligned16(group_offsets) ||
-        (a_row_gather && !aligned16(a_row_gather)) || !aligned16(a_scales) || ((uintptr_t)b_scales & 3u))
+        (a_row_gather && !aligned16(a_row_gather)) || !aligned16(a_scales))
         return W8A8_ERR_ALIGNMENT;
     if (ws_bytes < gemm_ws_bytes(M_total, N, G)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
     if (M_total == 0) return W8A8_OK;
-    return hip_status(launch_grouped_gemm_w4(A, A_rows, a_scales, a_row_gather, gather_div, B_packed, b_scales,
-                                             b_offsets, group_offsets, G, M_total, N, K, epilogue, out_dtype, out,
-                                             ws, (hipStream_t)stream));
+    return hip_status(launch_grouped_gemm_w4(A, A_rows, a_scales, a_row_gather, gather_div, B_packed, group_offsets,
+                                             G, M_total, N, K, epilogue, out_dtype, out, ws, (hipStream_t)stream));
 }
 
 static int check_linear(int64_t M, int64_t K, int64_t N, const int8_t *w_packed, const float *w_scales, const void *out,

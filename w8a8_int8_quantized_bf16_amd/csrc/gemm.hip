@@ -64,8 +64,8 @@ struct GemmArgs {
     const int4 *tiles;            // per launched block: {group, first grouped row, rows, column block}
     int nblocks_n;                // column blocks per group
     int packed_b;                 // B in the MFMA-fragment packed layout (see w8a8_pack_weights)
-    const float *b_gscales;       // W4: per (group, column, 128-step) scales [G][N][KS]
-    const int8_t *b_goffs;        //     and offsets [G][N][KS]
+    const float *b_gscales;       // W4: per (group, 128-step, column) scales [G][KS][N]
+    const int8_t *b_goffs;        //     and offsets [G][KS][N] (step-major: one coalesced read per step)
     int G_routed;                 // groups g >= G_routed take their weights from
     const int8_t *B_extra;        //   B_extra / b_extra_scales (one group's worth,
     const float *b_extra_scales;  //   same layout) instead of B and b_scales
@@ -615,14 +615,15 @@ void grouped_gemm_w4_kernel(GemmArgs a)
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(a.B + (int64_t)g * b_bytes, b_bytes);
     const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.b_gscales + (int64_t)g * N * nk, (int64_t)N * nk * 4);
     const __amdgpu_buffer_rsrc_t rO = make_rsrc(a.b_goffs + (int64_t)g * N * nk, (int64_t)N * nk);
+    const uint32_t sstep = (uint32_t)N * 4, ostep = (uint32_t)N;   // bytes per step
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
     // byte offsets of the column's codes, step-0 scale and step-0 offset
     uint32_t boff[WN], soff[WN], ooff[WN];
 #pragma unroll
     for (int f = 0; f < WN; ++f) {
         boff[f] = cvalid[f] ? (uint32_t)((col[f] >> 5) * nk * 2048 + lane * 32) : OOB_BASE;
-        soff[f] = cvalid[f] ? (uint32_t)(col[f] * nk * 4) : OOB_BASE;
-        ooff[f] = cvalid[f] ? (uint32_t)(col[f] * nk) : OOB_BASE;
+        soff[f] = cvalid[f] ? (uint32_t)(col[f] * 4) : OOB_BASE;
+        ooff[f] = cvalid[f] ? (uint32_t)col[f] : OOB_BASE;
     }
     float ones[WN];
 #pragma unroll
@@ -666,9 +667,9 @@ void grouped_gemm_w4_kernel(GemmArgs a)
 #pragma unroll
         for (int f = 0; f < WN; ++f) {
             gsc[slot][f] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rS, live ? soff[f] + it * 4 : OOB_BASE, 0, 0));
+                float, __builtin_amdgcn_raw_buffer_load_b32(rS, live ? soff[f] + it * sstep : OOB_BASE, 0, 0));
             gof[slot][f] =
-                (float)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rO, live ? ooff[f] + it : OOB_BASE, 0, 0);
+                (float)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rO, live ? ooff[f] + it * ostep : OOB_BASE, 0, 0);
         }
     };
     auto load_a = [&](int slot, int it) {
@@ -921,14 +922,49 @@ void gemm_tile_params_w4(int64_t M_total, int64_t N, int G, int epilogue, int *B
     *nblocks_n = gemm_nblocks(N, epilogue, c.WN);
 }
 
-size_t packed_w4_bytes(int64_t G, int64_t N, int64_t K) { return (size_t)(G * ((N + 31) / 32) * ((K + 127) / 128) * 2048); }
-
-hipError_t launch_pack_w4(const int8_t *B, int64_t G, int64_t N, int64_t K, uint8_t *P, hipStream_t st)
+// Packed W4 buffer: the codes (pack_w4_kernel), then the group scales
+// [G][KS][N] fp32 and offsets [G][KS][N] int8, each part 256-byte aligned.
+static size_t w4_codes_bytes(int64_t G, int64_t N, int64_t K)
 {
-    const int64_t nd = (int64_t)packed_w4_bytes(G, N, K) / 4;
+    return (size_t)(G * ((N + 31) / 32) * ((K + 127) / 128) * 2048);
+}
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t w4_scales_offset(int64_t G, int64_t N, int64_t K) { return align256(w4_codes_bytes(G, N, K)); }
+size_t w4_offsets_offset(int64_t G, int64_t N, int64_t K)
+{
+    return w4_scales_offset(G, N, K) + align256((size_t)(G * ((K + 127) / 128) * N) * 4);
+}
+size_t packed_w4_bytes(int64_t G, int64_t N, int64_t K)
+{
+    return w4_offsets_offset(G, N, K) + align256((size_t)(G * ((K + 127) / 128) * N));
+}
+
+// scales / offsets [G][N][KS] (as quantised, one row per output channel) to
+// step-major [G][KS][N]
+__global__ __launch_bounds__(256) void w4_scales_t_kernel(const float *__restrict__ s, const int8_t *__restrict__ o,
+                                                          int64_t G, int64_t N, int64_t KS, float *__restrict__ st,
+                                                          int8_t *__restrict__ ot)
+{
+    const int64_t n_all = G * KS * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_all; i += (int64_t)gridDim.x * 256) {
+        const int64_t n = i % N, ks = (i / N) % KS, g = i / (N * KS);
+        st[i] = s[(g * N + n) * KS + ks];
+        ot[i] = o[(g * N + n) * KS + ks];
+    }
+}
+
+hipError_t launch_pack_w4(const int8_t *B, const float *scales, const int8_t *offs, int64_t G, int64_t N, int64_t K,
+                          uint8_t *P, hipStream_t st)
+{
+    const int64_t nd = (int64_t)w4_codes_bytes(G, N, K) / 4;
     if (nd == 0) return hipSuccess;
     const int64_t blocks = std::min<int64_t>((nd + 255) / 256, 65536);
     hipLaunchKernelGGL(pack_w4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, B, G, N, K, (uint32_t *)P);
+    const int64_t KS = (K + 127) / 128;
+    const int64_t ns = G * KS * N;
+    hipLaunchKernelGGL(w4_scales_t_kernel, dim3((unsigned)std::min<int64_t>((ns + 255) / 256, 16384)), dim3(256), 0,
+                       st, scales, offs, G, N, KS, (float *)(P + w4_scales_offset(G, N, K)),
+                       (int8_t *)(P + w4_offsets_offset(G, N, K)));
     return hipGetLastError();
 }
 
@@ -949,10 +985,12 @@ static hipError_t launch_w4_bm(const GemmArgs &ga, int epilogue, int out_dtype, 
 }
 
 hipError_t launch_gemm_w4_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
-                               int gather_div, const uint8_t *Bp, const float *gscales, const int8_t *goffs,
-                               const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                               int out_dtype, void *out, const void *ws, hipStream_t st)
+                               int gather_div, const uint8_t *Bp, const int32_t *offsets, int G, int64_t M_total,
+                               int64_t N, int64_t K, int epilogue, int out_dtype, void *out, const void *ws,
+                               hipStream_t st)
 {
+    const float *gscales = (const float *)(Bp + w4_scales_offset(G, N, K));
+    const int8_t *goffs = (const int8_t *)(Bp + w4_offsets_offset(G, N, K));
     if (M_total == 0) return hipSuccess;
     GemmArgs ga{};
     ga.G_routed = G;
@@ -981,15 +1019,15 @@ hipError_t launch_gemm_w4_main(const int8_t *A, int64_t A_rows, const float *a_s
 }
 
 hipError_t launch_grouped_gemm_w4(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
-                                  int gather_div, const uint8_t *Bp, const float *gscales, const int8_t *goffs,
-                                  const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K,
-                                  int epilogue, int out_dtype, void *out, void *ws, hipStream_t st)
+                                  int gather_div, const uint8_t *Bp, const int32_t *offsets, int G, int64_t M_total,
+                                  int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws,
+                                  hipStream_t st)
 {
     if (M_total == 0) return hipSuccess;
     hipError_t e = launch_tilemap_cfg(offsets, G, M_total, N, gemm_cfg_w4(M_total, G), epilogue, ws, st);
     if (e != hipSuccess) return e;
-    return launch_gemm_w4_main(A, A_rows, a_scales, gather, gather_div, Bp, gscales, goffs, offsets, G, M_total, N,
-                               K, epilogue, out_dtype, out, ws, st);
+    return launch_gemm_w4_main(A, A_rows, a_scales, gather, gather_div, Bp, offsets, G, M_total, N, K, epilogue,
+                               out_dtype, out, ws, st);
 }
 
 hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,

@@ -77,20 +77,22 @@ hipError_t launch_linear(const int8_t *xq, const float *sx, int64_t M, int64_t K
 size_t packed_weights_bytes(int64_t G, int64_t N, int64_t K);
 hipError_t launch_pack_weights(const int8_t *B, int64_t G, int64_t N, int64_t K, int8_t *P, hipStream_t st);
 
-// W4A8: packed 4-bit weights (pack_w4_kernel layout), the grouped GEMM with
+// W4A8: packed 4-bit weights (pack_w4_kernel layout) followed by the group
+// scales and offsets re-laid step-major ([G][KS][N]); the grouped GEMM with
 // per-(column, 128-step) scales and offsets; epilogue 1 (dequant) or 2
 // (dequant + SwiGLU).  The tile table comes from gemm_tile_params_w4.
 size_t packed_w4_bytes(int64_t G, int64_t N, int64_t K);
-hipError_t launch_pack_w4(const int8_t *B, int64_t G, int64_t N, int64_t K, uint8_t *P, hipStream_t st);
+hipError_t launch_pack_w4(const int8_t *B, const float *scales, const int8_t *offs, int64_t G, int64_t N, int64_t K,
+                          uint8_t *P, hipStream_t st);
 void gemm_tile_params_w4(int64_t M_total, int64_t N, int G, int epilogue, int *BM, int *nblocks_n);
 hipError_t launch_gemm_w4_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
-                               int gather_div, const uint8_t *Bp, const float *gscales, const int8_t *goffs,
-                               const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                               int out_dtype, void *out, const void *ws, hipStream_t st);
+                               int gather_div, const uint8_t *Bp, const int32_t *offsets, int G, int64_t M_total,
+                               int64_t N, int64_t K, int epilogue, int out_dtype, void *out, const void *ws,
+                               hipStream_t st);
 hipError_t launch_grouped_gemm_w4(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
-                                  int gather_div, const uint8_t *Bp, const float *gscales, const int8_t *goffs,
-                                  const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K,
-                                  int epilogue, int out_dtype, void *out, void *ws, hipStream_t st);
+                                  int gather_div, const uint8_t *Bp, const int32_t *offsets, int G, int64_t M_total,
+                                  int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws,
+                                  hipStream_t st);
 
 hipError_t launch_combine(const void *y, int y_dtype, const float *w, const int32_t *pair_pos, int64_t T,
                           int k, int64_t H, void *out, int out_dtype, hipStream_t st);
