@@ -384,6 +384,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay measurement after the timed region")
     ap.add_argument("--w4", action="store_true",
                     help="W4A8 gate_up_proj weights (4-bit codes, groups of 128 with scale and offset)")
     ap.add_argument("--ep-share", type=int, default=0, metavar="G",
@@ -486,6 +488,34 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     dom_us = sum(evs[i][dom].elapsed_time(evs[i][dom + 1]) for i in range(args.steps)) * 1e3 / args.steps
+    # After the timed region: the same steps as replays of a HIP graph of
+    # `cap` consecutive layer calls (the layer launches kernels only, so it
+    # captures whole).  Reported beside the eager rate, as the share of the
+    # step that is launch overhead; marks cannot time stages inside a replay.
+    graph_rec = None
+    if not args.no_graph:
+        cap = next(c for c in (10, 5, 4, 2, 1) if args.steps % c == 0)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(cap):
+                w8.moe_layer(Ws[i % copies], xd, ws=ws, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(cap):
+                w8.moe_layer(Ws[i % copies], xd, ws=ws, out=out)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps // cap):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+        graph_rec = {"ms_per_step": g_ms, "value": cfg.T / (g_ms * 1e-3), "layer_calls_per_graph": cap}
+        del graph
 
     inter = w8.moe_layer_intermediates(W0, cfg.T, ws, w8.BF16 if x.dtype == np.uint16 else w8.F32)
     counts = np.diff(inter["offsets"].cpu().numpy())
@@ -530,6 +560,8 @@ def main():
                   "stage_us": dict(zip(w8.STAGE_NAMES, [round(v, 2) for v in stage_us])),
                   "expert_rows_min_max": [int(counts.min()), int(counts.max())]},
     }
+    if graph_rec is not None:
+        result["hip_graph_replay"] = graph_rec
     if cfg.Is:
         result["config"]["shared_expert_intermediate"] = cfg.Is
         # the stage's time covers the routed and the shared expert's launches

@@ -341,7 +341,9 @@ int w8a8_moe_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_
  * stage i, stages in the order route, quantise x, permute, gate_up GEMM,
  * quantise h, down GEMM, combine.  A null entry skips that mark, so a caller
  * can bracket one stage without adding records between the others.  Used to
- * time the stages from the host.
+ * time the stages from the host.  Marks recorded while `stream` is being
+ * captured into a HIP graph only order the graph's nodes; they do not time
+ * its replays.
  */
 #define W8A8_LAYER_STAGES 7
 int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T,

@@ -855,3 +855,52 @@ def test_attention_projection_workloads(name):
         torch.cuda.synchronize()
         assert torch.equal(out[:, col:col + n], sep), (name, col, n)
         col += n
+
+
+# ------------------------------------------------------------ HIP graphs ---
+
+@pytest.mark.parametrize("name,variant", [("moe_30b_decode_T64", "w8a8"), ("moe_tiny_shared_T16_H64_E8_k2_I32_Is64", "shared"),
+                                          ("moe_30b_decode_T64", "w4a8"), ("moe_tiny_T16_H64_E8_k2_I32", "w8a8")])
+def test_layer_in_hip_graph(name, variant):
+    """The layer call captured in a HIP graph (it launches kernels only: no host
+    synchronisation, allocation or memset) and replayed several times, with
+    eager work and synchronisations between the replays: every replay equals
+    the eager call bit for bit, also after the input changes in place."""
+    cfg = synth.MOE_CONFIGS[name]
+    say("graph", name, variant)
+    x, wg, gu, dn = synth.moe_inputs(cfg)
+    shared = None
+    if variant == "shared":
+        sgu, sdn, wsg = synth.shared_expert(cfg)
+        shared = (to_dev(sgu), to_dev(sdn), dev_bf16(wsg))
+    W = w8.MoEWeights.quantize(dev_bf16(wg), to_dev(gu), to_dev(dn), cfg.k, w4=variant == "w4a8", shared=shared)
+    xd = to_dev(x)
+    dt = w8.BF16 if x.dtype == np.uint16 else w8.F32
+    ws = w8.moe_layer_workspace(W, cfg.T, dt)
+    out = torch.empty_like(xd)
+    eager = w8.moe_layer(W, xd, ws=ws, out=torch.empty_like(xd)).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm the side stream once before capture
+        w8.moe_layer(W, xd, ws=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.moe_layer(W, xd, ws=ws, out=out)
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d" % i
+        junk = torch.randn(1024, 1024, device=DEV) @ torch.randn(1024, 1024, device=DEV)   # eager work between
+        torch.cuda.synchronize()
+        del junk
+    # new input values in place: the replay follows them
+    x2 = (xd.float() * 0.5).to(xd.dtype)
+    eager2 = w8.moe_layer(W, x2, ws=torch.empty_like(ws), out=torch.empty_like(xd)).clone()
+    xd.copy_(x2)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager2)
