@@ -495,44 +495,62 @@ void grouped_gemm_kernel(GemmArgs a)
     // The trip count is padded to a multiple of DEPTH; the padding steps issue
     // only out-of-range (zero, no traffic) loads.  Loads are never inside a
     // branch, so the compiler counts outstanding loads exactly and each wait
-    // covers only the data it needs.
+    // covers only the data it needs.  The last row tile of a group is usually
+    // ragged: with RAGGED the MFMAs of the 32-row blocks that hold no row are
+    // skipped (ma is uniform over the block, so each test is a scalar branch).
+    // The tests split the step into blocks that scheduling groups cannot span,
+    // which costs more than it saves with four fragments per wave (16 MFMAs
+    // per sub-step); those tiles keep the fixed issue order.  A second copy of
+    // the loop in one kernel makes the register allocator spill, so the choice
+    // is per instantiation.
+    constexpr bool RAGGED = MI > 1 && WN == 2;
+    const int ma = (rows + 31) >> 5;
     const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
-    for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
+    {
+        for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int it = it0 + d;
-            // Padding steps (it >= nk) multiply zeros: their A rows and B
-            // fragments were loaded out of range.  Each sub-step's B registers
-            // are refilled with step it + DEPTH as soon as its MFMAs are
-            // issued, so the weight loads are spread through the step.
-            const int8_t *Ab = As[d & 1];
+            for (int d = 0; d < DEPTH; ++d) {
+                const int it = it0 + d;
+                // Padding steps (it >= nk) multiply zeros: their A rows and B
+                // fragments were loaded out of range.  Each sub-step's B
+                // registers are refilled with step it + DEPTH as soon as its
+                // MFMAs are issued, so the weight loads are spread through the
+                // step.
+                const int8_t *Ab = As[d & 1];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+                for (int s = 0; s < 4; ++s) {
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi) {
-                    const int r = mi * 32 + (lane & 31);
-                    const int ch = 4 * (lane >> 5) + s;
-                    const v4i av = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
+                    for (int mi = 0; mi < MI; ++mi) {
+                        const int r = mi * 32 + (lane & 31);
+                        const int ch = 4 * (lane >> 5) + s;
+                        const v4i av = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
+                        if (!RAGGED || mi == 0 || mi < ma) {
 #pragma unroll
-                    for (int f = 0; f < WN; ++f)
-                        acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, breg[d][f][s], acc[mi][f], 0, 0, 0);
+                            for (int f = 0; f < WN; ++f)
+                                acc[mi][f] =
+                                    __builtin_amdgcn_mfma_i32_32x32x32_i8(av, breg[d][f][s], acc[mi][f], 0, 0, 0);
+                        }
+                    }
+                    load_b_sub(d, it + DEPTH, s);
                 }
-                load_b_sub(d, it + DEPTH, s);
-            }
-            const int dn = (d + 1) % DEPTH;
-            store_a(dn, (d + 1) & 1);     // A(it+1), loaded DEPTH steps ago
-            load_a(dn, it + 1 + DEPTH);
-            // issue order of the step: per sub-step the A fragment reads, its
-            // MFMAs, then the refill of its B registers; then the A staging
+                const int dn = (d + 1) % DEPTH;
+                store_a(dn, (d + 1) & 1);     // A(it+1), loaded DEPTH steps ago
+                load_a(dn, it + 1 + DEPTH);
+                if constexpr (!RAGGED) {
+                    // issue order of the step: per sub-step the A fragment
+                    // reads, its MFMAs, then the refill of its B registers;
+                    // then the A staging
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);        // LDS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);   // MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);        // B loads
+                    for (int s = 0; s < 4; ++s) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);        // LDS reads
+                        __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);   // MFMAs
+                        __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);        // B loads
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x200, APASS, 0);         // LDS stores
+                    __builtin_amdgcn_sched_group_barrier(0x020, APASS, 0);         // A loads
+                }
+                __syncthreads();
             }
-            __builtin_amdgcn_sched_group_barrier(0x200, APASS, 0);         // LDS stores
-            __builtin_amdgcn_sched_group_barrier(0x020, APASS, 0);         // A loads
-            __syncthreads();
         }
     }
 
