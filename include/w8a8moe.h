@@ -118,6 +118,17 @@ int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T
 int moe_router_widen(const uint16_t *w_gate, int E, int64_t H, float *w_gate_f32, void *stream);
 
 /*
+ * The router weight re-laid once for few-token layers (w8a8_moe_weights
+ * .w_gate_packed): w_gate_packed[(j * E + e) * 8 + i] = w_gate[e * H + 8 j + i]
+ * for j < H / 8, i < 8, i.e. [H/8][E][8] bf16: per group of 8 hidden indices
+ * the experts' 16-byte pieces lie side by side, so a wavefront that runs 64
+ * experts' score chains reads one contiguous kilobyte per step.  A pure copy:
+ * the scores do not change.  w_gate device [E][H] bf16; w_gate_packed device,
+ * E * H bf16, written.  H % 16 == 0.
+ */
+int moe_router_pack(const uint16_t *w_gate, int E, int64_t H, uint16_t *w_gate_packed, void *stream);
+
+/*
  * Group the routed pairs by expert (the packed MoE grouped matmul,
  * "Qwen3-Next-80B-A3B-Instruct in AMCT" case, section 6).  Pair p = t*k + j is
  * routed to expert topk_ids[p]; pairs are stably sorted by (expert, p).
@@ -284,6 +295,10 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
  *   w_gate_f32 [E][H]   fp32: w_gate widened by moe_router_widen (exact), or
  *             NULL.  When given, the router stages it as is instead of
  *             widening w_gate inside every call; the scores are identical.
+ *   w_gate_packed  w_gate re-laid by moe_router_pack, or NULL.  When given,
+ *             few-token layers read it instead of w_gate's rows (coalesced,
+ *             and the chunks of each score run on several waves); the scores
+ *             are identical.
  *   w4_gate_up W4A8 gate_up_proj: the w4a8_pack_weights buffer of its codes
  *             [E][2I][H] with their scales and offsets, or NULL.  When given,
  *             gate_up runs as the W4A8 GEMM and w_gate_up, s_gate_up may be
@@ -320,6 +335,7 @@ typedef struct {
     const int8_t *w_shared_down;
     const float *s_shared_down;
     const uint16_t *w_shared_gate;
+    const uint16_t *w_gate_packed;
 } w8a8_moe_weights;
 
 /*

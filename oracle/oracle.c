@@ -35,8 +35,11 @@
  *       rint(x / s) with a second IEEE fp32 divide (not x * (127 / amax)).
  *   R4  a row whose amax is 0 gets s = 0 and all codes 0.
  *   R5  scales are fp32.
- *   R6  router logits: fp32, accumulated as one fused multiply-add chain over
- *       the hidden index in ascending order, starting from +0.0f.
+ *   R6  router logits: fp32.  The hidden index is cut into chunks of 512
+ *       (the last may be shorter); each chunk is one fused multiply-add chain
+ *       over its indices in ascending order, starting from +0.0f, and the
+ *       chunk sums are added in ascending chunk order (fp32 adds, the first
+ *       chunk's sum as the start).  For H <= 512 this is the single chain.
  *   R7  top-k selects on the fp32 logits, larger first, equal logits ordered
  *       by the lower expert index.
  *   R8  the k selected softmax probabilities are renormalised to sum to 1.
@@ -201,6 +204,9 @@ void oracle_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int
  *   w      [T][k]  out, routing weights
  *   logits [T][E]  out, may be NULL
  */
+/* R6: hidden indices per chain of the router score */
+#define OR_ROUTE_CHUNK 512
+
 void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H,
                        int E, int k, int renormalize, int32_t *ids, float *w, float *logits)
 {
@@ -213,11 +219,16 @@ void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, 
         const void *xrow = (dtype == 0) ? (const void *)((const uint16_t *)x + t * H)
                                         : (const void *)((const float *)x + t * H);
         for (int e = 0; e < E; ++e) {
-            float acc = 0.0f;
-            for (int64_t h = 0; h < H; ++h)
-                acc = fmaf(or_load(xrow, dtype, h), or_bf16_to_f32(wg[(int64_t)e * H + h]), acc);
-            l[e] = acc;
-            if (logits) logits[t * E + e] = acc;
+            float total = 0.0f;
+            for (int64_t c0 = 0; c0 < H; c0 += OR_ROUTE_CHUNK) {
+                const int64_t c1 = (c0 + OR_ROUTE_CHUNK < H) ? c0 + OR_ROUTE_CHUNK : H;
+                float acc = 0.0f;
+                for (int64_t h = c0; h < c1; ++h)
+                    acc = fmaf(or_load(xrow, dtype, h), or_bf16_to_f32(wg[(int64_t)e * H + h]), acc);
+                total = (c0 == 0) ? acc : total + acc;
+            }
+            l[e] = total;
+            if (logits) logits[t * E + e] = total;
         }
         /* top-k by repeated selection: strict ">" over ascending e keeps the
          * lower index first among equal logits. */

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
               "w8a8_moe_layer", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm", "w8a8_linear",
               "w8a8_linear_q", "w8a8_linear_workspace_size", "w8a8_linear_q_workspace_size"):
@@ -123,6 +123,15 @@ def test_router_widen_rejects(L):
     assert L.moe_router_widen(FAKE, 0, 64, FAKE, s) == INVALID
     assert L.moe_router_widen(None, 8, 64, FAKE, s) == INVALID
     assert L.moe_router_widen(FAKE, 8, 64, MIS, s) == ALIGN
+
+
+def test_router_pack_rejects(L):
+    s = None
+    assert L.moe_router_pack(FAKE, 8, 72, FAKE, s) == SHAPE
+    assert L.moe_router_pack(FAKE, 0, 64, FAKE, s) == INVALID
+    assert L.moe_router_pack(FAKE, 8, 64, None, s) == INVALID
+    assert L.moe_router_pack(MIS, 8, 64, FAKE, s) == ALIGN
+    assert L.moe_router_pack(FAKE, 8, 64, MIS, s) == ALIGN
 
 
 def test_combine_rejects(L):

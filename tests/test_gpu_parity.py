@@ -187,14 +187,18 @@ def test_route_ties_lower_index_first():
                                      (17, 128, 65, 3), (33, 256, 96, 8), (12, 4096, 128, 8), (7, 80, 200, 11),
                                      (40, 32, 256, 16), (256, 2064, 128, 8), (128, 112, 200, 8),
                                      (257, 2064, 128, 8), (520, 2064, 63, 8), (300, 80, 200, 11),
-                                     (700, 32, 256, 16), (600, 48, 8, 2)])
+                                     (700, 32, 256, 16), (600, 48, 8, 2), (3, 8192, 128, 8),
+                                     (2, 1040, 64, 4), (5, 1536, 256, 8), (300, 1040, 128, 8),
+                                     (33, 528, 130, 5)])
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
 def test_route_shapes(T, H, E, k, xdt):
     """Expert counts that fill 1..4 slices of 64 (ragged ones included), odd
     token counts, short and long hidden sizes; bf16 and fp32 activations.
     With bf16 activations up to 512 (token, expert-slice) pairs take the
     vector-ALU router, more take the matrix-core one: both sides of that
-    switch are here, with hidden sizes that leave a tail of W_g steps."""
+    switch are here, with hidden sizes that leave a tail of W_g steps, and
+    hidden sizes of 1 to 16 chunks of 512 (short last chunks included), which
+    the vector-ALU router spreads over 1 to 8 waves per expert slice."""
     rng = np.random.default_rng(T * 1000 + E)
     x = rng.standard_t(4, (T, H)).astype(np.float32)
     xa = synth.f32_to_bf16_bits(x) if xdt == "bf16" else x
@@ -548,6 +552,27 @@ def test_router_widen_and_both_router_inputs():
         out2 = w8.moe_layer(case.W, case.xd)
     finally:
         case.W.c.w_gate_f32 = saved
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["moe_30b_decode_T64", "moe_tiny_T16_H64_E8_k2_I32"])
+def test_router_pack_and_both_few_token_paths(name):
+    """The packed router weight is the [H/8][E][8] re-lay of the bf16 one,
+    and a few-token layer gives bit-identical results whether the router reads
+    that copy (the score's chunks on several waves) or the [E][H] rows (one
+    wave per expert slice)."""
+    case = get_case(name)
+    E, H = case.cfg.E, case.cfg.H
+    wp = w8.router_pack(case.W.w_gate)
+    want = case.wg.reshape(E, H // 8, 8).transpose(1, 0, 2)
+    assert np.array_equal(to_host(wp.view(torch.int16)).view(np.uint16), want)
+    out1, _, _ = case.run_layer()
+    saved = case.W.c.w_gate_packed
+    try:
+        case.W.c.w_gate_packed = None
+        out2 = w8.moe_layer(case.W, case.xd)
+    finally:
+        case.W.c.w_gate_packed = saved
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 

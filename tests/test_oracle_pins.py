@@ -174,6 +174,18 @@ def test_router_fma_order_golden(orc):
         assert float(logits[0, 0]) == float(want)
 
 
+def test_router_chunk_order_golden(orc):
+    for hs, entries, want in _rows("router_chunk_order.txt"):
+        H = int(hs)
+        x = np.ones((1, H), np.float32)
+        w = np.zeros((2, H), np.float32)
+        for item in entries.split():
+            i, v = item.split(":")
+            w[0, int(i)] = float(v)
+        _, _, logits = orc.route_topk(x, synth.f32_to_bf16_bits(w), 1)
+        assert float(logits[0, 0]) == float(want)
+
+
 def _tiny_router():
     wg = synth.moe_router(TINY)
     x = synth.moe_x(TINY)

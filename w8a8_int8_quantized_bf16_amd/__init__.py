@@ -41,7 +41,7 @@ class _Weights(ctypes.Structure):
                 ("w4_gate_up", ctypes.c_void_p), ("I_shared", ctypes.c_int64),
                 ("w_shared_gate_up", ctypes.c_void_p), ("s_shared_gate_up", ctypes.c_void_p),
                 ("w_shared_down", ctypes.c_void_p), ("s_shared_down", ctypes.c_void_p),
-                ("w_shared_gate", ctypes.c_void_p)]
+                ("w_shared_gate", ctypes.c_void_p), ("w_gate_packed", ctypes.c_void_p)]
 
 
 _lib = None
@@ -61,6 +61,7 @@ def lib():
     L.w8a8_quant_act.argtypes = [P, i32, i64, i64, i64, P, P, P]
     L.moe_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, P]
     L.moe_router_widen.argtypes = [P, i32, i64, P, P]
+    L.moe_router_pack.argtypes = [P, i32, i64, P, P]
     L.w8a8_linear_workspace_size.argtypes = [i64, i64, i64]
     L.w8a8_linear_workspace_size.restype = sz
     L.w8a8_linear_q_workspace_size.argtypes = [i64, i64, i64]
@@ -335,6 +336,15 @@ def router_widen(w_gate):
     return out
 
 
+def router_pack(w_gate):
+    """The bf16 router weight re-laid [H/8][E][8] by the library (a copy)."""
+    _need(w_gate, "w_gate", torch.bfloat16, 2)
+    E, H = w_gate.shape
+    out = torch.empty((H // 8, E, 8), dtype=torch.bfloat16, device=w_gate.device)
+    _check(lib().moe_router_pack(_p(w_gate), E, H, _p(out), _stream()), "moe_router_pack")
+    return out
+
+
 class MoEWeights:
     """Device tensors of one layer.
     w_gate [E,H] bf16; w_gate_up [E,2I,H] int8 codes (gate rows, then up rows);
@@ -364,6 +374,7 @@ class MoEWeights:
         self.p_gate_up = pack_weights(w_gate_up) if w_gate_up is not None else None
         self.p_down = pack_weights(w_down)
         self.w_gate_f32 = router_widen(w_gate)
+        self.w_gate_packed = router_pack(w_gate)
         self.p4_gate_up = w4a8_pack_weights(*w4) if w4 is not None else None
         self.shared = shared
         self.Is = 0
@@ -381,7 +392,7 @@ class MoEWeights:
         ptr = lambda t: None if t is None else t.data_ptr()
         self.c = _Weights(E, self.k, H, self.I, w_gate.data_ptr(), ptr(self.p_gate_up), ptr(s_gate_up),
                           self.p_down.data_ptr(), s_down.data_ptr(), self.w_gate_f32.data_ptr(),
-                          ptr(self.p4_gate_up), self.Is, *[ptr(t) for t in sp])
+                          ptr(self.p4_gate_up), self.Is, *[ptr(t) for t in sp], self.w_gate_packed.data_ptr())
 
     @classmethod
     def quantize(cls, w_gate, gate_up_f32, down_f32, k, w4=False, shared=None):

@@ -120,7 +120,7 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
     if (!w4 && (!W->w_gate_up || !W->s_gate_up)) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!x || !out)) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(W->w_gate) || !aligned16(W->w_down) || !aligned16(W->s_down) ||
-        (W->w_gate_f32 && !aligned16(W->w_gate_f32)))
+        (W->w_gate_f32 && !aligned16(W->w_gate_f32)) || (W->w_gate_packed && !aligned16(W->w_gate_packed)))
         return W8A8_ERR_ALIGNMENT;
     if (w4 ? !aligned16(W->w4_gate_up) : (!aligned16(W->w_gate_up) || !aligned16(W->s_gate_up)))
         return W8A8_ERR_ALIGNMENT;
@@ -195,7 +195,7 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
     // 1 route; with bf16 tokens the router also quantises them (stage 2 is then empty)
     const bool fused_q = route_fuses_quant(x_dtype, T, H, E);
     if ((e = launch_route_topk(x, x_dtype, W->w_gate, W->w_gate_f32, T, H, E, k, 1, ids, w, nullptr, st,
-                               fused_q ? xq : nullptr, fused_q ? sx : nullptr)) != hipSuccess ||
+                               fused_q ? xq : nullptr, fused_q ? sx : nullptr, W->w_gate_packed)) != hipSuccess ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 2 quantise x once per token (before the permutation: one scale per token
@@ -315,6 +315,14 @@ int moe_router_widen(const uint16_t *w_gate, int E, int64_t H, float *w_gate_f32
     if (H % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(w_gate) || !aligned16(w_gate_f32)) return W8A8_ERR_ALIGNMENT;
     return hip_status(launch_widen_bf16(w_gate, (int64_t)E * H, w_gate_f32, (hipStream_t)stream));
+}
+
+int moe_router_pack(const uint16_t *w_gate, int E, int64_t H, uint16_t *w_gate_packed, void *stream)
+{
+    if (E <= 0 || H <= 0 || !w_gate || !w_gate_packed) return W8A8_ERR_INVALID_ARG;
+    if (H % 16) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(w_gate) || !aligned16(w_gate_packed)) return W8A8_ERR_ALIGNMENT;
+    return hip_status(launch_pack_router(w_gate, E, H, w_gate_packed, (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_size(int64_t T, int k, int E)

@@ -14,15 +14,20 @@ hipError_t launch_quant_w4(const float *w, int64_t rows, int64_t cols, int8_t *q
                            hipStream_t st);
 
 // wg_f32: the same router weight widened to fp32, or nullptr (then the
-// kernel widens wg while staging it).  xq/sx: when route_fuses_quant() holds,
-// the router may also write the tokens' int8 codes [T,H] and scales [T]
-// (pass nullptr otherwise; non-null where it does not hold is an error).
+// kernel widens wg while staging it).  wg_packed: the same weight in the
+// moe_router_pack layout ([H/8][E][8] bf16), or nullptr.  xq/sx: when
+// route_fuses_quant() holds, the router may also write the tokens' int8 codes
+// [T,H] and scales [T] (pass nullptr otherwise; non-null where it does not
+// hold is an error).
 bool route_fuses_quant(int dtype, int64_t T, int64_t H, int E);
 hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
                              int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
-                             hipStream_t st, int8_t *xq = nullptr, float *sx = nullptr);
+                             hipStream_t st, int8_t *xq = nullptr, float *sx = nullptr,
+                             const uint16_t *wg_packed = nullptr);
 // n bf16 values (n % 8 == 0, 16-byte aligned) widened to fp32
 hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStream_t st);
+// router weight [E][H] bf16 -> [H/8][E][8] bf16 (H % 8 == 0, 16-byte aligned)
+hipError_t launch_pack_router(const uint16_t *wg, int E, int64_t H, uint16_t *dst, hipStream_t st);
 
 size_t permute_ws_bytes(int64_t T, int k, int E);
 // Tile tables the permutation builds for grouped GEMMs (up to four): over its

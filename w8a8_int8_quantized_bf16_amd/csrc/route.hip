@@ -3,9 +3,12 @@
 // the gate maps the hidden state to one score per expert, softmax, top-8; it
 // stays in bf16 because a swapped ranking is a discrete error).
 //
-// Scores: fp32 fused multiply-add chain over the hidden index, ascending, from
-// +0.  The chain order is fixed so that every implementation that follows it
-// produces bit-identical scores, and therefore identical expert ids.
+// Scores: the hidden index is cut into chunks of RT_CHUNK = 512; each chunk is
+// an fp32 fused multiply-add chain over its indices, ascending, from +0, and
+// the chunk sums are added in ascending chunk order.  The order is fixed so
+// that every implementation that follows it produces bit-identical scores,
+// and therefore identical expert ids; the chunks let several waves share one
+// score when there are few tokens.
 //
 // Two kernels compute the same chains: route_mfma_kernel for bf16 x (matrix
 // cores, below) and route_topk_kernel for fp32 x (vector FMA: a bf16 x fp32
@@ -28,6 +31,7 @@ namespace w8a8 {
 namespace {
 constexpr int RT_TOK = 16;   // tokens per block
 constexpr int RT_KC = 32;    // hidden slice staged per step
+constexpr int RT_CHUNK = 512;   // hidden indices per chain of a score
 }
 
 template <typename T>
@@ -195,12 +199,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
 
-    float acc[4][4];
+    float acc[4][4], tot[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < 4; ++j) acc[i][j] = tot[i][j] = 0.0f;
 
+    static_assert(RT_CHUNK % RT_KC == 0, "chunks end at slice ends");
     for (int64_t k0 = 0; k0 < H; k0 += RT_KC) {
         const int kend = (int)((H - k0) < RT_KC ? (H - k0) : RT_KC);
         for (int idx = tid; idx < RT_TOK * RT_KC; idx += 256) {
@@ -226,6 +231,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x
                 }
             }
         }
+        if ((k0 + RT_KC) % RT_CHUNK == 0 || k0 + RT_KC >= H) {   // a chunk ends: add its sums
+            const bool first = k0 < RT_CHUNK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    tot[i][j] = first ? acc[i][j] : tot[i][j] + acc[i][j];
+                    acc[i][j] = 0.0f;
+                }
+        }
         __syncthreads();
     }
 
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x
     for (int i = 0; i < 4; ++i) {
         const int64_t t = t0 + wave * 4 + i;
         if (t >= T_) break;
-        select_topk<4>(acc[i], t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
+        select_topk<4>(tot[i], t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
     }
 }
 
@@ -367,7 +382,9 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     load(0, RM_STAGES);
     __syncthreads();
 
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f}, tot = acc;
+    constexpr int SPC = RT_CHUNK / RM_KC;   // slices per chunk of the score
+    static_assert(RT_CHUNK % RM_KC == 0, "chunks end at slice ends");
     const unsigned char *wrow0 = &wl[0][(sl * 64 + lane) * RM_ROW];
     const unsigned char *xrow0 = &xl[0][(ch * 4 + (lane & 3)) * RM_ROW];
     const int nsl_pad = (nsl + RM_STAGES - 1) / RM_STAGES * RM_STAGES;
@@ -396,6 +413,11 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
                     wv = wn;
                     xa = xan;
                 }
+                if ((slc + 1) % SPC == 0 || slc + 1 == nsl) {   // a chunk ends: add its sums
+                    if (slc < SPC) tot = acc;
+                    else tot = tot + acc;
+                    acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                }
             }
             // slice slc+1 (loaded RM_STAGES slices ago) into the other buffer
 #pragma unroll
@@ -406,7 +428,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     }
     // lane l, value i: score of token 4 ch + i for expert 64 sl + l
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[ch * 4 + i][sl * 64 + lane] = acc[i];
+    for (int i = 0; i < 4; ++i) lg[ch * 4 + i][sl * 64 + lane] = tot[i];
     __syncthreads();
     for (int tt = wave; tt < XROWS; tt += 8) {
         const int64_t t = tb + tt;
@@ -446,53 +468,76 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     }
 }
 
-// Vector-ALU router for few tokens.  A wavefront owns TPW tokens and one
-// slice of 64 experts: lane l runs the TPW fma chains of expert 64 sl + l
-// (v_fma_f32 is exactly the chain's fmaf), so every W_g value a lane loads
-// feeds TPW chains.  The block first widens its tokens' rows of x into LDS
-// (fp32); the chains then take them as broadcast LDS reads issued XP steps
-// ahead, while each lane streams its expert's bf16 W_g row D steps of 8
-// values ahead and widens it in registers.  The S waves of a block cover all
-// experts of the same tokens.  With few tokens the router is bound by one
-// wave's issue of its H-long chain, so a step holds as few instructions as it
-// can: 8 fmas, 8 widening ops, one W load at a fixed offset from the row
-// base, two LDS reads.  (The fp32 copy of W_g would double the load
-// instructions; the bf16 rows are faster here.)
+// Vector-ALU router for few tokens.  A wavefront owns TPW tokens, one slice
+// of 64 experts and a run of the score's 512-index chunks: lane l runs the TPW
+// fma chains of expert 64 sl + l over those chunks (v_fma_f32 is exactly the
+// chain's fmaf), so every W_g value a lane loads feeds TPW chains.  With few
+// tokens the router is bound by one wave's issue of its chain, so the chunks
+// of a score can be spread over CW waves (the launch's choice, up to 8 / S)
+// that run side by side; their chunk sums meet in LDS and are added in chunk
+// order.  That pays only with PACKED W_g ([H/8][E][8], a wave's step one
+// contiguous kilobyte): read from the [E][H] rows every lane's 16-byte step
+// lies on its own cache line, and more waves streaming rows at once slow the
+// loads down more than the shorter chains gain (so the launch takes CW = 1).
+// The block first widens its tokens' rows of x into LDS (fp32); the chains
+// then take them as broadcast LDS reads issued XP steps ahead, while each lane
+// streams its expert's bf16 W_g values D steps of 8 ahead and widens them in
+// registers.  A step holds as few instructions as it can: 8 fmas, 8 widening
+// ops, one W load at a fixed offset from the pass base, two LDS reads.  (The
+// fp32 copy of W_g would double the load instructions; the bf16 rows are
+// faster here.)
 //
-// With xq != nullptr the block has one more wave, which quantises the staged
-// token rows (per-token int8 codes and scale, the same arithmetic as the
-// quantisation kernels) while the other waves run their chains.
-template <int S, int TPW>
-__global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t *__restrict__ x,
-                                                                  const uint16_t *__restrict__ wg, int64_t T_,
-                                                                  int64_t H, int E, int k, int renorm,
-                                                                  int32_t *__restrict__ ids, float *__restrict__ wout,
-                                                                  float *__restrict__ logits_out,
-                                                                  int8_t *__restrict__ xq, float *__restrict__ sx)
+// Waves: S * CW chain waves (wave w: slice w % S, chunk run w / S), then, with
+// xq != nullptr, one more that quantises the staged token rows (per-token int8
+// codes and scale, the same arithmetic as the quantisation kernels) while the
+// others run their chains.
+namespace {
+constexpr int RV_MAX_CHUNKS = 16;   // H <= 8192
+constexpr int RV_STEPS_PER_CHUNK = RT_CHUNK / 8;
+}
+
+template <int S, int TPW, bool PACKED>
+__global__ __launch_bounds__(576) void route_valu_kernel(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
+                                                         int E, int k, int renorm, int CW,
+                                                         int32_t *__restrict__ ids, float *__restrict__ wout,
+                                                         float *__restrict__ logits_out, int8_t *__restrict__ xq,
+                                                         float *__restrict__ sx)
 {
     constexpr int D = 16;   // W_g steps (8 values each) in flight per lane
     constexpr int XP = 2;   // x steps read ahead from LDS
+    static_assert(RV_STEPS_PER_CHUNK % D == 0, "passes end at chunk ends");
     // [TPW][H] fp32, plus the XP * 8 floats that the read-ahead past the last row touches
     extern __shared__ __attribute__((aligned(16))) float xs[];
-    __shared__ float lg[TPW][64 * S + 1];
+    __shared__ float lg[RV_MAX_CHUNKS][TPW][64 * S + 1];   // chunk sums
     __shared__ __attribute__((aligned(16))) uint32_t tk_scr[S][512];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int e = 64 * wave + lane;
+    const int nchain = S * CW;
+    const int sl = wave % S, run = wave / S;
+    const int e = 64 * sl + lane;
     const int64_t tb = (int64_t)blockIdx.x * TPW;
+    const int nst = (int)(H / 8);
+    const int nch = (nst + RV_STEPS_PER_CHUNK - 1) / RV_STEPS_PER_CHUNK;
+    const int cpw = (nch + CW - 1) / CW;   // chunks per wave
+    const int c_beg = min(nch, run * cpw), c_end = min(nch, c_beg + cpw);
+    const int st_b = c_beg * RV_STEPS_PER_CHUNK, st_e = min(nst, c_end * RV_STEPS_PER_CHUNK);
     // the resource spans W_g exactly: a read past its end (the look-ahead of
-    // the last rows, the lanes past E) returns zeros
+    // the last steps, the lanes past E) returns zeros
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, (int)(E * H * 2), 0x00020000);
-    const uint32_t wrow = e < E ? (uint32_t)((int64_t)e * H * 2) : 0x80000000u;
-    const int nst = (int)(H / 8);
+    // byte offset of this lane's step st: wrow + st * stepb
+    const uint32_t stepb = PACKED ? (uint32_t)E * 16u : 16u;
+    const uint32_t wrow = e < E ? (PACKED ? (uint32_t)e * 16u : (uint32_t)((int64_t)e * H * 2)) : 0x80000000u;
 
     uint4 wr[D];
-    // step st of the row; within a pass the offset is the pass base plus an immediate
-    auto load_w = [&](int slot, uint32_t base, int imm) {
-        wr[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, base, imm, 0));
+    // within a pass the offset is the pass base plus a uniform d * stepb
+    auto load_w = [&](int slot, uint32_t base, uint32_t soff) {
+        wr[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, base, soff, 0));
     };
+    if (wave < nchain) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_w(d, wrow, 16 * d);
+        for (int d = 0; d < D; ++d) load_w(d, wrow + (uint32_t)st_b * stepb, (uint32_t)d * stepb);
+    }
     // x rows into LDS (a token past T stages zeros; its result is never stored)
     for (int64_t i = (int64_t)tid * 8; i < TPW * H; i += (int64_t)blockDim.x * 8) {
         const int t = (int)(i / H);
@@ -503,7 +548,7 @@ __global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t
     }
     __syncthreads();
 
-    if (wave == S) {   // the quantisation wave (present only when xq is given)
+    if (wave == nchain) {   // the quantisation wave (present only when xq is given)
         for (int t = 0; t < TPW && tb + t < T_; ++t) {
             const float *xr = xs + t * H;
             float amax = 0.0f;
@@ -527,7 +572,7 @@ __global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t
             }
         }
     }
-    if (wave >= S) {   // no chain: meet the chain waves at the barrier before the top-k
+    if (wave >= nchain) {   // no chain: meet the chain waves at the barrier before the top-k
         __syncthreads();
         return;
     }
@@ -557,14 +602,22 @@ __global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t
             for (int i = 0; i < 8; ++i) acc[t] = fmaf(x8[i], w8[i], acc[t]);
         }
     };
+    // the sum of the chunk that ends here goes to LDS; the next chain starts at +0
+    auto close_chunk = [&](int c, float acc[TPW]) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            lg[c][t][e] = acc[t];
+            acc[t] = 0.0f;
+        }
+    };
     float acc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = 0.0f;
 #pragma unroll
-    for (int p = 0; p < XP; ++p) load_x(p, p);
-    const int nmain = nst / D * D;
-    for (int st0 = 0; st0 < nmain; st0 += D) {
-        const uint32_t base = wrow + (uint32_t)(st0 + D) * 16u;   // the next pass's steps
+    for (int p = 0; p < XP; ++p) load_x(p, st_b + p);
+    const int nmain = st_b + (st_e - st_b) / D * D;
+    for (int st0 = st_b; st0 < nmain; st0 += D) {
+        const uint32_t base = wrow + (uint32_t)(st0 + D) * stepb;   // the next pass's steps
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             float w8[8];
@@ -574,16 +627,17 @@ __global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t
             for (int t = 0; t < TPW; ++t) xv[t][0] = xr[d % XP][t][0], xv[t][1] = xr[d % XP][t][1];
             load_x(d % XP, st0 + d + XP);   // past the rows it reads the pad (unused)
             chain8(xv, w8, acc);
-            load_w(d, base, 16 * d);   // after the fmas: the slot's registers are free again
+            load_w(d, base, (uint32_t)d * stepb);   // after the fmas: the slot's registers are free again
             // keep each step's loads in place: the scheduler would otherwise batch
             // them at the end of the body, and every pass would wait for them all
             __builtin_amdgcn_sched_barrier(0);
         }
+        if ((st0 + D) % RV_STEPS_PER_CHUNK == 0) close_chunk((st0 + D) / RV_STEPS_PER_CHUNK - 1, acc);
     }
-    // tail: the last nst - nmain (< D) steps; slot d holds step nmain + d
+    // tail: the last st_e - nmain (< D) steps; slot d holds step nmain + d
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        if (nmain + d < nst) {
+        if (nmain + d < st_e) {
             float w8[8];
             widen_w(d, w8);
             float4 xv[TPW][2];
@@ -595,15 +649,22 @@ __global__ __launch_bounds__(64 * (S + 1)) void route_valu_kernel(const uint16_t
             chain8(xv, w8, acc);
         }
     }
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) lg[t][e] = acc[t];
+    if (st_e > st_b && st_e % RV_STEPS_PER_CHUNK != 0) close_chunk(c_end - 1, acc);   // the short last chunk
     __syncthreads();
+    if (wave >= S) return;
     for (int tt = wave; tt < TPW; tt += S) {
         const int64_t t = tb + tt;
         if (t >= T_) break;
         float l4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? lg[tt][lane + 64 * j] : 0.0f;
+        for (int j = 0; j < 4; ++j) {
+            float v = 0.0f;
+            if (j < S) {
+                v = lg[0][tt][lane + 64 * j];
+                for (int c = 1; c < nch; ++c) v = v + lg[c][tt][lane + 64 * j];
+            }
+            l4[j] = v;
+        }
         select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[wave]);
     }
 }
@@ -617,6 +678,26 @@ __global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t *__restr
         load8_f32(src + i, v);
         store8(dst + i, v);
     }
+}
+
+// [E][H] -> [H/8][E][8]: thread i copies the 16-byte piece (j, e) = (i / E, i % E)
+__global__ __launch_bounds__(256) void pack_router_kernel(const uint16_t *__restrict__ src, int E, int64_t H,
+                                                          uint16_t *__restrict__ dst)
+{
+    const int64_t n = H / 8 * E;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t j = i / E, e = i % E;
+        *reinterpret_cast<uint4 *>(dst + i * 8) = *reinterpret_cast<const uint4 *>(src + e * H + j * 8);
+    }
+}
+
+hipError_t launch_pack_router(const uint16_t *wg, int E, int64_t H, uint16_t *dst, hipStream_t st)
+{
+    const int64_t n = H / 8 * E;
+    if (n == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(pack_router_kernel, dim3((unsigned)blocks), dim3(256), 0, st, wg, E, H, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_widen_bf16(const uint16_t *src, int64_t n, float *dst, hipStream_t st)
@@ -640,7 +721,7 @@ bool route_fuses_quant(int dtype, int64_t, int64_t, int) { return dtype == 0; }
 
 hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const float *wg_f32, int64_t T,
                              int64_t H, int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
-                             hipStream_t st, int8_t *xq, float *sx)
+                             hipStream_t st, int8_t *xq, float *sx, const uint16_t *wg_packed)
 {
     if (T == 0) return hipSuccess;
     if (dtype == 0) {
@@ -648,17 +729,30 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
         const uint16_t *xb = (const uint16_t *)x;
         const void *wp = wg_f32 ? (const void *)wg_f32 : (const void *)wg;
         if (route_valu_path(T, H, E)) {
-            // few tokens: vector-ALU chains over the bf16 W_g, one token per block
+            // few tokens: vector-ALU chains over the bf16 W_g, one token per
+            // block; with the packed W_g the score's chunks are spread over up
+            // to 8 / S waves per slice
             constexpr int TP = 1;
             const size_t lds = ((size_t)TP * H + 16) * sizeof(float);
-            const dim3 blk(64 * (S + (xq ? 1 : 0)));
+            const int nch = (int)((H + RT_CHUNK - 1) / RT_CHUNK);
+            const int cwmax = wg_packed ? std::max(1, 8 / S) : 1;
+            const int cpw = (nch + cwmax - 1) / cwmax;
+            const int CW = (nch + cpw - 1) / cpw;
+            const dim3 blk(64 * (S * CW + (xq ? 1 : 0)));
+            const uint16_t *wv = wg_packed ? wg_packed : wg;
             auto go = [&](auto kern) {
-                hipLaunchKernelGGL(kern, dim3((unsigned)((T + TP - 1) / TP)), blk, lds, st, xb, wg, T, H, E, k,
-                                   renormalize, ids, w, logits, xq, sx);
+                hipLaunchKernelGGL(kern, dim3((unsigned)((T + TP - 1) / TP)), blk, lds, st, xb, wv, T, H, E, k,
+                                   renormalize, CW, ids, w, logits, xq, sx);
             };
-            if (S == 1) go(route_valu_kernel<1, TP>);
-            else if (S == 2) go(route_valu_kernel<2, TP>);
-            else go(route_valu_kernel<4, TP>);
+            if (wg_packed) {
+                if (S == 1) go(route_valu_kernel<1, TP, true>);
+                else if (S == 2) go(route_valu_kernel<2, TP, true>);
+                else go(route_valu_kernel<4, TP, true>);
+            } else {
+                if (S == 1) go(route_valu_kernel<1, TP, false>);
+                else if (S == 2) go(route_valu_kernel<2, TP, false>);
+                else go(route_valu_kernel<4, TP, false>);
+            }
             return hipGetLastError();
         }
         const int64_t nblk = (T + 32 / S - 1) / (32 / S);
