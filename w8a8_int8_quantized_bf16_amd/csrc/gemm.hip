@@ -724,6 +724,12 @@ void grouped_gemm_w4_kernel(GemmArgs a)
     __syncthreads();
 
     const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
+    // 32-row blocks that hold rows of this tile: the fold of an empty block
+    // (the last row tile of a group is usually ragged), the vector work that
+    // bounds this kernel, is skipped (ma is uniform over the block: a scalar
+    // branch); its MFMAs and offset term still run on zero rows (guarding
+    // them too made the 64-row tiles spill)
+    const int ma = (rows + 31) >> 5;
     float so_even[WN];   // -s*o of the even step of the current pair
     for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
 #pragma unroll
@@ -761,8 +767,11 @@ void grouped_gemm_w4_kernel(GemmArgs a)
                 const float sc = gsc[d][f] * 0.0625f;
 #pragma unroll
                 for (int mi = 0; mi < MI; ++mi)
+                    if (mi == 0 || mi < ma) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) accf[mi][f][i] = fmaf((float)acs[mi][f][i], sc, accf[mi][f][i]);
+                        for (int i = 0; i < 16; ++i)
+                            accf[mi][f][i] = fmaf((float)acs[mi][f][i], sc, accf[mi][f][i]);
+                    }
             }
             if ((d & 1) == 0) {
 #pragma unroll

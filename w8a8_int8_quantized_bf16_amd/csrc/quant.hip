@@ -107,7 +107,7 @@ static void launch_typed(const T *x, int64_t rows, int64_t cols, int64_t ld, int
     const int64_t nc = (cols + 511) / 512;
     auto grid = [&](int R) { return dim3((unsigned)((rows + 4 * R - 1) / (4 * R))); };
     if (nc <= 1) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 1, 4>), grid(4), block, 0, st, x, rows, cols, ld, q, scales);
-    else if (nc <= 2) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 2, 2>), grid(2), block, 0, st, x, rows, cols, ld, q, scales);
+    else if (nc <= 2) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 2, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
     else if (nc <= 4) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 4, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
     else if (nc <= 8) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 8, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
     else hipLaunchKernelGGL(quant_rows_kernel<T>, grid(1), block, 0, st, x, rows, cols, ld, q, scales);
