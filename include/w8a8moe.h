@@ -91,9 +91,11 @@ int w8a8_quant_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
 /*
  * MoE router ("Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer,
  * section 3.1: hidden state -> one score per expert -> softmax -> top-k).
- *   logit[t][e] = fp32 fused multiply-add chain over h = 0..H-1 in ascending
- *                 order from +0 of x[t][h] * w_gate[e][h] (bf16 operands widened
- *                 exactly; fp32 x used as is)
+ *   logit[t][e] = sum over the chunks h = 512c .. min(H, 512c + 512) - 1, in
+ *                 ascending c (fp32 adds, the first chunk's sum as the start),
+ *                 of each chunk's fp32 fused multiply-add chain in ascending h
+ *                 from +0 of x[t][h] * w_gate[e][h] (bf16 operands widened
+ *                 exactly; fp32 x used as is); for H <= 512 one chain
  *   topk_ids[t][0..k) = the k largest logits, larger first, equal logits by
  *                 lower expert index
  *   topk_w[t][j]  = softmax probability of topk_ids[t][j]; with renormalize != 0
@@ -108,6 +110,17 @@ int w8a8_quant_act(const void *x, int x_dtype, int64_t rows, int64_t cols, int64
 int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, int64_t H,
                    int E, int k, int renormalize, int32_t *topk_ids, float *topk_w,
                    float *logits_out, void *stream);
+
+/*
+ * The same router with the weight's moe_router_pack copy as well
+ * (w_gate_packed, device, [H/8][E][8] bf16, or NULL for moe_route_topk's
+ * behaviour): with bf16 tokens, few-token calls then read it (coalesced, the
+ * chunks of each score on several waves).  The results are identical.  Same
+ * arguments and limits otherwise.
+ */
+int moe_route_topk_packed(const void *x, int x_dtype, const uint16_t *w_gate, const uint16_t *w_gate_packed,
+                          int64_t T, int64_t H, int E, int k, int renormalize, int32_t *topk_ids,
+                          float *topk_w, float *logits_out, void *stream);
 
 /*
  * The router weight widened once to fp32 for the layer (w8a8_moe_weights

@@ -24,7 +24,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
               "w8a8_moe_layer", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm", "w8a8_linear",
               "w8a8_linear_q", "w8a8_linear_workspace_size", "w8a8_linear_q_workspace_size"):
@@ -70,6 +70,11 @@ def test_route_rejects(L):
     assert L.moe_route_topk(FAKE, 0, FAKE, 8, 64, 8, 2, 1, MIS, FAKE, None, s) == ALIGN
     assert L.moe_route_topk(FAKE, 2, FAKE, 8, 64, 8, 2, 1, FAKE, FAKE, None, s) == INVALID  # dtype
     assert L.moe_route_topk(None, 0, None, 0, 64, 8, 2, 1, None, None, None, s) == OK
+    # the variant with the packed copy: the same checks, and that copy's alignment
+    assert L.moe_route_topk_packed(FAKE, 0, FAKE, FAKE, 8, 72, 8, 2, 1, FAKE, FAKE, None, s) == SHAPE
+    assert L.moe_route_topk_packed(FAKE, 0, FAKE, FAKE, 8, 64, 8, 9, 1, FAKE, FAKE, None, s) == INVALID
+    assert L.moe_route_topk_packed(FAKE, 0, FAKE, MIS, 8, 64, 8, 2, 1, FAKE, FAKE, None, s) == ALIGN
+    assert L.moe_route_topk_packed(None, 0, None, None, 0, 64, 8, 2, 1, None, None, None, s) == OK
 
 
 def test_permute_rejects(L):

@@ -198,16 +198,21 @@ def test_route_shapes(T, H, E, k, xdt):
     vector-ALU router, more take the matrix-core one: both sides of that
     switch are here, with hidden sizes that leave a tail of W_g steps, and
     hidden sizes of 1 to 16 chunks of 512 (short last chunks included), which
-    the vector-ALU router spreads over 1 to 8 waves per expert slice."""
+    the vector-ALU router spreads over 1 to 8 waves per expert slice.  Each
+    case runs with the [E][H] weight and with its packed copy (with bf16
+    tokens and few of them: the chunk-parallel kernel)."""
     rng = np.random.default_rng(T * 1000 + E)
     x = rng.standard_t(4, (T, H)).astype(np.float32)
     xa = synth.f32_to_bf16_bits(x) if xdt == "bf16" else x
     wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
-    ids, w, logits = w8.route_topk(to_dev(xa), dev_bf16(wg), k, True, return_logits=True)
     oids, ow, ologits = oracle.route_topk(xa, wg, k)
-    assert np.array_equal(to_host(logits), ologits)
-    assert np.array_equal(to_host(ids), oids)
-    assert np.abs(to_host(w) - ow).max() <= 2e-6
+    wgd = dev_bf16(wg)
+    # the [E][H] weight, then its packed copy (the few-token kernel's other path)
+    for packed in (None, w8.router_pack(wgd)):
+        ids, w, logits = w8.route_topk(to_dev(xa), wgd, k, True, return_logits=True, w_gate_packed=packed)
+        assert np.array_equal(to_host(logits), ologits)
+        assert np.array_equal(to_host(ids), oids)
+        assert np.abs(to_host(w) - ow).max() <= 2e-6
 
 
 @pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_30b_decode_T64", "moe_235b_zipf_T8192"])

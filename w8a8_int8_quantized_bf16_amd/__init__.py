@@ -60,6 +60,7 @@ def lib():
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_quant_act.argtypes = [P, i32, i64, i64, i64, P, P, P]
     L.moe_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, P]
+    L.moe_route_topk_packed.argtypes = [P, i32, P, P, i64, i64, i32, i32, i32, P, P, P, P]
     L.moe_router_widen.argtypes = [P, i32, i64, P, P]
     L.moe_router_pack.argtypes = [P, i32, i64, P, P]
     L.w8a8_linear_workspace_size.argtypes = [i64, i64, i64]
@@ -157,8 +158,9 @@ def quant_act(x):
     return q, s
 
 
-def route_topk(x, w_gate, k, renormalize=True, return_logits=False):
-    """Router: (ids int32 [T,k], weights fp32 [T,k][, logits fp32 [T,E]])."""
+def route_topk(x, w_gate, k, renormalize=True, return_logits=False, w_gate_packed=None):
+    """Router: (ids int32 [T,k], weights fp32 [T,k][, logits fp32 [T,E]]).
+    w_gate_packed: optional router_pack() copy of w_gate (same results)."""
     _need(x, "x", dim=2)
     _need(w_gate, "w_gate", torch.bfloat16, 2)
     T, H = x.shape
@@ -166,8 +168,14 @@ def route_topk(x, w_gate, k, renormalize=True, return_logits=False):
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
-    _check(lib().moe_route_topk(_p(x), _act_dtype(x), _p(w_gate), T, H, E, k, int(bool(renormalize)), _p(ids),
-                                _p(w), _p(logits), _stream(x.device)), "moe_route_topk")
+    if w_gate_packed is None:
+        _check(lib().moe_route_topk(_p(x), _act_dtype(x), _p(w_gate), T, H, E, k, int(bool(renormalize)), _p(ids),
+                                    _p(w), _p(logits), _stream(x.device)), "moe_route_topk")
+    else:
+        _need(w_gate_packed, "w_gate_packed", torch.bfloat16, 3)
+        _check(lib().moe_route_topk_packed(_p(x), _act_dtype(x), _p(w_gate), _p(w_gate_packed), T, H, E, k,
+                                           int(bool(renormalize)), _p(ids), _p(w), _p(logits), _stream(x.device)),
+               "moe_route_topk_packed")
     return (ids, w, logits) if return_logits else (ids, w)
 
 

@@ -309,6 +309,18 @@ int moe_route_topk(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T
                                         (hipStream_t)stream));
 }
 
+int moe_route_topk_packed(const void *x, int x_dtype, const uint16_t *w_gate, const uint16_t *w_gate_packed,
+                          int64_t T, int64_t H, int E, int k, int renormalize, int32_t *topk_ids, float *topk_w,
+                          float *logits_out, void *stream)
+{
+    int rc = check_route(x, x_dtype, w_gate, T, H, E, k, topk_ids, topk_w, logits_out);
+    if (rc) return rc;
+    if (w_gate_packed && !aligned16(w_gate_packed)) return W8A8_ERR_ALIGNMENT;
+    if (T == 0) return W8A8_OK;
+    return hip_status(launch_route_topk(x, x_dtype, w_gate, nullptr, T, H, E, k, renormalize, topk_ids, topk_w,
+                                        logits_out, (hipStream_t)stream, nullptr, nullptr, w_gate_packed));
+}
+
 int moe_router_widen(const uint16_t *w_gate, int E, int64_t H, float *w_gate_f32, void *stream)
 {
     if (E <= 0 || H <= 0 || !w_gate || !w_gate_f32) return W8A8_ERR_INVALID_ARG;
