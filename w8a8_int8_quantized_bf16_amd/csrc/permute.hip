@@ -183,8 +183,10 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32
     scatter_rounds(ids, P, (int64_t)blockIdx.x * PM_CHUNK, PM_PER_THREAD, E, base, wcnt, sorted_pair, pair_pos);
 }
 
-// P <= PM_SMALL_P: the whole permutation (histogram, offsets, tile tables,
-// stable scatter) in one block, one launch.
+// P <= PM_SMALL_P: the whole permutation in one launch of 1 + tt.n blocks.
+// Every block forms the histogram and offsets of the (at most 4096) ids
+// itself; block 0 then stores the offsets and scatters the pairs, block
+// 1 + j builds tile table j, side by side.
 __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t *__restrict__ ids, int64_t P, int E,
                                                                    int32_t *__restrict__ offsets,
                                                                    int32_t *__restrict__ sorted_pair,
@@ -215,14 +217,21 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(const int32_t
     __syncthreads();
     int all;
     const int32_t ex = block_excl_scan256(tid < E ? hist[tid] : 0, &wcnt[1][0], &all);
-    if (tid < E) off_l[tid] = offsets[tid] = ex;
+    if (tid < E) {
+        off_l[tid] = ex;
+        if (blockIdx.x == 0) offsets[tid] = ex;
+    }
     if (tid == 0) {
-        off_l[E] = offsets[E] = (int32_t)P;
+        off_l[E] = (int32_t)P;
+        if (blockIdx.x == 0) offsets[E] = (int32_t)P;
         off_l[E + 1] = (int32_t)P + tt.extra;
     }
-    for (int t = tid; t < tt.extra; t += PM_THREADS) sorted_pair[P + t] = t * tt.k;
     __syncthreads();
-    for (int j = 0; j < tt.n; ++j) build_table(tt, j, off_l, E, pre, &wcnt[2][0], dn, true, tid, PM_THREADS);
+    if (blockIdx.x > 0) {   // one tile table
+        build_table(tt, blockIdx.x - 1, off_l, E, pre, &wcnt[2][0], dn, true, tid, PM_THREADS);
+        return;
+    }
+    for (int t = tid; t < tt.extra; t += PM_THREADS) sorted_pair[P + t] = t * tt.k;
     if (tid < E) base[tid] = off_l[tid];
     scatter_rounds(ids_l, P, 0, (int)((P + PM_THREADS - 1) / PM_THREADS), E, base, wcnt, sorted_pair, pair_pos);
 }
@@ -240,8 +249,8 @@ hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *
     tt.k = k;
     const int64_t P = T * k;
     if (P > 0 && P <= PM_SMALL_P) {
-        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PM_THREADS), 0, st, ids, P, E, offsets, sorted_pair,
-                           pair_pos, tt);
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1 + tt.n), dim3(PM_THREADS), 0, st, ids, P, E, offsets,
+                           sorted_pair, pair_pos, tt);
         return hipGetLastError();
     }
     const int64_t nch = pm_chunks(P);
