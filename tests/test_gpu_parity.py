@@ -268,6 +268,7 @@ def _groups(rng, sizes):
     ([3] * 40, 256, 2048, 2),                 # decode-like: tiny groups
     ([60, 70, 0, 45], 272, 1040, 0),          # N tail, mid-size groups
     ([300, 129, 1000], 512, 384, 8),          # large groups
+    ([257, 200, 33, 384], 256, 512, 0),       # 128-row tiles whose last one holds 1, 72 or 33 rows
     ([17], 16, 16, 0),                        # minimum sizes
 ])
 def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather, packed):
@@ -661,10 +662,12 @@ def _w4_problem(G, N, K, counts, seed, A_rows=None):
 @pytest.mark.parametrize("G,N,K,counts,gather,epi,od", [
     (3, 64, 304, [7, 0, 33], False, 1, "f32"), (3, 128, 256, [5, 70, 1], True, 2, "bf16"),
     (2, 64, 64, [16, 16], False, 2, "f32"), (16, 1536, 2048, [128] * 16, True, 2, "bf16"),
-    (128, 1536, 2048, [4] * 128, True, 2, "bf16"), (8, 2048, 768, [40] * 8, False, 1, "bf16")])
+    (128, 1536, 2048, [4] * 128, True, 2, "bf16"), (8, 2048, 768, [40] * 8, False, 1, "bf16"),
+    (4, 256, 512, [100, 33, 64, 1], True, 2, "bf16"), (4, 256, 512, [100, 33, 64, 1], False, 1, "f32")])
 def test_w4a8_grouped_gemm(G, N, K, counts, gather, epi, od):
     """The W4A8 GEMM through the C ABI against the oracle (32- and 64-row
-    tiles, ragged and empty groups, gathered rows, both epilogues)."""
+    tiles, ragged and empty groups, 64-row tiles holding 1 to 36 rows,
+    gathered rows, both epilogues)."""
     M = int(sum(counts))
     k = 4
     A, sa, q, s, o, off = _w4_problem(G, N, K, counts, G + N + K, A_rows=(M + k - 1) // k if gather else M)
