@@ -123,7 +123,8 @@ def get_case(name, seed=0):
 
 @pytest.mark.parametrize("rows,cols,dtype,scale", [
     (1, 16, "bf16", 1.0), (5, 48, "f32", 3.0), (37, 1040, "bf16", 0.01), (16, 64, "f32", 1.0),
-    (300, 2048, "bf16", 5.0), (3, 4096, "f32", 1e-3), (64, 768, "bf16", 100.0)])
+    (300, 2048, "bf16", 5.0), (3, 4096, "f32", 1e-3), (64, 768, "bf16", 100.0), (9, 768, "f32", 0.5),
+    (33, 1536, "f32", 2.0), (70, 1536, "bf16", 30.0)])
 def test_quant_act_bit_exact(rows, cols, dtype, scale):
     rng = np.random.default_rng(rows * 7 + cols)
     x = (rng.standard_t(4, (rows, cols)) * scale).astype(np.float32)

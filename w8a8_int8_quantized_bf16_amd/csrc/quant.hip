@@ -99,6 +99,62 @@ __global__ __launch_bounds__(256) void quant_rows_reg_kernel(const T *__restrict
     }
 }
 
+// Rows of 256 * G4 columns with G4 not a power of two (768, 1536: the
+// models' expert widths), where 512-wide stripes would leave lanes idle: lane
+// l holds the 4-value groups l + 64 g (g < G4), contiguous across the wave.
+// Same arithmetic per element as the stripe kernel.
+template <typename T>
+__device__ __forceinline__ void load4_f32(const T *p, float v[4]);
+template <>
+__device__ __forceinline__ void load4_f32<uint16_t>(const uint16_t *p, float v[4])
+{
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void load4_f32<float>(const float *p, float v[4])
+{
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+}
+
+template <typename T, int G4>
+__global__ __launch_bounds__(256) void quant_rows_g4_kernel(const T *__restrict__ x, int64_t rows, int64_t ld,
+                                                            int8_t *__restrict__ q, float *__restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    constexpr int64_t cols = 256 * G4;
+    float v[G4][4];
+#pragma unroll
+    for (int g = 0; g < G4; ++g) load4_f32<T>(x + r * ld + 4 * (lane + 64 * g), v[g]);
+    float amax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[g][i]));
+    amax = wave_max_nonneg(amax);
+    const float s = amax / 127.0f;
+    const float y = s > 0.0f ? 1.0f / s : 0.0f;
+    const bool fast = s >= QUANT_FAST_MIN_SCALE;
+    if (lane == 0) scales[r] = s;
+#pragma unroll
+    for (int g = 0; g < G4; ++g) {
+        uint32_t c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = fast ? quant_code_fma(v[g][i], s, y) : quant_code(v[g][i], s);
+        *reinterpret_cast<uint32_t *>(q + r * cols + 4 * (lane + 64 * g)) =
+            s != 0.0f ? pack_low_bytes(c[0], c[1], c[2], c[3]) : 0u;
+    }
+}
+
 template <typename T>
 static void launch_typed(const T *x, int64_t rows, int64_t cols, int64_t ld, int8_t *q, float *scales,
                          hipStream_t st)
@@ -106,6 +162,14 @@ static void launch_typed(const T *x, int64_t rows, int64_t cols, int64_t ld, int
     dim3 block(256);
     const int64_t nc = (cols + 511) / 512;
     auto grid = [&](int R) { return dim3((unsigned)((rows + 4 * R - 1) / (4 * R))); };
+    if (cols == 768 && ld % 4 == 0) {
+        hipLaunchKernelGGL((quant_rows_g4_kernel<T, 3>), grid(1), block, 0, st, x, rows, ld, q, scales);
+        return;
+    }
+    if (cols == 1536 && ld % 4 == 0) {
+        hipLaunchKernelGGL((quant_rows_g4_kernel<T, 6>), grid(1), block, 0, st, x, rows, ld, q, scales);
+        return;
+    }
     if (nc <= 1) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 1, 4>), grid(4), block, 0, st, x, rows, cols, ld, q, scales);
     else if (nc <= 2) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 2, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
     else if (nc <= 4) hipLaunchKernelGGL((quant_rows_reg_kernel<T, 4, 1>), grid(1), block, 0, st, x, rows, cols, ld, q, scales);
