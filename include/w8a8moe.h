@@ -16,7 +16,10 @@
  *      GEMMs against static per-output-channel symmetric int8 weights
  *      (group_0 "weights" of the same walkthrough), with a per-token x
  *      per-channel dequantisation and SwiGLU;
- *   5. the expert outputs are summed with the routing weights.
+ *   5. each token's output is the sum of its k selected experts' outputs,
+ *      weighted by their routing weights (the same explainer, section 3.1:
+ *      the top-k experts the router picks are the ones that take part in the
+ *      token's forward pass).
  *
  * Conventions shared by every call
  *   - Every pointer argument named as device memory is a device pointer owned
@@ -288,7 +291,9 @@ int w8a8_linear_q(const int8_t *xq, const float *x_scales, int64_t M, int64_t K,
                   void *stream);
 
 /*
- * Weighted combine of the expert outputs:
+ * Weighted combine of the expert outputs ("Qwen3-30B-A3B-Instruct-2507-
+ * quantized.w8a8" explainer, section 3.1: only the top-k experts the router
+ * picks take part in a token's forward pass, weighted by its scores):
  *   out[t][n] = sum_{j<k} topk_w[t][j] * y[pair_pos[t*k+j]][n]
  * accumulated in fp32 in slot order, then rounded once to out_dtype.
  *   y device [T*k][H] y_dtype;  topk_w device [T][k];  pair_pos device [T*k]
@@ -330,7 +335,10 @@ int moe_combine(const void *y, int y_dtype, const float *topk_w, const int32_t *
  *   times its output after the k routed slots; the logit is an fp32 sum.
  *   A shared expert with W4A8 routed gate_up weights is not supported
  *   (W8A8_ERR_UNSUPPORTED_SHAPE).
- * H % 16 == 0, I % 32 == 0.
+ * H % 16 == 0, I % 32 == 0.  32-bit byte offsets address the operands, so
+ * T * H * 4, E * H * 2 (E * H * 4 with w_gate_f32), T * k * I and one
+ * expert's packed weights must stay below 2^31; larger layers return
+ * W8A8_ERR_UNSUPPORTED_SHAPE.
  */
 typedef struct {
     int E, k;
@@ -352,7 +360,12 @@ typedef struct {
 } w8a8_moe_weights;
 
 /*
- * The whole layer: route -> quantise x -> permute -> gate_up GEMM + SwiGLU ->
+ * The whole layer ("Qwen3-30B-A3B-Instruct-2507-quantized.w8a8" explainer,
+ * sections 2 and 3.1: a bf16 router picks the top-k experts of each token,
+ * whose int8 gate/up/down Linears run on per-token int8 activations, and the
+ * token's output sums their outputs with the routing weights; the steps and
+ * their sources are listed at the top of this header):
+ * route -> quantise x -> permute -> gate_up GEMM + SwiGLU ->
  * quantise h -> down GEMM -> combine, all launched on `stream` (with a shared
  * expert, its GEMMs and h quantisation run in the same stages as the routed
  * ones and the combine adds its gated output).
@@ -365,7 +378,7 @@ int w8a8_moe_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
- * The same layer, recording `n_events` (<= W8A8_LAYER_STAGES + 1) hipEvent_t
+ * The same layer (same sources), recording `n_events` (<= W8A8_LAYER_STAGES + 1) hipEvent_t
  * handles on `stream`: events[0] before the first stage and events[i] after
  * stage i, stages in the order route, quantise x, permute, gate_up GEMM,
  * quantise h, down GEMM, combine.  A null entry skips that mark, so a caller
@@ -380,7 +393,8 @@ int w8a8_moe_layer_events(const w8a8_moe_weights *W, const void *x, int x_dtype,
                           void *const *events, int n_events);
 
 /*
- * Pointers into the layer workspace of the intermediate results of the last
+ * Pointers into the layer workspace (the layer's steps, see w8a8_moe_layer)
+ * of the intermediate results of the last
  * call with the same (W, T, x_dtype, ws): ids [T][k] i32, w [T][k] f32,
  * xq [T][H] i8, sx [T] f32, offsets [E+1] i32, sorted_pair / pair_pos [T*k] i32,
  * h [T*k][I] bf16, hq [T*k][I] i8, sh [T*k] f32,

@@ -217,6 +217,27 @@ def test_layer_rejects_and_sizes_workspace(L):
     assert L.w8a8_moe_layer_workspace_size(ctypes.byref(big), 8192, 0) > 8192 * 8 * 4096 * 2
 
 
+def test_layer_rejects_router_offsets_beyond_32_bits(L):
+    """The router kernels address token rows (T*H*4 bytes at most) and the
+    router weight (E*H*2 bytes, E*H*4 for its fp32 copy) with 32-bit offsets:
+    the layer returns SHAPE for larger inputs, as moe_route_topk does, instead
+    of routing the far tokens wrongly."""
+    s = None
+    huge = 1 << 62
+    W = _weights(E=8, k=1, H=4096, I=32)
+    T = (1 << 31) // (4 * 4096) + 1            # T*H*4 just above 2^31, T*H below 2^31
+    assert T * 4096 < (1 << 31)
+    assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 0, T, FAKE, FAKE, huge, s) == SHAPE
+    assert L.moe_route_topk(FAKE, 0, FAKE, T, 4096, 8, 1, 1, FAKE, FAKE, None, s) == SHAPE
+    # one token below the bound passes the shape checks (the workspace check follows)
+    assert L.w8a8_moe_layer(ctypes.byref(W), FAKE, 0, T - 2, FAKE, FAKE, 0, s) == WS_SMALL
+    # the router weight: E*H*2 bytes fit, its fp32 copy's E*H*4 do not
+    Wr = _weights(E=256, k=2, H=1 << 21, I=32)
+    assert L.w8a8_moe_layer(ctypes.byref(Wr), FAKE, 0, 1, FAKE, FAKE, 0, s) == WS_SMALL
+    Wr.w_gate_f32 = FAKE.value
+    assert L.w8a8_moe_layer(ctypes.byref(Wr), FAKE, 0, 1, FAKE, FAKE, huge, s) == SHAPE
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(w8, "_lib", None)
     monkeypatch.setattr(w8, "LIB_PATH", "/nonexistent/libw8a8moe.so")

@@ -112,6 +112,11 @@ int check_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T
         (int64_t)packed_weights_bytes(1, W->H, W->I) > INT32_MAX - 256 || T * W->k * W->I > INT32_MAX - 256 ||
         T * W->H > INT32_MAX - 256)
         return W8A8_ERR_UNSUPPORTED_SHAPE;
+    // the router kernels the layer launches address the token rows (up to fp32
+    // wide) and the router weight (bf16, or its fp32 copy) the same way: the
+    // bounds of moe_route_topk
+    if (T * W->H * 4 > INT32_MAX - 256 || (int64_t)W->E * W->H * (W->w_gate_f32 ? 4 : 2) > INT32_MAX - 256)
+        return W8A8_ERR_UNSUPPORTED_SHAPE;
     const bool w4 = W->w4_gate_up != nullptr;
     if (w4 && ((int64_t)packed_w4_bytes(1, 2 * W->I, W->H) > INT32_MAX - 256 ||
                2 * W->I * ((W->H + 127) / 128) * 4 > INT32_MAX - 256))
