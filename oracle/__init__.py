@@ -48,6 +48,7 @@ def lib():
         P, i64, i32, d = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
         L.oracle_quant_rows.argtypes = [P, i32, i64, i64, i64, P, P]
         L.oracle_route_topk.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P]
+        L.oracle_route_topk_chunked.argtypes = [P, i32, P, i64, i64, i32, i32, i32, P, P, P, i64]
         L.oracle_permute.argtypes = [P, i64, i32, i32, P, P, P]
         L.oracle_grouped_gemm.argtypes = [P, P, P, i32, P, P, P, i32, i64, i64, i32, i32, P]
         L.oracle_combine.argtypes = [P, i32, P, P, i64, i32, i64, P, i32]
@@ -111,8 +112,13 @@ def quant_rows(x):
     return q, s
 
 
-def route_topk(x, wg, k, renormalize=True):
-    """Router: returns ids [T,k] int32, w [T,k] fp32, logits [T,E] fp32."""
+ROUTE_CHUNK = 512   # R6: hidden indices per fma chain of a router score
+
+
+def route_topk(x, wg, k, renormalize=True, chunk=ROUTE_CHUNK):
+    """Router: returns ids [T,k] int32, w [T,k] fp32, logits [T,E] fp32.
+    chunk: hidden indices per fma chain (R6's 512; 0 for one chain over all
+    of H, a study of how the order moves the selection, not the layer's)."""
     x = np.ascontiguousarray(x)
     wg = _c(wg, np.uint16)
     T, H = x.shape
@@ -121,8 +127,8 @@ def route_topk(x, wg, k, renormalize=True):
     ids = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
     logits = np.empty((T, E), np.float32)
-    lib().oracle_route_topk(_p(x), _xdtype(x), _p(wg), T, H, E, k, int(bool(renormalize)),
-                            _p(ids), _p(w), _p(logits))
+    lib().oracle_route_topk_chunked(_p(x), _xdtype(x), _p(wg), T, H, E, k, int(bool(renormalize)),
+                                    _p(ids), _p(w), _p(logits), int(chunk))
     return ids, w, logits
 
 

@@ -207,10 +207,15 @@ void oracle_quant_rows(const void *x, int dtype, int64_t rows, int64_t cols, int
 /* R6: hidden indices per chain of the router score */
 #define OR_ROUTE_CHUNK 512
 
-void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H,
-                       int E, int k, int renormalize, int32_t *ids, float *w, float *logits)
+/* The router with chains of `chunk` hidden indices (R6 is chunk = 512; a
+ * chunk <= 0 or >= H gives the single fma chain over all of h, kept to study
+ * how far the choice of order moves the selected experts). */
+void oracle_route_topk_chunked(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H,
+                               int E, int k, int renormalize, int32_t *ids, float *w, float *logits,
+                               int64_t chunk)
 {
     int64_t t;
+    if (chunk <= 0 || chunk > H) chunk = H;
 #pragma omp parallel for schedule(static)
     for (t = 0; t < T; ++t) {
         float *l = (float *)malloc(sizeof(float) * (size_t)E);
@@ -220,8 +225,8 @@ void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, 
                                         : (const void *)((const float *)x + t * H);
         for (int e = 0; e < E; ++e) {
             float total = 0.0f;
-            for (int64_t c0 = 0; c0 < H; c0 += OR_ROUTE_CHUNK) {
-                const int64_t c1 = (c0 + OR_ROUTE_CHUNK < H) ? c0 + OR_ROUTE_CHUNK : H;
+            for (int64_t c0 = 0; c0 < H; c0 += chunk) {
+                const int64_t c1 = (c0 + chunk < H) ? c0 + chunk : H;
                 float acc = 0.0f;
                 for (int64_t h = c0; h < c1; ++h)
                     acc = fmaf(or_load(xrow, dtype, h), or_bf16_to_f32(wg[(int64_t)e * H + h]), acc);
@@ -259,6 +264,12 @@ void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, 
         free(p);
         free(taken);
     }
+}
+
+void oracle_route_topk(const void *x, int dtype, const uint16_t *wg, int64_t T, int64_t H,
+                       int E, int k, int renormalize, int32_t *ids, float *w, float *logits)
+{
+    oracle_route_topk_chunked(x, dtype, wg, T, H, E, k, renormalize, ids, w, logits, OR_ROUTE_CHUNK);
 }
 
 /* --------------------------------------------------------------- permute --- */

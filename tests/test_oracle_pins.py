@@ -186,6 +186,37 @@ def test_router_chunk_order_golden(orc):
         assert float(logits[0, 0]) == float(want)
 
 
+@pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_235b_zipf_T8192"])
+def test_router_order_reading_moves_only_near_ties(orc, name):
+    """R6 fixes the router's fp32 summation order (512-index fma chains added in
+    order) because the pages fix none.  Against the other plain reading, one fma
+    chain over all of h, on the full 30B-prefill and 235B router inputs: the two
+    orders round most logits apart in the last bits, and a token's selected
+    experts may differ only where two of its logits lie within the two orders'
+    rounding error of each other (each order is within gamma_H * sum|x_h w_h| of
+    the exact dot product).  On these inputs no token's top-k differs."""
+    cfg = synth.MOE_CONFIGS[name]
+    wg = synth.moe_router(cfg)
+    x = synth.moe_x(cfg, wg_bits=wg)
+    ic, _, lc = orc.route_topk(x, wg, cfg.k)
+    ich, _, lch = orc.route_topk(x, wg, cfg.k, chunk=0)
+    moved = np.nonzero(np.any(ic != ich, axis=1))[0]
+    frac_apart = float(np.mean(lc != lch))
+    print("%s: %d of %d tokens with another top-%d under one chain; %.1f%% of logits differ"
+          % (name, len(moved), cfg.T, cfg.k, 100 * frac_apart))
+    assert frac_apart > 0.5            # the orders are really different
+    if len(moved):
+        xf = (synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x).astype(np.float64)
+        S = np.abs(xf[moved]) @ np.abs(synth.bf16_bits_to_f32(wg).astype(np.float64)).T
+        u = 2.0 ** -24
+        gamma = cfg.H * u / (1 - cfg.H * u)
+        for i, t in enumerate(moved):
+            j = int(np.argmax(ic[t] != ich[t]))
+            a, b = int(ic[t, j]), int(ich[t, j])
+            assert abs(float(lc[t, a]) - float(lc[t, b])) <= 2 * gamma * (S[i, a] + S[i, b])
+    assert len(moved) <= cfg.T // 1000
+
+
 def _tiny_router():
     wg = synth.moe_router(TINY)
     x = synth.moe_x(TINY)
