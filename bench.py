@@ -7,11 +7,19 @@ tokens already resident in HBM.  Weights are quantised once before timing
 (static per-channel weights) and rotated over several copies so that no step
 finds the previous step's weights in the 256 MB last-level cache.
 
-Prints one JSON line.  `value` is tokens/s of the layer; `roofline` describes
+The default workload is the largest MoE layer that fits one GPU, the
+235B-shaped layer (T=8192, H=4096, 128 experts, top-8, I=1536, Zipf(1.1)
+expert loads); the 30B-shaped prefill and decode layers, the shared-expert and
+W4A8 variants and the dense linears are other `--workload` lines.
+
+Prints one JSON line.  `value` is tokens/s of the layer over the timed loop
+(wall clock between synchronisations); `step_ms_p10_p50_p90` are per-step
+times from HIP events at each layer call's start and end; `roofline` describes
 the dominant kernel (the stage with the largest average time in a separate
-pass with a HIP event after every stage; in the timed loop only that stage is
-bracketed by events, on the layer's stream); `cpu_baseline`
-is the CPU oracle timed on a bounded sample of the same tokens.
+pass with a HIP event after every stage; in the timed loop that stage is
+bracketed by events too, on the layer's stream); `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same tokens, with its threads and on
+one thread.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -28,7 +36,7 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5033.0       # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
 RIDGE = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-DEFAULT_WORKLOAD = "moe_30b_prefill_T4096"
+DEFAULT_WORKLOAD = "moe_235b_zipf_T8192"
 
 
 def log(*a):
@@ -152,12 +160,32 @@ def write_traffic(args):
     print(json.dumps(rec))
 
 
-def cpu_baseline(case, target_s):
-    """The CPU oracle, as is, on a bounded sample of the workload's tokens."""
+def cpu_model():
+    """The host CPU's model name and logical core count."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return name, os.cpu_count()
+
+
+def _time_tokens(layer_tokens, case, wq, tok):
+    t0 = time.perf_counter()
+    layer_tokens(case["x"], *wq, tok)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(case, target_s, min_tokens=2048, single_s=6.0):
+    """The CPU oracle, as is, on a bounded sample of the workload's tokens (at
+    least min_tokens of them, or all): once with the oracle's threads, once on
+    a single thread over a smaller sample."""
     import numpy as np
 
     import oracle
-    import synth
     cfg = case["cfg"]
     t0 = time.time()
     qgu, sgu = oracle.quant_rows(case["gu"].reshape(-1, cfg.H))
@@ -173,22 +201,29 @@ def cpu_baseline(case, target_s):
         layer_tokens = oracle.moe_layer_shared_tokens
     log("oracle weight quantisation (untimed setup): %.1f s" % (time.time() - t0))
     rng = np.random.default_rng(0)
-    n = min(32, cfg.T)
+    threads = oracle.num_threads()
+    # a short probe sizes the sample so that the timed run takes about target_s
+    n = min(64, cfg.T)
+    dt = _time_tokens(layer_tokens, case, wq, np.sort(rng.choice(cfg.T, n, replace=False)))
+    n = int(min(cfg.T, max(min(min_tokens, cfg.T), n * target_s / max(dt, 1e-6))))
     tok = np.sort(rng.choice(cfg.T, n, replace=False))
-    t0 = time.perf_counter()
-    layer_tokens(case["x"], *wq, tok)
-    dt = time.perf_counter() - t0
-    n2 = int(min(cfg.T, max(n, n * target_s / max(dt, 1e-6))))
-    if n2 > n:
-        tok = np.sort(rng.choice(cfg.T, n2, replace=False))
-        t0 = time.perf_counter()
-        layer_tokens(case["x"], *wq, tok)
-        dt = time.perf_counter() - t0
-        n = n2
-    del synth
-    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of the %d tokens of %s (the layer couples no tokens), %.1f s of CPU time; "
-                      "weights quantised by the oracle beforehand, untimed" % (n, cfg.T, cfg.name, dt)}
+    dt = _time_tokens(layer_tokens, case, wq, tok)
+    log("oracle, %d threads: %d tokens in %.1f s" % (threads, n, dt))
+    # single thread: the same oracle on fewer tokens
+    oracle.set_num_threads(1)
+    try:
+        n1 = max(1, min(n, int(n / dt / threads * single_s)))
+        tok1 = np.sort(rng.choice(cfg.T, n1, replace=False))
+        dt1 = _time_tokens(layer_tokens, case, wq, tok1)
+    finally:
+        oracle.set_num_threads(threads)
+    log("oracle, 1 thread: %d tokens in %.1f s" % (n1, dt1))
+    model, ncpu = cpu_model()
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d tokens of %s (the layer couples no tokens), %.1f s with %d threads; "
+                      "weights quantised by the oracle beforehand, untimed" % (n, cfg.T, cfg.name, dt, threads),
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "tokens": n1, "seconds": round(dt1, 2)},
+            "cpu_model": model, "logical_cpus": ncpu}
 
 
 def bench_dense(args, cfg):
@@ -294,9 +329,11 @@ def cpu_baseline_dense(cfg, xb, Wf, target_s):
     n2 = int(min(cfg.M, max(n, n * target_s / max(dt, 1e-6))))
     if n2 > n:
         n, dt = n2, run(n2)
+    model, ncpu = cpu_model()
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d of the %d rows of %s (rows are independent), %.1f s of CPU time; weights quantised by "
-                      "the oracle beforehand, untimed" % (n, cfg.M, cfg.name, dt)}
+                      "the oracle beforehand, untimed" % (n, cfg.M, cfg.name, dt),
+            "cpu_model": model, "logical_cpus": ncpu}
 
 
 def bench_ep_shares(args, cfg, ngpu):
@@ -478,9 +515,11 @@ def main():
         for j in range(nst):
             stage_us[j] += evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 / nbr
     dom = int(np.argmax(stage_us))
-    # timed region: the layer with marks only around the dominant stage
+    # timed region: the layer with marks only at its start and end and around
+    # the dominant stage (HIP events on the layer's stream)
     evs = make_events(args.steps)
-    sel = [[row[j] if j in (dom, dom + 1) else None for j in range(nst + 1)] for row in evs]
+    keep = (0, dom, dom + 1, nst)
+    sel = [[row[j] if j in keep else None for j in range(nst + 1)] for row in evs]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -488,6 +527,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     dom_us = sum(evs[i][dom].elapsed_time(evs[i][dom + 1]) for i in range(args.steps)) * 1e3 / args.steps
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(args.steps)])
+    p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
     # After the timed region: the same steps as replays of a HIP graph of
     # `cap` consecutive layer calls (the layer launches kernels only, so it
     # captures whole).  Reported beside the eager rate, as the share of the
@@ -541,6 +582,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_p10_p50_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
+        "tokens_per_s_at_median_step": cfg.T / (p50 * 1e-3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

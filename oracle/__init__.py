@@ -63,6 +63,7 @@ def lib():
         L.oracle_moe_layer_shared_tokens.argtypes = [P, i32, i64, i32, i32, i64, P, P, P, P, P, i64, P, P, P, P, P,
                                                      P, i64, P]
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
         L.oracle_f64_to_bf16.argtypes = [d]
         L.oracle_f64_to_bf16.restype = ctypes.c_uint16
         L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -91,6 +92,12 @@ def _xdtype(x):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's loops over independent rows (results do not
+    depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def f64_to_bf16(v: float) -> int:

@@ -99,6 +99,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads for the OpenMP loops below (n >= 1).  The results do not depend on
+ * it: every row is computed by one thread in the serial order. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ bf16 --- */
 
 /* bf16 is the upper half of an IEEE binary32; widening is exact. */

@@ -3,8 +3,7 @@
 Bit-exact: int8 codes and scales, router scores and expert ids, the
 permutation, int32 accumulators.  Within tolerance: dequantised outputs, routing
 weights and the layer output (max|d| / max|ref| <= 1e-2 and mean |d| <= 1e-3).
-Full-size workloads compare every token where the oracle is fast enough and a
-seeded sample of tokens otherwise (the layer couples no tokens)."""
+Full-size workloads are compared on every token and every grouped row."""
 import time
 
 import numpy as np
@@ -185,6 +184,108 @@ def test_route_ties_lower_index_first():
     assert np.allclose(to_host(w), 1.0 / 3.0, atol=1e-7)
 
 
+def _tie_router(E, H, groups, rng):
+    """Router rows N(0, 0.05) except the rows of each group, which are copies of
+    one all-positive row (scaled down group by group), so that on tokens with
+    a positive mean every group's logits are equal and rank above the rest."""
+    w = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    base = (0.05 * (1.0 + 0.1 * rng.standard_normal(H))).astype(np.float32)
+    for gi, rows in enumerate(groups):
+        w[rows] = base * np.float32(1.0 - 0.2 * gi)
+    return synth.f32_to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("E,groups", [
+    (128, [[5, 69], [63, 64]]),                          # equal rows in both 64-expert slices, and astride them
+    (256, [[5, 69, 133, 197], [63, 64, 127, 128, 191, 192]]),   # four slices; the 8th slot falls inside a tie
+    (128, [[3, 60, 63, 64, 65, 100, 127, 126, 90, 64 + 3]]),     # one tie of 10 rows for 8 slots
+    (256, [[255, 200, 130, 129, 66, 65, 2, 1, 0, 190]]),
+])
+@pytest.mark.parametrize("T", [16, 1024])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_route_exact_ties_across_slices(E, groups, T, xdt):
+    """Exact ties of router scores (duplicated router rows give bit-identical
+    fma chains) between experts in different 64-expert slices and at the top-k
+    threshold: ids bit-exact with the oracle, equal scores ordered by the lower
+    expert index.  T = 16 runs the few-token vector-ALU router, T = 1024 with
+    bf16 tokens the matrix-core one, fp32 tokens the vector-fma one; each with
+    and without the packed router copy."""
+    H, k = 2048, 8
+    rng = np.random.default_rng(E + T + len(groups))
+    x = (rng.standard_t(4, (T, H)) + 0.5).astype(np.float32)
+    xa = synth.f32_to_bf16_bits(x) if xdt == "bf16" else x
+    wg = _tie_router(E, H, groups, rng)
+    oids, ow, ologits = oracle.route_topk(xa, wg, k)
+    want_top = sorted(groups[0])[:k]
+    wgd = dev_bf16(wg)
+    for packed in (None, w8.router_pack(wgd)):
+        ids, w, logits = w8.route_topk(to_dev(xa), wgd, k, True, return_logits=True, w_gate_packed=packed)
+        lg = to_host(logits)
+        for rows in groups:
+            for r in rows[1:]:
+                assert np.array_equal(lg[:, rows[0]], lg[:, r])
+        assert np.array_equal(lg, ologits)
+        got = to_host(ids)
+        assert np.array_equal(got, oids)
+        assert np.abs(to_host(w) - ow).max() <= 2e-6
+        # the first group ranks on top for every token: its lowest indices, in order
+        n0 = min(k, len(groups[0]))
+        assert np.all(got[:, :n0] == np.array(want_top[:n0]))
+
+
+def test_route_all_zero_router_matrix_core():
+    """An all-zero router at E = 128 with 1024 tokens (the matrix-core router):
+    every score is +0, every token selects experts 0..7 in order, weights 1/8."""
+    rng = np.random.default_rng(9)
+    x = synth.f32_to_bf16_bits(rng.standard_t(4, (1024, 2048)).astype(np.float32))
+    wg = np.zeros((128, 2048), np.uint16)
+    for packed in (None, w8.router_pack(dev_bf16(wg))):
+        ids, w = w8.route_topk(to_dev(x), dev_bf16(wg), 8, w_gate_packed=packed)
+        assert np.all(to_host(ids) == np.arange(8))
+        assert np.all(to_host(w) == np.float32(0.125))
+
+
+def _half_step_rows(rng, n, cols, amax_lo, amax_hi):
+    """Rows whose elements lie one ulp off half-integer multiples of the row's
+    scale (element 0 fixes the maximum), where a quotient that is not the
+    correctly rounded x / s rounds to the other code."""
+    amax0 = rng.uniform(amax_lo, amax_hi, (n, 1)).astype(np.float32)
+    s0 = amax0 / np.float32(127.0)
+    half = (rng.integers(-126, 126, (n, cols)) + 0.5).astype(np.float32)
+    cand = (half * s0).astype(np.float32)
+    cand = np.nextafter(cand, np.float32(np.inf) * rng.choice([-1, 1], (n, cols))).astype(np.float32)
+    cand[:, 0] = amax0[:, 0]
+    return cand
+
+
+@pytest.mark.parametrize("cols", [64, 768, 1536, 2048, 4096, 1040])
+def test_quant_act_adversarial_rows(cols):
+    """The quantiser on rows built to sit one ulp off the rounding boundaries
+    (the rows that separate the IEEE quotient x / s from x * (127 / amax)),
+    at the widths of every quantiser kernel shape, with scales in the fast
+    reciprocal-and-fma path and below 2^-100 (the divide path): codes and
+    scales bit-exact with the oracle."""
+    rng = np.random.default_rng(cols)
+    x = np.concatenate([_half_step_rows(rng, 48, cols, 0.5, 40.0), _half_step_rows(rng, 8, cols, 1e-33, 1e-30)])
+    amax = np.max(np.abs(x), axis=1, keepdims=True)
+    alt = np.clip(np.rint(x * (np.float32(127.0) / amax)), -127, 127)
+    div = np.clip(np.rint(x / (amax / np.float32(127.0))), -127, 127)
+    say("cols %d: %d codes where the two quotients round apart" % (cols, int(np.sum(alt != div))))
+    q, s = w8.quant_act(to_dev(x))
+    oq, os_ = oracle.quant_rows(x)
+    assert np.array_equal(to_host(s), os_)
+    assert np.array_equal(to_host(q), oq)
+    # bf16 rows with power-of-two scales: exact half-integer quotients (ties to even)
+    m = rng.integers(-8, 8, (16, 1)).astype(np.float32)
+    halves = (rng.integers(-127, 127, (16, cols)) + 0.5).astype(np.float32) * np.exp2(m)
+    halves[:, 0] = 127.0 * np.exp2(m[:, 0])
+    hb = synth.f32_to_bf16_bits(halves)
+    assert np.array_equal(synth.bf16_bits_to_f32(hb), halves)
+    q, s = w8.quant_act(to_dev(hb))
+    oq, os_ = oracle.quant_rows(hb)
+    assert np.array_equal(to_host(q), oq) and np.array_equal(to_host(s), os_)
+
+
 @pytest.mark.parametrize("T,H,E,k", [(1, 16, 1, 1), (5, 48, 8, 2), (37, 2048, 63, 8), (9, 64, 64, 64),
                                      (17, 128, 65, 3), (33, 256, 96, 8), (12, 4096, 128, 8), (7, 80, 200, 11),
                                      (40, 32, 256, 16), (256, 2064, 128, 8), (128, 112, 200, 8),
@@ -224,12 +325,11 @@ def test_route_full_size(name):
     x = synth.moe_x(cfg, wg_bits=wg)
     ids, w, logits = w8.route_topk(to_dev(x), dev_bf16(wg), cfg.k, True, return_logits=True)
     t0 = time.time()
-    tok = np.arange(cfg.T) if cfg.T <= 4096 else np.sort(np.random.default_rng(4).choice(cfg.T, 2048, replace=False))
-    oids, ow, ologits = oracle.route_topk(x[tok], wg, cfg.k)
-    say("oracle router %s on %d tokens: %.1f s" % (name, len(tok), time.time() - t0))
-    assert np.array_equal(to_host(logits)[tok], ologits)
-    assert np.array_equal(to_host(ids)[tok], oids)
-    assert np.abs(to_host(w)[tok] - ow).max() <= 2e-6
+    oids, ow, ologits = oracle.route_topk(x, wg, cfg.k)
+    say("oracle router %s on all %d tokens: %.1f s" % (name, cfg.T, time.time() - t0))
+    assert np.array_equal(to_host(logits), ologits)
+    assert np.array_equal(to_host(ids), oids)
+    assert np.abs(to_host(w) - ow).max() <= 2e-6
 
 
 # --------------------------------------------------------------- permute ---
@@ -391,122 +491,124 @@ def _check_stages(case, inter, tokens=None):
         assert np.array_equal(to_host(inter["pair_pos"]), pos)
 
 
-def _check_gate_up_int32(case, inter, n_rows=48):
-    """int32 gate/up accumulators of sampled grouped rows, bit-exact (exact
-    float64 products of the codes), recomputed through the RAW_I32 epilogue on
-    the layer's own permutation."""
-    cfg = case.cfg
-    P = cfg.T * cfg.k
-    acc = w8.grouped_gemm(inter["xq"], None, inter["sorted_pair"], cfg.k, case.W.w_gate_up, None, inter["offsets"],
-                          w8.EPI_RAW_I32, M_total=P)
-    rows = np.random.default_rng(7).choice(P, min(n_rows, P), replace=False)
-    acc_h = to_host(acc[torch.from_numpy(rows).to(DEV)])
-    sp = to_host(inter["sorted_pair"])
-    off = to_host(inter["offsets"])
-    xq = to_host(inter["xq"])
-    for i, r in enumerate(rows):
-        e = int(np.searchsorted(off, r, side="right") - 1)
-        t = sp[r] // cfg.k
-        want = case.o_qgu[e].astype(np.float64) @ xq[t].astype(np.float64)
-        assert np.array_equal(acc_h[i].astype(np.float64), want)
-    # down accumulators on the GPU's own h codes
-    accd = w8.grouped_gemm(inter["hq"], None, None, 1, case.W.w_down, None, inter["offsets"], w8.EPI_RAW_I32,
-                           M_total=P)
-    accd_h = to_host(accd[torch.from_numpy(rows).to(DEV)])
-    hq = to_host(inter["hq"])
-    for i, r in enumerate(rows):
-        e = int(np.searchsorted(off, r, side="right") - 1)
-        want = case.o_qd[e].astype(np.float64) @ hq[r].astype(np.float64)
-        assert np.array_equal(accd_h[i].astype(np.float64), want)
-    # h quantisation of the GPU's own h is bit-exact
-    h = to_host(inter["h"])[rows]
-    oq, os_ = oracle.quant_rows(h)
-    assert np.array_equal(hq[rows], oq) and np.array_equal(to_host(inter["sh"])[rows], os_)
-    # y, carried as 16-bit fixed point with one power-of-two exponent per row and
-    # 64-column segment: within 2^-14 of its segment's largest magnitude of the
-    # exact dequantised value, and the segment maximum lands in [2^13, 2^14]
-    sh = to_host(inter["sh"])
-    y16 = to_host(inter["y"])[rows].astype(np.float64)
-    yexp = to_host(inter["y_exp"])[rows].astype(np.int64)
-    H = cfg.H
+def _group_of_rows(off, rows):
+    return np.searchsorted(off, rows, side="right") - 1
+
+
+def _raw_rows(A_rows_codes, Bq, off, rows):
+    """The oracle's int32 accumulators of grouped rows `rows` (ascending) whose
+    codes are A_rows_codes, against the groups' weights Bq [G, N, K]."""
+    g = _group_of_rows(off, rows)
+    counts = np.bincount(g, minlength=Bq.shape[0])
+    sub_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return oracle.grouped_gemm(A_rows_codes, None, None, 1, Bq, None, sub_off, oracle.RAW_I32)
+
+
+def _check_fixed16_rows(accd, sh, y16, yexp, off, sd, H, rows):
+    """y carried as 16-bit fixed point (one power-of-two exponent per row and
+    64-column segment): within 2^-14 of its segment's largest magnitude of the
+    exact dequantised value acc * s_h * s_w, and each segment's largest code in
+    [2^13, 2^14].  accd, y16, yexp: these rows; sd [E, H] the weight scales."""
     nseg = (H + 63) // 64
-    for i, r in enumerate(rows):
-        e = int(np.searchsorted(off, r, side="right") - 1)
-        ref = accd_h[i].astype(np.float64) * float(sh[r]) * case.o_sd[e].astype(np.float64)
-        got = y16[i] * np.exp2(np.repeat(yexp[i], 64)[:H])
-        for sg in range(nseg):
-            cols = slice(64 * sg, min(H, 64 * sg + 64))
-            m = np.abs(ref[cols]).max()
-            assert np.all(np.abs(got[cols] - ref[cols]) <= 2.0 ** -14 * m * 1.0001 + 1e-6 * np.abs(ref[cols]) + 1e-30)
-            if m > 0:
-                cm = np.abs(y16[i][cols]).max()
-                assert 2 ** 13 - 1 <= cm <= 2 ** 14
+    e = _group_of_rows(off, rows)
+    ref = np.zeros((len(rows), nseg * 64))
+    ref[:, :H] = accd.astype(np.float64) * sh[rows].astype(np.float64)[:, None] * sd[e].astype(np.float64)
+    got = np.zeros_like(ref)
+    got[:, :H] = y16.astype(np.float64) * np.exp2(np.repeat(yexp.astype(np.int64), 64, axis=1)[:, :H])
+    ref3, got3 = ref.reshape(len(rows), nseg, 64), got.reshape(len(rows), nseg, 64)
+    m = np.abs(ref3).max(axis=2, keepdims=True)
+    assert np.all(np.abs(got3 - ref3) <= 2.0 ** -14 * m * 1.0001 + 1e-6 * np.abs(ref3) + 1e-30)
+    codes = np.zeros((len(rows), nseg * 64))
+    codes[:, :H] = np.abs(y16.astype(np.float64))
+    cm = codes.reshape(len(rows), nseg, 64).max(axis=2)
+    live = m[:, :, 0] > 0
+    assert np.all((cm[live] >= 2 ** 13 - 1) & (cm[live] <= 2 ** 14))
 
 
-def test_layer_tiny_full():
-    case = get_case("moe_tiny_T16_H64_E8_k2_I32")
-    case.check_weights_bit_exact()
-    out, inter, _ = case.run_layer()
-    _check_stages(case, inter)
-    _check_gate_up_int32(case, inter, 32)
-    want, oi = oracle.moe_layer(case.x, *case.oracle_args(), intermediates=True)
-    mism = int(np.sum(to_host(inter["hq"]) != oi["hq"]))
-    say("tiny: h-code mismatches %d of %d" % (mism, oi["hq"].size))
-    tol_check(to_host(out), want, "tiny layer")
-
-
-def test_layer_30b_decode_full():
-    case = get_case("moe_30b_decode_T64")
-    case.check_weights_bit_exact()
-    out, inter, _ = case.run_layer()
-    _check_stages(case, inter)
-    _check_gate_up_int32(case, inter)
+def _check_layer_full(case, out, inter, want, oi, what):
+    """One layer run compared with the oracle's run of the same layer on every
+    token and every grouped row: router ids (bit-exact) and weights, x codes
+    and scales, the permutation, the gate_up int32 accumulators (RAW_I32 on the
+    layer's own permutation), h within tolerance with its code mismatches
+    bounded, h codes and scales of the GPU's own h, the down int32 accumulators
+    of the GPU's own h codes, y's fixed-point bound, and the output."""
+    cfg = case.cfg
+    T, k, H, I = cfg.T, cfg.k, cfg.H, cfg.I
+    P = T * k
     t0 = time.time()
-    want, oi = oracle.moe_layer(case.x, *case.oracle_args(), intermediates=True)
-    say("oracle decode layer: %.1f s" % (time.time() - t0))
-    hit = int(np.sum(np.diff(oi["offsets"]) > 0))
-    say("decode: %d of %d experts hit; h-code mismatches %d of %d" %
-        (hit, case.cfg.E, int(np.sum(to_host(inter["hq"]) != oi["hq"])), oi["hq"].size))
-    tol_check(to_host(out), want, "30b decode layer")
+    assert np.array_equal(to_host(inter["ids"]), oi["ids"])
+    assert np.abs(to_host(inter["w"]) - oi["w"]).max() <= 2e-6
+    assert np.array_equal(to_host(inter["xq"]), oi["xq"]) and np.array_equal(to_host(inter["sx"]), oi["sx"])
+    off = to_host(inter["offsets"])
+    assert np.array_equal(off, oi["offsets"])
+    assert np.array_equal(to_host(inter["sorted_pair"]), oi["sorted_pair"])
+    assert np.array_equal(to_host(inter["pair_pos"]), oi["pair_pos"])
+    acc = w8.grouped_gemm(inter["xq"], None, inter["sorted_pair"], k, case.W.w_gate_up, None, inter["offsets"],
+                          w8.EPI_RAW_I32, M_total=P)
+    assert np.array_equal(to_host(acc), oi["acc_gu"]), "gate_up int32"
+    del acc
+    h = to_host(inter["h"])
+    tol_check(h, oi["h"], what + " h")
+    hq, sh = to_host(inter["hq"]), to_host(inter["sh"])
+    q_, s_ = oracle.quant_rows(h)
+    assert np.array_equal(hq, q_) and np.array_equal(sh, s_), "h codes of the GPU's own h"
+    # h differs from the oracle's only where the hardware exponential moves a
+    # bf16 rounding; its codes then differ by at most one step
+    dq = np.abs(hq.astype(np.int16) - oi["hq"].astype(np.int16))
+    frac = float(np.mean(dq > 0))
+    say("%s: h-code mismatches %d of %d (%.2e), max |d| %d" % (what, int(np.sum(dq > 0)), dq.size, frac,
+                                                               int(dq.max())))
+    assert dq.max() <= 1 and frac <= 1e-3
+    accd = to_host(w8.grouped_gemm(inter["hq"], None, None, 1, case.W.w_down, None, inter["offsets"],
+                                   w8.EPI_RAW_I32, M_total=P))
+    same = np.all(dq == 0, axis=1)
+    assert np.array_equal(accd[same], oi["acc_d"][same]), "down int32"
+    moved = np.nonzero(~same)[0]
+    if len(moved):
+        assert np.array_equal(accd[moved], _raw_rows(hq[moved], case.o_qd, off, moved)), "down int32 (moved rows)"
+    y16, yexp = to_host(inter["y"]), to_host(inter["y_exp"])
+    for r0 in range(0, P, 4096):
+        rows = np.arange(r0, min(P, r0 + 4096))
+        _check_fixed16_rows(accd[rows], sh, y16[rows], yexp[rows], off, case.o_sd, H, rows)
+    del accd
+    tol_check(to_host(out), want, what)
+    counts = np.diff(off)
+    say("%s: all %d tokens and %d grouped rows compared in %.1f s; expert loads min %d max %d cv %.2f"
+        % (what, T, P, time.time() - t0, counts.min(), counts.max(), counts.std() / counts.mean()))
 
 
-def _sampled_layer(name, n_tok=48, seed=0):
+def _full_layer(name, seed=0):
     case = get_case(name, seed)
-    if name == "moe_30b_prefill_T4096":
+    if seed == 0:
         case.check_weights_bit_exact()
     out, inter, _ = case.run_layer()
-    tokens = np.sort(np.random.default_rng(3).choice(case.cfg.T, n_tok, replace=False))
-    _check_stages(case, inter, tokens)
-    _check_gate_up_int32(case, inter)
     t0 = time.time()
-    want = oracle.moe_layer_tokens(case.x, *case.oracle_args(), tokens)
-    say("oracle %s on %d tokens: %.1f s" % (name, n_tok, time.time() - t0))
-    tol_check(to_host(out)[tokens], want, name + " (sampled tokens)")
-    counts = np.diff(to_host(inter["offsets"]))
-    say("%s expert loads: min %d max %d mean %.1f cv %.2f" % (name, counts.min(), counts.max(), counts.mean(),
-                                                             counts.std() / counts.mean()))
+    want, oi = oracle.moe_layer(case.x, *case.oracle_args(), intermediates=True)
+    say("oracle %s (seed %d), all %d tokens with intermediates: %.1f s" % (name, seed, case.cfg.T, time.time() - t0))
+    _check_layer_full(case, out, inter, want, oi, "%s seed %d" % (name, seed))
     return case, out, inter
 
 
-def test_layer_30b_prefill_sampled():
-    _sampled_layer("moe_30b_prefill_T4096")
+def test_layer_tiny_full():
+    _full_layer("moe_tiny_T16_H64_E8_k2_I32")
+
+
+def test_layer_30b_decode_full():
+    case, _, inter = _full_layer("moe_30b_decode_T64")
+    hit = int(np.sum(np.diff(to_host(inter["offsets"])) > 0))
+    say("decode: %d of %d experts hit" % (hit, case.cfg.E))
+
+
+def test_layer_30b_prefill_full():
+    _full_layer("moe_30b_prefill_T4096")
 
 
 @pytest.mark.parametrize("name,seed", [("moe_30b_decode_T64", 1), ("moe_30b_decode_T64", 2),
                                        ("moe_30b_prefill_T4096", 1)])
 def test_layer_other_seeds(name, seed):
     """Other draws of the same workloads (other expert loads, so other ragged
-    row tiles): stages and int32 accumulators bit-exact, the output within
-    tolerance (every token at decode, a sample at prefill)."""
-    if name == "moe_30b_prefill_T4096":
-        _sampled_layer(name, seed=seed)
-        return
-    case = get_case(name, seed)
-    out, inter, _ = case.run_layer()
-    _check_stages(case, inter)
-    _check_gate_up_int32(case, inter)
-    want = oracle.moe_layer(case.x, *case.oracle_args())
-    tol_check(to_host(out), want, "%s seed %d" % (name, seed))
+    row tiles), compared on every token and grouped row."""
+    _full_layer(name, seed)
 
 
 def test_layer_determinism_and_token_shuffle():
@@ -619,13 +721,13 @@ def test_layer_edge_cases():
         tol_check(to_host(out), want, "tiny layer k=%d" % k)
 
 
-def test_layer_235b_zipf_sampled():
-    case, out, inter = _sampled_layer("moe_235b_zipf_T8192", 32)
+def test_layer_235b_zipf_full():
+    case, out, inter = _full_layer("moe_235b_zipf_T8192")
     counts = np.diff(to_host(inter["offsets"]))
     assert counts.max() > 5 * counts.mean()      # the Zipf skew is there
 
 
-def test_dense_linear_sampled():
+def test_dense_linear_full():
     cfg = synth.DENSE_CONFIGS["dense_M4096_K2048_N4096"]
     xb, Wf = synth.dense_inputs(cfg)
     qx, sx = w8.quant_act(to_dev(xb))
@@ -636,13 +738,13 @@ def test_dense_linear_sampled():
     assert np.array_equal(to_host(qw), oqw) and np.array_equal(to_host(sw), osw)
     off = to_dev(np.array([0, cfg.M], np.int32))
     out = w8.grouped_gemm(qx, sx, None, 1, qw.view(1, cfg.N, cfg.K), sw.view(1, cfg.N), off, w8.EPI_DEQUANT, w8.BF16)
-    rows = np.sort(np.random.default_rng(2).choice(cfg.M, 96, replace=False))
-    want = oracle.grouped_gemm(oqx[rows], osx[rows], None, 1, oqw[None], osw[None],
-                               np.array([0, len(rows)], np.int32), oracle.DEQUANT, oracle.BF16)
-    tol_check(to_host(out)[rows], want, "dense W8A8 linear (sampled rows)")
+    want = oracle.grouped_gemm(oqx, osx, None, 1, oqw[None], osw[None], np.array([0, cfg.M], np.int32),
+                               oracle.DEQUANT, oracle.BF16)
+    tol_check(to_host(out), want, "dense W8A8 linear (all rows)")
     acc = w8.grouped_gemm(qx, None, None, 1, qw.view(1, cfg.N, cfg.K), None, off, w8.EPI_RAW_I32)
-    r = rows[:8]
-    assert np.array_equal(to_host(acc)[r].astype(np.float64), oqx[r].astype(np.float64) @ oqw.astype(np.float64).T)
+    want_acc = oracle.grouped_gemm(oqx, None, None, 1, oqw[None], None, np.array([0, cfg.M], np.int32),
+                                   oracle.RAW_I32)
+    assert np.array_equal(to_host(acc), want_acc)
 
 
 # ------------------------------------------------------------------- W4A8 ---
@@ -706,8 +808,8 @@ def test_w4a8_grouped_gemm(G, N, K, counts, gather, epi, od):
 def test_w4_layer(name):
     """The layer with W4A8 gate_up weights (quantised on the GPU, bit-exact with
     the oracle's codes) against the oracle's W4 layer: ids and x codes bit-exact,
-    h codes of the GPU's own h bit-exact, the output within tolerance (all
-    tokens for tiny and decode, a sample for prefill)."""
+    h codes of the GPU's own h bit-exact, the output within tolerance on every
+    token."""
     cfg = synth.MOE_CONFIGS[name]
     x, wg, gu, dn = synth.moe_inputs(cfg)
     E, I, H = cfg.E, cfg.I, cfg.H
@@ -725,20 +827,16 @@ def test_w4_layer(name):
     out = w8.moe_layer(W, xd, ws=ws)
     torch.cuda.synchronize()
     inter = w8.moe_layer_intermediates(W, cfg.T, ws, dt)
-    if cfg.T <= 64:
-        want, it = oracle.moe_layer_w4(x, *args, intermediates=True)
-        assert np.array_equal(to_host(inter["ids"]), it["ids"])
-        assert np.array_equal(to_host(inter["xq"]), it["xq"])
-        tol_check(to_host(inter["h"]), it["h"], "%s w4 h" % name)
-        tol_check(to_host(out), want, "%s w4 layer" % name)
-    else:
-        tok = np.sort(np.random.default_rng(3).choice(cfg.T, 96, replace=False))
-        want = oracle.moe_layer_w4_tokens(x, *args, tok)
-        tol_check(to_host(out)[tok], want, "%s w4 layer (sampled tokens)" % name)
+    t0 = time.time()
+    want, it = oracle.moe_layer_w4(x, *args, intermediates=True)
+    say("oracle %s w4 layer, all %d tokens: %.1f s" % (name, cfg.T, time.time() - t0))
+    for key in ("ids", "xq", "sx", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(to_host(inter[key]), it[key]), key
+    tol_check(to_host(inter["h"]), it["h"], "%s w4 h" % name)
+    tol_check(to_host(out), want, "%s w4 layer (all tokens)" % name)
     h = to_host(inter["h"])
-    rows = np.random.default_rng(4).choice(h.shape[0], min(64, h.shape[0]), replace=False)
-    oq, os_ = oracle.quant_rows(h[rows])
-    assert np.array_equal(to_host(inter["hq"])[rows], oq) and np.array_equal(to_host(inter["sh"])[rows], os_)
+    oq, os_ = oracle.quant_rows(h)
+    assert np.array_equal(to_host(inter["hq"]), oq) and np.array_equal(to_host(inter["sh"]), os_)
 
 
 # ---------------------------------------------------------- shared expert ---
@@ -750,8 +848,8 @@ def test_shared_expert_layer(name):
     weights' codes bit-exact, each shared stage checked on the GPU's own inputs
     to it (h within tolerance, h codes bit-exact, the down output within the
     16-bit fixed-point bound of the exact dequantised sums), the gate within
-    1e-5 of the oracle's sigmoid, and the output within tolerance (every token
-    for tiny and decode, a sample for prefill)."""
+    1e-5 of the oracle's sigmoid, and the output within tolerance on every
+    token."""
     cfg = synth.MOE_CONFIGS[name]
     say("shared expert layer", name)
     x, wg, gu, dn = synth.moe_inputs(cfg)
@@ -777,7 +875,7 @@ def test_shared_expert_layer(name):
     oxq, osx = oracle.quant_rows(x)
     assert np.array_equal(xq, oxq) and np.array_equal(sx, osx)
     # shared gate_up + SwiGLU on the GPU's codes
-    rows = np.arange(T) if T <= 64 else np.sort(np.random.default_rng(5).choice(T, 64, replace=False))
+    rows = np.arange(T)
     hs = to_host(inter["hs"])
     want_hs = oracle.grouped_gemm(xq[rows], sx[rows], None, 1, oqs[None], oss[None], np.array([0, len(rows)], np.int32),
                                   oracle.DEQUANT_SWIGLU, oracle.BF16)
@@ -799,18 +897,16 @@ def test_shared_expert_layer(name):
     # the layer output, and the gate
     oargs = (wg, oq[0], oq[1], oq[2], oq[3], k, se)
     gate = to_host(inter["gate"]).astype(np.float64)
-    if T <= 64:
-        want, it = oracle.moe_layer_shared(x, *oargs, intermediates=True)
-        assert np.abs(gate - it["gate"]).max() <= 1e-5
-        say("%s: gates in [%.3f, %.3f]" % (name, gate.min(), gate.max()))
-        tol_check(to_host(out), want, "%s layer" % name)
-    else:
-        tok = np.sort(np.random.default_rng(3).choice(T, 48, replace=False))
-        want = oracle.moe_layer_shared_tokens(x, *oargs, tok)
-        _, it = oracle.moe_layer_shared(x[tok], *oargs, intermediates=True)
-        assert np.abs(gate[tok] - it["gate"]).max() <= 1e-5
-        tol_check(to_host(out)[tok], want, "%s layer (sampled tokens)" % name)
-    # the routed part is unchanged by the shared expert: same ids and codes as the plain layer
+    t0 = time.time()
+    want, it = oracle.moe_layer_shared(x, *oargs, intermediates=True)
+    say("oracle %s, all %d tokens: %.1f s" % (name, T, time.time() - t0))
+    assert np.abs(gate - it["gate"]).max() <= 1e-5
+    say("%s: gates in [%.3f, %.3f]" % (name, gate.min(), gate.max()))
+    tol_check(to_host(out), want, "%s layer (all tokens)" % name)
+    # the routed part is unchanged by the shared expert: same ids and
+    # permutation as the plain layer
+    for key in ("ids", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(to_host(inter[key]), it[key]), key
     assert np.array_equal(to_host(inter["ids"]), oracle.route_topk(x, wg, k)[0])
 
 
@@ -887,8 +983,7 @@ def test_linear_zero_rows():
                                   "attn_qkv_235b_T8192", "attn_o_235b_T8192"])
 def test_attention_projection_workloads(name):
     """The attention projections at the layer shapes: the whole linear on the
-    GPU, checked against the oracle on every row (decode) or a sample of rows
-    (rows are independent).  For the fused QKV shapes, the q, k and v column
+    GPU, checked against the oracle on every row.  For the fused QKV shapes, the q, k and v column
     ranges equal separate linears over their own weight rows, bit for bit."""
     cfg = synth.DENSE_CONFIGS[name]
     say("attention projection", name)
@@ -897,9 +992,10 @@ def test_attention_projection_workloads(name):
     xd = to_dev(xb)
     out = w8.linear(xd, pw, sw, cfg.N)
     torch.cuda.synchronize()
-    rows = np.arange(cfg.M) if cfg.M <= 64 else np.sort(np.random.default_rng(2).choice(cfg.M, 64, replace=False))
-    want = oracle.linear(xb[rows], oq, os_)
-    tol_check(to_host(out)[rows], want, name)
+    t0 = time.time()
+    want = oracle.linear(xb, oq, os_)
+    say("oracle %s, all %d rows: %.1f s" % (name, cfg.M, time.time() - t0))
+    tol_check(to_host(out), want, name + " (all rows)")
     col = 0
     for n in cfg.split:
         part = w8.pack_weights(qw[col:col + n].contiguous().view(1, n, cfg.K))
