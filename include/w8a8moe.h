@@ -57,6 +57,7 @@ extern "C" {
 #define W8A8_ERR_ALIGNMENT (-3)          /* a pointer or leading dimension not 16-byte aligned */
 #define W8A8_ERR_WORKSPACE_TOO_SMALL (-4)
 #define W8A8_ERR_HIP (-5)                /* a HIP launch failed */
+#define W8A8_ERR_SCRATCH_LIMIT (-6)      /* more scratch than w8a8_grouped_gemm_noalloc's fixed buffer */
 
 /* element types */
 #define W8A8_BF16 0
@@ -205,6 +206,28 @@ int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales,
                       const float *b_scales, const int32_t *group_offsets, int G, int64_t M_total,
                       int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *ws,
                       size_t ws_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code being captured into a
+ * HIP graph, tight serving loops, hosts that forbid allocation): the same
+ * grouped GEMM without a workspace argument.  Its only scratch, the tile table
+ * that a first kernel builds from group_offsets on the device, lives in a
+ * fixed array of W8A8_NOALLOC_SCRATCH_BYTES in each GPU's memory, reserved
+ * with the library's code and held until the process ends; the call allocates
+ * nothing.  Arguments, results and limits are those of w8a8_grouped_gemm (the
+ * same kernels, the same bits).  A problem whose tile table would exceed the
+ * array (w8a8_grouped_gemm_workspace_size(M_total, N, G) >
+ * W8A8_NOALLOC_SCRATCH_BYTES) returns W8A8_ERR_SCRATCH_LIMIT before anything
+ * is launched.  Every call on one GPU shares that GPU's array: calls on one
+ * stream are ordered, but calls that may overlap on one GPU (other streams,
+ * other host threads) race and must not be issued.  Nothing in the array has
+ * to start cleared: each call writes every table entry it reads.
+ */
+#define W8A8_NOALLOC_SCRATCH_BYTES (4 << 20)
+int w8a8_grouped_gemm_noalloc(const int8_t *A, int64_t A_rows, const float *a_scales,
+                              const int32_t *a_row_gather, int gather_div, const int8_t *B, int b_layout,
+                              const float *b_scales, const int32_t *group_offsets, int G, int64_t M_total,
+                              int64_t N, int64_t K, int epilogue, int out_dtype, void *out, void *stream);
 
 /*
  * W4A8 weights ("Qwen3-1.7B-W4A8 on Ascend", section on 4bit weights, items 1

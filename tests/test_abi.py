@@ -9,7 +9,7 @@ import pytest
 
 import w8a8_int8_quantized_bf16_amd as w8
 
-OK, INVALID, SHAPE, ALIGN, WS_SMALL, HIP = 0, -1, -2, -3, -4, -5
+OK, INVALID, SHAPE, ALIGN, WS_SMALL, HIP, SCRATCH = 0, -1, -2, -3, -4, -5, -6
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: every call below returns before any launch
 MIS = ctypes.c_void_p((1 << 20) + 4)
 
@@ -24,10 +24,11 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = w8.header_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in ("w8a8_quant_act", "moe_route_topk", "moe_permute", "w8a8_grouped_gemm", "moe_combine",
               "w8a8_moe_layer", "w4a8_quant_weights", "w4a8_pack_weights", "w4a8_grouped_gemm", "w8a8_linear",
-              "w8a8_linear_q", "w8a8_linear_workspace_size", "w8a8_linear_q_workspace_size"):
+              "w8a8_linear_q", "w8a8_linear_workspace_size", "w8a8_linear_q_workspace_size",
+              "w8a8_grouped_gemm_noalloc"):
         assert n in names
     for n in names:
         assert hasattr(L, n), n
@@ -44,7 +45,7 @@ def test_library_holds_gfx950_code(L):
 
 
 def test_status_strings(L):
-    for code in (OK, INVALID, SHAPE, ALIGN, WS_SMALL, HIP):
+    for code in (OK, INVALID, SHAPE, ALIGN, WS_SMALL, HIP, SCRATCH):
         assert w8.status_string(code)
     assert w8.status_string(-99) == "unknown status"
 
@@ -111,6 +112,29 @@ def test_grouped_gemm_rejects(L):
     assert L.w8a8_grouped_gemm(*args(M=0, A=None, out=None)) == OK
     assert L.w8a8_grouped_gemm(*args(Arows=1 << 20, K=4096)) == SHAPE        # 32-bit offsets
     assert L.w8a8_grouped_gemm(*args(Arows=-1)) == INVALID
+
+
+def test_grouped_gemm_noalloc_rejects(L):
+    """The allocation-free grouped GEMM checks the arguments of
+    w8a8_grouped_gemm and refuses, before any launch, a problem whose tile
+    table exceeds its fixed scratch array."""
+    s = None
+    args = lambda **kw: [kw.get("A", FAKE), kw.get("Arows", 1024), kw.get("sa", FAKE), kw.get("gat", None),
+                         kw.get("div", 1), kw.get("B", FAKE), kw.get("lay", 0), kw.get("sb", FAKE),
+                         kw.get("off", FAKE), kw.get("G", 8), kw.get("M", 1024), kw.get("N", 256), kw.get("K", 256),
+                         kw.get("epi", 1), kw.get("od", 0), kw.get("out", FAKE), s]
+    assert L.w8a8_grouped_gemm_noalloc(*args(K=200)) == SHAPE
+    assert L.w8a8_grouped_gemm_noalloc(*args(epi=0, od=0)) == INVALID
+    assert L.w8a8_grouped_gemm_noalloc(*args(A=MIS)) == ALIGN
+    assert L.w8a8_grouped_gemm_noalloc(*args(off=None)) == INVALID
+    assert L.w8a8_grouped_gemm_noalloc(*args(M=0, A=None, out=None)) == OK
+    limit = 4 << 20
+    # the tile table of the 235B layer's GEMMs (65,536 rows and a shared group) fits; 4M rows do not
+    assert L.w8a8_grouped_gemm_workspace_size(65536, 4096, 129) <= limit
+    big = 1 << 22
+    assert L.w8a8_grouped_gemm_workspace_size(big, 4096, 1) > limit
+    assert L.w8a8_grouped_gemm_noalloc(*args(M=big, G=1, N=4096, gat=FAKE, div=8)) == SCRATCH
+    assert w8.status_string(SCRATCH) != "unknown status"
 
 
 def test_pack_rejects(L):

@@ -75,6 +75,7 @@ def lib():
     L.w8a8_grouped_gemm_workspace_size.argtypes = [i64, i64, i32]
     L.w8a8_grouped_gemm_workspace_size.restype = sz
     L.w8a8_grouped_gemm.argtypes = [P, i64, P, P, i32, P, i32, P, P, i32, i64, i64, i64, i32, i32, P, P, sz, P]
+    L.w8a8_grouped_gemm_noalloc.argtypes = [P, i64, P, P, i32, P, i32, P, P, i32, i64, i64, i64, i32, i32, P, P]
     L.w8a8_packed_weights_size.argtypes = [i32, i64, i64]
     L.w8a8_packed_weights_size.restype = sz
     L.w8a8_pack_weights.argtypes = [P, i32, i64, i64, P, P]

@@ -4,10 +4,43 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/w8a8moe.h"
 #include "launch.h"
 
 using namespace w8a8;
+
+// Scratch memory of the allocation-free grouped GEMM (its tile table): a
+// fixed array in every GPU's memory, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it names a stand-in,
+// not device memory): it uses the device address that hipGetSymbolAddress
+// returns, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[W8A8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void *scratch_addr[SCRATCH_MAX_DEVICES];   // per device, filled on its first use
+
+// The current device's copy of `scratch`.
+hipError_t scratch_of_current_device(void **addr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_addr[dev] = p;
+    }
+    *addr = scratch_addr[dev];
+    return hipSuccess;
+}
+}  // namespace
 
 namespace {
 
@@ -34,6 +67,32 @@ int check_route(const void *x, int x_dtype, const uint16_t *w_gate, int64_t T, i
     if (T > 0 && (!x || !w_gate || !ids || !w)) return W8A8_ERR_INVALID_ARG;
     if (T > 0 && (!aligned16(x) || !aligned16(w_gate) || !aligned16(ids) || !aligned16(w) ||
                   (logits && !aligned16(logits))))
+        return W8A8_ERR_ALIGNMENT;
+    return W8A8_OK;
+}
+
+// Arguments of a grouped GEMM, everything but its workspace.
+int check_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *a_row_gather,
+                       int gather_div, const int8_t *B, int b_layout, const float *b_scales,
+                       const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                       int out_dtype, const void *out)
+{
+    if (M_total < 0 || A_rows < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
+    if (G > 4096) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (b_layout != W8A8_B_ROWMAJOR && b_layout != W8A8_B_PACKED) return W8A8_ERR_INVALID_ARG;
+    if (epilogue < W8A8_EPI_RAW_I32 || epilogue > W8A8_EPI_DEQUANT_SWIGLU) return W8A8_ERR_INVALID_ARG;
+    if (epilogue == W8A8_EPI_RAW_I32 ? out_dtype != W8A8_I32 : !act_dtype_ok(out_dtype))
+        return W8A8_ERR_INVALID_ARG;
+    if (a_row_gather && gather_div <= 0) return W8A8_ERR_INVALID_ARG;
+    if (K % 16 || N % 16 || (epilogue == W8A8_EPI_DEQUANT_SWIGLU && N % 64)) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    const int64_t group_bytes = b_layout == W8A8_B_PACKED ? (int64_t)packed_weights_bytes(1, N, K) : N * K;
+    if (A_rows * K > INT32_MAX - 256 || group_bytes > INT32_MAX - 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
+    if (!B || !group_offsets) return W8A8_ERR_INVALID_ARG;
+    if (M_total > 0 && (!A || !out)) return W8A8_ERR_INVALID_ARG;
+    if (epilogue != W8A8_EPI_RAW_I32 && (!b_scales || (M_total > 0 && !a_scales))) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(out) || !aligned16(group_offsets) ||
+        (a_row_gather && !aligned16(a_row_gather)) || (a_scales && !aligned16(a_scales)) ||
+        (b_scales && !aligned16(b_scales)))
         return W8A8_ERR_ALIGNMENT;
     return W8A8_OK;
 }
@@ -288,6 +347,7 @@ const char *w8a8_status_string(int status)
     case W8A8_ERR_ALIGNMENT: return "pointer or leading dimension not 16-byte aligned";
     case W8A8_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case W8A8_ERR_HIP: return "HIP launch failed";
+    case W8A8_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the fixed buffer of the allocation-free entry point";
     default: return "unknown status";
     }
 }
@@ -388,27 +448,33 @@ int w8a8_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, co
                       const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
                       int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream)
 {
-    if (M_total < 0 || A_rows < 0 || N <= 0 || K <= 0 || G <= 0) return W8A8_ERR_INVALID_ARG;
-    if (G > 4096) return W8A8_ERR_UNSUPPORTED_SHAPE;
-    if (b_layout != W8A8_B_ROWMAJOR && b_layout != W8A8_B_PACKED) return W8A8_ERR_INVALID_ARG;
-    if (epilogue < W8A8_EPI_RAW_I32 || epilogue > W8A8_EPI_DEQUANT_SWIGLU) return W8A8_ERR_INVALID_ARG;
-    if (epilogue == W8A8_EPI_RAW_I32 ? out_dtype != W8A8_I32 : !act_dtype_ok(out_dtype))
-        return W8A8_ERR_INVALID_ARG;
-    if (a_row_gather && gather_div <= 0) return W8A8_ERR_INVALID_ARG;
-    if (K % 16 || N % 16 || (epilogue == W8A8_EPI_DEQUANT_SWIGLU && N % 64)) return W8A8_ERR_UNSUPPORTED_SHAPE;
-    const int64_t group_bytes = b_layout == W8A8_B_PACKED ? (int64_t)packed_weights_bytes(1, N, K) : N * K;
-    if (A_rows * K > INT32_MAX - 256 || group_bytes > INT32_MAX - 256) return W8A8_ERR_UNSUPPORTED_SHAPE;
-    if (!B || !group_offsets || !ws) return W8A8_ERR_INVALID_ARG;
-    if (M_total > 0 && (!A || !out)) return W8A8_ERR_INVALID_ARG;
-    if (epilogue != W8A8_EPI_RAW_I32 && (!b_scales || (M_total > 0 && !a_scales))) return W8A8_ERR_INVALID_ARG;
-    if (!aligned16(A) || !aligned16(B) || !aligned16(out) || !aligned16(ws) || !aligned16(group_offsets) ||
-        (a_row_gather && !aligned16(a_row_gather)) || (a_scales && !aligned16(a_scales)) ||
-        (b_scales && !aligned16(b_scales)))
-        return W8A8_ERR_ALIGNMENT;
+    int rc = check_grouped_gemm(A, A_rows, a_scales, a_row_gather, gather_div, B, b_layout, b_scales, group_offsets,
+                                G, M_total, N, K, epilogue, out_dtype, out);
+    if (rc) return rc;
+    if (!ws) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(ws)) return W8A8_ERR_ALIGNMENT;
     if (ws_bytes < gemm_ws_bytes(M_total, N, G)) return W8A8_ERR_WORKSPACE_TOO_SMALL;
     if (M_total == 0) return W8A8_OK;
     return hip_status(launch_grouped_gemm(A, A_rows, a_scales, a_row_gather, gather_div, B, b_layout, b_scales,
                                           group_offsets, G, M_total, N, K, epilogue, out_dtype, out, ws,
+                                          (hipStream_t)stream));
+}
+
+int w8a8_grouped_gemm_noalloc(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *a_row_gather,
+                              int gather_div, const int8_t *B, int b_layout, const float *b_scales,
+                              const int32_t *group_offsets, int G, int64_t M_total, int64_t N, int64_t K,
+                              int epilogue, int out_dtype, void *out, void *stream)
+{
+    int rc = check_grouped_gemm(A, A_rows, a_scales, a_row_gather, gather_div, B, b_layout, b_scales, group_offsets,
+                                G, M_total, N, K, epilogue, out_dtype, out);
+    if (rc) return rc;
+    if (gemm_ws_bytes(M_total, N, G) > (size_t)W8A8_NOALLOC_SCRATCH_BYTES) return W8A8_ERR_SCRATCH_LIMIT;
+    if (M_total == 0) return W8A8_OK;
+    void *table = nullptr;
+    hipError_t e = scratch_of_current_device(&table);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_grouped_gemm(A, A_rows, a_scales, a_row_gather, gather_div, B, b_layout, b_scales,
+                                          group_offsets, G, M_total, N, K, epilogue, out_dtype, out, table,
                                           (hipStream_t)stream));
 }
 
