@@ -160,6 +160,58 @@ def write_traffic(args):
     print(json.dumps(rec))
 
 
+SIMDS = 1024                  # 256 CUs x 4 SIMDs
+XCDS = 8                      # rocprofv3 sums GRBM_GUI_ACTIVE over the 8 XCDs' graphics blocks
+PEAK_CLOCK_HZ = 2.4e9
+
+
+def _csv_rows(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def counter_summary(args):
+    """Per-kernel summary of one rocprofv3 --pmc run with --kernel-trace:
+    int8 matrix-core operations (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512), matrix-core
+    busy cycles (SQ_VALU_MFMA_BUSY_CYCLES, summed over the SIMDs) against the
+    active cycles of one XCD (GRBM_GUI_ACTIVE, summed over the XCDs, / 8) times
+    the SIMDs, the clock those cycles imply over the traced duration, and the
+    int8 rate against the dense peak at 2.4 GHz and at that clock.  Prints
+    markdown."""
+    pmc_csv, trace_csv = args.counter_summary
+    disp = {}
+    for r in _csv_rows(pmc_csv):
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        d = disp.setdefault(key, {"kernel": r["Kernel_Name"], "c": {}})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    dur = {}
+    for r in _csv_rows(trace_csv):
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        dur[key] = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9
+    by_kernel = {}
+    for key, d in disp.items():
+        if key in dur:
+            by_kernel.setdefault(d["kernel"], []).append((d["c"], dur[key]))
+    lines = ["| kernel | dispatches | avg us | int8 ops (MOPS_I8 x 512) | MFMA busy / (XCD active cycles x SIMDs) | "
+             "clock = XCD active cycles / duration | int8 TOPS | of peak at 2.4 GHz | of peak at that clock |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for kern, rows in sorted(by_kernel.items(), key=lambda kv: -sum(t for _, t in kv[1])):
+        n = len(rows)
+        t = sum(r[1] for r in rows) / n
+        c = {name: sum(r[0].get(name, 0.0) for r in rows) / n for name in rows[0][0]}
+        ops = c.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0) * 512
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        util = busy / (gui * SIMDS) if gui else 0.0
+        clk = gui / t if t else 0.0
+        tops = ops / t / 1e12 if t else 0.0
+        at_clk = ops / t / (INT8_PEAK_TOPS * 1e12 * clk / PEAK_CLOCK_HZ) if ops and clk else 0.0
+        name = kern if len(kern) < 90 else kern[:87] + "..."
+        lines.append("| `%s` | %d | %.1f | %.4g | %.3f | %.2f GHz | %.0f | %.3f | %.3f |"
+                     % (name, n, t * 1e6, ops, util, clk / 1e9, tops, tops / INT8_PEAK_TOPS, at_clk))
+    print("\n".join(lines))
+
+
 def cpu_model():
     """The host CPU's model name and logical core count."""
     name = "unknown"
@@ -436,7 +488,12 @@ def main():
                     default=["gate_up_gemm", "void w8a8::grouped_gemm_kernel<128, 2, 2, 2, unsigned short, true>",
                              "gemm.hip"])
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--counter-summary", nargs=2, metavar=("PMC_CSV", "TRACE_CSV"),
+                    help="print a per-kernel summary of a rocprofv3 --pmc run (matrix-core counters) and exit")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args)
+        return
     if args.traffic:
         write_traffic(args)
         return

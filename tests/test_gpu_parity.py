@@ -558,7 +558,7 @@ def _check_layer_full(case, out, inter, want, oi, what):
     frac = float(np.mean(dq > 0))
     say("%s: h-code mismatches %d of %d (%.2e), max |d| %d" % (what, int(np.sum(dq > 0)), dq.size, frac,
                                                                int(dq.max())))
-    assert dq.max() <= 1 and frac <= 1e-3
+    assert dq.max() <= 1 and frac <= 1e-5
     accd = to_host(w8.grouped_gemm(inter["hq"], None, None, 1, case.W.w_down, None, inter["offsets"],
                                    w8.EPI_RAW_I32, M_total=P))
     same = np.all(dq == 0, axis=1)
