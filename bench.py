@@ -207,8 +207,12 @@ def counter_summary(args):
         tops = ops / t / 1e12 if t else 0.0
         at_clk = ops / t / (INT8_PEAK_TOPS * 1e12 * clk / PEAK_CLOCK_HZ) if ops and clk else 0.0
         name = kern if len(kern) < 90 else kern[:87] + "..."
-        lines.append("| `%s` | %d | %.1f | %.4g | %.3f | %.2f GHz | %.0f | %.3f | %.3f |"
-                     % (name, n, t * 1e6, ops, util, clk / 1e9, tops, tops / INT8_PEAK_TOPS, at_clk))
+        # GRBM_GUI_ACTIVE also counts the dispatch's own start and drain, so the
+        # implied clock means something only for launches far longer than that
+        clk_s = "%.2f GHz" % (clk / 1e9) if t >= 100e-6 else "-"
+        at_s = "%.3f" % at_clk if t >= 100e-6 else "-"
+        lines.append("| `%s` | %d | %.1f | %.4g | %.3f | %s | %.0f | %.3f | %s |"
+                     % (name, n, t * 1e6, ops, util, clk_s, tops, tops / INT8_PEAK_TOPS, at_s))
     print("\n".join(lines))
 
 
