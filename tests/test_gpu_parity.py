@@ -371,6 +371,7 @@ def _groups(rng, sizes):
     ([60, 70, 0, 45], 272, 1040, 0),          # N tail, mid-size groups
     ([300, 129, 1000], 512, 384, 8),          # large groups
     ([257, 200, 33, 384], 256, 512, 0),       # 128-row tiles whose last one holds 1, 72 or 33 rows
+    ([400, 3, 900, 0], 272, 1040, 4),         # 128 x 512 tiles: N tail, K tail, a near-empty group
     ([17], 16, 16, 0),                        # minimum sizes
 ])
 def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather, packed):
@@ -404,7 +405,7 @@ def test_grouped_gemm_raw_i32_exact(sizes, N, K, gather, packed):
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("epi,od", [(w8.EPI_DEQUANT, w8.BF16), (w8.EPI_DEQUANT, w8.F32),
                                     (w8.EPI_DEQUANT_SWIGLU, w8.BF16), (w8.EPI_DEQUANT_SWIGLU, w8.F32)])
-@pytest.mark.parametrize("sizes", [[7, 0, 90, 33], [200, 300]])
+@pytest.mark.parametrize("sizes", [[7, 0, 90, 33], [200, 300], [500, 0, 777]])   # the last on 128 x 512 tiles
 def test_grouped_gemm_dequant_epilogues(epi, od, sizes, packed):
     rng = np.random.default_rng(len(sizes) + epi * 10 + od)
     G, M, N, K = len(sizes), sum(sizes), 320, 528

@@ -203,6 +203,32 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_bit_cast(v4i, v);
 }
 
+// Direct memory-to-LDS transfer: lane l's 16 bytes at offset off of r land in
+// LDS at lds + 16 l (lds wave-uniform, through M0).  Written in asm so that
+// the compiler, which would otherwise make every later LDS read wait for all
+// outstanding loads, leaves the waits to lds_barrier; the asm names M0, the
+// only register it changes besides the memory.  Offsets out of range return
+// zeros, as for buf_load16.
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier after this wave's LDS operations have completed and at
+// most N of its memory loads (transfers included, oldest first) are still in
+// flight.  A compiler memory barrier too: no load or LDS access moves across.
+template <int N>
+__device__ __forceinline__ void lds_barrier()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt counts up to 63");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Epilogue of one tile.  Each wave stages its results through its own LDS
 // region (stage_base + wave * 32 * ROWB, see gemm_stage_bytes), one 32-row
 // block and at most two 32-column fragments at a time, and writes them back
@@ -319,6 +345,134 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, v16i (&acc)[BM 
                 }
             }
             __syncthreads();
+        }
+    }
+}
+
+// 16-bit fixed point of y, one 64-column segment of a row at a time: the
+// segment's largest magnitude m fixes a power-of-two scale 2^e (e = the
+// exponent of m less 13, at least -126) that maps it into [2^13, 2^14); the
+// codes rint(v * 2^-e) then fit int16 with room.
+__device__ __forceinline__ int fixed16_exponent(float m)
+{
+    const int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 13 : 0;
+    return e < -126 ? -126 : e;
+}
+__device__ __forceinline__ float fixed16_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }   // 2^-e, exact
+// rint(v * sc) as a 16-bit two's complement code: adding 1.5 * 2^23 rounds the
+// (exact) product half-to-even into the mantissa
+__device__ __forceinline__ uint32_t fixed16_code(float v, float sc)
+{
+    return (uint32_t)(__float_as_int(fmaf(v, sc, 12582912.0f)) - 0x4B400000) & 0xffffu;
+}
+
+// Epilogue of one tile straight from registers.  With the weights as the
+// MFMA's first operand, lane l holds token row l % 32 of each 32-row block
+// and, of each 32-column fragment, columns 8 g + 4 (l / 32) + j in
+// acc[..][4 g + j]: four consecutive columns per group g, written as one 8- or
+// 16-byte piece.  ascale: the tile's row scales (LDS); csc: this wave's column
+// scales (LDS, 32 per fragment).  The 16-bit fixed-point segment of a row
+// (two fragments) lies in lanes l and l ^ 32, so its largest magnitude takes
+// one lane exchange.  The arithmetic per value is that of gemm_epilogue.
+template <int BM, int WN, int EPI, typename OutT>
+__device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs &a, v16i (&acc)[BM / 32][WN], const float *ascale,
+                                                   const float *csc, int rows, int64_t row0, int nb, int N)
+{
+    constexpr int MI = BM / 32;
+    constexpr int WCOLS = 32 * WN;
+    constexpr int NOF = EPI == 2 ? WN / 2 : WN;   // output fragments of 32 columns
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ldo = EPI == 2 ? (N >> 1) : N;
+    // first output column of this wave's fragment f is ocol0 + 32 f
+    const int ocol0 = EPI == 2 ? nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) : nb * (4 * WCOLS) + wave * WCOLS;
+    const int half = 4 * (lane >> 5);
+    auto scales4 = [&](int f, int g) { return *reinterpret_cast<const float4 *>(csc + 32 * f + 8 * g + half); };
+    auto pack2 = [](float x, float y) {
+        return (uint32_t)float_to_bf16_bits(x) | ((uint32_t)float_to_bf16_bits(y) << 16);
+    };
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+        const int r = mi * 32 + (lane & 31);
+        const bool live = r < rows;
+        const float sa = EPI != 0 ? ascale[r] : 0.0f;
+        const int64_t obase = (row0 + r) * (int64_t)ldo;
+        if constexpr (EPI == EPI_FIXED16) {
+#pragma unroll
+            for (int p = 0; p < NOF; p += 2) {
+                float v[2][16];
+                float m = 0.0f;
+#pragma unroll
+                for (int ff = 0; ff < 2; ++ff)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float4 cs = scales4(p + ff, g);
+                        const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            v[ff][4 * g + j] = ((float)acc[mi][p + ff][4 * g + j] * sa) * c4[j];
+                            m = fmaxf(m, fabsf(v[ff][4 * g + j]));
+                        }
+                    }
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const int e = fixed16_exponent(m);
+                const float sc = fixed16_scale(e);
+#pragma unroll
+                for (int ff = 0; ff < 2; ++ff)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int c = ocol0 + 32 * (p + ff) + 8 * g + half;
+                        if (live && c < ldo) {
+                            const float *vv = &v[ff][4 * g];
+                            *reinterpret_cast<uint2 *>(reinterpret_cast<int16_t *>(a.out) + obase + c) =
+                                make_uint2(fixed16_code(vv[0], sc) | (fixed16_code(vv[1], sc) << 16),
+                                           fixed16_code(vv[2], sc) | (fixed16_code(vv[3], sc) << 16));
+                        }
+                    }
+                if (live && lane < 32 && ocol0 + 32 * p < ldo)
+                    a.out_exp[(row0 + r) * ((ldo + 63) / 64) + (ocol0 + 32 * p) / 64] = (int8_t)e;
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < NOF; ++f)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = ocol0 + 32 * f + 8 * g + half;
+                    if (!(live && c < ldo)) continue;
+                    int q[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) q[j] = acc[mi][f][4 * g + j];
+                    if constexpr (EPI == 0) {
+                        *reinterpret_cast<int4 *>(reinterpret_cast<int32_t *>(a.out) + obase + c) =
+                            make_int4(q[0], q[1], q[2], q[3]);
+                    } else {
+                        float o[4];
+                        const float4 cs = scales4(f, g);
+                        const float c4[4] = {cs.x, cs.y, cs.z, cs.w};
+                        if constexpr (EPI == 1) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) o[j] = ((float)q[j] * sa) * c4[j];
+                        } else {
+                            int u[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) u[j] = acc[mi][NOF + f][4 * g + j];
+                            const float4 cu = scales4(NOF + f, g);
+                            const float u4[4] = {cu.x, cu.y, cu.z, cu.w};
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const float gate = ((float)q[j] * sa) * c4[j];
+                                const float up = ((float)u[j] * sa) * u4[j];
+                                // silu(g) = g / (1 + e^-g), as in gemm_epilogue
+                                o[j] = gate * up * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
+                            }
+                        }
+                        if constexpr (sizeof(OutT) == 4)
+                            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(a.out) + obase + c) =
+                                make_float4(o[0], o[1], o[2], o[3]);
+                        else
+                            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + obase + c) =
+                                make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+                    }
+                }
         }
     }
 }
@@ -565,6 +719,271 @@ void grouped_gemm_kernel(GemmArgs a)
         }
     }
     gemm_epilogue<BM, WN, EPI, OutT>(a, acc, ascale, bsc, smem, rows, row0, nb, N);
+}
+
+// The same tiles and results as grouped_gemm_kernel, for the 128 x 512 tiles
+// (one block per CU, every register taken by the accumulators and the B ring).
+// There the A staging registers are better spent on A fragments: the A steps
+// go from memory straight into a ring of three LDS buffers, each sub-step's A
+// fragments are read one sub-step ahead so that no MFMA waits on LDS, and a
+// step has one barrier.  The weights are the MFMAs' first operand, so a lane
+// ends with four consecutive output columns per group and the epilogue writes
+// from registers (gemm_epilogue_rows), with no staging and no barrier.  On the
+// narrower tiles, which run two or three blocks per CU, the extra registers of
+// this loop cost more than it saves, and the 16-bit fixed-point output is
+// written faster in rows staged through LDS.
+template <int BM, int WN, int DEPTH, int EPI, typename OutT, bool PACKED>
+__global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(1, 8)))
+void grouped_gemm_ring_kernel(GemmArgs a)
+{
+    static_assert(WN == 4 && EPI != EPI_FIXED16, "built for the 128 x 512 tiles");
+    static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH");
+    static_assert(EPI != 2 || WN % 2 == 0, "SwiGLU pairs gate and up fragments");
+    static_assert(EPI != EPI_FIXED16 || WN % 2 == 0, "16-bit fixed point takes 64-column segments");
+    constexpr int MI = BM / 32;      // 32-row MFMA tiles per wave
+    constexpr int WCOLS = 32 * WN;   // B rows (output columns) per wave
+    // LDS: the ring of A_BUFS A buffers of the K loop
+    constexpr int A_BUFS = 3;
+    constexpr int ABUF = BM * G_BK;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[A_BUFS * ABUF];
+    __shared__ int32_t arow[BM];
+    // each wave's column scales, fragment-major (32 per fragment)
+    __shared__ __attribute__((aligned(16))) float csc[4 * WCOLS];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ float ascale[BM];
+
+    // ---- which tile (one table load, or from the block index)
+    const int bid = blockIdx.x;
+    int4 tinfo;
+    int kbeg = 0;   // first K step of this tile's slice (dense, split K)
+    if (a.dense_rows > 0) {
+        if (!dense_tile(bid, a.dense_rows, BM, a.nblocks_n, a.ksplit, &tinfo)) return;
+        kbeg = tinfo.x * a.ksteps;
+        tinfo.x = 0;
+    } else {
+        if (bid >= a.tile_prefix[a.G]) return;
+        tinfo = a.tiles[bid];
+    }
+    const int g = tinfo.x, rows = tinfo.z, nb = tinfo.w;
+    const int64_t row0 = tinfo.y;
+    const int N = (int)a.N, K = (int)a.K;
+    const int nk_all = (K + G_BK - 1) / G_BK;
+    // steps of this tile: all of K, or its slice (packed B only, so no K
+    // masking of A: bytes beyond K meet zero weights)
+    const int nk = a.ksplit > 1 ? min(nk_all - kbeg, a.ksteps) : nk_all;
+
+    // ---- B rows (output columns) of this lane, one per fragment
+    int col[WN];
+    bool cvalid[WN];
+    if constexpr (EPI == 2) {
+        const int Nh = N >> 1;
+        const int hc0 = nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) + (lane & 31);
+#pragma unroll
+        for (int f = 0; f < WN / 2; ++f) {
+            col[f] = hc0 + 32 * f;
+            col[WN / 2 + f] = Nh + hc0 + 32 * f;
+            cvalid[f] = cvalid[WN / 2 + f] = hc0 + 32 * f < Nh;
+        }
+    } else {
+        const int c0 = nb * (4 * WCOLS) + wave * WCOLS + (lane & 31);
+#pragma unroll
+        for (int f = 0; f < WN; ++f) {
+            col[f] = c0 + 32 * f;
+            cvalid[f] = col[f] < N;
+        }
+    }
+    // B is [N][K] row-major, or packed: per 32-row block and 128-byte K step a
+    // 4 KiB chunk holding, for sub-step s and lane l, the 16 bytes that lane l
+    // feeds to the MFMA (row l%32, bytes 64*(l/32) + 16*s of the step), zero
+    // padded in N and K.  Offsets are unsigned: an invalid lane starts at
+    // OOB_BASE, above every resource size, and stays out of range as steps are
+    // added, so its loads return zeros.
+    const int64_t b_bytes = PACKED ? (int64_t)((N + 31) / 32) * nk_all * 4096 : (int64_t)N * K;
+    const bool xg = g >= a.G_routed;   // the extra group: weights of its own
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(xg ? a.B_extra : a.B + (int64_t)g * b_bytes, b_bytes);
+    const float *bsg = xg ? a.b_extra_scales : a.b_scales + (int64_t)g * N;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
+    const int khalf = 64 * (lane >> 5);
+    uint32_t boff[WN];
+#pragma unroll
+    for (int f = 0; f < WN; ++f)
+        boff[f] = !cvalid[f] ? OOB_BASE
+                             : (PACKED ? (uint32_t)(((col[f] >> 5) * nk_all + kbeg) * 4096 + lane * 16)
+                                       : (uint32_t)(col[f] * K + khalf));
+    constexpr uint32_t BSTEP = PACKED ? 4096 : G_BK, BSUB = PACKED ? 1024 : 16;
+
+    // per-column weight scales, for the epilogue: lane l < 32 holds the
+    // scale of column l of each fragment, which the epilogue needs in the
+    // lanes that hold that column's outputs
+    float *cscw = csc + wave * WCOLS;
+    if (lane < 32) {
+#pragma unroll
+        for (int f = 0; f < WN; ++f) cscw[32 * f + lane] = (EPI != 0 && cvalid[f]) ? bsg[col[f]] : 0.0f;
+    }
+
+    // ---- activation rows of the tile and their scales
+    if (tid < BM) {
+        int32_t src = -1;
+        if (tid < rows) src = a.gather ? a.gather[row0 + tid] / a.gather_div : (int32_t)(row0 + tid);
+        arow[tid] = src;
+        ascale[tid] = (EPI != 0 && src >= 0) ? a.a_scales[src] : 0.0f;
+    }
+    __syncthreads();
+
+    // ---- A staging: the A tile of a K step (BM rows x 128 bytes) goes from
+    // memory straight into an LDS buffer, AD 1 KiB transfers per wave (8 rows
+    // each, lane l writes bytes 16l..16l+15 of its transfer).  The buffer keeps
+    // a row's 16-byte chunk ch at slot ch ^ (row & 7), so lane l fetches chunk
+    // (l & 7) ^ ((l >> 3) & 7) of row 8 * transfer + (l >> 3): the swizzle is in
+    // the source addresses, and the fragment reads below hit distinct banks.
+    constexpr int AD = BM / 32;
+    const int ach = (lane & 7) ^ ((lane >> 3) & 7);
+    uint32_t aoff[AD];
+#pragma unroll
+    for (int j = 0; j < AD; ++j) {
+        const int32_t sr = arow[(wave * AD + j) * 8 + (lane >> 3)];
+        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ach) : OOB_BASE;
+    }
+    const uint32_t lds_a = (uint32_t)(uintptr_t)(lds_u8_t *)&smem[0];
+
+    // Software pipeline over K steps of 128 bytes.  B fragments go to a ring
+    // of DEPTH register slots (step j in slot j % DEPTH, loaded DEPTH steps
+    // ahead, one sub-step's fragments refilled right after that sub-step's
+    // MFMAs); A steps go to a ring of three LDS buffers (step j in buffer
+    // j % 3, loaded three steps ahead).  The A fragments of a sub-step are read
+    // from LDS one sub-step ahead, into the other of two register sets, so the
+    // matrix cores never wait on an LDS read.  Each step has one barrier,
+    // between its sub-steps 2 and 3: before it every wave waits for its own
+    // transfer of the next step's A and for its fragment reads of this step;
+    // after it the next step's A is complete in LDS and this step's buffer is
+    // free, so the transfer of step + 3 into it is issued there.
+    v4i breg[DEPTH][WN][4];
+    v16i acc[MI][WN];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int f = 0; f < WN; ++f)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][f][i] = 0;
+
+    // Steps at or beyond nk (the padding of the trip count) load nothing: the
+    // step index is wave-uniform, so that choice is a scalar select.  With
+    // packed (zero-padded) weights the K tail needs no masking of A: whatever
+    // A bytes lie beyond K meet zero weights.
+    auto load_b_sub = [&](int slot, int it, int s) {
+        const bool live = it < nk;
+        const bool kin = PACKED || it * G_BK + khalf + 16 * s < K;
+#pragma unroll
+        for (int f = 0; f < WN; ++f)
+            breg[slot][f][s] = buf_load16(rB, (live && kin) ? boff[f] + it * BSTEP + s * BSUB : OOB_BASE);
+    };
+    auto load_a = [&](int it) {
+        const bool live = it < nk;
+        const bool kin = PACKED || it * G_BK + 16 * ach < K;
+        const uint32_t dst = lds_a + (uint32_t)((it % A_BUFS) * ABUF + wave * AD * 1024);
+#pragma unroll
+        for (int j = 0; j < AD; ++j)
+            lds_load16(rA, (live && kin) ? aoff[j] + it * G_BK : OOB_BASE,
+                       __builtin_amdgcn_readfirstlane(dst + j * 1024));
+    };
+    v4i av[2][MI];
+    auto read_a = [&](int set, int it, int s) {
+        const int8_t *Ab = reinterpret_cast<const int8_t *>(smem) + (it % A_BUFS) * ABUF;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int r = mi * 32 + (lane & 31);
+            const int ch = 4 * (lane >> 5) + s;
+            av[set][mi] = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
+        }
+    };
+    // The last row tile of a group is usually ragged: with RAGGED the MFMAs of
+    // the 32-row blocks that hold no row are skipped (ma is uniform over the
+    // block, so each test is a scalar branch).  The tests split the step into
+    // blocks that scheduling groups cannot span, which costs more than it
+    // saves with four fragments per wave (16 MFMAs per sub-step); those tiles
+    // keep the fixed issue order.  A second copy of the loop in one kernel
+    // makes the register allocator spill, so the choice is per instantiation.
+    constexpr bool RAGGED = MI > 1 && WN == 2;
+    const int ma = (rows + 31) >> 5;
+    auto mfma_sub = [&](int set, int d, int s) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            if (!RAGGED || mi == 0 || mi < ma) {
+#pragma unroll
+                for (int f = 0; f < WN; ++f)
+                    acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[d][f][s], av[set][mi], acc[mi][f], 0, 0, 0);
+            }
+        }
+    };
+
+    // Prologue, in an issue order that leaves as many loads behind each A
+    // transfer as the loop does (8 WN + AD behind the transfer a barrier waits
+    // for): A0, B0 sub-steps 0-2, A1, B0 sub-step 3, B1 sub-steps 0-2, A2, B1
+    // sub-step 3.
+    load_a(0);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) load_b_sub(0, 0, s);
+    load_a(1);
+    load_b_sub(0, 0, 3);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) load_b_sub(1 % DEPTH, 1, s);
+    load_a(2);
+    load_b_sub(1 % DEPTH, 1, 3);
+    static_assert(DEPTH == 2, "the prologue's issue order assumes a two-step B ring");
+    constexpr int VM_AFTER = 8 * WN + AD;   // loads issued behind an A transfer until its barrier
+    static_assert(VM_AFTER + AD <= 63, "vmcnt holds at most 63 outstanding loads");
+    lds_barrier<VM_AFTER + AD>();   // A0 complete (A1 and its followers may fly)
+    read_a(0, 0, 0);
+
+    // The trip count is padded to a multiple of DEPTH; the padding steps issue
+    // only out-of-range (zero, no traffic) loads.  B loads are never inside a
+    // branch, so the compiler counts outstanding loads exactly and each wait
+    // covers only the data it needs (the A transfers it does not see only make
+    // its waits a little later than needed).
+    const int nk_pad = (nk + DEPTH - 1) / DEPTH * DEPTH;
+    for (int it0 = 0; it0 < nk_pad; it0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int it = it0 + d;
+            // sub-steps 0-2: fragments of the next sub-step, this one's MFMAs,
+            // then the refill of its B registers with step it + DEPTH
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                read_a((s + 1) & 1, it, s + 1);
+                mfma_sub(s & 1, d, s);
+                load_b_sub(d, it + DEPTH, s);
+                if constexpr (!RAGGED) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);        // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);   // MFMAs
+                    __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);        // B loads
+                }
+            }
+            lds_barrier<VM_AFTER>();   // step it + 1's A is in LDS; buffer it % 3 is free
+            load_a(it + A_BUFS);
+            read_a(0, it + 1, 0);
+            mfma_sub(1, d, 3);
+            load_b_sub(d, it + DEPTH, 3);
+            if constexpr (!RAGGED) {
+                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);
+            }
+        }
+    }
+
+    // the transfers issued for steps past the end still write LDS: drain them
+    // (and every wave's last fragment reads) before the epilogue reuses it
+    lds_barrier<0>();
+    if constexpr (EPI == 0) {
+        if (a.ksplit > 1) {   // this slice's int32 sums
+            GemmArgs as = a;
+            as.out = reinterpret_cast<int32_t *>(a.out) + (int64_t)(kbeg / a.ksteps) * a.M_total * N;
+            gemm_epilogue_rows<BM, WN, EPI, OutT>(as, acc, ascale, cscw, rows, row0, nb, N);
+            return;
+        }
+    }
+    gemm_epilogue_rows<BM, WN, EPI, OutT>(a, acc, ascale, cscw, rows, row0, nb, N);
 }
 
 // Grouped W4A8 GEMM ("Qwen3-1.7B-W4A8 on Ascend", 4bit weights items 1-2):
@@ -871,25 +1290,36 @@ int64_t gemm_max_tiles(int64_t M_total, int64_t N, int G)
 
 size_t prefix_bytes(int G) { return ((size_t)(G + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
 
+template <int BM, int WN, int DEPTH, int EPI, typename OutT, bool PACKED>
+void launch_main_kernel(const GemmArgs &ga, dim3 grid, hipStream_t st)
+{
+    // 128 x 512 tiles: the LDS-ring kernel (the 16-bit fixed-point epilogue,
+    // which no tile table pairs with them, keeps the staged kernel)
+    if constexpr (WN == 4 && EPI != EPI_FIXED16)
+        hipLaunchKernelGGL((grouped_gemm_ring_kernel<BM, WN, DEPTH, EPI, OutT, PACKED>), grid, dim3(G_THREADS), 0, st,
+                           ga);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, EPI, OutT, PACKED>), grid, dim3(G_THREADS), 0, st, ga);
+}
+
 template <int BM, int WN, int DEPTH, bool PACKED>
 hipError_t launch_main_layout(const GemmArgs &ga, int epilogue, int out_dtype, hipStream_t st)
 {
     const int64_t max_tiles = ga.dense_rows > 0 ? (ga.M_total + BM - 1) / BM * ga.nblocks_n * ga.ksplit
                                                 : ((ga.M_total + BM - 1) / BM + ga.G) * ga.nblocks_n;
-    dim3 grid((unsigned)max_tiles), block(G_THREADS);
+    const dim3 grid((unsigned)max_tiles);
     if (epilogue == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 0, int32_t, PACKED>), grid, block, 0, st, ga);
+        launch_main_kernel<BM, WN, DEPTH, 0, int32_t, PACKED>(ga, grid, st);
     else if (epilogue == 1 && out_dtype == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, uint16_t, PACKED>), grid, block, 0, st, ga);
+        launch_main_kernel<BM, WN, DEPTH, 1, uint16_t, PACKED>(ga, grid, st);
     else if (epilogue == 1)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 1, float, PACKED>), grid, block, 0, st, ga);
+        launch_main_kernel<BM, WN, DEPTH, 1, float, PACKED>(ga, grid, st);
     else if (epilogue == EPI_FIXED16)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, EPI_FIXED16, int16_t, PACKED>), grid, block, 0, st,
-                           ga);
+        launch_main_kernel<BM, WN, DEPTH, EPI_FIXED16, int16_t, PACKED>(ga, grid, st);
     else if (out_dtype == 0)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, uint16_t, PACKED>), grid, block, 0, st, ga);
+        launch_main_kernel<BM, WN, DEPTH, 2, uint16_t, PACKED>(ga, grid, st);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, WN, DEPTH, 2, float, PACKED>), grid, block, 0, st, ga);
+        launch_main_kernel<BM, WN, DEPTH, 2, float, PACKED>(ga, grid, st);
     return hipGetLastError();
 }
 
