@@ -292,7 +292,7 @@ def test_quant_act_adversarial_rows(cols):
                                      (257, 2064, 128, 8), (520, 2064, 63, 8), (300, 80, 200, 11),
                                      (700, 32, 256, 16), (600, 48, 8, 2), (3, 8192, 128, 8),
                                      (2, 1040, 64, 4), (5, 1536, 256, 8), (300, 1040, 128, 8),
-                                     (33, 528, 130, 5)])
+                                     (33, 528, 130, 5), (600, 6160, 128, 8), (520, 9232, 60, 8)])
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
 def test_route_shapes(T, H, E, k, xdt):
     """Expert counts that fill 1..4 slices of 64 (ragged ones included), odd
@@ -300,8 +300,9 @@ def test_route_shapes(T, H, E, k, xdt):
     With bf16 activations up to 512 (token, expert-slice) pairs take the
     vector-ALU router, more take the matrix-core one: both sides of that
     switch are here, with hidden sizes that leave a tail of W_g steps, and
-    hidden sizes of 1 to 16 chunks of 512 (short last chunks included), which
-    the vector-ALU router spreads over 1 to 8 waves per expert slice.  Each
+    hidden sizes of 1 to 19 chunks of 512 (short last chunks included), which
+    the vector-ALU router spreads over 1 to 8 waves per expert slice and the
+    matrix-core one over 1 to 16 waves of one or two chunks each.  Each
     case runs with the [E][H] weight and with its packed copy (with bf16
     tokens and few of them: the chunk-parallel kernel)."""
     rng = np.random.default_rng(T * 1000 + E)
@@ -316,6 +317,33 @@ def test_route_shapes(T, H, E, k, xdt):
         assert np.array_equal(to_host(logits), ologits)
         assert np.array_equal(to_host(ids), oids)
         assert np.abs(to_host(w) - ow).max() <= 2e-6
+
+
+@pytest.mark.parametrize("T,H,E,k", [(8192, 2064, 128, 8),    # two slices, 5 chunks (a short last one)
+                                     (8200, 1040, 60, 4),     # one slice, a last block of 8 tokens
+                                     (8192, 4624, 128, 8),    # two slices, two chunks per wave
+                                     (8192, 8720, 64, 8)])    # one slice, two chunks per wave
+def test_route_matrix_core_many_tokens(T, H, E, k):
+    """bf16 tokens in 256 or more blocks of 32 (the 32 x 32 x 1 matrix-core
+    router): logits, ids and weights against the oracle with the [E][H] and
+    the packed router weight; then an all-zero router (every score +0,
+    experts 0..k-1 in order) and the fused token quantisation of that kernel
+    against the quantiser's oracle."""
+    rng = np.random.default_rng(T + H + E)
+    x = synth.f32_to_bf16_bits(rng.standard_t(4, (T, H)).astype(np.float32))
+    wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    oids, ow, ologits = oracle.route_topk(x, wg, k)
+    wgd = dev_bf16(wg)
+    for packed in (None, w8.router_pack(wgd)):
+        ids, w, logits = w8.route_topk(to_dev(x), wgd, k, True, return_logits=True, w_gate_packed=packed)
+        assert np.array_equal(to_host(logits), ologits)
+        assert np.array_equal(to_host(ids), oids)
+        assert np.abs(to_host(w) - ow).max() <= 2e-6
+    if (T, H) == (8192, 2064):
+        z = np.zeros((E, H), np.uint16)
+        ids, w = w8.route_topk(to_dev(x), dev_bf16(z), k, w_gate_packed=w8.router_pack(dev_bf16(z)))
+        assert np.all(to_host(ids) == np.arange(k))
+        assert np.all(to_host(w) == np.float32(1.0 / k))
 
 
 @pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_30b_decode_T64", "moe_235b_zipf_T8192"])

@@ -468,6 +468,192 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
     }
 }
 
+// bf16 activations, many tokens: the score chains on the 32 x 32 x 1 fp32
+// matrix instruction (v_mfma_f32_32x32x1_2b_f32).  Its two blocks each add a
+// 32 x 32 outer product of one hidden index to their accumulators; every
+// product of two bf16 values is exact in fp32, so each step is exactly one
+// fused multiply-add of each of the 2048 chains it holds.  A wave takes 32
+// tokens (lane l feeds token l % 32 to both blocks), all 64 S experts (S
+// accumulators; lane l feeds expert 64 j + l of slice j: block l / 32), and
+// one run of CPW of the score's 512-index chunks.  Each x operand is used 64 S
+// times and each W_g operand 32 times, so the lanes load them straight from
+// memory (x rows and W_g, both L2-resident after the first touch) into
+// registers, D steps of 8 indices ahead, and widen the bf16 pairs in
+// registers: no LDS staging and no barrier until the chains end.
+//
+// A block is 32 tokens and NCW waves, one per chunk run.  The chunk sums then
+// meet in LDS in ascending chunk order (the run of wave 0 first, each later
+// run adding its chunks one at a time to the running total), the top-k runs
+// on the totals, and with xq the block quantises its tokens (per-token amax
+// from the values the waves loaded, codes from a second, L2-resident read of
+// the rows).
+//
+// Output layout of the instruction: block b of the result sits in registers
+// 16 b .. 16 b + 15; register 16 b + 4 q + r of lane l holds row 8 q + 4 (l / 32)
+// + r, column l % 32 (rows: tokens, columns: experts).
+namespace {
+constexpr int R32_TOK = 32;   // tokens per block
+constexpr int R32_STEPS = RT_CHUNK / 8;
+constexpr int R32_MAX_WAVES = 16;   // waves (chunk runs) per block: 16 with one slice, 8 with two
+constexpr int r32_max_waves(int S) { return S == 1 ? 16 : 8; }
+// 8-index steps in flight per lane: 8 with two slices (a block of at most 8
+// waves, 256 registers each), 4 with one (16 waves, 128 registers)
+constexpr int r32_depth(int S) { return S == 1 ? 4 : 8; }
+}
+
+template <int S, int CPW, bool PACKED>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
+__global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
+                                                            int E, int k, int renorm, int NCW,
+                                                            int32_t *__restrict__ ids, float *__restrict__ wout,
+                                                            float *__restrict__ logits_out, int8_t *__restrict__ xq,
+                                                            float *__restrict__ sx)
+{
+    static_assert(S == 1 || S == 2, "slices");
+    constexpr int R32_D = r32_depth(S);
+    static_assert(R32_STEPS % R32_D == 0, "chunks end at pass ends");
+    typedef float v32f __attribute__((ext_vector_type(32)));
+    __shared__ float rt[S][R32_TOK][64 + 1];    // running totals, then the scores
+    __shared__ __attribute__((aligned(16))) uint32_t tk_scr[8][512];
+    __shared__ float xm[R32_MAX_WAVES][R32_TOK];   // per-run |x| maxima of the block's tokens
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int run = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the run bounds stay scalar
+    const int64_t tb = (int64_t)blockIdx.x * R32_TOK;
+    const int nst = (int)(H / 8);
+    const int nch = (nst + R32_STEPS - 1) / R32_STEPS;
+    const int c_beg = min(nch, run * CPW), c_end = min(nch, c_beg + CPW);
+    const int s_beg = c_beg * R32_STEPS, s_end = min(nst, c_end * R32_STEPS);
+
+    // offsets: an out-of-range one (absent token or expert, or a step past the
+    // run) starts at OOB and stays above the resource size, so it reads zeros
+    constexpr uint32_t OOB = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, 0x7ffffff0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, 0x7ffffff0, 0x00020000);
+    const int tok = lane & 31;
+    const uint32_t xrow = tb + tok < T_ ? (uint32_t)((tb + tok) * H * 2) : OOB;
+    uint32_t wrow[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int e = 64 * j + lane;
+        wrow[j] = e < E ? (PACKED ? (uint32_t)e * 16u : (uint32_t)((int64_t)e * H * 2)) : OOB;
+    }
+    const uint32_t wstep = PACKED ? (uint32_t)E * 16u : 16u;   // bytes between steps of one expert
+    uint4 xr[R32_D], wr[R32_D][S];
+    auto load = [&](int slot, int st) {
+        const bool live = st < s_end;
+        xr[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rx, live ? xrow + (uint32_t)st * 16u : OOB, 0, 0));
+#pragma unroll
+        for (int j = 0; j < S; ++j)
+            wr[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rw, live ? wrow[j] + (uint32_t)st * wstep : OOB, 0, 0));
+    };
+#pragma unroll
+    for (int d = 0; d < R32_D; ++d) load(d, s_beg + d);
+
+    v32f acc[CPW][S];
+    float xmax = 0.0f;
+    // one step: the 8 indices of slot d into the chains, then the slot's
+    // refill with step st + R32_D (st % R32_D == d: chunks start at multiples)
+    auto step = [&](v32f (&a)[S], int d, int st) {
+        const uint32_t u[4] = {xr[d].x, xr[d].y, xr[d].z, xr[d].w};
+        // hidden 8 st + 2 i is the low half of word i, 8 st + 2 i + 1 the high half
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x0 = __uint_as_float(u[i] << 16), x1 = __uint_as_float(u[i] & 0xffff0000u);
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                const uint32_t w = (&wr[d][j].x)[i];
+                a[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(x0, __uint_as_float(w << 16), a[j], 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                const uint32_t w = (&wr[d][j].x)[i];
+                a[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(x1, __uint_as_float(w & 0xffff0000u), a[j], 0, 0, 0);
+            }
+            xmax = fmaxf(xmax, fmaxf(fabsf(x0), fabsf(x1)));
+        }
+        load(d, st + R32_D);
+        // keep the refill here: scheduled to the end of the pass, each load
+        // would be waited for right after it is issued
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) {
+        v32f a[S];
+#pragma unroll
+        for (int j = 0; j < S; ++j) a[j] = v32f{};
+        const int cs = s_beg + ci * R32_STEPS;
+        const int ce = min(s_end, cs + R32_STEPS);
+        const int cf = cs + max(0, ce - cs) / R32_D * R32_D;   // end of the whole passes
+        for (int st0 = cs; st0 < cf; st0 += R32_D) {
+#pragma unroll
+            for (int d = 0; d < R32_D; ++d) step(a, d, st0 + d);
+        }
+#pragma unroll
+        for (int d = 0; d < R32_D; ++d)   // a chunk's last, partial pass (only where H ends inside it)
+            if (cf + d < ce) step(a, d, cf + d);
+#pragma unroll
+        for (int j = 0; j < S; ++j) acc[ci][j] = a[j];
+    }
+    if (xq && lane < 32) xm[run][tok] = xmax;
+
+    // chunk sums into the running totals, runs in ascending order
+    for (int r = 0; r < NCW; ++r) {
+        if (run == r && c_beg < c_end) {
+#pragma unroll
+            for (int j = 0; j < S; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int reg = 4 * q + i;   // block reg / 16
+                        const int row = 8 * (q & 3) + 4 * (lane >> 5) + i;
+                        const int col = 32 * (q >> 2) + (lane & 31);
+                        float t = r == 0 ? acc[0][j][reg] : rt[j][row][col] + acc[0][j][reg];
+#pragma unroll
+                        for (int ci = 1; ci < CPW; ++ci)
+                            if (c_beg + ci < c_end) t = t + acc[ci][j][reg];
+                        rt[j][row][col] = t;
+                    }
+        }
+        __syncthreads();
+    }
+
+    const int ntk = min(NCW, 8);   // waves that run the top-k
+    for (int tt = run; tt < R32_TOK && run < 8; tt += ntk) {
+        const int64_t t = tb + tt;
+        if (t >= T_) break;
+        float l4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? rt[j][tt][lane] : 0.0f;
+        select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[run]);
+    }
+
+    // Per-token int8 codes, when asked for, with the quantisation kernels'
+    // arithmetic: the waves saw every element of the block's rows.
+    if (xq) {
+        const int tpr = 64 * NCW / R32_TOK;   // threads per token row
+        const int row = tid / tpr, t8 = tid % tpr;
+        const int64_t t = tb + row;
+        if (t < T_) {
+            float amax = 0.0f;
+            for (int r = 0; r < NCW; ++r) amax = fmaxf(amax, xm[r][row]);
+            const float s = amax / 127.0f;
+            const float y = s > 0.0f ? 1.0f / s : 0.0f;
+            const bool fast = s >= QUANT_FAST_MIN_SCALE;
+            if (t8 == 0) sx[t] = s;
+            for (int64_t c = (int64_t)t8 * 8; c < H; c += tpr * 8) {
+                float v[8];
+                load8_f32(x + t * H + c, v);
+                *reinterpret_cast<uint2 *>(xq + t * H + c) = s != 0.0f ? pack8(v, s, y, fast) : make_uint2(0u, 0u);
+            }
+        }
+    }
+}
+
 // Vector-ALU router for few tokens.  A wavefront owns TPW tokens, one slice
 // of 64 experts and a run of the score's 512-index chunks: lane l runs the TPW
 // fma chains of expert 64 sl + l over those chunks (v_fma_f32 is exactly the
@@ -753,6 +939,25 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
                 else if (S == 2) go(route_valu_kernel<2, TP, false>);
                 else go(route_valu_kernel<4, TP, false>);
             }
+            return hipGetLastError();
+        }
+        // up to 128 experts: the 32 x 32 x 1 kernel, one wave per slice and
+        // run of one or two chunks, at most 16 waves
+        const int nch = (int)((H / 8 + R32_STEPS - 1) / R32_STEPS);
+        const int64_t ngrp = (T + R32_TOK - 1) / R32_TOK;
+        if (S <= 2 && nch <= 2 * r32_max_waves(S) && ngrp >= 256) {
+            const int cpw = nch <= r32_max_waves(S) ? 1 : 2;
+            const int ncw = (nch + cpw - 1) / cpw;
+            const dim3 g32((unsigned)ngrp), b32(64 * ncw);
+            const uint16_t *wv = wg_packed ? wg_packed : wg;
+            auto go32 = [&](auto kern) {
+                hipLaunchKernelGGL(kern, g32, b32, 0, st, xb, wv, T, H, E, k, renormalize, ncw, ids, w, logits, xq,
+                                   sx);
+            };
+            if (S == 1 && cpw == 1) wg_packed ? go32(route_mfma32_kernel<1, 1, true>) : go32(route_mfma32_kernel<1, 1, false>);
+            else if (S == 1) wg_packed ? go32(route_mfma32_kernel<1, 2, true>) : go32(route_mfma32_kernel<1, 2, false>);
+            else if (cpw == 1) wg_packed ? go32(route_mfma32_kernel<2, 1, true>) : go32(route_mfma32_kernel<2, 1, false>);
+            else wg_packed ? go32(route_mfma32_kernel<2, 2, true>) : go32(route_mfma32_kernel<2, 2, false>);
             return hipGetLastError();
         }
         const int64_t nblk = (T + 32 / S - 1) / (32 / S);
