@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5033.0       # 256 CU x 2.4 GHz x 8192 int8 ops/clk/CU (dense)
 HBM_PEAK_GBS = 8000.0
+FP32_MATRIX_PEAK_TFLOPS = 157.3
 RIDGE = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 DEFAULT_WORKLOAD = "moe_235b_zipf_T8192"
 
@@ -172,12 +173,13 @@ def _csv_rows(path):
 
 def counter_summary(args):
     """Per-kernel summary of one rocprofv3 --pmc run with --kernel-trace:
-    int8 matrix-core operations (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512), matrix-core
-    busy cycles (SQ_VALU_MFMA_BUSY_CYCLES, summed over the SIMDs) against the
-    active cycles of one XCD (GRBM_GUI_ACTIVE, summed over the XCDs, / 8) times
-    the SIMDs, the clock those cycles imply over the traced duration, and the
-    int8 rate against the dense peak at 2.4 GHz and at that clock.  Prints
-    markdown."""
+    matrix-core operations (SQ_INSTS_VALU_MFMA_MOPS_I8, or _F32 for the fp32
+    router, x 512), matrix-core busy cycles (SQ_VALU_MFMA_BUSY_CYCLES, summed
+    over the SIMDs) against the active cycles of one XCD (GRBM_GUI_ACTIVE,
+    summed over the XCDs, / 8) times the SIMDs, the clock those cycles imply
+    over the traced duration, and the rate against the dense peak of that
+    type (int8 5.0 POP/s, fp32 matrix 157.3 TFLOP/s) at 2.4 GHz and at that
+    clock.  Prints markdown."""
     pmc_csv, trace_csv = args.counter_summary
     disp = {}
     for r in _csv_rows(pmc_csv):
@@ -192,27 +194,30 @@ def counter_summary(args):
     for key, d in disp.items():
         if key in dur:
             by_kernel.setdefault(d["kernel"], []).append((d["c"], dur[key]))
-    lines = ["| kernel | dispatches | avg us | int8 ops (MOPS_I8 x 512) | MFMA busy / (XCD active cycles x SIMDs) | "
-             "clock = XCD active cycles / duration | int8 TOPS | of peak at 2.4 GHz | of peak at that clock |",
+    f32 = any("SQ_INSTS_VALU_MFMA_MOPS_F32" in r[0] for rows in by_kernel.values() for r in rows)
+    mops, kind, peak = ("SQ_INSTS_VALU_MFMA_MOPS_F32", "fp32", FP32_MATRIX_PEAK_TFLOPS) if f32 else \
+        ("SQ_INSTS_VALU_MFMA_MOPS_I8", "int8", INT8_PEAK_TOPS)
+    lines = ["| kernel | dispatches | avg us | %s ops (MOPS x 512) | MFMA busy / (XCD active cycles x SIMDs) | "
+             "clock = XCD active cycles / duration | %s TOP/s | of peak at 2.4 GHz | of peak at that clock |" % (kind, kind),
              "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for kern, rows in sorted(by_kernel.items(), key=lambda kv: -sum(t for _, t in kv[1])):
         n = len(rows)
         t = sum(r[1] for r in rows) / n
         c = {name: sum(r[0].get(name, 0.0) for r in rows) / n for name in rows[0][0]}
-        ops = c.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0) * 512
+        ops = c.get(mops, 0.0) * 512
         gui = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
         busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
         util = busy / (gui * SIMDS) if gui else 0.0
         clk = gui / t if t else 0.0
         tops = ops / t / 1e12 if t else 0.0
-        at_clk = ops / t / (INT8_PEAK_TOPS * 1e12 * clk / PEAK_CLOCK_HZ) if ops and clk else 0.0
+        at_clk = ops / t / (peak * 1e12 * clk / PEAK_CLOCK_HZ) if ops and clk else 0.0
         name = kern if len(kern) < 90 else kern[:87] + "..."
         # GRBM_GUI_ACTIVE also counts the dispatch's own start and drain, so the
         # implied clock means something only for launches far longer than that
         clk_s = "%.2f GHz" % (clk / 1e9) if t >= 100e-6 else "-"
         at_s = "%.3f" % at_clk if t >= 100e-6 else "-"
         lines.append("| `%s` | %d | %.1f | %.4g | %.3f | %s | %.0f | %.3f | %s |"
-                     % (name, n, t * 1e6, ops, util, clk_s, tops, tops / INT8_PEAK_TOPS, at_s))
+                     % (name, n, t * 1e6, ops, util, clk_s, tops, tops / peak, at_s))
     print("\n".join(lines))
 
 
