@@ -55,12 +55,14 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(int32_t *__res
     int32_t run = 0;
     if (tid < E) {
         int64_t c = 0;
-        for (; c + 8 <= nchunks; c += 8) {   // eight independent loads in flight
-            int32_t v[8];
+        // 32 independent loads in flight (a thread's walk over the chunks is a
+        // chain of memory round trips: 128 chunks take four, not sixteen)
+        for (; c + 32 <= nchunks; c += 32) {
+            int32_t v[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = chunk_counts[(c + u) * E + tid];
+            for (int u = 0; u < 32; ++u) v[u] = chunk_counts[(c + u) * E + tid];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 chunk_counts[(c + u) * E + tid] = run;
                 run += v[u];
             }
