@@ -738,8 +738,6 @@ void grouped_gemm_ring_kernel(GemmArgs a)
 {
     static_assert(WN == 4 && EPI != EPI_FIXED16, "built for the 128 x 512 tiles");
     static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH");
-    static_assert(EPI != 2 || WN % 2 == 0, "SwiGLU pairs gate and up fragments");
-    static_assert(EPI != EPI_FIXED16 || WN % 2 == 0, "16-bit fixed point takes 64-column segments");
     constexpr int MI = BM / 32;      // 32-row MFMA tiles per wave
     constexpr int WCOLS = 32 * WN;   // B rows (output columns) per wave
     // LDS: the ring of A_BUFS A buffers of the K loop
@@ -897,24 +895,15 @@ void grouped_gemm_ring_kernel(GemmArgs a)
             av[set][mi] = *reinterpret_cast<const v4i *>(Ab + r * G_BK + ((ch ^ (r & 7)) << 4));
         }
     };
-    // The last row tile of a group is usually ragged: with RAGGED the MFMAs of
-    // the 32-row blocks that hold no row are skipped (ma is uniform over the
-    // block, so each test is a scalar branch).  The tests split the step into
-    // blocks that scheduling groups cannot span, which costs more than it
-    // saves with four fragments per wave (16 MFMAs per sub-step); those tiles
-    // keep the fixed issue order.  A second copy of the loop in one kernel
-    // makes the register allocator spill, so the choice is per instantiation.
-    constexpr bool RAGGED = MI > 1 && WN == 2;
-    const int ma = (rows + 31) >> 5;
+    // Every 32-row block of the tile is multiplied, ragged tiles included:
+    // skipping the empty blocks (a branch per block, or a loop copy per count
+    // of occupied blocks) measured slower on these tiles.
     auto mfma_sub = [&](int set, int d, int s) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            if (!RAGGED || mi == 0 || mi < ma) {
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int f = 0; f < WN; ++f)
-                    acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[d][f][s], av[set][mi], acc[mi][f], 0, 0, 0);
-            }
-        }
+            for (int f = 0; f < WN; ++f)
+                acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[d][f][s], av[set][mi], acc[mi][f], 0, 0, 0);
     };
 
     // Prologue, in an issue order that leaves as many loads behind each A
@@ -953,22 +942,18 @@ void grouped_gemm_ring_kernel(GemmArgs a)
                 read_a((s + 1) & 1, it, s + 1);
                 mfma_sub(s & 1, d, s);
                 load_b_sub(d, it + DEPTH, s);
-                if constexpr (!RAGGED) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);        // LDS reads
-                    __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);   // MFMAs
-                    __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);        // B loads
-                }
+                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);        // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);   // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);        // B loads
             }
             lds_barrier<VM_AFTER>();   // step it + 1's A is in LDS; buffer it % 3 is free
             load_a(it + A_BUFS);
             read_a(0, it + 1, 0);
             mfma_sub(1, d, 3);
             load_b_sub(d, it + DEPTH, 3);
-            if constexpr (!RAGGED) {
-                __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);
-            }
+            __builtin_amdgcn_sched_group_barrier(0x100, MI, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * WN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, WN, 0);
         }
     }
 
