@@ -474,6 +474,66 @@ def bench_ep_shares(args, cfg, ngpu):
     print(json.dumps(result), flush=True)
 
 
+def vendor_int8(args, cfg):
+    """The workload's two expert GEMMs as one dense int8 GEMM each (all T*k
+    routed rows against one expert's weights: the same operations, none of the
+    grouping), timed in the ROCm BLAS library's int8 GEMM (torch._int_mm,
+    int32 out) and in this library's one-group grouped GEMM on the same
+    operands (int32 out, and the bf16 dequantised out the layer's GEMMs write).
+    The codes are rounded normal draws (std 32, clipped to +-127), seeded.
+    Context for the kernels' fractions of peak, not a layer measurement."""
+    import torch
+
+    import w8a8_int8_quantized_bf16_amd as w8
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    M = cfg.T * cfg.k
+
+    def codes(r, c):
+        return (torch.randn(r, c, device=dev, generator=gen) * 32).round_().clamp_(-127, 127).to(torch.int8)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(args.steps):
+            e_a.record()
+            fn()
+            e_b.record()
+            torch.cuda.synchronize()
+            ts.append(e_a.elapsed_time(e_b) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    rows = []
+    for name, K, N in (("gate_up", cfg.H, 2 * cfg.I), ("down", cfg.I, cfg.H)):
+        A, B = codes(M, K), codes(N, K)
+        ops = 2.0 * M * N * K
+        ref = torch._int_mm(A, B.t())
+        t_lib = timed(lambda: torch._int_mm(A, B.t()))
+        Bp = w8.pack_weights(B.view(1, N, K))
+        off = torch.tensor([0, M], dtype=torch.int32, device=dev)
+        sa = torch.ones(M, dtype=torch.float32, device=dev)
+        sb = torch.ones(N, dtype=torch.float32, device=dev)
+        raw = lambda: w8.grouped_gemm(A, sa, None, 1, Bp, sb, off, w8.EPI_RAW_I32, M_total=M, b_shape=(1, N, K))
+        same = bool(torch.equal(raw(), ref))
+        t_raw = timed(raw)
+        t_bf = timed(lambda: w8.grouped_gemm(A, sa, None, 1, Bp, sb, off, w8.EPI_DEQUANT, w8.BF16, M_total=M,
+                                             b_shape=(1, N, K)))
+        rows.append({"gemm": name, "M": M, "K": K, "N": N, "torch_int_mm_us": round(t_lib, 1),
+                     "own_int32_us": round(t_raw, 1), "own_bf16_us": round(t_bf, 1), "int32_equal": same,
+                     "torch_int_mm_tops": round(ops / t_lib / 1e6), "own_int32_tops": round(ops / t_raw / 1e6),
+                     "own_bf16_tops": round(ops / t_bf / 1e6)})
+        log("%s M=%d K=%d N=%d: torch._int_mm %.1f us, own int32 %.1f us (equal %s), own bf16 %.1f us"
+            % (name, M, K, N, t_lib, t_raw, same, t_bf))
+        del A, B, Bp, ref
+        torch.cuda.empty_cache()
+    print(json.dumps({"vendor_int8": cfg.name, "median_of": args.steps, "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +557,8 @@ def main():
                     default=["gate_up_gemm", "void w8a8::grouped_gemm_kernel<128, 2, 2, 2, unsigned short, true>",
                              "gemm.hip"])
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--vendor-int8", action="store_true",
+                    help="time the workload's GEMMs as dense int8 GEMMs in torch._int_mm and in this library, and exit")
     ap.add_argument("--counter-summary", nargs=2, metavar=("PMC_CSV", "TRACE_CSV"),
                     help="print a per-kernel summary of a rocprofv3 --pmc run (matrix-core counters) and exit")
     args = ap.parse_args()
@@ -525,6 +587,8 @@ def main():
         return bench_dense(args, synth.DENSE_CONFIGS[args.workload])
     if args.ep_share:
         return bench_ep_shares(args, synth.MOE_CONFIGS[args.workload], args.ep_share)
+    if args.vendor_int8:
+        return vendor_int8(args, synth.MOE_CONFIGS[args.workload])
     cfg = synth.MOE_CONFIGS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)

@@ -387,9 +387,6 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs &a, v16i (&acc
     const int ocol0 = EPI == 2 ? nb * (4 * WCOLS / 2) + wave * (WCOLS / 2) : nb * (4 * WCOLS) + wave * WCOLS;
     const int half = 4 * (lane >> 5);
     auto scales4 = [&](int f, int g) { return *reinterpret_cast<const float4 *>(csc + 32 * f + 8 * g + half); };
-    auto pack2 = [](float x, float y) {
-        return (uint32_t)float_to_bf16_bits(x) | ((uint32_t)float_to_bf16_bits(y) << 16);
-    };
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
         const int r = mi * 32 + (lane & 31);
@@ -470,7 +467,7 @@ __device__ __forceinline__ void gemm_epilogue_rows(const GemmArgs &a, v16i (&acc
                                 make_float4(o[0], o[1], o[2], o[3]);
                         else
                             *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(a.out) + obase + c) =
-                                make_uint2(pack2(o[0], o[1]), pack2(o[2], o[3]));
+                                make_uint2(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]));
                     }
                 }
         }

@@ -501,7 +501,8 @@ constexpr int r32_max_waves(int S) { return S == 1 ? 16 : 8; }
 constexpr int r32_depth(int S) { return S == 1 ? 4 : 8; }
 }
 
-template <int S, int CPW, bool PACKED>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
+// QX: the block also quantises its tokens (xq and sx are then given)
+template <int S, int CPW, bool PACKED, bool QX>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
 __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
                                                             int E, int k, int renorm, int NCW,
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
                 const uint32_t w = (&wr[d][j].x)[i];
                 a[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(x1, __uint_as_float(w & 0xffff0000u), a[j], 0, 0, 0);
             }
-            xmax = fmaxf(xmax, fmaxf(fabsf(x0), fabsf(x1)));
+            if constexpr (QX) xmax = fmaxf(xmax, fmaxf(fabsf(x0), fabsf(x1)));
         }
         load(d, st + R32_D);
         // keep the refill here: scheduled to the end of the pass, each load
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
 #pragma unroll
         for (int j = 0; j < S; ++j) acc[ci][j] = a[j];
     }
-    if (xq && lane < 32) xm[run][tok] = xmax;
+    if (QX && lane < 32) xm[run][tok] = xmax;
 
     // chunk sums into the running totals, runs in ascending order
     for (int r = 0; r < NCW; ++r) {
@@ -622,6 +623,31 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         __syncthreads();
     }
 
+    // Per-token int8 codes, when asked for, with the quantisation kernels'
+    // arithmetic: the waves saw every element of the block's rows, so each
+    // token's scale is known; the codes need a second read of the rows.  A
+    // thread takes every tpr-th 8-element piece of one row and reads its pieces
+    // QB at a time into one of two register batches, the first batch before the
+    // top-k (its latency then hides behind the top-k) and each next one before
+    // the codes of the current (one load waited for per piece left the block's
+    // tail bound by memory latency).
+    constexpr int QB = 8;
+    const int tpr = 64 * NCW / R32_TOK;   // threads per token row
+    const int qrow = tid / tpr, t8 = tid % tpr;
+    const int64_t qt = tb + qrow;
+    const int npc = (int)(H / 8);   // 8-element pieces per row
+    const uint32_t qbase = (QX && qt < T_) ? (uint32_t)(qt * H * 2) : OOB;
+    uint4 qa[QB], qb[QB];
+    auto qload = [&](uint4(&q)[QB], int i0) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const int p = t8 + tpr * (i0 + b);
+            q[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rx, (qbase != OOB && p < npc) ? qbase + (uint32_t)p * 16u : OOB, 0, 0));
+        }
+    };
+    if constexpr (QX) qload(qa, 0);
+
     const int ntk = min(NCW, 8);   // waves that run the top-k
     for (int tt = run; tt < R32_TOK && run < 8; tt += ntk) {
         const int64_t t = tb + tt;
@@ -632,24 +658,37 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[run]);
     }
 
-    // Per-token int8 codes, when asked for, with the quantisation kernels'
-    // arithmetic: the waves saw every element of the block's rows.
-    if (xq) {
-        const int tpr = 64 * NCW / R32_TOK;   // threads per token row
-        const int row = tid / tpr, t8 = tid % tpr;
-        const int64_t t = tb + row;
-        if (t < T_) {
-            float amax = 0.0f;
-            for (int r = 0; r < NCW; ++r) amax = fmaxf(amax, xm[r][row]);
-            const float s = amax / 127.0f;
-            const float y = s > 0.0f ? 1.0f / s : 0.0f;
-            const bool fast = s >= QUANT_FAST_MIN_SCALE;
-            if (t8 == 0) sx[t] = s;
-            for (int64_t c = (int64_t)t8 * 8; c < H; c += tpr * 8) {
-                float v[8];
-                load8_f32(x + t * H + c, v);
-                *reinterpret_cast<uint2 *>(xq + t * H + c) = s != 0.0f ? pack8(v, s, y, fast) : make_uint2(0u, 0u);
+    if (QX && qbase != OOB) {
+        float amax = 0.0f;
+        for (int r = 0; r < NCW; ++r) amax = fmaxf(amax, xm[r][qrow]);
+        const float s = amax / 127.0f;
+        const float y = s > 0.0f ? 1.0f / s : 0.0f;
+        const bool fast = s >= QUANT_FAST_MIN_SCALE;
+        if (t8 == 0) sx[qt] = s;
+        int8_t *qdst = xq + qt * H;
+        auto qstore = [&](const uint4(&q)[QB], int i0) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int p = t8 + tpr * (i0 + b);
+                if (p < npc) {
+                    const uint32_t u[4] = {q[b].x, q[b].y, q[b].z, q[b].w};
+                    float v[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[2 * i] = __uint_as_float(u[i] << 16);
+                        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+                    }
+                    *reinterpret_cast<uint2 *>(qdst + 8 * p) = s != 0.0f ? pack8(v, s, y, fast) : make_uint2(0u, 0u);
+                }
             }
+        };
+        const int nit = (npc + tpr - 1) / tpr;   // pieces of the threads with the most
+        for (int i0 = 0; i0 < nit; i0 += 2 * QB) {
+            qload(qb, i0 + QB);
+            qstore(qa, i0);
+            if (i0 + QB >= nit) break;
+            qload(qa, i0 + 2 * QB);
+            qstore(qb, i0 + QB);
         }
     }
 }
@@ -954,10 +993,19 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
                 hipLaunchKernelGGL(kern, g32, b32, 0, st, xb, wv, T, H, E, k, renormalize, ncw, ids, w, logits, xq,
                                    sx);
             };
-            if (S == 1 && cpw == 1) wg_packed ? go32(route_mfma32_kernel<1, 1, true>) : go32(route_mfma32_kernel<1, 1, false>);
-            else if (S == 1) wg_packed ? go32(route_mfma32_kernel<1, 2, true>) : go32(route_mfma32_kernel<1, 2, false>);
-            else if (cpw == 1) wg_packed ? go32(route_mfma32_kernel<2, 1, true>) : go32(route_mfma32_kernel<2, 1, false>);
-            else wg_packed ? go32(route_mfma32_kernel<2, 2, true>) : go32(route_mfma32_kernel<2, 2, false>);
+            auto pick = [&](auto qx) {
+                constexpr bool QX = decltype(qx)::value;
+                if (S == 1 && cpw == 1)
+                    wg_packed ? go32(route_mfma32_kernel<1, 1, true, QX>) : go32(route_mfma32_kernel<1, 1, false, QX>);
+                else if (S == 1)
+                    wg_packed ? go32(route_mfma32_kernel<1, 2, true, QX>) : go32(route_mfma32_kernel<1, 2, false, QX>);
+                else if (cpw == 1)
+                    wg_packed ? go32(route_mfma32_kernel<2, 1, true, QX>) : go32(route_mfma32_kernel<2, 1, false, QX>);
+                else
+                    wg_packed ? go32(route_mfma32_kernel<2, 2, true, QX>) : go32(route_mfma32_kernel<2, 2, false, QX>);
+            };
+            if (xq) pick(std::true_type{});
+            else pick(std::false_type{});
             return hipGetLastError();
         }
         const int64_t nblk = (T + 32 / S - 1) / (32 / S);
