@@ -327,8 +327,10 @@ def test_route_matrix_core_many_tokens(T, H, E, k):
     """bf16 tokens in 256 or more blocks of 32 (the 32 x 32 x 1 matrix-core
     router): logits, ids and weights against the oracle with the [E][H] and
     the packed router weight; then an all-zero router (every score +0,
-    experts 0..k-1 in order) and the fused token quantisation of that kernel
-    against the quantiser's oracle."""
+    experts 0..k-1 in order) and, inside a layer, the fused token quantisation
+    of that kernel against the quantiser's oracle (rows read once where they
+    fit the wave's registers, twice where not: H = 4624 and 8720; a ragged
+    last block at T = 8200)."""
     rng = np.random.default_rng(T + H + E)
     x = synth.f32_to_bf16_bits(rng.standard_t(4, (T, H)).astype(np.float32))
     wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
@@ -344,6 +346,20 @@ def test_route_matrix_core_many_tokens(T, H, E, k):
         ids, w = w8.route_topk(to_dev(x), dev_bf16(z), k, w_gate_packed=w8.router_pack(dev_bf16(z)))
         assert np.all(to_host(ids) == np.arange(k))
         assert np.all(to_host(w) == np.float32(1.0 / k))
+    # the fused token quantisation, which only the layer asks for: a layer of
+    # small experts (I = 32) around the same router, its ids, codes and scales
+    I = 32
+    gu = (rng.standard_normal((E, 2 * I, H)) * 0.02).astype(np.float32)
+    dn = (rng.standard_normal((E, H, I)) * 0.02).astype(np.float32)
+    W = w8.MoEWeights.quantize(wgd, to_dev(gu), to_dev(dn), k)
+    del gu, dn
+    ws = w8.moe_layer_workspace(W, T, w8.BF16)
+    w8.moe_layer(W, to_dev(x), ws=ws)
+    torch.cuda.synchronize()
+    inter = w8.moe_layer_intermediates(W, T, ws, w8.BF16)
+    assert np.array_equal(to_host(inter["ids"]), oids)
+    oxq, osx = oracle.quant_rows(x)
+    assert np.array_equal(to_host(inter["xq"]), oxq) and np.array_equal(to_host(inter["sx"]), osx)
 
 
 @pytest.mark.parametrize("name", ["moe_30b_prefill_T4096", "moe_30b_decode_T64", "moe_235b_zipf_T8192"])

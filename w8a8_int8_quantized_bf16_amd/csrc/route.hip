@@ -481,12 +481,14 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
 // registers, D steps of 8 indices ahead, and widen the bf16 pairs in
 // registers: no LDS staging and no barrier until the chains end.
 //
-// A block is 32 tokens and NCW waves, one per chunk run.  The chunk sums then
-// meet in LDS in ascending chunk order (the run of wave 0 first, each later
-// run adding its chunks one at a time to the running total), the top-k runs
-// on the totals, and with xq the block quantises its tokens (per-token amax
-// from the values the waves loaded, codes from a second, L2-resident read of
-// the rows).
+// A block is 32 tokens and NCW waves, one per chunk run.  The chunk sums meet
+// in LDS in ascending chunk order (the run of wave 0 first, each later run
+// adding its chunks one at a time to the running total as soon as the runs
+// before it are in), and the top-k runs on the totals.  The waves of a block
+// share their compute unit's matrix cores unevenly (measured: the first wave
+// on each SIMD ends its chain about a fifth of the chain time before the
+// second), so with xq the waves that are done quantise the block's tokens
+// while the others finish (each row read and coded by one wave).
 //
 // Output layout of the instruction: block b of the result sits in registers
 // 16 b .. 16 b + 15; register 16 b + 4 q + r of lane l holds row 8 q + 4 (l / 32)
@@ -494,7 +496,6 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
 namespace {
 constexpr int R32_TOK = 32;   // tokens per block
 constexpr int R32_STEPS = RT_CHUNK / 8;
-constexpr int R32_MAX_WAVES = 16;   // waves (chunk runs) per block: 16 with one slice, 8 with two
 constexpr int r32_max_waves(int S) { return S == 1 ? 16 : 8; }
 // 8-index steps in flight per lane: 8 with two slices (a block of at most 8
 // waves, 256 registers each), 4 with one (16 waves, 128 registers)
@@ -516,7 +517,8 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
     typedef float v32f __attribute__((ext_vector_type(32)));
     __shared__ float rt[S][R32_TOK][64 + 1];    // running totals, then the scores
     __shared__ __attribute__((aligned(16))) uint32_t tk_scr[8][512];
-    __shared__ float xm[R32_MAX_WAVES][R32_TOK];   // per-run |x| maxima of the block's tokens
+    __shared__ int q_next;   // next token row of the block to quantise
+    __shared__ int r_done;   // chunk runs added to the running totals
     const int tid = threadIdx.x, lane = tid & 63;
     const int run = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the run bounds stay scalar
     const int64_t tb = (int64_t)blockIdx.x * R32_TOK;
@@ -541,6 +543,11 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         wrow[j] = e < E ? (PACKED ? (uint32_t)e * 16u : (uint32_t)((int64_t)e * H * 2)) : OOB;
     }
     const uint32_t wstep = PACKED ? (uint32_t)E * 16u : 16u;   // bytes between steps of one expert
+    if (tid == 0) {
+        q_next = 0;
+        r_done = 0;
+    }
+    __syncthreads();
     uint4 xr[R32_D], wr[R32_D][S];
     auto load = [&](int slot, int st) {
         const bool live = st < s_end;
@@ -555,7 +562,6 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
     for (int d = 0; d < R32_D; ++d) load(d, s_beg + d);
 
     v32f acc[CPW][S];
-    float xmax = 0.0f;
     // one step: the 8 indices of slot d into the chains, then the slot's
     // refill with step st + R32_D (st % R32_D == d: chunks start at multiples)
     auto step = [&](v32f (&a)[S], int d, int st) {
@@ -574,7 +580,6 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
                 const uint32_t w = (&wr[d][j].x)[i];
                 a[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(x1, __uint_as_float(w & 0xffff0000u), a[j], 0, 0, 0);
             }
-            if constexpr (QX) xmax = fmaxf(xmax, fmaxf(fabsf(x0), fabsf(x1)));
         }
         load(d, st + R32_D);
         // keep the refill here: scheduled to the end of the pass, each load
@@ -599,54 +604,132 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
 #pragma unroll
         for (int j = 0; j < S; ++j) acc[ci][j] = a[j];
     }
-    if (QX && lane < 32) xm[run][tok] = xmax;
-
-    // chunk sums into the running totals, runs in ascending order
-    for (int r = 0; r < NCW; ++r) {
-        if (run == r && c_beg < c_end) {
+    // Chunk sums into the running totals, runs in ascending order: run r waits
+    // until runs 0 .. r - 1 are in (r_done == r), adds its chunks one at a
+    // time, then lets run r + 1 go.  Every earlier run ends without waiting on
+    // a later one, so each wait ends.
+    if (run > 0)
+        while (__hip_atomic_load(&r_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < run)
+            __builtin_amdgcn_s_sleep(1);
+    if (c_beg < c_end) {
+        // lane l's element reg of block j: row 8 (q & 3) + 4 (l / 32) + i,
+        // column 32 (q / 4) + l % 32 of that slice (reg = 4 q + i)
+        auto rt_at = [&](int j, int reg) -> float & {
+            const int q = reg >> 2, i = reg & 3;
+            return rt[j][8 * (q & 3) + 4 * (lane >> 5) + i][32 * (q >> 2) + (lane & 31)];
+        };
+        // the run's chunk sums added in order to what the earlier runs left
+        // (all loads first, then the sums and stores)
+        auto add_run = [&](const float(&before)[S][32], bool first) {
 #pragma unroll
             for (int j = 0; j < S; ++j)
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
+                for (int reg = 0; reg < 32; ++reg) {
+                    float t = first ? acc[0][j][reg] : before[j][reg] + acc[0][j][reg];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int reg = 4 * q + i;   // block reg / 16
-                        const int row = 8 * (q & 3) + 4 * (lane >> 5) + i;
-                        const int col = 32 * (q >> 2) + (lane & 31);
-                        float t = r == 0 ? acc[0][j][reg] : rt[j][row][col] + acc[0][j][reg];
+                    for (int ci = 1; ci < CPW; ++ci)
+                        if (c_beg + ci < c_end) t = t + acc[ci][j][reg];
+                    rt_at(j, reg) = t;
+                }
+        };
+        float tot[S][32];
+        if (run == 0) {
+            add_run(tot, true);
+        } else {
 #pragma unroll
-                        for (int ci = 1; ci < CPW; ++ci)
-                            if (c_beg + ci < c_end) t = t + acc[ci][j][reg];
-                        rt[j][row][col] = t;
-                    }
+            for (int j = 0; j < S; ++j)
+#pragma unroll
+                for (int reg = 0; reg < 32; ++reg) tot[j][reg] = rt_at(j, reg);
+            add_run(tot, false);
         }
-        __syncthreads();
     }
+    __hip_atomic_store(&r_done, run + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
     // Per-token int8 codes, when asked for, with the quantisation kernels'
-    // arithmetic: the waves saw every element of the block's rows, so each
-    // token's scale is known; the codes need a second read of the rows.  A
-    // thread takes every tpr-th 8-element piece of one row and reads its pieces
-    // QB at a time into one of two register batches, the first batch before the
-    // top-k (its latency then hides behind the top-k) and each next one before
-    // the codes of the current (one load waited for per piece left the block's
-    // tail bound by memory latency).
-    constexpr int QB = 8;
-    const int tpr = 64 * NCW / R32_TOK;   // threads per token row
-    const int qrow = tid / tpr, t8 = tid % tpr;
-    const int64_t qt = tb + qrow;
-    const int npc = (int)(H / 8);   // 8-element pieces per row
-    const uint32_t qbase = (QX && qt < T_) ? (uint32_t)(qt * H * 2) : OOB;
-    uint4 qa[QB], qb[QB];
-    auto qload = [&](uint4(&q)[QB], int i0) {
+    // arithmetic: a wave that has added its chunk sums takes the block's token
+    // rows one at a time (a shared counter) while the waves behind it still
+    // run their chains, so the codes cost little time after the chains.  A
+    // wave reads a row in pieces of 8 elements, QP per lane at a time, the
+    // next row's first pieces while it codes the current one: one read where
+    // the row fits (H <= 512 QP), else one read for the largest magnitude and
+    // one for the codes.  (QP: 8, or 4 in the 128-register waves of one-slice
+    // blocks.)
+    if constexpr (QX) {
+        constexpr int QP = S == 1 ? 4 : 8;
+        const int npc = (int)(H / 8);   // 8-element pieces per row
+        auto grab = [&]() {
+            int u = 0;
+            if (lane == 0) u = atomicAdd(&q_next, 1);
+            return __builtin_amdgcn_readfirstlane(u);
+        };
+        // pieces p0 + lane + 64 i of the block's row u (zeros past the row or the tokens)
+        auto qload = [&](uint4(&v)[QP], int u, int p0) {
+            const bool live = u < R32_TOK && tb + u < T_;
+            const uint32_t rb = live ? (uint32_t)((tb + u) * H * 2) : 0u;
 #pragma unroll
-        for (int b = 0; b < QB; ++b) {
-            const int p = t8 + tpr * (i0 + b);
-            q[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rx, (qbase != OOB && p < npc) ? qbase + (uint32_t)p * 16u : OOB, 0, 0));
+            for (int i = 0; i < QP; ++i) {
+                const int p = p0 + lane + 64 * i;
+                v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rx, (live && p < npc) ? rb + (uint32_t)p * 16u : OOB, 0, 0));
+            }
+        };
+        auto widen = [](const uint4 &q, float f[8]) {
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(w[i] << 16);
+                f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            }
+        };
+        // codes of row u, whose first QP pieces per lane are in v
+        auto qrow = [&](uint4(&v)[QP], int u) {
+            const int64_t t = tb + u;
+            if (t >= T_) return;
+            float amax = 0.0f;
+            for (int p0 = 0; p0 < npc; p0 += 64 * QP) {
+                if (p0 > 0) qload(v, u, p0);
+#pragma unroll
+                for (int i = 0; i < QP; ++i) {
+                    float f[8];
+                    widen(v[i], f);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+                }
+            }
+            amax = wave_max_nonneg(amax);
+            const float s = amax / 127.0f;
+            const float y = s > 0.0f ? 1.0f / s : 0.0f;
+            const bool fast = s >= QUANT_FAST_MIN_SCALE;
+            if (lane == 0) sx[t] = s;
+            int8_t *qdst = xq + t * H;
+            for (int p0 = 0; p0 < npc; p0 += 64 * QP) {
+                if (npc > 64 * QP) qload(v, u, p0);   // the row did not fit: read this part again
+#pragma unroll
+                for (int i = 0; i < QP; ++i) {
+                    const int p = p0 + lane + 64 * i;
+                    if (p < npc) {
+                        float f[8];
+                        widen(v[i], f);
+                        *reinterpret_cast<uint2 *>(qdst + 8 * p) =
+                            s != 0.0f ? pack8(f, s, y, fast) : make_uint2(0u, 0u);
+                    }
+                }
+            }
+        };
+        uint4 va[QP], vb[QP];
+        int u = grab();
+        qload(va, u, 0);
+        while (u < R32_TOK) {
+            const int u2 = grab();
+            qload(vb, u2, 0);
+            qrow(va, u);
+            if (u2 >= R32_TOK) break;
+            u = grab();
+            qload(va, u, 0);
+            qrow(vb, u2);
         }
-    };
-    if constexpr (QX) qload(qa, 0);
+    }
+    __syncthreads();
 
     const int ntk = min(NCW, 8);   // waves that run the top-k
     for (int tt = run; tt < R32_TOK && run < 8; tt += ntk) {
@@ -656,40 +739,6 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
 #pragma unroll
         for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? rt[j][tt][lane] : 0.0f;
         select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[run]);
-    }
-
-    if (QX && qbase != OOB) {
-        float amax = 0.0f;
-        for (int r = 0; r < NCW; ++r) amax = fmaxf(amax, xm[r][qrow]);
-        const float s = amax / 127.0f;
-        const float y = s > 0.0f ? 1.0f / s : 0.0f;
-        const bool fast = s >= QUANT_FAST_MIN_SCALE;
-        if (t8 == 0) sx[qt] = s;
-        int8_t *qdst = xq + qt * H;
-        auto qstore = [&](const uint4(&q)[QB], int i0) {
-#pragma unroll
-            for (int b = 0; b < QB; ++b) {
-                const int p = t8 + tpr * (i0 + b);
-                if (p < npc) {
-                    const uint32_t u[4] = {q[b].x, q[b].y, q[b].z, q[b].w};
-                    float v[8];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        v[2 * i] = __uint_as_float(u[i] << 16);
-                        v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-                    }
-                    *reinterpret_cast<uint2 *>(qdst + 8 * p) = s != 0.0f ? pack8(v, s, y, fast) : make_uint2(0u, 0u);
-                }
-            }
-        };
-        const int nit = (npc + tpr - 1) / tpr;   // pieces of the threads with the most
-        for (int i0 = 0; i0 < nit; i0 += 2 * QB) {
-            qload(qb, i0 + QB);
-            qstore(qa, i0);
-            if (i0 + QB >= nit) break;
-            qload(qa, i0 + 2 * QB);
-            qstore(qb, i0 + QB);
-        }
     }
 }
 
