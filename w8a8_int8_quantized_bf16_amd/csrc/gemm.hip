@@ -808,24 +808,6 @@ void grouped_gemm_ring_kernel(GemmArgs a)
                                        : (uint32_t)(col[f] * K + khalf));
     constexpr uint32_t BSTEP = PACKED ? 4096 : G_BK, BSUB = PACKED ? 1024 : 16;
 
-    // per-column weight scales, for the epilogue: lane l < 32 holds the
-    // scale of column l of each fragment, which the epilogue needs in the
-    // lanes that hold that column's outputs
-    float *cscw = csc + wave * WCOLS;
-    if (lane < 32) {
-#pragma unroll
-        for (int f = 0; f < WN; ++f) cscw[32 * f + lane] = (EPI != 0 && cvalid[f]) ? bsg[col[f]] : 0.0f;
-    }
-
-    // ---- activation rows of the tile and their scales
-    if (tid < BM) {
-        int32_t src = -1;
-        if (tid < rows) src = a.gather ? a.gather[row0 + tid] / a.gather_div : (int32_t)(row0 + tid);
-        arow[tid] = src;
-        ascale[tid] = (EPI != 0 && src >= 0) ? a.a_scales[src] : 0.0f;
-    }
-    __syncthreads();
-
     // ---- A staging: the A tile of a K step (BM rows x 128 bytes) goes from
     // memory straight into an LDS buffer, AD 1 KiB transfers per wave (8 rows
     // each, lane l writes bytes 16l..16l+15 of its transfer).  The buffer keeps
@@ -835,11 +817,6 @@ void grouped_gemm_ring_kernel(GemmArgs a)
     constexpr int AD = BM / 32;
     const int ach = (lane & 7) ^ ((lane >> 3) & 7);
     uint32_t aoff[AD];
-#pragma unroll
-    for (int j = 0; j < AD; ++j) {
-        const int32_t sr = arow[(wave * AD + j) * 8 + (lane >> 3)];
-        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ach) : OOB_BASE;
-    }
     const uint32_t lds_a = (uint32_t)(uintptr_t)(lds_u8_t *)&smem[0];
 
     // Software pipeline over K steps of 128 bytes.  B fragments go to a ring
@@ -903,23 +880,50 @@ void grouped_gemm_ring_kernel(GemmArgs a)
                 acc[mi][f] = __builtin_amdgcn_mfma_i32_32x32x32_i8(breg[d][f][s], av[set][mi], acc[mi][f], 0, 0, 0);
     };
 
-    // Prologue, in an issue order that leaves as many loads behind each A
-    // transfer as the loop does (8 WN + AD behind the transfer a barrier waits
-    // for): A0, B0 sub-steps 0-2, A1, B0 sub-step 3, B1 sub-steps 0-2, A2, B1
-    // sub-step 3.
-    load_a(0);
+    // Prologue.  Three memory round trips lie on its path: the tile's
+    // descriptor, its gathered row indices, then the first A steps.  The row
+    // indices are loaded first; the column scales and the weight steps 0 and
+    // 1 (which need only the descriptor) fly beside them, and the row scales
+    // beside the A transfers.  Then A0, A1, A2 and B1's last sub-step: a wait
+    // for A0 and A1 leaves A2 with as many loads behind it as the loop leaves
+    // behind each A transfer (8 WN + AD) when its barrier waits for it.
+    const bool has_row = tid < BM && tid < rows;
+    int32_t graw = 0;
+    if (has_row && a.gather) graw = a.gather[row0 + tid];   // used after the weight loads are issued
+    // per-column weight scales, for the epilogue: lane l < 32 holds the
+    // scale of column l of each fragment, which the epilogue needs in the
+    // lanes that hold that column's outputs
+    float cs_reg[WN];
 #pragma unroll
-    for (int s = 0; s < 3; ++s) load_b_sub(0, 0, s);
-    load_a(1);
-    load_b_sub(0, 0, 3);
+    for (int f = 0; f < WN; ++f) cs_reg[f] = (EPI != 0 && lane < 32 && cvalid[f]) ? bsg[col[f]] : 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) load_b_sub(0, 0, s);
 #pragma unroll
     for (int s = 0; s < 3; ++s) load_b_sub(1 % DEPTH, 1, s);
+    const int32_t src = !has_row ? -1 : (a.gather ? graw / a.gather_div : (int32_t)(row0 + tid));
+    if (tid < BM) arow[tid] = src;
+    __syncthreads();
+    const float as_reg = (EPI != 0 && tid < BM && src >= 0) ? a.a_scales[src] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < AD; ++j) {
+        const int32_t sr = arow[(wave * AD + j) * 8 + (lane >> 3)];
+        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ach) : OOB_BASE;
+    }
+    load_a(0);
+    load_a(1);
     load_a(2);
     load_b_sub(1 % DEPTH, 1, 3);
     static_assert(DEPTH == 2, "the prologue's issue order assumes a two-step B ring");
     constexpr int VM_AFTER = 8 * WN + AD;   // loads issued behind an A transfer until its barrier
     static_assert(VM_AFTER + AD <= 63, "vmcnt holds at most 63 outstanding loads");
-    lds_barrier<VM_AFTER + AD>();   // A0 complete (A1 and its followers may fly)
+    lds_barrier<AD + WN>();   // A0 and A1 complete (A2 and B1's last sub-step may fly)
+    // the scales into LDS for the epilogue (the loop's barriers publish them)
+    float *cscw = csc + wave * WCOLS;
+    if (tid < BM) ascale[tid] = as_reg;
+    if (lane < 32) {
+#pragma unroll
+        for (int f = 0; f < WN; ++f) cscw[32 * f + lane] = cs_reg[f];
+    }
     read_a(0, 0, 0);
 
     // The trip count is padded to a multiple of DEPTH; the padding steps issue
