@@ -322,7 +322,9 @@ def test_route_shapes(T, H, E, k, xdt):
 @pytest.mark.parametrize("T,H,E,k", [(8192, 2064, 128, 8),    # two slices, 5 chunks (a short last one)
                                      (8200, 1040, 60, 4),     # one slice, a last block of 8 tokens
                                      (8192, 4624, 128, 8),    # two slices, two chunks per wave
-                                     (8192, 8720, 64, 8)])    # one slice, two chunks per wave
+                                     (8192, 8720, 64, 8),     # one slice, two chunks per wave
+                                     (8230, 1552, 100, 6)])   # a part-filled second slice, a last chunk
+                                                              # of two steps, a last block of 6 tokens
 def test_route_matrix_core_many_tokens(T, H, E, k):
     """bf16 tokens in 256 or more blocks of 32 (the 32 x 32 x 1 matrix-core
     router): logits, ids and weights against the oracle with the [E][H] and
