@@ -187,6 +187,125 @@ __device__ __forceinline__ void select_topk(const float l4[4], int64_t t, int E,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Top-k for k <= 8 with renormalised weights (the layer's case), 8 / S
+// tokens per wavefront at once, lanes working side by side instead of one
+// token's 32 ballot rounds at a time.  Lane l takes token l / (8 S) and its
+// experts 8 (l % (8 S)) .. + 7.  A (score, expert) pair is coded as the
+// double whose bits are 1.0's with key << 8 | (255 - expert) in the low
+// mantissa bits: a positive normal number, so doubles order like the codes,
+// larger scores first and, among equal scores, lower expert indices, and
+// the k largest are the selection in output order; one max and one min
+// (v_max_f64, v_min_f64, exact: they return an operand) order a pair.  Each
+// lane sorts its 8 values (Batcher's 19-comparator network), then exchanges
+// its list with a lane of the other half of a growing lane group (DPP moves:
+// xor 1, xor 2, mirror in 8, mirror in 16) and keeps the 8 largest of both:
+// the elementwise maximum of its list and the partner's reversed one holds
+// them as a bitonic sequence, which 12 comparators sort.  After log2(8 S)
+// rounds each lane of a token holds the token's sorted top 8.  The weights
+// take select_topk's arithmetic, so both give the same bits: the largest
+// score as the offset, and the k exponentials (one per lane) summed in
+// ascending expert order, which a 19-comparator sort of (expert, value)
+// codes gives.
+namespace {
+constexpr int kBatcher8[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {1, 2}, {5, 6},
+                                  {0, 4}, {1, 5}, {2, 6}, {3, 7}, {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
+constexpr int kBitonic8[12][2] = {{0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 2}, {1, 3},
+                                  {4, 6}, {5, 7}, {0, 1}, {2, 3}, {4, 5}, {6, 7}};
+constexpr uint64_t kOneBits = 0x3ff0000000000000ull;   // 1.0
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_move_f64(double v)
+{
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// larger first
+__device__ __forceinline__ void cmpx_desc(double &a, double &b)
+{
+    const double x = __builtin_fmax(a, b), y = __builtin_fmin(a, b);
+    a = x;
+    b = y;
+}
+
+// one exchange round: the 8 largest of this lane's and the partner's lists
+template <int CTRL>
+__device__ __forceinline__ void topk8_round(double (&c)[8])
+{
+    double p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = dpp_move_f64<CTRL>(c[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_fmax(c[i], p[7 - i]);
+#pragma unroll
+    for (int n = 0; n < 12; ++n) cmpx_desc(c[kBitonic8[n][0]], c[kBitonic8[n][1]]);
+}
+
+// Tokens tt0 .. tt0 + 8 / S - 1 of a block (block row tt holds the scores of
+// token tb + tt, expert 64 j + c at score(j, tt, c)).  Every lane of the wave
+// must call it (DPP and the lane exchange read the neighbours); rows past T_
+// write nothing.
+template <int S, typename ScoreFn>
+__device__ __forceinline__ void topk8_renorm_tokens(ScoreFn score, int tt0, int64_t tb, int64_t T_, int E, int k,
+                                                    int32_t *__restrict__ ids, float *__restrict__ wout,
+                                                    float *__restrict__ logits_out)
+{
+    constexpr int NSUB = 8 * S;   // lanes per token
+    const int lane = threadIdx.x & 63;
+    const int sub = lane % NSUB, tt = tt0 + lane / NSUB;
+    const int64_t t = tb + tt;
+    const bool live = t < T_;
+    double c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = 8 * sub + i;
+        const float v = score(e >> 6, tt, e & 63);
+        const bool valid = e < E;
+        c[i] = __longlong_as_double(
+            (long long)(kOneBits | ((uint64_t)score_key(v, valid) << 8) | (uint64_t)(255 - e)));
+        if (live && valid && logits_out) logits_out[t * E + e] = v;
+    }
+#pragma unroll
+    for (int n = 0; n < 19; ++n) cmpx_desc(c[kBatcher8[n][0]], c[kBatcher8[n][1]]);
+    topk8_round<0xB1>(c);    // xor 1
+    topk8_round<0x4E>(c);    // xor 2
+    topk8_round<0x141>(c);   // mirror within 8 lanes
+    if constexpr (S == 2) topk8_round<0x140>(c);   // mirror within 16 lanes
+    auto key_of = [](double d) { return (uint32_t)((uint64_t)__double_as_longlong(d) >> 8); };
+    auto expert_of = [](double d) { return 255 - (int)((uint64_t)__double_as_longlong(d) & 0xff); };
+    const float mx = key_score(key_of(c[0]));
+    // this lane's selection (lane sub < k takes the sub-th) and its exponential
+    double mine = c[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q)
+        if (sub == q) mine = c[q];
+    const int my_e = expert_of(mine);
+    const float my_x = sub < k ? expf(key_score(key_of(mine)) - mx) : 0.0f;
+    // the token's k exponentials (lanes sub = 0 .. 7 of its group), coded as
+    // (expert << 32 | value bits) in the same way and sorted by expert
+    const int base = lane - sub;
+    double d[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int eq = __shfl(my_e, base + q, 64);
+        const float xq = __shfl(my_x, base + q, 64);
+        d[q] = __longlong_as_double((long long)(kOneBits | ((uint64_t)(q < k ? eq : 256 + q) << 32) |
+                                                (uint64_t)__float_as_uint(xq)));
+    }
+#pragma unroll
+    for (int n = 0; n < 19; ++n) cmpx_desc(d[kBatcher8[n][1]], d[kBatcher8[n][0]]);   // ascending
+    float denom = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) denom += __uint_as_float((uint32_t)__double_as_longlong(d[q]));
+    if (live && sub < k) {
+        ids[t * k + sub] = my_e;
+        wout[t * k + sub] = my_x / denom;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void route_topk_kernel(const T *__restrict__ x, const uint16_t *__restrict__ wg,
                                                          int64_t T_, int64_t H, int E, int k, int renorm,
@@ -494,17 +613,19 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
 // 16 b .. 16 b + 15; register 16 b + 4 q + r of lane l holds row 8 q + 4 (l / 32)
 // + r, column l % 32 (rows: tokens, columns: experts).
 namespace {
-constexpr int R32_TOK = 32;   // tokens per block
 constexpr int R32_STEPS = RT_CHUNK / 8;
 constexpr int r32_max_waves(int S) { return S == 1 ? 16 : 8; }
 // 8-index steps in flight per lane: 8 with two slices (a block of at most 8
-// waves, 256 registers each), 4 with one (16 waves, 128 registers)
-constexpr int r32_depth(int S) { return S == 1 ? 4 : 8; }
+// waves, 256 registers each) or with 16-token blocks (16-register
+// accumulators), 4 with one slice of 32 tokens (16 waves, 128 registers)
+constexpr int r32_depth(int TOK, int S) { return (S == 1 && TOK == 32) ? 4 : 8; }
 }
 
-// QX: the block also quantises its tokens (xq and sx are then given)
-template <int S, int CPW, bool PACKED, bool QX>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
-__global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(const uint16_t *__restrict__ x,
+// TOK: tokens per block, 32 (the 32 x 32 x 1 instruction) or 16 (its
+// 16 x 16 x 1 four-block form, for fewer tokens: twice the blocks).  QX: the
+// block also quantises its tokens (xq and sx are then given)
+template <int TOK, int S, int CPW, bool PACKED, bool QX>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
+__global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
                                                             int E, int k, int renorm, int NCW,
                                                             int32_t *__restrict__ ids, float *__restrict__ wout,
@@ -512,16 +633,18 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
                                                             float *__restrict__ sx)
 {
     static_assert(S == 1 || S == 2, "slices");
-    constexpr int R32_D = r32_depth(S);
+    static_assert(TOK == 32 || TOK == 16, "tokens per block");
+    constexpr int R32_D = r32_depth(TOK, S);
     static_assert(R32_STEPS % R32_D == 0, "chunks end at pass ends");
-    typedef float v32f __attribute__((ext_vector_type(32)));
-    __shared__ float rt[S][R32_TOK][64 + 1];    // running totals, then the scores
+    // a lane's accumulator: TOK x 64 results over 64 lanes
+    typedef float vacc __attribute__((ext_vector_type(TOK)));
+    __shared__ float rt[S][TOK][64 + 1];    // running totals, then the scores
     __shared__ __attribute__((aligned(16))) uint32_t tk_scr[8][512];
     __shared__ int q_next;   // next token row of the block to quantise
     __shared__ int r_done;   // chunk runs added to the running totals
     const int tid = threadIdx.x, lane = tid & 63;
     const int run = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the run bounds stay scalar
-    const int64_t tb = (int64_t)blockIdx.x * R32_TOK;
+    const int64_t tb = (int64_t)blockIdx.x * TOK;
     const int nst = (int)(H / 8);
     const int nch = (nst + R32_STEPS - 1) / R32_STEPS;
     const int c_beg = min(nch, run * CPW), c_end = min(nch, c_beg + CPW);
@@ -534,7 +657,7 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x), 0, 0x7ffffff0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, 0x7ffffff0, 0x00020000);
-    const int tok = lane & 31;
+    const int tok = lane & (TOK - 1);
     const uint32_t xrow = tb + tok < T_ ? (uint32_t)((tb + tok) * H * 2) : OOB;
     uint32_t wrow[S];
 #pragma unroll
@@ -561,10 +684,15 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
 #pragma unroll
     for (int d = 0; d < R32_D; ++d) load(d, s_beg + d);
 
-    v32f acc[CPW][S];
+    vacc acc[CPW][S];
+    // c += a * b for one hidden index: TOK tokens x 64 experts
+    auto mfma = [](float av, float bv, const vacc &c) -> vacc {
+        if constexpr (TOK == 32) return __builtin_amdgcn_mfma_f32_32x32x1f32(av, bv, c, 0, 0, 0);
+        else return __builtin_amdgcn_mfma_f32_16x16x1f32(av, bv, c, 0, 0, 0);
+    };
     // one step: the 8 indices of slot d into the chains, then the slot's
     // refill with step st + R32_D (st % R32_D == d: chunks start at multiples)
-    auto step = [&](v32f (&a)[S], int d, int st) {
+    auto step = [&](vacc (&a)[S], int d, int st) {
         const uint32_t u[4] = {xr[d].x, xr[d].y, xr[d].z, xr[d].w};
         // hidden 8 st + 2 i is the low half of word i, 8 st + 2 i + 1 the high half
 #pragma unroll
@@ -573,12 +701,12 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
 #pragma unroll
             for (int j = 0; j < S; ++j) {
                 const uint32_t w = (&wr[d][j].x)[i];
-                a[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(x0, __uint_as_float(w << 16), a[j], 0, 0, 0);
+                a[j] = mfma(x0, __uint_as_float(w << 16), a[j]);
             }
 #pragma unroll
             for (int j = 0; j < S; ++j) {
                 const uint32_t w = (&wr[d][j].x)[i];
-                a[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(x1, __uint_as_float(w & 0xffff0000u), a[j], 0, 0, 0);
+                a[j] = mfma(x1, __uint_as_float(w & 0xffff0000u), a[j]);
             }
         }
         load(d, st + R32_D);
@@ -588,9 +716,9 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
     };
 #pragma unroll
     for (int ci = 0; ci < CPW; ++ci) {
-        v32f a[S];
+        vacc a[S];
 #pragma unroll
-        for (int j = 0; j < S; ++j) a[j] = v32f{};
+        for (int j = 0; j < S; ++j) a[j] = vacc{};
         const int cs = s_beg + ci * R32_STEPS;
         const int ce = min(s_end, cs + R32_STEPS);
         const int cf = cs + max(0, ce - cs) / R32_D * R32_D;   // end of the whole passes
@@ -612,19 +740,23 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         while (__hip_atomic_load(&r_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < run)
             __builtin_amdgcn_s_sleep(1);
     if (c_beg < c_end) {
-        // lane l's element reg of block j: row 8 (q & 3) + 4 (l / 32) + i,
-        // column 32 (q / 4) + l % 32 of that slice (reg = 4 q + i)
+        // lane l's element reg of slice j (reg = 4 q + i).  32 tokens: row
+        // 8 (q & 3) + 4 (l / 32) + i, column 32 (q / 4) + l % 32; 16 tokens
+        // (block q of the instruction): row 4 (l / 16) + i, column 16 q + l % 16
         auto rt_at = [&](int j, int reg) -> float & {
             const int q = reg >> 2, i = reg & 3;
-            return rt[j][8 * (q & 3) + 4 * (lane >> 5) + i][32 * (q >> 2) + (lane & 31)];
+            if constexpr (TOK == 32)
+                return rt[j][8 * (q & 3) + 4 * (lane >> 5) + i][32 * (q >> 2) + (lane & 31)];
+            else
+                return rt[j][4 * (lane >> 4) + i][16 * q + (lane & 15)];
         };
         // the run's chunk sums added in order to what the earlier runs left
         // (all loads first, then the sums and stores)
-        auto add_run = [&](const float(&before)[S][32], bool first) {
+        auto add_run = [&](const float(&before)[S][TOK], bool first) {
 #pragma unroll
             for (int j = 0; j < S; ++j)
 #pragma unroll
-                for (int reg = 0; reg < 32; ++reg) {
+                for (int reg = 0; reg < TOK; ++reg) {
                     float t = first ? acc[0][j][reg] : before[j][reg] + acc[0][j][reg];
 #pragma unroll
                     for (int ci = 1; ci < CPW; ++ci)
@@ -632,14 +764,14 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
                     rt_at(j, reg) = t;
                 }
         };
-        float tot[S][32];
+        float tot[S][TOK];
         if (run == 0) {
             add_run(tot, true);
         } else {
 #pragma unroll
             for (int j = 0; j < S; ++j)
 #pragma unroll
-                for (int reg = 0; reg < 32; ++reg) tot[j][reg] = rt_at(j, reg);
+                for (int reg = 0; reg < TOK; ++reg) tot[j][reg] = rt_at(j, reg);
             add_run(tot, false);
         }
     }
@@ -664,7 +796,7 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         };
         // pieces p0 + lane + 64 i of the block's row u (zeros past the row or the tokens)
         auto qload = [&](uint4(&v)[QP], int u, int p0) {
-            const bool live = u < R32_TOK && tb + u < T_;
+            const bool live = u < TOK && tb + u < T_;
             const uint32_t rb = live ? (uint32_t)((tb + u) * H * 2) : 0u;
 #pragma unroll
             for (int i = 0; i < QP; ++i) {
@@ -719,11 +851,11 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
         uint4 va[QP], vb[QP];
         int u = grab();
         qload(va, u, 0);
-        while (u < R32_TOK) {
+        while (u < TOK) {
             const int u2 = grab();
             qload(vb, u2, 0);
             qrow(va, u);
-            if (u2 >= R32_TOK) break;
+            if (u2 >= TOK) break;
             u = grab();
             qload(va, u, 0);
             qrow(vb, u2);
@@ -731,8 +863,16 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma32_kernel(con
     }
     __syncthreads();
 
+    if (renorm && k <= 8) {
+        // 8 / S tokens per wave at once, every wave taking groups in turn
+        constexpr int TPW = 8 / S;
+        auto score = [&](int j, int tt, int c) { return rt[j][tt][c]; };
+        for (int tt0 = run * TPW; tt0 < TOK; tt0 += NCW * TPW)
+            topk8_renorm_tokens<S>(score, tt0, tb, T_, E, k, ids, wout, logits_out);
+        return;
+    }
     const int ntk = min(NCW, 8);   // waves that run the top-k
-    for (int tt = run; tt < R32_TOK && run < 8; tt += ntk) {
+    for (int tt = run; tt < TOK && run < 8; tt += ntk) {
         const int64_t t = tb + tt;
         if (t >= T_) break;
         float l4[4];
@@ -1029,32 +1169,42 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
             }
             return hipGetLastError();
         }
-        // up to 128 experts: the 32 x 32 x 1 kernel, one wave per slice and
-        // run of one or two chunks, at most 16 waves
+        // up to 128 experts: the K = 1 matrix-core kernel, one wave per slice
+        // and run of one or two chunks (at most 16 waves), on 32-token blocks
+        // where they fill the chip, else on 16-token blocks where H spans two
+        // chunks or more
         const int nch = (int)((H / 8 + R32_STEPS - 1) / R32_STEPS);
-        const int64_t ngrp = (T + R32_TOK - 1) / R32_TOK;
-        if (S <= 2 && nch <= 2 * r32_max_waves(S) && ngrp >= 256) {
+        const int64_t ngrp32 = (T + 31) / 32;
+        if (S <= 2 && nch <= 2 * r32_max_waves(S) && (ngrp32 >= 256 || nch >= 2)) {
             const int cpw = nch <= r32_max_waves(S) ? 1 : 2;
             const int ncw = (nch + cpw - 1) / cpw;
-            const dim3 g32((unsigned)ngrp), b32(64 * ncw);
+            const bool t32 = ngrp32 >= 256;
+            const dim3 g32((unsigned)(t32 ? ngrp32 : (T + 15) / 16)), b32(64 * ncw);
             const uint16_t *wv = wg_packed ? wg_packed : wg;
             auto go32 = [&](auto kern) {
                 hipLaunchKernelGGL(kern, g32, b32, 0, st, xb, wv, T, H, E, k, renormalize, ncw, ids, w, logits, xq,
                                    sx);
             };
-            auto pick = [&](auto qx) {
+            auto pick = [&](auto tok, auto qx) {
+                constexpr int TK = decltype(tok)::value;
                 constexpr bool QX = decltype(qx)::value;
                 if (S == 1 && cpw == 1)
-                    wg_packed ? go32(route_mfma32_kernel<1, 1, true, QX>) : go32(route_mfma32_kernel<1, 1, false, QX>);
+                    wg_packed ? go32(route_mfma_k1_kernel<TK, 1, 1, true, QX>)
+                              : go32(route_mfma_k1_kernel<TK, 1, 1, false, QX>);
                 else if (S == 1)
-                    wg_packed ? go32(route_mfma32_kernel<1, 2, true, QX>) : go32(route_mfma32_kernel<1, 2, false, QX>);
+                    wg_packed ? go32(route_mfma_k1_kernel<TK, 1, 2, true, QX>)
+                              : go32(route_mfma_k1_kernel<TK, 1, 2, false, QX>);
                 else if (cpw == 1)
-                    wg_packed ? go32(route_mfma32_kernel<2, 1, true, QX>) : go32(route_mfma32_kernel<2, 1, false, QX>);
+                    wg_packed ? go32(route_mfma_k1_kernel<TK, 2, 1, true, QX>)
+                              : go32(route_mfma_k1_kernel<TK, 2, 1, false, QX>);
                 else
-                    wg_packed ? go32(route_mfma32_kernel<2, 2, true, QX>) : go32(route_mfma32_kernel<2, 2, false, QX>);
+                    wg_packed ? go32(route_mfma_k1_kernel<TK, 2, 2, true, QX>)
+                              : go32(route_mfma_k1_kernel<TK, 2, 2, false, QX>);
             };
-            if (xq) pick(std::true_type{});
-            else pick(std::false_type{});
+            using T32 = std::integral_constant<int, 32>;
+            using T16 = std::integral_constant<int, 16>;
+            if (t32) xq ? pick(T32{}, std::true_type{}) : pick(T32{}, std::false_type{});
+            else xq ? pick(T16{}, std::true_type{}) : pick(T16{}, std::false_type{});
             return hipGetLastError();
         }
         const int64_t nblk = (T + 32 / S - 1) / (32 / S);
