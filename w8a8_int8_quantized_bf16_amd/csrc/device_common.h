@@ -60,6 +60,16 @@ __device__ __forceinline__ float wave_max_nonneg(float m)
     return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
+// Order this wavefront's LDS accesses: the LDS performs one wave's operations
+// in issue order, so a compiler barrier is all it takes for lanes to read
+// what other lanes of the same wave wrote before it (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll

@@ -298,7 +298,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, v16i (&acc)[BM 
                     *reinterpret_cast<ET *>(stage + rl * ROWB + (32 * ff + (lane & 31)) * (int)sizeof(ET)) = val;
                 }
             }
-            __syncthreads();
+            wave_lds_sync();   // the staging region is this wave's own
             if constexpr (EPI == EPI_FIXED16) {
                 // 16 lanes hold one row's 64 columns (4 each): the row's largest
                 // magnitude over them fixes a power-of-two scale 2^e that maps it
@@ -344,7 +344,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, v16i (&acc)[BM 
                             *reinterpret_cast<const uint4 *>(stage + rl * ROWB + ch * 16);
                 }
             }
-            __syncthreads();
+            wave_lds_sync();   // the staging region is this wave's own
         }
     }
 }
