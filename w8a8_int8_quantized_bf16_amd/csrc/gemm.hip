@@ -570,25 +570,16 @@ void grouped_gemm_kernel(GemmArgs a)
 #pragma unroll
     for (int f = 0; f < WN; ++f) bsc[f] = (EPI != 0 && cvalid[f]) ? bsg[col[f]] : 0.0f;
 
-    // ---- activation rows of the tile and their scales
-    if (tid < BM) {
-        int32_t src = -1;
-        if (tid < rows) src = a.gather ? a.gather[row0 + tid] / a.gather_div : (int32_t)(row0 + tid);
-        arow[tid] = src;
-        ascale[tid] = (EPI != 0 && src >= 0) ? a.a_scales[src] : 0.0f;
-    }
-    __syncthreads();
+    // ---- activation rows of the tile: the gathered row index is loaded
+    // first (used after the weight loads below are issued)
+    const bool has_row = tid < BM && tid < rows;
+    int32_t graw = 0;
+    if (has_row && a.gather) graw = a.gather[row0 + tid];
 
     // ---- A staging assignment: 16-byte chunk ac of rows (tid/8) + 32j
     const int ac = tid & 7;
     uint32_t aoff[APASS];
     int arr[APASS];
-#pragma unroll
-    for (int j = 0; j < APASS; ++j) {
-        arr[j] = (tid >> 3) + 32 * j;
-        const int32_t sr = arow[arr[j]];
-        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ac) : OOB_BASE;
-    }
 
     // Software pipeline over K steps of 128 bytes.  A ring of DEPTH register
     // slots holds the B fragments of the next DEPTH steps and the A chunks of
@@ -633,13 +624,28 @@ void grouped_gemm_kernel(GemmArgs a)
             *reinterpret_cast<v4i *>(&As[buf][arr[j] * G_BK + ((ac ^ (arr[j] & 7)) << 4)]) = areg[slot][j];
     };
 
-    // Prologue, in the loop's own issue order (B, then A) so that the wait
-    // counts at the loop entry match the steady state.
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_a(d, d);
+    // Prologue.  Three memory round trips lie on its path: the tile's
+    // descriptor, the gathered row indices, then the first A steps.  The
+    // first DEPTH weight steps (which need only the descriptor) fly beside
+    // the row-index gather, the row scales beside the A loads; the row scales
+    // reach LDS after the first A step, and the loop's barriers publish them
+    // before the epilogue reads them.
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_b(d, d);
+    const int32_t src = !has_row ? -1 : (a.gather ? graw / a.gather_div : (int32_t)(row0 + tid));
+    if (tid < BM) arow[tid] = src;
+    __syncthreads();
+    const float as_reg = (EPI != 0 && tid < BM && src >= 0) ? a.a_scales[src] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < APASS; ++j) {
+        arr[j] = (tid >> 3) + 32 * j;
+        const int32_t sr = arow[arr[j]];
+        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ac) : OOB_BASE;
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_a(d, d);
     store_a(0, 0);
+    if (tid < BM) ascale[tid] = as_reg;
     load_a(0, DEPTH);
     __syncthreads();
 
