@@ -310,17 +310,23 @@ int run_layer(const w8a8_moe_weights *W, const void *x, int x_dtype, int64_t T, 
                               2 * Is, H, W8A8_EPI_DEQUANT_SWIGLU, W8A8_BF16, hs, gws3, st)) != hipSuccess)
         return hip_status(e);
     if ((e = mark()) != hipSuccess) return hip_status(e);
-    // quantise h per grouped row (and a separate shared expert's h per token)
-    if ((e = launch_quant_rows(h, W8A8_BF16, Pg, I, I, hq, sh, st)) != hipSuccess ||
+    // quantise h per grouped row (and a separate shared expert's h per token);
+    // with few rows per expert the down GEMM's tiles quantise their own rows
+    // (and still store hq and sh), so the pass is skipped
+    const bool down_qa = gemm_down_fuses_quant(Pg, H, I, Gg);
+    if ((!down_qa && (e = launch_quant_rows(h, W8A8_BF16, Pg, I, I, hq, sh, st)) != hipSuccess) ||
         (shared && !sg && (e = launch_quant_rows(hs, W8A8_BF16, T, Is, Is, hqs, shs, st)) != hipSuccess) ||
         (e = mark()) != hipSuccess)
         return hip_status(e);
     // 4b down GEMM -> y (16-bit fixed point + exponents); the shared expert's
     //    rows follow the routed ones
     const int64_t nseg = (H + 63) / 64;
-    if ((e = launch_gemm_main(hq, Pg, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, Gg, Pg, H, I, EPI_FIXED16,
-                              W8A8_F32, y, gws2, st, yexp, sg ? W->w_shared_down : nullptr,
-                              sg ? W->s_shared_down : nullptr)) != hipSuccess ||
+    e = down_qa ? launch_gemm_down_qa(h, Pg, hq, sh, W->w_down, W->s_down, offsets, Gg, H, I, y, yexp, gws2, st,
+                                      sg ? W->w_shared_down : nullptr, sg ? W->s_shared_down : nullptr)
+                : launch_gemm_main(hq, Pg, sh, nullptr, 1, W->w_down, 1, W->s_down, offsets, Gg, Pg, H, I, EPI_FIXED16,
+                                   W8A8_F32, y, gws2, st, yexp, sg ? W->w_shared_down : nullptr,
+                                   sg ? W->s_shared_down : nullptr);
+    if (e != hipSuccess ||
         (shared && !sg &&
          (e = launch_gemm_main(hqs, T, shs, nullptr, 1, W->w_shared_down, 1, W->s_shared_down, nullptr, 1, T, H, Is,
                                EPI_FIXED16, W8A8_F32, y + P * H, gws4, st, yexp + P * nseg)) != hipSuccess) ||

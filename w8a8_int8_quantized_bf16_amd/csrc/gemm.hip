@@ -39,6 +39,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "quant_common.h"
 #include "tiles.h"
 
 namespace w8a8 {
@@ -73,6 +74,9 @@ struct GemmArgs {
                                   //   the block index (no tile table)
     int ksplit, ksteps;           // dense: K in ksplit slices of ksteps 128-byte
                                   //   steps, each writing int32 sums to out + slice * M * N
+    const uint16_t *A_h;          // quantise on load: A as bf16 rows (no gather, A_bytes
+    int8_t *a_codes_out;          //   still rows * K); the tiles of column block 0 also
+    float *a_scales_out;          //   store the rows' int8 codes [rows][K] and scales
 };
 
 // The tile of block `bid` of a one-group GEMM without a table: the same
@@ -487,10 +491,19 @@ constexpr int gemm_min_waves(int BM, int WN, int EPI, int out_bytes, bool packed
     return BM * WN <= 256 ? 2 : 1;
 }
 
-template <int BM, int WN, int DEPTH, int EPI, typename OutT, bool PACKED>
+// QA: A arrives as bf16 rows (a.A_h, in grouped order) and the tile forms
+// their int8 codes itself, with the per-row quantisation of the quantiser
+// kernels: the prologue finds each row's largest magnitude over all of K
+// (the tile's rows are whole rows of A), and every staged A chunk is coded
+// from its bf16 values on the way into LDS.  The tiles of column block 0 also
+// store the codes and scales (a.a_codes_out, a.a_scales_out).  Built for the
+// down GEMM of few rows per expert, where the weight stream bounds the tile
+// and the coding costs no time of its own.
+template <int BM, int WN, int DEPTH, int EPI, typename OutT, bool PACKED, bool QA = false>
 __global__ __launch_bounds__(G_THREADS) __attribute__((amdgpu_waves_per_eu(gemm_min_waves(BM, WN, EPI, (int)sizeof(OutT), PACKED), 8)))
 void grouped_gemm_kernel(GemmArgs a)
 {
+    static_assert(!QA || (PACKED && BM == 32), "quantise-on-load: packed weights, 32-row tiles");
     static_assert(DEPTH % 2 == 0, "the K loop is unrolled by DEPTH and alternates two LDS buffers");
     static_assert(EPI != 2 || WN % 2 == 0, "SwiGLU pairs gate and up fragments");
     constexpr int MI = BM / 32;      // 32-row MFMA tiles per wave
@@ -555,7 +568,8 @@ void grouped_gemm_kernel(GemmArgs a)
     const bool xg = g >= a.G_routed;   // the extra group: weights of its own
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(xg ? a.B_extra : a.B + (int64_t)g * b_bytes, b_bytes);
     const float *bsg = xg ? a.b_extra_scales : a.b_scales + (int64_t)g * N;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A, a.A_bytes);
+    const __amdgpu_buffer_rsrc_t rA =
+        QA ? make_rsrc(a.A_h, 2 * a.A_bytes) : make_rsrc(a.A, a.A_bytes);   // QA: bf16 rows
     const int khalf = 64 * (lane >> 5);
     uint32_t boff[WN];
 #pragma unroll
@@ -587,7 +601,8 @@ void grouped_gemm_kernel(GemmArgs a)
     // load (DEPTH steps ahead) until it is copied into LDS at the end of step
     // j - 1.  LDS holds two A buffers (current step, next step).
     v4i breg[DEPTH][WN][4];
-    v4i areg[DEPTH][APASS];
+    constexpr int AH = QA ? 2 : 1;   // 16-byte loads per A chunk (bf16 rows: two)
+    v4i areg[DEPTH][APASS][AH];
     v16i acc[MI][WN];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -595,6 +610,13 @@ void grouped_gemm_kernel(GemmArgs a)
         for (int f = 0; f < WN; ++f)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][f][i] = 0;
+    // QA: this thread's row scale s, its reciprocal and the fast-quotient flag
+    // (the quantiser's arithmetic, quant_common.h), and whether this tile
+    // stores the codes
+    float qs = 0.0f, qy = 0.0f;
+    bool qfast = true;
+    int32_t qrow = -1;   // the grouped row this thread stages (QA: one per thread)
+    const bool qstore = QA && nb == 0;
 
     // Steps at or beyond nk (the padding of the trip count) load nothing: the
     // step index is wave-uniform, so that choice is a scalar select.  With
@@ -616,12 +638,38 @@ void grouped_gemm_kernel(GemmArgs a)
         const bool kin = PACKED || it * G_BK + 16 * ac < K;
 #pragma unroll
         for (int j = 0; j < APASS; ++j)
-            areg[slot][j] = buf_load16(rA, (live && kin) ? aoff[j] + it * G_BK : OOB_BASE);
-    };
-    auto store_a = [&](int slot, int buf) {
 #pragma unroll
-        for (int j = 0; j < APASS; ++j)
-            *reinterpret_cast<v4i *>(&As[buf][arr[j] * G_BK + ((ac ^ (arr[j] & 7)) << 4)]) = areg[slot][j];
+            for (int h = 0; h < AH; ++h)   // QA: element offsets, two bytes each
+                areg[slot][j][h] = buf_load16(
+                    rA, (live && kin && aoff[j] != OOB_BASE) ? (aoff[j] + it * G_BK) * AH + 16 * h : OOB_BASE);
+    };
+    // A(it) from register slot `slot` into LDS buffer `buf`; with QA its 16
+    // bf16 values per chunk are coded first (bytes past K meet zero weights,
+    // so whatever they code to does not matter, and they are not stored)
+    auto store_a = [&](int slot, int buf, int it) {
+#pragma unroll
+        for (int j = 0; j < APASS; ++j) {
+            v4i v = areg[slot][j][0];
+            if constexpr (QA) {
+                uint2 c[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float f[8];
+                    const v4i u = areg[slot][j][h];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        f[2 * w] = __uint_as_float((uint32_t)u[w] << 16);
+                        f[2 * w + 1] = __uint_as_float((uint32_t)u[w] & 0xffff0000u);
+                    }
+                    c[h] = qs != 0.0f ? pack8(f, qs, qy, qfast) : make_uint2(0u, 0u);
+                }
+                v = v4i{(int)c[0].x, (int)c[0].y, (int)c[1].x, (int)c[1].y};
+                const int kc = it * G_BK + 16 * ac;
+                if (qstore && qrow >= 0 && it < nk && kc < K)
+                    *reinterpret_cast<v4i *>(a.a_codes_out + (int64_t)qrow * K + kc) = v;
+            }
+            *reinterpret_cast<v4i *>(&As[buf][arr[j] * G_BK + ((ac ^ (arr[j] & 7)) << 4)]) = v;
+        }
     };
 
     // Prologue.  Three memory round trips lie on its path: the tile's
@@ -629,23 +677,63 @@ void grouped_gemm_kernel(GemmArgs a)
     // first DEPTH weight steps (which need only the descriptor) fly beside
     // the row-index gather, the row scales beside the A loads; the row scales
     // reach LDS after the first A step, and the loop's barriers publish them
-    // before the epilogue reads them.
+    // before the epilogue reads them.  QA (rows not gathered): the rows follow
+    // from the descriptor, so the weights, the first A steps and the rows'
+    // largest magnitudes are all loaded at once (two round trips).
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_b(d, d);
-    const int32_t src = !has_row ? -1 : (a.gather ? graw / a.gather_div : (int32_t)(row0 + tid));
-    if (tid < BM) arow[tid] = src;
-    __syncthreads();
-    const float as_reg = (EPI != 0 && tid < BM && src >= 0) ? a.a_scales[src] : 0.0f;
+    float as_reg = 0.0f;
+    if constexpr (QA) {
+        arr[0] = tid >> 3;   // one 32-row block: one A chunk per thread
+        qrow = arr[0] < rows ? (int32_t)(row0 + arr[0]) : -1;
+        aoff[0] = qrow >= 0 ? (uint32_t)(qrow * K + 16 * ac) : OOB_BASE;
 #pragma unroll
-    for (int j = 0; j < APASS; ++j) {
-        arr[j] = (tid >> 3) + 32 * j;
-        const int32_t sr = arow[arr[j]];
-        aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ac) : OOB_BASE;
+        for (int d = 0; d < DEPTH; ++d) load_a(d, d);
+        // the largest magnitude of row qrow (the row this thread stages): its
+        // 8 threads read 8 elements each per 64-element pass, QB loads in
+        // flight per thread, then a max over the 8 lanes
+        constexpr int QB = 8;
+        float m = 0.0f;
+        for (int c0 = 8 * ac; c0 < K; c0 += 64 * QB) {
+            v4i u[QB];
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+                const int c = c0 + 64 * q;
+                u[q] = buf_load16(rA, (qrow >= 0 && c < K) ? (uint32_t)(qrow * K + c) * 2u : OOB_BASE);
+            }
+#pragma unroll
+            for (int q = 0; q < QB; ++q)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    m = fmaxf(m, fmaxf(fabsf(__uint_as_float((uint32_t)u[q][w] << 16)),
+                                       fabsf(__uint_as_float((uint32_t)u[q][w] & 0xffff0000u))));
+        }
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        qs = m / 127.0f;
+        qy = qs > 0.0f ? 1.0f / qs : 0.0f;
+        qfast = qs >= QUANT_FAST_MIN_SCALE;
+        if (ac == 0) {
+            ascale[arr[0]] = qs;
+            if (qstore && qrow >= 0) a.a_scales_out[qrow] = qs;
+        }
+    } else {
+        const int32_t src = !has_row ? -1 : (a.gather ? graw / a.gather_div : (int32_t)(row0 + tid));
+        if (tid < BM) arow[tid] = src;
+        __syncthreads();
+        as_reg = (EPI != 0 && tid < BM && src >= 0) ? a.a_scales[src] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < APASS; ++j) {
+            arr[j] = (tid >> 3) + 32 * j;
+            const int32_t sr = arow[arr[j]];
+            aoff[j] = sr >= 0 ? (uint32_t)(sr * K + kbeg * G_BK + 16 * ac) : OOB_BASE;
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_a(d, d);
     }
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_a(d, d);
-    store_a(0, 0);
-    if (tid < BM) ascale[tid] = as_reg;
+    store_a(0, 0, 0);
+    if (!QA && tid < BM) ascale[tid] = as_reg;
     load_a(0, DEPTH);
     __syncthreads();
 
@@ -691,7 +779,7 @@ void grouped_gemm_kernel(GemmArgs a)
                     load_b_sub(d, it + DEPTH, s);
                 }
                 const int dn = (d + 1) % DEPTH;
-                store_a(dn, (d + 1) & 1);     // A(it+1), loaded DEPTH steps ago
+                store_a(dn, (d + 1) & 1, it + 1);   // A(it+1), loaded DEPTH steps ago
                 load_a(dn, it + 1 + DEPTH);
                 if constexpr (!RAGGED) {
                     // issue order of the step: per sub-step the A fragment
@@ -1479,13 +1567,11 @@ hipError_t launch_grouped_gemm_w4(const int8_t *A, int64_t A_rows, const float *
                                out_dtype, out, ws, st);
 }
 
-hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
-                            int gather_div, const int8_t *B, int b_packed, const float *b_scales,
-                            const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
-                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp,
-                            const int8_t *B_extra, const float *b_extra_scales)
+static GemmArgs main_args(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                          int gather_div, const int8_t *B, int b_packed, const float *b_scales,
+                          const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, void *out,
+                          const void *ws, int8_t *out_exp, const int8_t *B_extra, const float *b_extra_scales)
 {
-    if (M_total == 0) return hipSuccess;
     GemmArgs ga{};
     ga.ksplit = 1;
     ga.G_routed = B_extra ? G - 1 : G;
@@ -1508,12 +1594,48 @@ hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scal
     ga.tiles = (const int4 *)((const char *)ws + prefix_bytes(G));
     ga.A_bytes = A_rows * K;
     ga.packed_b = b_packed;
+    return ga;
+}
+
+hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
+                            int gather_div, const int8_t *B, int b_packed, const float *b_scales,
+                            const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
+                            int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp,
+                            const int8_t *B_extra, const float *b_extra_scales)
+{
+    if (M_total == 0) return hipSuccess;
+    GemmArgs ga = main_args(A, A_rows, a_scales, gather, gather_div, B, b_packed, b_scales, offsets, G, M_total, N, K,
+                            out, ws, out_exp, B_extra, b_extra_scales);
     const TileCfg c = gemm_cfg(M_total, N, G, epilogue);
     ga.nblocks_n = gemm_nblocks(N, epilogue, c.WN);
     if (c.BM == 32) return launch_main_cfg<32, 2, 2>(ga, epilogue, out_dtype, st);
     if (c.BM == 64) return launch_main_cfg<64, 2, 2>(ga, epilogue, out_dtype, st);
     if (c.WN == 2) return launch_main_cfg<128, 2, 2>(ga, epilogue, out_dtype, st);
     return launch_main_cfg<128, 4, 2>(ga, epilogue, out_dtype, st);
+}
+
+bool gemm_down_fuses_quant(int64_t M_total, int64_t N, int64_t K, int G)
+{
+    return M_total > 0 && gemm_cfg(M_total, N, G, EPI_FIXED16).BM == 32 && 2 * M_total * K <= INT32_MAX - 256;
+}
+
+hipError_t launch_gemm_down_qa(const uint16_t *A_h, int64_t M_total, int8_t *a_codes_out, float *a_scales_out,
+                               const int8_t *B, const float *b_scales, const int32_t *offsets, int G, int64_t N,
+                               int64_t K, void *out, int8_t *out_exp, const void *ws, hipStream_t st,
+                               const int8_t *B_extra, const float *b_extra_scales)
+{
+    if (M_total == 0) return hipSuccess;
+    if (!gemm_down_fuses_quant(M_total, N, K, G)) return hipErrorInvalidValue;
+    GemmArgs ga = main_args(nullptr, M_total, nullptr, nullptr, 1, B, 1, b_scales, offsets, G, M_total, N, K, out,
+                            ws, out_exp, B_extra, b_extra_scales);
+    ga.A_h = A_h;
+    ga.a_codes_out = a_codes_out;
+    ga.a_scales_out = a_scales_out;
+    ga.nblocks_n = gemm_nblocks(N, EPI_FIXED16, 2);
+    const dim3 grid((unsigned)(((M_total + 31) / 32 + G) * ga.nblocks_n));
+    hipLaunchKernelGGL((grouped_gemm_kernel<32, 2, 2, EPI_FIXED16, int16_t, true, true>), grid, dim3(G_THREADS), 0,
+                       st, ga);
+    return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,

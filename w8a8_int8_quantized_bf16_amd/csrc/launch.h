@@ -66,6 +66,18 @@ hipError_t launch_gemm_main(const int8_t *A, int64_t A_rows, const float *a_scal
                             const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
                             int out_dtype, void *out, const void *ws, hipStream_t st, int8_t *out_exp = nullptr,
                             const int8_t *B_extra = nullptr, const float *b_extra_scales = nullptr);
+// The layer's down GEMM (EPI_FIXED16, packed weights) with its A given as the
+// bf16 rows of h in grouped order [M_total][K]: each tile quantises its rows
+// itself (per-row scale amax / 127, the quantiser's arithmetic) and the tiles
+// of column block 0 store the int8 codes [M_total][K] and scales [M_total] to
+// a_codes_out / a_scales_out.  Only where gemm_down_fuses_quant holds (tiles
+// of 32 rows: few rows per expert, the weight stream bounds the tile); the
+// tile table in ws is the one the permutation builds for EPI_FIXED16.
+bool gemm_down_fuses_quant(int64_t M_total, int64_t N, int64_t K, int G);
+hipError_t launch_gemm_down_qa(const uint16_t *A_h, int64_t M_total, int8_t *a_codes_out, float *a_scales_out,
+                               const int8_t *B, const float *b_scales, const int32_t *offsets, int G, int64_t N,
+                               int64_t K, void *out, int8_t *out_exp, const void *ws, hipStream_t st,
+                               const int8_t *B_extra = nullptr, const float *b_extra_scales = nullptr);
 hipError_t launch_grouped_gemm(const int8_t *A, int64_t A_rows, const float *a_scales, const int32_t *gather,
                                int gather_div, const int8_t *B, int b_packed, const float *b_scales,
                                const int32_t *offsets, int G, int64_t M_total, int64_t N, int64_t K, int epilogue,
