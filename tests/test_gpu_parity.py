@@ -210,6 +210,17 @@ def test_route_exact_ties_across_slices(E, groups, T, xdt):
     expert index.  T = 16 runs the few-token vector-ALU router, T = 1024 with
     bf16 tokens the matrix-core one, fp32 tokens the vector-fma one; each with
     and without the packed router copy."""
+    _check_route_ties(E, groups, T, xdt)
+
+
+@pytest.mark.parametrize("groups", [[[5, 69], [63, 64]], [[3, 60, 63, 64, 65, 100, 127, 126, 90, 64 + 3]]])
+def test_route_exact_ties_many_tokens(groups):
+    """The same ties at 8192 bf16 tokens and 128 experts, on the 32-token
+    blocks of the 32 x 32 x 1 matrix-core router and its lane-parallel top-k."""
+    _check_route_ties(128, groups, 8192, "bf16")
+
+
+def _check_route_ties(E, groups, T, xdt):
     H, k = 2048, 8
     rng = np.random.default_rng(E + T + len(groups))
     x = (rng.standard_t(4, (T, H)) + 0.5).astype(np.float32)
