@@ -623,8 +623,11 @@ constexpr int r32_depth(int TOK, int S) { return (S == 1 && TOK == 32) ? 4 : 8; 
 
 // TOK: tokens per block, 32 (the 32 x 32 x 1 instruction) or 16 (its
 // 16 x 16 x 1 four-block form, for fewer tokens: twice the blocks).  QX: the
-// block also quantises its tokens (xq and sx are then given)
-template <int TOK, int S, int CPW, bool PACKED, bool QX>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
+// block also quantises its tokens (xq and sx are then given).  SPLIT (two
+// slices): each chunk run takes two waves, one per 64-expert slice (wave w:
+// run w / 2, slice w % 2), for blocks of few runs whose waves would otherwise
+// leave a SIMD with one chain pair; both waves load the run's x operands.
+template <int TOK, int S, int CPW, bool PACKED, bool QX, bool SPLIT = false>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
 __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
                                                             int E, int k, int renorm, int NCW,
@@ -634,6 +637,8 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
 {
     static_assert(S == 1 || S == 2, "slices");
     static_assert(TOK == 32 || TOK == 16, "tokens per block");
+    static_assert(!SPLIT || S == 2, "a split run is two slices");
+    constexpr int SW = SPLIT ? 1 : S;   // slices per wave
     constexpr int R32_D = r32_depth(TOK, S);
     static_assert(R32_STEPS % R32_D == 0, "chunks end at pass ends");
     // a lane's accumulator: TOK x 64 results over 64 lanes
@@ -641,9 +646,12 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
     __shared__ float rt[S][TOK][64 + 1];    // running totals, then the scores
     __shared__ __attribute__((aligned(16))) uint32_t tk_scr[8][512];
     __shared__ int q_next;   // next token row of the block to quantise
-    __shared__ int r_done;   // chunk runs added to the running totals
+    __shared__ int r_done[SPLIT ? 2 : 1];   // chunk runs added to the running totals (per slice if split)
     const int tid = threadIdx.x, lane = tid & 63;
-    const int run = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the run bounds stay scalar
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the run bounds stay scalar
+    const int nwv = NCW * (SPLIT ? 2 : 1);                      // waves of the block
+    const int run = SPLIT ? wv >> 1 : wv;
+    const int js = SPLIT ? wv & 1 : 0;                          // the wave's first slice
     const int64_t tb = (int64_t)blockIdx.x * TOK;
     const int nst = (int)(H / 8);
     const int nch = (nst + R32_STEPS - 1) / R32_STEPS;
@@ -659,32 +667,33 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(wg), 0, 0x7ffffff0, 0x00020000);
     const int tok = lane & (TOK - 1);
     const uint32_t xrow = tb + tok < T_ ? (uint32_t)((tb + tok) * H * 2) : OOB;
-    uint32_t wrow[S];
+    uint32_t wrow[SW];
 #pragma unroll
-    for (int j = 0; j < S; ++j) {
-        const int e = 64 * j + lane;
+    for (int j = 0; j < SW; ++j) {
+        const int e = 64 * (js + j) + lane;
         wrow[j] = e < E ? (PACKED ? (uint32_t)e * 16u : (uint32_t)((int64_t)e * H * 2)) : OOB;
     }
     const uint32_t wstep = PACKED ? (uint32_t)E * 16u : 16u;   // bytes between steps of one expert
     if (tid == 0) {
         q_next = 0;
-        r_done = 0;
+        r_done[0] = 0;
+        if constexpr (SPLIT) r_done[1] = 0;
     }
     __syncthreads();
-    uint4 xr[R32_D], wr[R32_D][S];
+    uint4 xr[R32_D], wr[R32_D][SW];
     auto load = [&](int slot, int st) {
         const bool live = st < s_end;
         xr[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rx, live ? xrow + (uint32_t)st * 16u : OOB, 0, 0));
 #pragma unroll
-        for (int j = 0; j < S; ++j)
+        for (int j = 0; j < SW; ++j)
             wr[slot][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                         rw, live ? wrow[j] + (uint32_t)st * wstep : OOB, 0, 0));
     };
 #pragma unroll
     for (int d = 0; d < R32_D; ++d) load(d, s_beg + d);
 
-    vacc acc[CPW][S];
+    vacc acc[CPW][SW];
     // c += a * b for one hidden index: TOK tokens x 64 experts
     auto mfma = [](float av, float bv, const vacc &c) -> vacc {
         if constexpr (TOK == 32) return __builtin_amdgcn_mfma_f32_32x32x1f32(av, bv, c, 0, 0, 0);
@@ -692,19 +701,19 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
     };
     // one step: the 8 indices of slot d into the chains, then the slot's
     // refill with step st + R32_D (st % R32_D == d: chunks start at multiples)
-    auto step = [&](vacc (&a)[S], int d, int st) {
+    auto step = [&](vacc (&a)[SW], int d, int st) {
         const uint32_t u[4] = {xr[d].x, xr[d].y, xr[d].z, xr[d].w};
         // hidden 8 st + 2 i is the low half of word i, 8 st + 2 i + 1 the high half
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float x0 = __uint_as_float(u[i] << 16), x1 = __uint_as_float(u[i] & 0xffff0000u);
 #pragma unroll
-            for (int j = 0; j < S; ++j) {
+            for (int j = 0; j < SW; ++j) {
                 const uint32_t w = (&wr[d][j].x)[i];
                 a[j] = mfma(x0, __uint_as_float(w << 16), a[j]);
             }
 #pragma unroll
-            for (int j = 0; j < S; ++j) {
+            for (int j = 0; j < SW; ++j) {
                 const uint32_t w = (&wr[d][j].x)[i];
                 a[j] = mfma(x1, __uint_as_float(w & 0xffff0000u), a[j]);
             }
@@ -716,9 +725,9 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
     };
 #pragma unroll
     for (int ci = 0; ci < CPW; ++ci) {
-        vacc a[S];
+        vacc a[SW];
 #pragma unroll
-        for (int j = 0; j < S; ++j) a[j] = vacc{};
+        for (int j = 0; j < SW; ++j) a[j] = vacc{};
         const int cs = s_beg + ci * R32_STEPS;
         const int ce = min(s_end, cs + R32_STEPS);
         const int cf = cs + max(0, ce - cs) / R32_D * R32_D;   // end of the whole passes
@@ -730,14 +739,15 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
         for (int d = 0; d < R32_D; ++d)   // a chunk's last, partial pass (only where H ends inside it)
             if (cf + d < ce) step(a, d, cf + d);
 #pragma unroll
-        for (int j = 0; j < S; ++j) acc[ci][j] = a[j];
+        for (int j = 0; j < SW; ++j) acc[ci][j] = a[j];
     }
     // Chunk sums into the running totals, runs in ascending order: run r waits
     // until runs 0 .. r - 1 are in (r_done == r), adds its chunks one at a
-    // time, then lets run r + 1 go.  Every earlier run ends without waiting on
-    // a later one, so each wait ends.
+    // time, then lets run r + 1 go (split: the runs of each slice in order, a
+    // counter per slice).  Every earlier run ends without waiting on a later
+    // one, so each wait ends.
     if (run > 0)
-        while (__hip_atomic_load(&r_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < run)
+        while (__hip_atomic_load(&r_done[js], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < run)
             __builtin_amdgcn_s_sleep(1);
     if (c_beg < c_end) {
         // lane l's element reg of slice j (reg = 4 q + i).  32 tokens: row
@@ -752,30 +762,30 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
         };
         // the run's chunk sums added in order to what the earlier runs left
         // (all loads first, then the sums and stores)
-        auto add_run = [&](const float(&before)[S][TOK], bool first) {
+        auto add_run = [&](const float(&before)[SW][TOK], bool first) {
 #pragma unroll
-            for (int j = 0; j < S; ++j)
+            for (int j = 0; j < SW; ++j)
 #pragma unroll
                 for (int reg = 0; reg < TOK; ++reg) {
                     float t = first ? acc[0][j][reg] : before[j][reg] + acc[0][j][reg];
 #pragma unroll
                     for (int ci = 1; ci < CPW; ++ci)
                         if (c_beg + ci < c_end) t = t + acc[ci][j][reg];
-                    rt_at(j, reg) = t;
+                    rt_at(js + j, reg) = t;
                 }
         };
-        float tot[S][TOK];
+        float tot[SW][TOK];
         if (run == 0) {
             add_run(tot, true);
         } else {
 #pragma unroll
-            for (int j = 0; j < S; ++j)
+            for (int j = 0; j < SW; ++j)
 #pragma unroll
-                for (int reg = 0; reg < TOK; ++reg) tot[j][reg] = rt_at(j, reg);
+                for (int reg = 0; reg < TOK; ++reg) tot[j][reg] = rt_at(js + j, reg);
             add_run(tot, false);
         }
     }
-    __hip_atomic_store(&r_done, run + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&r_done[js], run + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
     // Per-token int8 codes, when asked for, with the quantisation kernels'
     // arithmetic: a wave that has added its chunk sums takes the block's token
@@ -867,18 +877,18 @@ __global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(co
         // 8 / S tokens per wave at once, every wave taking groups in turn
         constexpr int TPW = 8 / S;
         auto score = [&](int j, int tt, int c) { return rt[j][tt][c]; };
-        for (int tt0 = run * TPW; tt0 < TOK; tt0 += NCW * TPW)
+        for (int tt0 = wv * TPW; tt0 < TOK; tt0 += nwv * TPW)
             topk8_renorm_tokens<S>(score, tt0, tb, T_, E, k, ids, wout, logits_out);
         return;
     }
-    const int ntk = min(NCW, 8);   // waves that run the top-k
-    for (int tt = run; tt < TOK && run < 8; tt += ntk) {
+    const int ntk = min(nwv, 8);   // waves that run the top-k
+    for (int tt = wv; tt < TOK && wv < 8; tt += ntk) {
         const int64_t t = tb + tt;
         if (t >= T_) break;
         float l4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) l4[j] = (j < S) ? rt[j][tt][lane] : 0.0f;
-        select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[run]);
+        select_topk<S>(l4, t, E, k, renorm, ids, wout, logits_out, tk_scr[wv]);
     }
 }
 
@@ -1179,7 +1189,9 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
             const int cpw = nch <= r32_max_waves(S) ? 1 : 2;
             const int ncw = (nch + cpw - 1) / cpw;
             const bool t32 = ngrp32 >= 256;
-            const dim3 g32((unsigned)(t32 ? ngrp32 : (T + 15) / 16)), b32(64 * ncw);
+            // two slices and at most 4 chunk runs: a wave per (run, slice)
+            const bool split = S == 2 && cpw == 1 && ncw <= 4;
+            const dim3 g32((unsigned)(t32 ? ngrp32 : (T + 15) / 16)), b32(64 * ncw * (split ? 2 : 1));
             const uint16_t *wv = wg_packed ? wg_packed : wg;
             auto go32 = [&](auto kern) {
                 hipLaunchKernelGGL(kern, g32, b32, 0, st, xb, wv, T, H, E, k, renormalize, ncw, ids, w, logits, xq,
@@ -1188,7 +1200,10 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
             auto pick = [&](auto tok, auto qx) {
                 constexpr int TK = decltype(tok)::value;
                 constexpr bool QX = decltype(qx)::value;
-                if (S == 1 && cpw == 1)
+                if (split)
+                    wg_packed ? go32(route_mfma_k1_kernel<TK, 2, 1, true, QX, true>)
+                              : go32(route_mfma_k1_kernel<TK, 2, 1, false, QX, true>);
+                else if (S == 1 && cpw == 1)
                     wg_packed ? go32(route_mfma_k1_kernel<TK, 1, 1, true, QX>)
                               : go32(route_mfma_k1_kernel<TK, 1, 1, false, QX>);
                 else if (S == 1)
