@@ -330,6 +330,27 @@ def test_route_shapes(T, H, E, k, xdt):
         assert np.abs(to_host(w) - ow).max() <= 2e-6
 
 
+@pytest.mark.parametrize("T,H,E,k,renorm", [(600, 2048, 128, 8, False),    # a wave per chunk run and slice
+                                            (300, 1040, 100, 10, True),    # the same with k > 8
+                                            (300, 4624, 128, 3, False),    # two chunks per wave, both slices
+                                            (8192, 2048, 128, 8, False)])  # 32-token blocks, a wave per run and slice
+def test_route_matrix_core_ballot_topk(T, H, E, k, renorm):
+    """The K = 1 matrix-core router with the ballot top-k (weights not
+    renormalised, or k > 8) on blocks whose waves split the expert slices and
+    on blocks whose waves hold both: logits, ids and weights against the
+    oracle, with the [E][H] and the packed router weight."""
+    rng = np.random.default_rng(T + H + E + k)
+    x = synth.f32_to_bf16_bits(rng.standard_t(4, (T, H)).astype(np.float32))
+    wg = synth.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    oids, ow, ologits = oracle.route_topk(x, wg, k, renorm)
+    wgd = dev_bf16(wg)
+    for packed in (None, w8.router_pack(wgd)):
+        ids, w, logits = w8.route_topk(to_dev(x), wgd, k, renorm, return_logits=True, w_gate_packed=packed)
+        assert np.array_equal(to_host(logits), ologits)
+        assert np.array_equal(to_host(ids), oids)
+        assert np.abs(to_host(w) - ow).max() <= 2e-6
+
+
 @pytest.mark.parametrize("T,H,E,k", [(8192, 2064, 128, 8),    # two slices, 5 chunks (a short last one)
                                      (8200, 1040, 60, 4),     # one slice, a last block of 8 tokens
                                      (8192, 4624, 128, 8),    # two slices, two chunks per wave
