@@ -625,10 +625,10 @@ constexpr int r32_depth(int TOK, int S) { return (S == 1 && TOK == 32) ? 4 : 8; 
 // 16 x 16 x 1 four-block form, for fewer tokens: twice the blocks).  QX: the
 // block also quantises its tokens (xq and sx are then given).  SPLIT (two
 // slices): each chunk run takes two waves, one per 64-expert slice (wave w:
-// run w / 2, slice w % 2), for blocks of few runs whose waves would otherwise
-// leave a SIMD with one chain pair; both waves load the run's x operands.
+// run w / 2, slice w % 2), so a SIMD interleaves twice the waves, each with
+// one chain; both waves load the run's x operands.
 template <int TOK, int S, int CPW, bool PACKED, bool QX, bool SPLIT = false>   // S: 64-expert slices (E <= 64 S), CPW: chunks per wave
-__global__ __launch_bounds__(64 * r32_max_waves(S)) void route_mfma_k1_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(64 * (SPLIT ? 16 : r32_max_waves(S))) void route_mfma_k1_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ wg, int64_t T_, int64_t H,
                                                             int E, int k, int renorm, int NCW,
                                                             int32_t *__restrict__ ids, float *__restrict__ wout,
@@ -1179,18 +1179,18 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
             }
             return hipGetLastError();
         }
-        // up to 128 experts: the K = 1 matrix-core kernel, one wave per slice
-        // and run of one or two chunks (at most 16 waves), on 32-token blocks
-        // where they fill the chip, else on 16-token blocks where H spans two
-        // chunks or more
+        // up to 128 experts: the K = 1 matrix-core kernel, a wave per run of
+        // one or two chunks (with one chunk per wave and two slices, a wave per
+        // run and slice; at most 16 waves), on 32-token blocks where they fill
+        // the chip, else on 16-token blocks where H spans two chunks or more
         const int nch = (int)((H / 8 + R32_STEPS - 1) / R32_STEPS);
         const int64_t ngrp32 = (T + 31) / 32;
         if (S <= 2 && nch <= 2 * r32_max_waves(S) && (ngrp32 >= 256 || nch >= 2)) {
             const int cpw = nch <= r32_max_waves(S) ? 1 : 2;
             const int ncw = (nch + cpw - 1) / cpw;
             const bool t32 = ngrp32 >= 256;
-            // two slices and at most 4 chunk runs: a wave per (run, slice)
-            const bool split = S == 2 && cpw == 1 && ncw <= 4;
+            // two slices, one chunk per wave: a wave per (run, slice), up to 16
+            const bool split = S == 2 && cpw == 1;
             const dim3 g32((unsigned)(t32 ? ngrp32 : (T + 15) / 16)), b32(64 * ncw * (split ? 2 : 1));
             const uint16_t *wv = wg_packed ? wg_packed : wg;
             auto go32 = [&](auto kern) {
@@ -1209,10 +1209,7 @@ hipError_t launch_route_topk(const void *x, int dtype, const uint16_t *wg, const
                 else if (S == 1)
                     wg_packed ? go32(route_mfma_k1_kernel<TK, 1, 2, true, QX>)
                               : go32(route_mfma_k1_kernel<TK, 1, 2, false, QX>);
-                else if (cpw == 1)
-                    wg_packed ? go32(route_mfma_k1_kernel<TK, 2, 1, true, QX>)
-                              : go32(route_mfma_k1_kernel<TK, 2, 1, false, QX>);
-                else
+                else   // two slices, two chunks per wave
                     wg_packed ? go32(route_mfma_k1_kernel<TK, 2, 2, true, QX>)
                               : go32(route_mfma_k1_kernel<TK, 2, 2, false, QX>);
             };
