@@ -691,8 +691,9 @@ void grouped_gemm_kernel(GemmArgs a)
         for (int d = 0; d < DEPTH; ++d) load_a(d, d);
         // the largest magnitude of row qrow (the row this thread stages): its
         // 8 threads read 8 elements each per 64-element pass, QB loads in
-        // flight per thread, then a max over the 8 lanes
-        constexpr int QB = 8;
+        // flight per thread (rows of up to 768 in one round trip), then a max
+        // over the 8 lanes
+        constexpr int QB = 12;
         float m = 0.0f;
         for (int c0 = 8 * ac; c0 < K; c0 += 64 * QB) {
             v4i u[QB];
