@@ -593,17 +593,19 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(const uint16_t *__restr
 // product of two bf16 values is exact in fp32, so each step is exactly one
 // fused multiply-add of each of the 2048 chains it holds.  A wave takes 32
 // tokens (lane l feeds token l % 32 to both blocks), all 64 S experts (S
-// accumulators; lane l feeds expert 64 j + l of slice j: block l / 32), and
-// one run of CPW of the score's 512-index chunks.  Each x operand is used 64 S
-// times and each W_g operand 32 times, so the lanes load them straight from
-// memory (x rows and W_g, both L2-resident after the first touch) into
-// registers, D steps of 8 indices ahead, and widen the bf16 pairs in
-// registers: no LDS staging and no barrier until the chains end.
+// accumulators; lane l feeds expert 64 j + l of slice j: block l / 32; with
+// SPLIT one slice per wave), and one run of CPW of the score's 512-index
+// chunks.  Each x operand is used 64 S times and each W_g operand 32 times, so
+// the lanes load them straight from memory (x rows and W_g, both L2-resident
+// after the first touch) into registers, D steps of 8 indices ahead, and widen
+// the bf16 pairs in registers: no LDS staging and no barrier until the chains
+// end.
 //
-// A block is 32 tokens and NCW waves, one per chunk run.  The chunk sums meet
-// in LDS in ascending chunk order (the run of wave 0 first, each later run
-// adding its chunks one at a time to the running total as soon as the runs
-// before it are in), and the top-k runs on the totals.  The waves of a block
+// A block is 32 tokens and NCW waves, one per chunk run (SPLIT: 2 NCW waves,
+// one per run and slice).  The chunk sums meet in LDS in ascending chunk order
+// (the run of wave 0 first, each later run adding its chunks one at a time to
+// the running total as soon as the runs before it are in), and the top-k runs
+// on the totals.  The waves of a block
 // share their compute unit's matrix cores unevenly (measured: the first wave
 // on each SIMD ends its chain about a fifth of the chain time before the
 // second), so with xq the waves that are done quantise the block's tokens
