@@ -304,36 +304,41 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, v16i (&acc)[BM 
             }
             wave_lds_sync();   // the staging region is this wave's own
             if constexpr (EPI == EPI_FIXED16) {
-                // 16 lanes hold one row's 64 columns (4 each): the row's largest
+                // 8 lanes hold one row's 64 columns (8 each): the row's largest
                 // magnitude over them fixes a power-of-two scale 2^e that maps it
-                // into [2^13, 2^14); codes = rint(v * 2^-e) fit int16 with room.
+                // into [2^13, 2^14); codes = rint(v * 2^-e) fit int16 with room,
+                // and each lane stores its 8 codes as one 16-byte piece.
                 static_assert(CPR == 16, "one 64-column segment per pass");
+                constexpr int CPR8 = CPR / 2;   // 8-value pieces per staged row
 #pragma unroll
-                for (int idx = lane; idx < 32 * CPR; idx += 64) {
-                    const int rl = idx / CPR, ch = idx % CPR;
+                for (int idx = lane; idx < 32 * CPR8; idx += 64) {
+                    const int rl = idx / CPR8, ch = idx % CPR8;
                     const int r = mi * 32 + rl;
-                    const int ocol = ocol0 + 32 * f0 + ch * 4;
-                    const float4 v = *reinterpret_cast<const float4 *>(stage + rl * ROWB + ch * 16);
-                    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-                    // max over the 16-lane row: lane swaps 1 and 2 within quads,
-                    // then mirrors within 8 and within 16 lanes
+                    const int ocol = ocol0 + 32 * f0 + ch * 8;
+                    const float4 v0 = *reinterpret_cast<const float4 *>(stage + rl * ROWB + ch * 32);
+                    const float4 v1 = *reinterpret_cast<const float4 *>(stage + rl * ROWB + ch * 32 + 16);
+                    const float vs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                    float m = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(vs[u]));
+                    // max over the 8-lane row: lane swaps 1 and 2 within quads,
+                    // then the mirror within 8 lanes
                     m = fmaxf(m, dpp_move<0xB1>(m));
                     m = fmaxf(m, dpp_move<0x4E>(m));
                     m = fmaxf(m, dpp_move<0x141>(m));
-                    m = fmaxf(m, dpp_move<0x140>(m));
                     int e = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 255u) - 127 - 13 : 0;
                     e = e < -126 ? -126 : e;
                     const float sc = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
                     // rint(v * 2^-e) as an integer: adding 1.5 * 2^23 rounds the
                     // (exact) product half-to-even into the mantissa
-                    const float vs[4] = {v.x, v.y, v.z, v.w};
-                    uint32_t q[4];
+                    uint32_t q[8];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
+                    for (int u = 0; u < 8; ++u)
                         q[u] = (uint32_t)(__float_as_int(fmaf(vs[u], sc, 12582912.0f)) - 0x4B400000) & 0xffffu;
                     if (r < rows && ocol < ldo) {
-                        *reinterpret_cast<uint2 *>(reinterpret_cast<int16_t *>(a.out) + (row0 + r) * ldo + ocol) =
-                            make_uint2(q[0] | (q[1] << 16), q[2] | (q[3] << 16));
+                        *reinterpret_cast<uint4 *>(reinterpret_cast<int16_t *>(a.out) + (row0 + r) * ldo + ocol) =
+                            make_uint4(q[0] | (q[1] << 16), q[2] | (q[3] << 16), q[4] | (q[5] << 16),
+                                       q[6] | (q[7] << 16));
                         if (ch == 0) a.out_exp[(row0 + r) * ((ldo + 63) / 64) + (ocol0 + 32 * f0) / 64] = (int8_t)e;
                     }
                 }
