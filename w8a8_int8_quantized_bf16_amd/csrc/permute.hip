@@ -4,13 +4,14 @@
 //
 // A deterministic, stable counting sort of the P = T*k pair ids by expert:
 //   1. count:   one block per chunk of 512 pairs -> per-chunk histograms
-//   2. scan:    one block; per expert an exclusive scan over the chunks, then
-//               an exclusive scan over experts -> offsets[E+1]
-//   (up to 4096 pairs one block does all three steps in a single launch)
-//   3. scatter: one block per chunk; pairs are ranked in pair order, 256 at a
-//               time: equal experts inside a wavefront are matched with eight
-//               ballots (one per bit of the id), waves are ordered through LDS.
-//               The same blocks first write the grouped GEMMs' tile tables.
+//   2. scan + scatter: one block per chunk.  Each block walks the histograms
+//               of all chunks (per expert: the pairs before its own chunk and
+//               the total), forms offsets[E+1] with one scan over experts, and
+//               places its chunk's pairs in pair order, 256 at a time: equal
+//               experts inside a wavefront are matched with eight ballots (one
+//               per bit of the id), waves are ordered through LDS.  The same
+//               blocks first write the grouped GEMMs' tile tables.
+//   (up to 4096 pairs one block does all of it in a single launch)
 // The result depends only on the ids: no atomics decide any position.
 #include "device_common.h"
 #include "launch.h"
@@ -157,11 +158,18 @@ __device__ inline void build_table(const ScanTables &tt, int j, const int32_t *o
     __syncthreads();
 }
 
-__global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
-                                                                     int E, const int32_t *__restrict__ chunk_base,
-                                                                     const int32_t *__restrict__ offsets,
-                                                                     int32_t *__restrict__ sorted_pair,
-                                                                     int32_t *__restrict__ pair_pos, ScanTables tt)
+// Steps 2 and 3 in one launch (P > PM_SMALL_P): block b's thread e walks
+// expert e's counts over all chunks, 32 loads in flight (the pairs of e before
+// chunk b, and its total); one block scan over the totals gives the offsets
+// (block 0 stores them), and the block scatters chunk b from offsets[e] plus
+// the pairs of e before it.
+__global__ __launch_bounds__(PM_THREADS) void permute_scan_scatter_kernel(const int32_t *__restrict__ ids, int64_t P,
+                                                                          int E,
+                                                                          const int32_t *__restrict__ chunk_counts,
+                                                                          int64_t nchunks,
+                                                                          int32_t *__restrict__ offsets,
+                                                                          int32_t *__restrict__ sorted_pair,
+                                                                          int32_t *__restrict__ pair_pos, ScanTables tt)
 {
     __shared__ int32_t base[PM_MAX_E];     // next free row of each expert inside this chunk
     __shared__ int32_t wcnt[4][PM_MAX_E];  // per-wave counts of the current round
@@ -169,20 +177,50 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scatter_kernel(const int32
     __shared__ int32_t pre[PM_MAX_E + 2];
     __shared__ int32_t dn[2];
     const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
 
+    // ---- this block's offsets and chunk base
+    int32_t before = 0, total = 0;
+    if (tid < E) {
+        int64_t c = 0;
+        for (; c + 32 <= nchunks; c += 32) {
+            int32_t v[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) v[u] = chunk_counts[(c + u) * E + tid];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                total += v[u];
+                before += c + u < b ? v[u] : 0;
+            }
+        }
+        for (; c < nchunks; ++c) {
+            const int32_t v = chunk_counts[c * E + tid];
+            total += v;
+            before += c < b ? v : 0;
+        }
+    }
+    int all;
+    const int32_t ex = block_excl_scan256(tid < E ? total : 0, &wcnt[0][0], &all);
+    if (tid < E) {
+        off_l[tid] = ex;
+        base[tid] = ex + before;
+        if (b == 0) offsets[tid] = ex;
+    }
+    if (tid == 0) {
+        off_l[E] = (int32_t)P;
+        off_l[E + 1] = (int32_t)P + tt.extra;
+        if (b == 0) offsets[E] = (int32_t)P;
+    }
     // ---- tile tables (and the extra group's rows)
-    for (int g = tid; g <= E; g += PM_THREADS) off_l[g] = offsets[g];
-    if (tid == 0) off_l[E + 1] = (int32_t)P + tt.extra;
-    for (int64_t t = (int64_t)blockIdx.x * PM_THREADS + tid; t < tt.extra; t += (int64_t)gridDim.x * PM_THREADS)
+    for (int64_t t = b * PM_THREADS + tid; t < tt.extra; t += (int64_t)gridDim.x * PM_THREADS)
         sorted_pair[P + t] = (int32_t)(t * tt.k);
     __syncthreads();
     for (int j = 0; j < tt.n; ++j)
-        build_table(tt, j, off_l, E, pre, &wcnt[0][0], dn, blockIdx.x == 0, blockIdx.x * PM_THREADS + tid,
+        build_table(tt, j, off_l, E, pre, &wcnt[0][0], dn, b == 0, (int)b * PM_THREADS + tid,
                     gridDim.x * PM_THREADS);
 
     // ---- scatter
-    if (tid < E) base[tid] = off_l[tid] + chunk_base[(int64_t)blockIdx.x * E + tid];
-    scatter_rounds(ids, P, (int64_t)blockIdx.x * PM_CHUNK, PM_PER_THREAD, E, base, wcnt, sorted_pair, pair_pos);
+    scatter_rounds(ids, P, b * PM_CHUNK, PM_PER_THREAD, E, base, wcnt, sorted_pair, pair_pos);
 }
 
 // P <= PM_SMALL_P: the whole permutation in one launch of 1 + tt.n blocks.
@@ -257,14 +295,15 @@ hipError_t launch_permute(const int32_t *ids, int64_t T, int k, int E, int32_t *
     }
     const int64_t nch = pm_chunks(P);
     int32_t *cc = (int32_t *)ws;
-    // with P == 0 only the scan runs: it writes all-zero offsets (and no tile
-    // table is needed: a GEMM over zero rows launches nothing)
-    if (nch > 0)
-        hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc);
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets);
-    if (nch > 0)
-        hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc,
-                           offsets, sorted_pair, pair_pos, tt);
+    if (nch == 0) {
+        // P == 0: only the scan runs, it writes all-zero offsets (and no tile
+        // table is needed: a GEMM over zero rows launches nothing)
+        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, st, cc, nch, E, P, offsets);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(permute_count_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc);
+    hipLaunchKernelGGL(permute_scan_scatter_kernel, dim3((unsigned)nch), dim3(PM_THREADS), 0, st, ids, P, E, cc,
+                       nch, offsets, sorted_pair, pair_pos, tt);
     return hipGetLastError();
 }
 
